@@ -1,0 +1,196 @@
+"""Plain CPU oracle for element-scan and matrix-scan.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call this package. It imports nothing from ``scan_primitives_amd``
+and the HIP library never reaches it: the two implementations share no code.
+
+What it computes is the plain definition of each scan, written out as a
+serial loop over the scanned axis, one trip at a time, with numpy doing the
+arithmetic of one trip for every lane at once. There is no chunking, no
+reassociation and no fusion. Arithmetic is float64 by default: inputs given
+as float32 or bfloat16 widen to float64 exactly, so the result is the exact
+recurrence up to float64 rounding. ``dtype=np.float32`` runs the same loop
+in float32 with one rounding per numpy operation (no fused multiply-add);
+for the max-plus body, whose subtract and maximum are correctly rounded,
+that mode reproduces a serial float32 evaluation bit for bit.
+
+Sources, all from the SexpGPU documentation pages:
+
+* "Nonlinear element scans", introduction: the tanh-affine body
+  ``h[t] = tanh(x[t] + decay[t] * h[t-1])`` from ``h[-1] = initial``, every
+  output position holding the state after its own trip; the vector state
+  (``:state-axis -1``) with the norm-capped body
+  ``h[t] = y / max(1, |y|)``, ``y = decay[t] * h[t-1] + x[t]``; ``:reverse``
+  running ``h[t] = f(h[t+1], x[t])`` from ``h[time] = initial``; the
+  right-to-left max-plus sweep ``max(h - c, x)``.
+* "Nonlinear element scans", "Arguments and body": operand shapes, the
+  axis rules, and the width-one sequence acting as a gate for the whole
+  vector state.
+* "Tensor operations", Operations table (matrix-scan row) and the
+  "matrix-scan" section: ``h[t] = a[t] @ h[t-1] + b[t]`` from ``h = 0``,
+  ``:reverse`` running from the end, NumPy broadcasting of the leading dims,
+  ``:axis`` counted among the leading dims, result in ``b``'s shape.
+
+Readings where the pages leave a point open (each is listed with its reason
+in the design notes of the repository):
+
+* matrix-scan ``:reverse`` is ``h[t] = a[t] @ h[t+1] + b[t]`` from
+  ``h[T] = 0``: the step at position t uses position t's operands, as the
+  reverse element scan does, so the result equals flipping, scanning forward
+  and flipping back.
+* the result shape of matrix-scan is the broadcast leading shape followed
+  by ``[n, m]``; this is ``b``'s shape whenever ``b`` already has the full
+  leading shape.
+* a matrix-scan over an axis of length zero returns an empty result; an
+  element scan over one is refused, since the pages require length >= 1.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+closed forms, inverse problems, invariants the pages state, and worked
+examples under ``tests/golden/``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["element_scan", "matrix_scan", "BODIES"]
+
+
+# --- element-scan bodies ----------------------------------------------------
+# Each body maps (incoming state, sequence values at this trip) to the new
+# state, in the operation order the page writes it.
+
+
+def _tanh_affine(h, x, a):
+    # "Nonlinear element scans", introduction: (tanh (+ x (* a h)))
+    return np.tanh(x + a * h)
+
+
+def _norm_cap(h, x, a):
+    # "Nonlinear element scans", introduction, vector state:
+    # y = (+ (* a h) x); y / (maximum 1.0 (sqrt (sum (* y y) :axes [-1])))
+    y = a * h + x
+    norm = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
+    return y / np.maximum(1.0, norm)
+
+
+def _max_plus(h, x, c):
+    # "Nonlinear element scans", introduction, :reverse: (maximum (- h c) x)
+    return np.maximum(h - c, x)
+
+
+BODIES = {
+    "tanh_affine": _tanh_affine,
+    "norm_cap": _norm_cap,
+    "max_plus": _max_plus,
+}
+
+# Bodies that reduce over the state vector need a vector state: the page's
+# "Arguments and body" section says a scalar state's body cannot reduce.
+_REDUCING = {"norm_cap"}
+
+
+def element_scan(body, initial, sequences, axis=0, state_axis=None,
+                 reverse=False, dtype=np.float64):
+    """Run an element scan the plain way: one trip at a time, all lanes at once.
+
+    ``body`` is one of ``BODIES``; ``sequences`` is the list of the body's
+    sequence arguments in page order (``[x, decay]`` or ``[x, cost]``).
+    ``state_axis`` is ``None`` (scalar state) or ``-1`` (the state is a
+    vector along the last axis). Returns an array of the sequences' shape
+    (with the last axis equal to the state's width under ``state_axis``).
+
+    Follows "Nonlinear element scans", introduction and "Arguments and body".
+    """
+    step = BODIES[body]
+    seqs = [np.asarray(s, dtype=dtype) for s in sequences]
+    h = np.array(initial, dtype=dtype, copy=True)
+    if not seqs:
+        raise ValueError("element_scan: sequences must be nonempty")
+    rank = seqs[0].ndim
+    if rank < 1:
+        raise ValueError("element_scan: sequences need at least one axis")
+    ax = axis + rank if axis < 0 else axis
+    if not 0 <= ax < rank:
+        raise ValueError(f"element_scan: axis {axis} out of range for rank {rank}")
+
+    if state_axis is None:
+        if body in _REDUCING:
+            raise ValueError(f"element_scan: body {body!r} reduces, so it needs a vector state")
+        shape = seqs[0].shape
+        for s in seqs:
+            if s.shape != shape:
+                raise ValueError("element_scan: sequences must share one shape")
+    else:
+        if state_axis not in (-1, rank - 1):
+            raise ValueError("element_scan: the state axis is the last axis")
+        if ax == rank - 1:
+            raise ValueError("element_scan: the scan axis cannot be the state axis")
+        n = h.shape[-1]
+        widened = []
+        for s in seqs:
+            if s.shape[:-1] != seqs[0].shape[:-1] or s.shape[-1] not in (1, n):
+                raise ValueError("element_scan: a sequence's last axis is 1 or the state width")
+            # A width-one sequence broadcasts over the whole state vector.
+            widened.append(np.broadcast_to(s, s.shape[:-1] + (n,)))
+        seqs = widened
+        shape = seqs[0].shape
+
+    expected_init = shape[:ax] + shape[ax + 1:]
+    if h.shape != expected_init:
+        raise ValueError(f"element_scan: initial has shape {h.shape}, expected {expected_init}")
+    T = shape[ax]
+    if T < 1:
+        raise ValueError("element_scan: the scan axis has length at least one")
+
+    # Time-major views: seq_t[t] is every lane's value at trip t.
+    seq_t = [np.moveaxis(s, ax, 0) for s in seqs]
+    out = np.empty((T,) + expected_init, dtype=dtype)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        h = step(h, *(s[t] for s in seq_t))
+        out[t] = h  # each position holds the state after its own trip
+    return np.moveaxis(out, 0, ax)
+
+
+def matrix_scan(a, b, axis=0, reverse=False, dtype=np.float64):
+    """Run a matrix scan the plain way: one matrix product per step.
+
+    ``a`` is ``[..., n, n]`` and ``b`` ``[..., n, m]``; the leading dims
+    broadcast (NumPy rules) and ``axis`` counts among them. Forward:
+    ``h[t] = a[t] @ h[t-1] + b[t]`` from ``h[-1] = 0``. Reverse:
+    ``h[t] = a[t] @ h[t+1] + b[t]`` from ``h[T] = 0``.
+
+    Follows "Tensor operations", Operations table (matrix-scan row) and the
+    "matrix-scan" section.
+    """
+    a = np.asarray(a, dtype=dtype)
+    b = np.asarray(b, dtype=dtype)
+    if a.ndim < 2 or b.ndim < 2:
+        raise ValueError("matrix_scan: a and b need two matrix dims")
+    n = a.shape[-1]
+    if a.shape[-2] != n or b.shape[-2] != n:
+        raise ValueError("matrix_scan: a must be [.., n, n] and b [.., n, m]")
+    if n > 16:
+        raise ValueError("matrix_scan: n is at most 16")
+    m = b.shape[-1]
+    lead = np.broadcast_shapes(a.shape[:-2], b.shape[:-2])
+    if len(lead) < 1:
+        raise ValueError("matrix_scan: the scan axis is one of the leading dims")
+    ax = axis + len(lead) if axis < 0 else axis
+    if not 0 <= ax < len(lead):
+        raise ValueError(f"matrix_scan: axis {axis} out of range for leading rank {len(lead)}")
+    a = np.broadcast_to(a, lead + (n, n))
+    b = np.broadcast_to(b, lead + (n, m))
+
+    a_t = np.moveaxis(a, ax, 0)
+    b_t = np.moveaxis(b, ax, 0)
+    T = lead[ax]
+    out = np.empty((T,) + b_t.shape[1:], dtype=dtype)
+    h = np.zeros(b_t.shape[1:], dtype=dtype)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        h = a_t[t] @ h + b_t[t]
+        out[t] = h
+    return np.moveaxis(out, 0, ax)

@@ -1,0 +1,137 @@
+"""The pins must fail on plausible mistakes: each case plants one in the oracle.
+
+A mutation replaces one oracle function for the duration of a test (on the
+CPU, through pytest's monkeypatch) and then runs the pins written for that
+operation. At least one pin has to fail, otherwise the pins would not have
+told a correct oracle from a wrong one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+_real_es = oracle.element_scan
+_real_ms = oracle.matrix_scan
+_real_bodies = dict(oracle.BODIES)
+
+
+def _time_shifted(body, initial, sequences, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    # reads x one trip late: x[t-1] at trip t
+    seqs = [np.asarray(s, dtype=np.float64) for s in sequences]
+    ax = axis % seqs[0].ndim
+    seqs[0] = np.roll(seqs[0], 1, axis=ax)
+    return _real_es(body, initial, seqs, axis, state_axis, reverse, dtype)
+
+
+def _gate_shifted(body, initial, sequences, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    # reads the second sequence (decay or cost) one trip early
+    seqs = [np.asarray(s, dtype=np.float64) for s in sequences]
+    ax = axis % seqs[0].ndim
+    seqs[1] = np.roll(seqs[1], -1, axis=ax)
+    return _real_es(body, initial, seqs, axis, state_axis, reverse, dtype)
+
+
+def _wrong_direction(body, initial, sequences, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    return _real_es(body, initial, sequences, axis, state_axis, not reverse, dtype)
+
+
+ES_MUTANTS = {
+    "tanh drops decay": ("tanh_affine", lambda h, x, a: np.tanh(x + h)),
+    "tanh swaps x and a": ("tanh_affine", lambda h, x, a: np.tanh(a + x * h)),
+    "tanh drops tanh": ("tanh_affine", lambda h, x, a: x + a * h),
+    "norm-cap drops sqrt": ("norm_cap", lambda h, x, a: (lambda y: y / np.maximum(1.0, np.sum(y * y, -1, keepdims=True)))(a * h + x)),
+    "norm-cap caps each component": ("norm_cap", lambda h, x, a: (lambda y: y / np.maximum(1.0, np.abs(y)))(a * h + x)),
+    "norm-cap drops x": ("norm_cap", lambda h, x, a: (lambda y: y / np.maximum(1.0, np.sqrt(np.sum(y * y, -1, keepdims=True))))(a * h)),
+    "max-plus adds cost": ("max_plus", lambda h, x, c: np.maximum(h + c, x)),
+    "max-plus takes min": ("max_plus", lambda h, x, c: np.minimum(h - c, x)),
+    "max-plus subtracts after max": ("max_plus", lambda h, x, c: np.maximum(h, x) - c),
+}
+
+ES_PINS = {
+    "tanh_affine": [
+        (pins.test_golden_tanh_affine, {}),
+        (pins.test_tanh_zero_decay_is_pointwise_tanh, {"axis": 1}),
+        (pins.test_tanh_inverse_problem, {"axis": 1, "reverse": False}),
+        (pins.test_tanh_inverse_problem, {"axis": 1, "reverse": True}),
+    ],
+    "norm_cap": [
+        (pins.test_golden_norm_cap, {}),
+        (pins.test_norm_cap_inverse_problem, {"n": 16, "gate_width": 1, "reverse": False}),
+        (pins.test_norm_cap_linear_regime_closed_form, {}),
+        (pins.test_norm_cap_saturated_is_unit_norm, {}),
+    ],
+    "max_plus": [
+        (pins.test_golden_max_plus, {"key": "max_plus_reverse", "reverse": True}),
+        (pins.test_max_plus_closed_form, {"reverse": True}),
+        (pins.test_max_plus_zero_cost_is_reverse_cummax, {}),
+    ],
+}
+
+
+def _some_pin_fails(pin_list):
+    for fn, kwargs in pin_list:
+        try:
+            fn(**kwargs)
+        except (AssertionError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(ES_MUTANTS))
+def test_element_scan_body_mutants_are_caught(name, monkeypatch):
+    body, fn = ES_MUTANTS[name]
+    monkeypatch.setitem(oracle.BODIES, body, fn)
+    assert _some_pin_fails(ES_PINS[body]), f"no pin caught mutant: {name}"
+
+
+@pytest.mark.parametrize("mutant", [_time_shifted, _gate_shifted, _wrong_direction])
+@pytest.mark.parametrize("body", sorted(ES_PINS))
+def test_element_scan_index_mutants_are_caught(mutant, body, monkeypatch):
+    monkeypatch.setattr(oracle, "element_scan", mutant)
+    assert _some_pin_fails(ES_PINS[body]), f"no {body} pin caught {mutant.__name__}"
+
+
+def _ms_transposed(a, b, axis=0, reverse=False, dtype=np.float64):
+    return _real_ms(np.swapaxes(np.asarray(a, dtype=np.float64), -1, -2), b, axis, reverse, dtype)
+
+
+def _ms_a_shifted(a, b, axis=0, reverse=False, dtype=np.float64):
+    # uses a[t-1] at step t
+    a = np.asarray(a, dtype=np.float64)
+    lead = len(np.broadcast_shapes(a.shape[:-2], np.shape(b)[:-2]))
+    ax = axis % lead
+    a_b = np.broadcast_to(a, np.broadcast_shapes(a.shape[:-2], np.shape(b)[:-2]) + a.shape[-2:])
+    return _real_ms(np.roll(a_b, 1, axis=ax), b, axis, reverse, dtype)
+
+
+def _ms_wrong_direction(a, b, axis=0, reverse=False, dtype=np.float64):
+    return _real_ms(a, b, axis, not reverse, dtype)
+
+
+def _ms_starts_from_b0_twice(a, b, axis=0, reverse=False, dtype=np.float64):
+    # starts from h = b[first] instead of h = 0, counting the first b twice
+    out = _real_ms(a, b, axis, reverse, dtype)
+    return out + np.take(np.asarray(b, dtype=np.float64), [-1 if reverse else 0], axis=axis % (np.ndim(b) - 2))
+
+
+MS_PINS = [
+    (pins.test_golden_matrix_scan, {"key": "matrix_scan_forward", "reverse": False}),
+    (pins.test_golden_matrix_scan, {"key": "matrix_scan_reverse", "reverse": True}),
+    (pins.test_matrix_scan_product_sum, {"n": 4, "m": 2, "reverse": True}),
+    (pins.test_matrix_scan_product_sum, {"n": 3, "m": 1, "reverse": False}),
+    (pins.test_matrix_scan_inverse_problem, {"reverse": False}),
+]
+
+
+@pytest.mark.parametrize("mutant", [_ms_transposed, _ms_a_shifted, _ms_wrong_direction, _ms_starts_from_b0_twice])
+def test_matrix_scan_mutants_are_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "matrix_scan", mutant)
+    assert _some_pin_fails(MS_PINS), f"no matrix-scan pin caught {mutant.__name__}"
+
+
+def test_unmutated_oracle_passes_the_same_pins():
+    for body in ES_PINS:
+        assert not _some_pin_fails(ES_PINS[body])
+    assert not _some_pin_fails(MS_PINS)

@@ -1,0 +1,434 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+None of these re-types the oracle's recurrence. Each pin is a closed form, an
+inverse problem (pick the states, solve for the inputs that produce them with
+a different function, run the scan, get the states back), an invariant the
+pages state, a special case that reduces to a library routine, or a worked
+example from ``tests/golden/``. Together they fail on a dropped term, a wrong
+sign, an off-by-one time index, a transposed operand, a wrong direction, or a
+wrong axis.
+"""
+
+import json
+import math
+import pathlib
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = json.loads((pathlib.Path(__file__).parent / "golden" / "worked_examples.json").read_text())
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _move_time_first(arr, axis):
+    return np.moveaxis(arr, axis, 0)
+
+
+# --- worked examples ------------------------------------------------------------
+
+
+def test_golden_tanh_affine():
+    g = GOLDEN["tanh_affine_forward"]
+    out = oracle.element_scan("tanh_affine", np.float64(g["initial"]), [g["x"], g["decay"]], axis=0)
+    np.testing.assert_allclose(out, g["expected"], rtol=0, atol=g["tolerance"])
+
+
+def test_golden_norm_cap():
+    g = GOLDEN["norm_cap_forward"]
+    out = oracle.element_scan("norm_cap", g["initial"], [g["x"], g["decay"]], axis=0, state_axis=-1)
+    np.testing.assert_allclose(out, g["expected"], rtol=0, atol=g["tolerance"])
+
+
+@pytest.mark.parametrize("key,reverse", [("max_plus_reverse", True), ("max_plus_forward", False)])
+def test_golden_max_plus(key, reverse):
+    g = GOLDEN[key]
+    out = oracle.element_scan("max_plus", np.float64(g["initial"]), [g["x"], g["cost"]], axis=0,
+                              reverse=reverse)
+    np.testing.assert_array_equal(out, g["expected"])
+    out32 = oracle.element_scan("max_plus", np.float32(g["initial"]), [g["x"], g["cost"]], axis=0,
+                                reverse=reverse, dtype=np.float32)
+    np.testing.assert_array_equal(out32, np.float32(g["expected"]))
+
+
+@pytest.mark.parametrize("key,reverse", [("matrix_scan_forward", False), ("matrix_scan_reverse", True)])
+def test_golden_matrix_scan(key, reverse):
+    g = GOLDEN[key]
+    out = oracle.matrix_scan(g["a"], g["b"], axis=0, reverse=reverse)
+    np.testing.assert_array_equal(out, g["expected"])
+
+
+# --- tanh-affine body -------------------------------------------------------------
+
+
+@pytest.mark.parametrize("axis", [0, 1, -1])
+def test_tanh_zero_decay_is_pointwise_tanh(axis):
+    # decay = 0 removes the state from every trip: h[t] = tanh(x[t]).
+    r = _rng(10)
+    x = r.standard_normal((3, 5, 4))
+    init_shape = tuple(d for i, d in enumerate(x.shape) if i != axis % 3)
+    out = oracle.element_scan("tanh_affine", r.standard_normal(init_shape), [x, np.zeros_like(x)],
+                              axis=axis)
+    np.testing.assert_array_equal(out, np.tanh(x))
+
+
+@pytest.mark.parametrize("axis,reverse", [(0, False), (1, False), (-1, True), (1, True)])
+def test_tanh_inverse_problem(axis, reverse):
+    # Pick states h in (-1, 1) and decays; x[t] = atanh(h[t]) - decay[t] * h_prev
+    # makes the scan reproduce h. Wrong time indices or operand roles fail.
+    r = _rng(11)
+    shape = (3, 6, 4)
+    ax = axis % 3
+    h = r.uniform(-0.95, 0.95, shape)
+    decay = r.uniform(-1.5, 1.5, shape)
+    init = r.uniform(-2, 2, tuple(d for i, d in enumerate(shape) if i != ax))
+    ht, dt = _move_time_first(h, ax), _move_time_first(decay, ax)
+    xt = np.empty_like(ht)
+    T = shape[ax]
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    prev = init
+    for t in order:
+        xt[t] = np.arctanh(ht[t]) - dt[t] * prev
+        prev = ht[t]
+    x = np.moveaxis(xt, 0, ax)
+    out = oracle.element_scan("tanh_affine", init, [x, decay], axis=axis, reverse=reverse)
+    np.testing.assert_allclose(out, h, rtol=0, atol=1e-12)
+
+
+def test_tanh_state_stays_in_open_interval():
+    r = _rng(12)
+    x = 3 * r.standard_normal((2, 50, 3))
+    out = oracle.element_scan("tanh_affine", 5 * r.standard_normal((2, 3)),
+                              [x, r.uniform(-2, 2, x.shape)], axis=1)
+    assert np.all(np.abs(out) <= 1.0)
+
+
+# --- norm-capped vector body -----------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,gate_width,reverse", [(16, 1, False), (16, 16, True), (5, 1, True), (1, 1, False)])
+def test_norm_cap_inverse_problem(n, gate_width, reverse):
+    # Pick states: some trips inside the unit ball (the cap does not fire, y = h),
+    # some on the sphere with y = lam * h, lam > 1 (the cap fires and divides by
+    # |y| = lam). Solve x = y - decay * h_prev and check the scan returns h.
+    r = _rng(13 + n)
+    B, T, H = 2, 9, 3
+    h = r.standard_normal((B, T, H, n))
+    h /= np.linalg.norm(h, axis=-1, keepdims=True)
+    capped = r.random((B, T, H, 1)) < 0.5
+    inside = r.uniform(0.1, 0.9, (B, T, H, 1))
+    h = np.where(capped, h, h * inside)
+    lam = np.where(capped, r.uniform(1.2, 3.0, (B, T, H, 1)), 1.0)
+    decay = r.uniform(0.2, 1.0, (B, T, H, gate_width))
+    init = 0.3 * r.standard_normal((B, H, n))
+    x = np.empty_like(h)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    prev = init
+    for t in order:
+        x[:, t] = lam[:, t] * h[:, t] - decay[:, t] * prev
+        prev = h[:, t]
+    out = oracle.element_scan("norm_cap", init, [x, decay], axis=1, state_axis=-1, reverse=reverse)
+    np.testing.assert_allclose(out, h, rtol=0, atol=1e-12)
+
+
+def test_norm_cap_norm_at_most_one():
+    r = _rng(14)
+    x = 2 * r.standard_normal((3, 40, 2, 16))
+    out = oracle.element_scan("norm_cap", 4 * r.standard_normal((3, 2, 16)),
+                              [x, r.uniform(-1.2, 1.2, (3, 40, 2, 1))], axis=1, state_axis=-1)
+    assert np.all(np.linalg.norm(out, axis=-1) <= 1 + 1e-12)
+
+
+def test_norm_cap_linear_regime_closed_form():
+    # With tiny inputs and |decay| < 1 the cap never fires, and the scan is the
+    # gated linear recurrence with closed form
+    # h[t] = prod_{r<=t} decay[r] * init + sum_{s<=t} prod_{s<r<=t} decay[r] * x[s].
+    r = _rng(15)
+    T, n = 7, 4
+    x = 1e-3 * r.standard_normal((T, n))
+    decay = r.uniform(0.1, 0.9, (T, 1))
+    init = 1e-3 * r.standard_normal(n)
+    expect = np.zeros((T, n))
+    for t in range(T):
+        acc = np.prod(decay[: t + 1, 0]) * init
+        for s in range(t + 1):
+            acc = acc + np.prod(decay[s + 1: t + 1, 0]) * x[s]
+        expect[t] = acc
+    out = oracle.element_scan("norm_cap", init, [x, decay], axis=0, state_axis=-1)
+    np.testing.assert_allclose(out, expect, rtol=1e-12, atol=1e-18)
+
+
+def test_norm_cap_saturated_is_unit_norm():
+    r = _rng(16)
+    x = 100 * r.standard_normal((2, 12, 16))
+    out = oracle.element_scan("norm_cap", np.zeros((2, 16)), [x, r.uniform(0, 1, (2, 12, 1))],
+                              axis=1, state_axis=-1)
+    np.testing.assert_allclose(np.linalg.norm(out, axis=-1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_norm_cap_needs_vector_state():
+    with pytest.raises(ValueError):
+        oracle.element_scan("norm_cap", np.zeros(3), [np.ones((4, 3)), np.ones((4, 3))], axis=0)
+
+
+# --- max-plus body ---------------------------------------------------------------
+
+
+def _max_plus_closed_form_reverse(x, c, init):
+    # h[t] = max( max_{s>=t} (x[s] - sum_{r=t}^{s-1} c[r]),  init - sum_{r=t}^{T-1} c[r] )
+    T = len(x)
+    out = np.empty(T)
+    for t in range(T):
+        best = init - np.sum(c[t:])
+        for s in range(t, T):
+            best = max(best, x[s] - np.sum(c[t:s]))
+        out[t] = best
+    return out
+
+
+def _max_plus_closed_form_forward(x, c, init):
+    # h[t] = max( max_{s<=t} (x[s] - sum_{r=s+1}^{t} c[r]),  init - sum_{r=0}^{t} c[r] )
+    T = len(x)
+    out = np.empty(T)
+    for t in range(T):
+        best = init - np.sum(c[: t + 1])
+        for s in range(t + 1):
+            best = max(best, x[s] - np.sum(c[s + 1: t + 1]))
+        out[t] = best
+    return out
+
+
+@pytest.mark.parametrize("reverse", [True, False])
+def test_max_plus_closed_form(reverse):
+    r = _rng(17)
+    T, L = 11, 6
+    x = r.standard_normal((T, L))
+    c = r.uniform(0, 0.7, (T, L))
+    init = r.standard_normal(L)
+    out = oracle.element_scan("max_plus", init, [x, c], axis=0, reverse=reverse)
+    ref = _max_plus_closed_form_reverse if reverse else _max_plus_closed_form_forward
+    for lane in range(L):
+        np.testing.assert_allclose(out[:, lane], ref(x[:, lane], c[:, lane], init[lane]),
+                                   rtol=0, atol=1e-12)
+
+
+def test_max_plus_zero_cost_is_reverse_cummax():
+    # c = 0: h[t] = max(initial, max_{s>=t} x[s]), the running maximum from the end.
+    r = _rng(18)
+    x = r.standard_normal((4, 20, 5))
+    init = r.standard_normal((4, 5))
+    out = oracle.element_scan("max_plus", init, [x, np.zeros_like(x)], axis=1, reverse=True)
+    ref = np.flip(np.maximum.accumulate(np.flip(x, 1), axis=1), 1)
+    np.testing.assert_array_equal(out, np.maximum(ref, init[:, None, :]))
+
+
+def test_max_plus_float32_mode_close_to_float64():
+    r = _rng(19)
+    x = r.standard_normal((300, 8)).astype(np.float32)
+    c = (0.1 * r.random((300, 8))).astype(np.float32)
+    init = r.standard_normal(8).astype(np.float32)
+    o64 = oracle.element_scan("max_plus", init, [x, c], axis=0, reverse=True)
+    o32 = oracle.element_scan("max_plus", init, [x, c], axis=0, reverse=True, dtype=np.float32)
+    assert o32.dtype == np.float32
+    np.testing.assert_allclose(o32, o64, rtol=1e-6, atol=1e-6)
+
+
+# --- direction, axis and shape invariants for all bodies -----------------------------
+
+
+@pytest.mark.parametrize("body,state_axis", [("tanh_affine", None), ("max_plus", None), ("norm_cap", -1),
+                                             ("tanh_affine", -1), ("max_plus", -1)])
+def test_reverse_is_flip_scan_flip(body, state_axis):
+    # "Nonlinear element scans": a reverse scan computes the same values as
+    # flipping the sequences along the axis, scanning forward and flipping back.
+    r = _rng(20)
+    x = r.standard_normal((3, 13, 2, 4))
+    s = r.uniform(0, 1, (3, 13, 2, 1 if state_axis is not None else 4))
+    if state_axis is None:
+        s = np.broadcast_to(s, x.shape).copy()
+    init = r.standard_normal((3, 2, 4))
+    rev = oracle.element_scan(body, init, [x, s], axis=1, state_axis=state_axis, reverse=True)
+    fwd = oracle.element_scan(body, init, [np.flip(x, 1), np.flip(s, 1)], axis=1, state_axis=state_axis)
+    np.testing.assert_array_equal(rev, np.flip(fwd, 1))
+
+
+def test_vector_elementwise_body_equals_scalar_lanes():
+    # A body without reductions applied to a vector state acts on each component
+    # as its own scalar lane, with a width-one sequence broadcast over the vector.
+    r = _rng(21)
+    x = r.standard_normal((2, 9, 5))
+    a = r.uniform(0, 1, (2, 9, 1))
+    init = r.standard_normal((2, 5))
+    vec = oracle.element_scan("tanh_affine", init, [x, a], axis=1, state_axis=-1)
+    sca = oracle.element_scan("tanh_affine", init, [x, np.broadcast_to(a, x.shape)], axis=1)
+    np.testing.assert_array_equal(vec, sca)
+
+
+def test_element_scan_rejects_bad_arguments():
+    x = np.ones((2, 3))
+    with pytest.raises(ValueError):
+        oracle.element_scan("tanh_affine", np.ones(2), [x, x], axis=0)  # initial must be [3]
+    with pytest.raises(ValueError):
+        oracle.element_scan("tanh_affine", np.ones(2), [x, x], axis=2)
+    with pytest.raises(ValueError):
+        oracle.element_scan("tanh_affine", np.ones(3), [x, np.ones((2, 4))], axis=0)
+    with pytest.raises(ValueError):
+        oracle.element_scan("max_plus", np.ones(3), [np.ones((0, 3)), np.ones((0, 3))], axis=0)
+
+
+# --- matrix-scan ----------------------------------------------------------------------
+
+
+def _product_sum_forward(a, b):
+    # h[t] = sum_{s<=t} (a[t] a[t-1] ... a[s+1]) b[s]: the recurrence unrolled.
+    T, n = a.shape[0], a.shape[1]
+    out = np.zeros((T,) + b.shape[1:])
+    for t in range(T):
+        for s in range(t + 1):
+            p = np.eye(n)
+            for r_ in range(s + 1, t + 1):
+                p = a[r_] @ p
+            out[t] += p @ b[s]
+    return out
+
+
+def _product_sum_reverse(a, b):
+    # h[t] = sum_{s>=t} (a[t] a[t+1] ... a[s-1]) b[s].
+    T, n = a.shape[0], a.shape[1]
+    out = np.zeros((T,) + b.shape[1:])
+    for t in range(T):
+        for s in range(t, T):
+            p = np.eye(n)
+            for r_ in range(s - 1, t - 1, -1):
+                p = a[r_] @ p
+            out[t] += p @ b[s]
+    return out
+
+
+@pytest.mark.parametrize("n,m,reverse", [(3, 1, False), (4, 2, True), (1, 1, False), (5, 3, True)])
+def test_matrix_scan_product_sum(n, m, reverse):
+    r = _rng(30 + n)
+    T = 6
+    a = r.standard_normal((T, n, n))
+    b = r.standard_normal((T, n, m))
+    out = oracle.matrix_scan(a, b, axis=0, reverse=reverse)
+    ref = (_product_sum_reverse if reverse else _product_sum_forward)(a, b)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_scan_zero_a_is_b():
+    r = _rng(31)
+    b = r.standard_normal((3, 7, 4, 2))
+    out = oracle.matrix_scan(np.zeros((3, 7, 4, 4)), b, axis=1)
+    np.testing.assert_array_equal(out, b)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_scan_identity_a_is_cumsum(reverse):
+    r = _rng(32)
+    b = r.standard_normal((2, 9, 3, 2))
+    eye = np.broadcast_to(np.eye(3), (2, 9, 3, 3))
+    out = oracle.matrix_scan(eye, b, axis=1, reverse=reverse)
+    ref = np.flip(np.cumsum(np.flip(b, 1), axis=1), 1) if reverse else np.cumsum(b, axis=1)
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_matrix_scan_geometric_series():
+    # Time-invariant a and b, given with a time axis of length one that
+    # broadcasts: h[t] = (I - a)^{-1} (I - a^{t+1}) b.
+    r = _rng(33)
+    n, m, T = 4, 2, 12
+    a = 0.3 * r.standard_normal((n, n))
+    b = r.standard_normal((n, m))
+    out = oracle.matrix_scan(a[None], np.broadcast_to(b, (T, n, m)), axis=0)
+    eye = np.eye(n)
+    for t in range(T):
+        ref = np.linalg.solve(eye - a, (eye - np.linalg.matrix_power(a, t + 1)) @ b)
+        np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_scan_first_a_unused_forward_last_unused_reverse():
+    r = _rng(34)
+    a = r.standard_normal((8, 3, 3))
+    b = r.standard_normal((8, 3, 2))
+    a2 = a.copy()
+    a2[0] = 1e6
+    np.testing.assert_array_equal(oracle.matrix_scan(a, b), oracle.matrix_scan(a2, b))
+    a3 = a.copy()
+    a3[-1] = 1e6
+    np.testing.assert_array_equal(oracle.matrix_scan(a, b, reverse=True), oracle.matrix_scan(a3, b, reverse=True))
+    np.testing.assert_array_equal(oracle.matrix_scan(a, b)[0], b[0])
+
+
+def test_matrix_scan_columns_are_independent():
+    # "Tensor operations", matrix-scan: every column of h is its own recurrence on the shared a.
+    r = _rng(35)
+    a = r.standard_normal((10, 4, 4)) * 0.5
+    b = r.standard_normal((10, 4, 3))
+    whole = oracle.matrix_scan(a, b)
+    for j in range(3):
+        # equal up to float64 rounding: BLAS may order the sums differently per shape
+        np.testing.assert_allclose(whole[..., j:j + 1], oracle.matrix_scan(a, b[..., j:j + 1]),
+                                   rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_scan_inverse_problem(reverse):
+    # Choose states h and matrices a; b[t] = h[t] - a[t] @ h_prev reproduces h.
+    r = _rng(36)
+    B, T, n, m = 3, 8, 5, 2
+    a = r.standard_normal((B, T, n, n))
+    h = r.standard_normal((B, T, n, m))
+    b = np.empty_like(h)
+    prev = np.zeros((B, n, m))
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        b[:, t] = h[:, t] - a[:, t] @ prev
+        prev = h[:, t]
+    out = oracle.matrix_scan(a, b, axis=1, reverse=reverse)
+    np.testing.assert_allclose(out, h, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_scan_broadcast_leading_dims():
+    # a shared across the batch (leading dim 1) is the same as each batch's own scan.
+    r = _rng(37)
+    a = 0.5 * r.standard_normal((1, 6, 3, 3))
+    b = r.standard_normal((4, 6, 3, 2))
+    out = oracle.matrix_scan(a, b, axis=-1)
+    assert out.shape == b.shape
+    for i in range(4):
+        np.testing.assert_allclose(out[i], oracle.matrix_scan(a[0], b[i], axis=0), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_scan_reverse_is_flip_scan_flip(reverse):
+    r = _rng(38)
+    a = r.standard_normal((2, 7, 3, 3))
+    b = r.standard_normal((2, 7, 3, 1))
+    got = oracle.matrix_scan(a, b, axis=1, reverse=not reverse)
+    ref = np.flip(oracle.matrix_scan(np.flip(a, 1), np.flip(b, 1), axis=1, reverse=reverse), 1)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_matrix_scan_empty_axis_and_limits():
+    assert oracle.matrix_scan(np.zeros((0, 2, 2)), np.zeros((0, 2, 1))).shape == (0, 2, 1)
+    oracle.matrix_scan(np.zeros((2, 16, 16)), np.zeros((2, 16, 1)))
+    with pytest.raises(ValueError):
+        oracle.matrix_scan(np.zeros((2, 17, 17)), np.zeros((2, 17, 1)))
+    with pytest.raises(ValueError):
+        oracle.matrix_scan(np.zeros((2, 3, 3)), np.zeros((2, 4, 1)))
+
+
+def test_matrix_scan_scalar_closed_form():
+    # n = m = 1 is the prelude's linear-scan: h[t] = sum_s (prod_{s<r<=t} a[r]) b[s].
+    r = _rng(39)
+    T = 9
+    a = r.uniform(-1.5, 1.5, T)
+    b = r.standard_normal(T)
+    out = oracle.matrix_scan(a.reshape(T, 1, 1), b.reshape(T, 1, 1))[:, 0, 0]
+    ref = [sum(math.prod(a[s + 1: t + 1]) * b[s] for s in range(t + 1)) for t in range(T)]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
