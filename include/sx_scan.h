@@ -1,0 +1,183 @@
+/*
+ * sx_scan.h: C ABI of the MI355X (gfx950) scan library, libsx_scan.so.
+ *
+ * Two scans, forward only, as the SexpGPU documentation pages define them:
+ *
+ *   element-scan  "Nonlinear element scans": a nonlinear recurrence run
+ *                 independently at every position outside one sequence axis,
+ *                 with one of three fixed bodies (tanh-affine, norm-capped
+ *                 vector state, max-plus), forward or reverse.
+ *   matrix-scan   "Tensor operations", Operations table (matrix-scan row) and
+ *                 the "matrix-scan" section: h[t] = a[t] @ h[t-1] + b[t] from
+ *                 h = 0, n <= 16, computed in f32, with :axis, :reverse and
+ *                 broadcast leading dims.
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers to tensor data are DEVICE pointers on the device that is
+ *    current on the calling thread. Shapes and strides are HOST arrays of
+ *    int64_t, read during the call only. Strides count elements (not bytes),
+ *    may be zero (a broadcast dimension) and may be passed as NULL to mean
+ *    row-major contiguous. Layouts are row-major, as PyTorch's default.
+ *  - The caller owns every buffer. The library keeps no pointer after it
+ *    returns and allocates no device memory. Where a workspace is needed,
+ *    the caller passes one of at least the queried size; its contents on
+ *    entry do not matter and the library clears what it needs on the stream.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *    and the call returns without waiting. Results follow stream order.
+ *    Concurrent calls that share one workspace race.
+ *  - Every argument is checked on the host before anything is enqueued. On
+ *    an error status nothing is launched and `out` is untouched;
+ *    sx_last_error() then returns a message that names the operands with
+ *    their shapes and dtypes, as the pages' error notes do.
+ *  - Status codes mirror the pages' error table ("Tensor operations",
+ *    Errors): E-DIM-001 shapes do not fit, E-DIM-002 dtypes differ or are
+ *    not allowed, E-DIM-003 a tensor was expected.
+ */
+#ifndef SX_SCAN_H
+#define SX_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest tensor rank the library accepts. */
+#define SX_MAX_RANK 8
+/* Largest matrix size n of matrix-scan ("n at most 16") and largest state
+ * width of a vector-state element scan ("vectors of 1 to 16 values"). */
+#define SX_MAX_N 16
+/* `state_axis` value that selects a scalar state (no :state-axis). */
+#define SX_STATE_SCALAR INT32_MIN
+
+typedef enum sx_status {
+  SX_OK = 0,
+  SX_E_DIM_001 = 1,     /* shapes do not fit, axis out of range, n > 16, empty element-scan axis */
+  SX_E_DIM_002 = 2,     /* dtypes differ, or a dtype the operand does not allow */
+  SX_E_DIM_003 = 3,     /* a tensor was expected: a required pointer is NULL */
+  SX_E_UNSUPPORTED = 4, /* well-formed but not provided: rank > 8, :projective, strided matrix dims */
+  SX_E_ALIAS = 5,       /* `out` overlaps an input */
+  SX_E_WORKSPACE = 6,   /* workspace NULL or smaller than the queried size */
+  SX_E_DEVICE = 7       /* a HIP call failed; sx_last_error() carries hipGetErrorString */
+} sx_status;
+
+typedef enum sx_dtype { SX_F32 = 0, SX_BF16 = 1 } sx_dtype;
+
+/* The three element-scan bodies ("Nonlinear element scans", introduction),
+ * each taking (state h, sequence x, sequence s) in the page's order:
+ *   SX_BODY_TANH_AFFINE  h' = tanh(x + s * h)              s = decay
+ *   SX_BODY_NORM_CAP     y = s * h + x; h' = y / max(1, |y|)  s = decay, |y| over the state vector
+ *   SX_BODY_MAX_PLUS     h' = max(h - s, x)                s = cost
+ * NORM_CAP reduces over the state vector and so needs a vector state; the
+ * other two act on each state component on its own and accept either. */
+typedef enum sx_body {
+  SX_BODY_TANH_AFFINE = 0,
+  SX_BODY_NORM_CAP = 1,
+  SX_BODY_MAX_PLUS = 2
+} sx_body;
+
+/*
+ * sx_element_scan: "Nonlinear element scans", introduction and "Arguments
+ * and body".
+ *
+ * For every lane (every index outside `axis`, and outside the state axis for
+ * a vector state) the state starts at `initial` and each trip applies the
+ * body: forward h[t] = f(h[t-1], x[t], s[t]) from h[-1] = initial, reverse
+ * h[t] = f(h[t+1], x[t], s[t]) from h[T] = initial. out[t] holds the state
+ * after trip t. Computation is f32.
+ *
+ *  body          one of sx_body.
+ *  rank, shape   the OUTPUT shape, rank 1..SX_MAX_RANK: the sequences' shape,
+ *                whose last axis, for a vector state, is the state width n.
+ *  axis          the sequence axis; negative counts from the end. Its length
+ *                must be at least one (E-DIM-001 otherwise).
+ *  state_axis    SX_STATE_SCALAR for a scalar state; -1 or rank-1 for a state
+ *                vector along the last axis (1 <= n <= 16, axis != last);
+ *                anything else is E-DIM-001.
+ *  reverse       0 forward, nonzero reverse.
+ *  initial       f32, shape = `shape` without `axis`; `initial_strides` has
+ *                rank-1 entries (or NULL for contiguous).
+ *  x, s          f32 sequences. Scalar state: shape = `shape`, widths
+ *                ignored. Vector state: shape = `shape` with the last axis
+ *                replaced by the sequence's own width, `x_width`/`s_width`,
+ *                each 1 (broadcast over the state, a per-trip gate) or n.
+ *                Strides have `rank` entries; a width-1 axis's stride is
+ *                ignored.
+ *  out           f32, contiguous, shape `shape`. Must not overlap an input.
+ *  workspace     may be NULL when sx_element_scan_workspace_bytes() is 0.
+ *  stream        hipStream_t.
+ *
+ * A shape with zero lanes returns SX_OK without launching.
+ */
+sx_status sx_element_scan(sx_body body, int rank, const int64_t* shape, int axis, int state_axis,
+                          int reverse, const float* initial, const int64_t* initial_strides,
+                          const float* x, int64_t x_width, const int64_t* x_strides, const float* s,
+                          int64_t s_width, const int64_t* s_strides, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sx_element_scan needs for these arguments (0 when none);
+ * returns 0 as well for arguments sx_element_scan would reject. */
+size_t sx_element_scan_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis,
+                                       int state_axis);
+
+/*
+ * sx_matrix_scan: "Tensor operations", Operations table (matrix-scan row)
+ * and the "matrix-scan" section.
+ *
+ * a is [lead_a..., n, n] and b [lead_b..., n, m], n <= 16, one float dtype.
+ * The leading dims broadcast (NumPy: right-aligned, each equal or 1) to one
+ * shape `lead`, and `axis` counts among them (-1 is the one before the
+ * matrices). For every other leading index the n-by-m state runs
+ *   forward  h[t] = a[t] @ h[t-1] + b[t]  from h[-1] = 0  (h[0] = b[0]),
+ *   reverse  h[t] = a[t] @ h[t+1] + b[t]  from h[T] = 0  (h[T-1] = b[T-1]),
+ * and out[t] = h[t]. Computation is f32 for f32 and bf16 operands alike
+ * (bf16 widens to f32 exactly).
+ *
+ *  dtype         SX_F32 or SX_BF16, shared by a and b.
+ *  a_*, b_*      rank (>= 2), shape, strides (NULL = contiguous) and data.
+ *                The two matrix dims must be row-major contiguous (strides
+ *                [n, 1] and [m, 1] where those dims exceed 1); leading dims may
+ *                have any stride, including 0. Otherwise SX_E_UNSUPPORTED.
+ *  axis          the scan axis among the broadcast leading dims.
+ *  reverse       0 forward, nonzero reverse.
+ *  projective    must be 0: the :projective variant is not provided
+ *                (SX_E_UNSUPPORTED).
+ *  out_dtype     SX_F32 or SX_BF16. The result is rounded to bf16 to nearest
+ *                even on store when SX_BF16.
+ *  out           contiguous, shape lead + [n, m] (see sx_matrix_scan_out_shape).
+ *  workspace     at least sx_matrix_scan_workspace_bytes() bytes, 256-byte
+ *                aligned; may be NULL when that is 0.
+ *
+ * An axis of length 0 (or m = 0) returns SX_OK with nothing to write.
+ */
+sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                         const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides,
+                         const void* b, int axis, int reverse, int projective, sx_dtype out_dtype,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sx_matrix_scan needs for these shapes (0 for invalid ones). */
+size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank,
+                                      const int64_t* b_shape, int axis);
+
+/* Writes the matrix-scan result shape to out_shape (room for SX_MAX_RANK + 2
+ * entries) and returns its rank, or -1 for shapes that do not fit. */
+int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                             int64_t* out_shape);
+
+/* "E-DIM-001" etc. for a status; "OK" for SX_OK. Static storage. */
+const char* sx_status_name(sx_status status);
+
+/* Message of the last failed call on this thread (thread-local storage,
+ * valid until the next call on the thread); "" after a success. */
+const char* sx_last_error(void);
+
+/* Library version string, e.g. "sx_scan 0.1 gfx950". Static storage. */
+const char* sx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SX_SCAN_H */

@@ -1,0 +1,216 @@
+"""ctypes binding over libsx_scan.so (C ABI in include/sx_scan.h).
+
+Argument marshalling only: shapes, strides, pointers, the workspace and the
+current torch stream go to the C library, whose HIP kernels do every step of
+the scan. There is no CPU fallback: without the built library every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsx_scan.so")
+
+SX_OK = 0
+SX_E_DIM_001 = 1
+SX_E_DIM_002 = 2
+SX_E_DIM_003 = 3
+SX_E_UNSUPPORTED = 4
+SX_E_ALIAS = 5
+SX_E_WORKSPACE = 6
+SX_E_DEVICE = 7
+SX_STATE_SCALAR = -(2 ** 31)
+SX_F32 = 0
+SX_BF16 = 1
+
+BODIES = {"tanh_affine": 0, "norm_cap": 1, "max_plus": 2}
+_DTYPES = {torch.float32: SX_F32, torch.bfloat16: SX_BF16}
+_STATUS_NAMES = {0: "OK", 1: "E-DIM-001", 2: "E-DIM-002", 3: "E-DIM-003", 4: "E-UNSUPPORTED",
+                 5: "E-ALIAS", 6: "E-WORKSPACE", 7: "E-DEVICE"}
+
+
+class SxError(RuntimeError):
+    """A call the library (or this binding, before calling it) refused."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(message)
+        self.code = code
+        self.name = _STATUS_NAMES.get(code, "E-UNKNOWN")
+
+
+_lib = None
+
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsx_scan.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m scan_primitives_amd.build_lib` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    lib.sx_element_scan.restype = c_int
+    lib.sx_element_scan.argtypes = [c_int, c_int, _i64p, c_int, c_int, c_int,
+                                    vp, _i64p, vp, ctypes.c_int64, _i64p, vp, ctypes.c_int64, _i64p,
+                                    vp, vp, c_size, vp]
+    lib.sx_element_scan_workspace_bytes.restype = c_size
+    lib.sx_element_scan_workspace_bytes.argtypes = [c_int, c_int, _i64p, c_int, c_int]
+    lib.sx_matrix_scan.restype = c_int
+    lib.sx_matrix_scan.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
+                                   c_int, c_int, c_int, c_int, vp, vp, c_size, vp]
+    lib.sx_matrix_scan_workspace_bytes.restype = c_size
+    lib.sx_matrix_scan_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int]
+    lib.sx_matrix_scan_out_shape.restype = c_int
+    lib.sx_matrix_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
+    lib.sx_status_name.restype = ctypes.c_char_p
+    lib.sx_status_name.argtypes = [c_int]
+    lib.sx_last_error.restype = ctypes.c_char_p
+    lib.sx_last_error.argtypes = []
+    lib.sx_version.restype = ctypes.c_char_p
+    lib.sx_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def i64_array(values) -> ctypes.Array:
+    values = list(values)
+    return (ctypes.c_int64 * max(len(values), 1))(*values)
+
+
+def _check(status: int) -> None:
+    if status != SX_OK:
+        msg = load_library().sx_last_error().decode()
+        raise SxError(status, msg or _STATUS_NAMES.get(status, str(status)))
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_device_tensor(name: str, t) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise SxError(SX_E_DIM_003, f"{name}: a tensor was expected, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise SxError(SX_E_UNSUPPORTED, f"{name}: the HIP library takes device tensors, got {t.device}")
+
+
+def element_scan(body: str, initial: torch.Tensor, sequences, axis: int = 0, state_axis=None,
+                 reverse: bool = False) -> torch.Tensor:
+    """Element scan on the GPU: ``"tanh_affine"``, ``"norm_cap"`` or ``"max_plus"``.
+
+    ``sequences`` is ``[x, decay]`` or ``[x, cost]`` (page order). ``state_axis``
+    is ``None`` for a scalar state or ``-1`` for a vector state along the last
+    axis. Returns a new f32 tensor of the sequences' shape.
+    """
+    if body not in BODIES:
+        raise SxError(SX_E_UNSUPPORTED, f"element-scan: unknown body {body!r}")
+    seqs = list(sequences)
+    if len(seqs) != 2:
+        raise SxError(SX_E_DIM_001, f"element-scan: the {body} body takes two sequences, got {len(seqs)}")
+    x, s = seqs
+    for name, t in (("initial", initial), ("x", x), ("sequence 2", s)):
+        _require_device_tensor(name, t)
+        if t.dtype != torch.float32:
+            raise SxError(SX_E_DIM_002, f"element-scan: {name} is {t.dtype}, sequences and initial are f32")
+    if not (x.device == s.device == initial.device):
+        raise SxError(SX_E_UNSUPPORTED, "element-scan: operands on different devices")
+    rank = x.dim()
+    vec = state_axis is not None
+    if vec:
+        if rank < 2 or initial.dim() < 1:
+            raise SxError(SX_E_DIM_001, "element-scan: a vector state needs sequences of rank >= 2")
+        n = initial.shape[-1]
+        out_shape = tuple(x.shape[:-1]) + (n,)
+        if tuple(s.shape[:-1]) != tuple(x.shape[:-1]):
+            raise SxError(SX_E_DIM_001, f"element-scan: sequences {tuple(x.shape)} and {tuple(s.shape)} "
+                                        "differ outside the state axis")
+        x_width, s_width = x.shape[-1], s.shape[-1]
+        sa = state_axis
+    else:
+        out_shape = tuple(x.shape)
+        if tuple(s.shape) != out_shape:
+            raise SxError(SX_E_DIM_001, f"element-scan: sequences {tuple(x.shape)} and {tuple(s.shape)} differ")
+        x_width = s_width = out_shape[-1] if rank else 1
+        sa = SX_STATE_SCALAR
+    ax = axis + rank if axis < 0 else axis
+    if 0 <= ax < rank:
+        expect_init = out_shape[:ax] + out_shape[ax + 1:]
+        if tuple(initial.shape) != expect_init:
+            raise SxError(SX_E_DIM_001, f"element-scan: initial {tuple(initial.shape)} f32 does not match the "
+                                        f"sequence shape {out_shape} without axis {axis}")
+    lib = load_library()
+    out = torch.empty(out_shape, dtype=torch.float32, device=x.device)
+    shape_a = i64_array(out_shape)
+    ws_bytes = lib.sx_element_scan_workspace_bytes(BODIES[body], rank, shape_a, axis, sa)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+    with torch.cuda.device(x.device):
+        status = lib.sx_element_scan(
+            BODIES[body], rank, shape_a, axis, sa, 1 if reverse else 0,
+            initial.data_ptr(), i64_array(initial.stride()),
+            x.data_ptr(), x_width, i64_array(x.stride()),
+            s.data_ptr(), s_width, i64_array(s.stride()),
+            out.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes,
+            _stream_handle(x.device))
+    _check(status)
+    return out
+
+
+def matrix_scan(a: torch.Tensor, b: torch.Tensor, axis: int = 0, reverse: bool = False,
+                out_dtype=None, projective: bool = False) -> torch.Tensor:
+    """Matrix scan on the GPU: ``h[t] = a[t] @ h[t-1] + b[t]`` along ``axis``.
+
+    ``a`` is ``[..., n, n]`` and ``b`` ``[..., n, m]`` of one dtype (f32 or
+    bf16); the leading dims broadcast. The result has the broadcast leading
+    shape plus ``[n, m]`` and ``b``'s dtype unless ``out_dtype`` says
+    otherwise. Computation is f32.
+    """
+    _require_device_tensor("a", a)
+    _require_device_tensor("b", b)
+    if a.dtype != b.dtype or a.dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"matrix-scan: a is {a.dtype} and b is {b.dtype}; one float dtype "
+                                    "(f32 or bf16) is required")
+    if a.device != b.device:
+        raise SxError(SX_E_UNSUPPORTED, "matrix-scan: operands on different devices")
+    out_dtype = b.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"matrix-scan: out dtype {out_dtype} is not f32 or bf16")
+    lib = load_library()
+    # The library reads the two matrix dims row-major; other layouts are copied to that one here.
+    if a.dim() >= 2 and not _matrix_dims_contiguous(a):
+        a = a.contiguous()
+    if b.dim() >= 2 and not _matrix_dims_contiguous(b):
+        b = b.contiguous()
+    a_shape, b_shape = i64_array(a.shape), i64_array(b.shape)
+    oshape = i64_array([0] * 10)
+    r = lib.sx_matrix_scan_out_shape(a.dim(), a_shape, b.dim(), b_shape, oshape)
+    if r < 0:
+        # let the library produce the precise status and message
+        _check(lib.sx_matrix_scan(_DTYPES[a.dtype], a.dim(), a_shape, None, None, b.dim(), b_shape, None, None,
+                                  axis, 0, 0, _DTYPES[out_dtype], None, None, 0, None))
+        raise SxError(SX_E_DIM_001, "matrix-scan: shapes do not fit")
+    out = torch.empty(tuple(oshape[:r]), dtype=out_dtype, device=a.device)
+    ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), a_shape, b.dim(), b_shape, axis)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+    with torch.cuda.device(a.device):
+        status = lib.sx_matrix_scan(
+            _DTYPES[a.dtype], a.dim(), a_shape, i64_array(a.stride()), a.data_ptr(),
+            b.dim(), b_shape, i64_array(b.stride()), b.data_ptr(),
+            axis, 1 if reverse else 0, 1 if projective else 0, _DTYPES[out_dtype], out.data_ptr(),
+            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(a.device))
+    _check(status)
+    return out
+
+
+def _matrix_dims_contiguous(t: torch.Tensor) -> bool:
+    rows, cols = t.shape[-2], t.shape[-1]
+    st = t.stride()
+    return (cols <= 1 or st[-1] == 1) and (rows <= 1 or cols == 0 or st[-2] == cols)

@@ -1,0 +1,453 @@
+// sx_api.cpp: the C ABI of libsx_scan.so (declared in include/sx_scan.h).
+//
+// Every argument is validated here, on the host, before anything touches the
+// device: a rejected call launches nothing and leaves `out` alone. The
+// shapes and strides are then reduced to the compact descriptors of
+// sx_common.hpp and handed to the launchers in element_scan.hip and
+// matrix_scan.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sx_common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sx_status fail(sx_status st, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string("error[") + sx_status_name(st) + "]: " + buf;
+  return st;
+}
+
+sx_status ok() {
+  g_last_error.clear();
+  return SX_OK;
+}
+
+std::string shape_str(int rank, const int64_t* shape) {
+  std::string s = "[";
+  for (int i = 0; i < rank; ++i) {
+    if (i) s += ", ";
+    s += std::to_string(shape[i]);
+  }
+  return s + "]";
+}
+
+const char* dtype_name(int dt) { return dt == SX_F32 ? "f32" : dt == SX_BF16 ? "bf16" : "?"; }
+
+void contiguous_strides(int rank, const int64_t* shape, int64_t* st) {
+  int64_t acc = 1;
+  for (int i = rank - 1; i >= 0; --i) {
+    st[i] = acc;
+    acc *= std::max<int64_t>(shape[i], 1);
+  }
+}
+
+// Checked product; returns false on overflow past 2^62.
+bool checked_numel(int rank, const int64_t* shape, int64_t* numel) {
+  int64_t n = 1;
+  for (int i = 0; i < rank; ++i) {
+    if (shape[i] < 0) return false;
+    if (shape[i] != 0 && n > (int64_t(1) << 62) / shape[i]) return false;
+    n *= shape[i];
+  }
+  *numel = n;
+  return true;
+}
+
+// Byte span [lo, hi) that a strided tensor touches (only meaningful when numel > 0).
+void span_bytes(const void* base, int rank, const int64_t* shape, const int64_t* st, size_t elem,
+                uintptr_t* lo, uintptr_t* hi) {
+  int64_t mn = 0, mx = 0;
+  for (int i = 0; i < rank; ++i) {
+    const int64_t e = (shape[i] - 1) * st[i];
+    if (e < 0) mn += e; else mx += e;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+  *lo = b + uintptr_t(mn * int64_t(elem));
+  *hi = b + uintptr_t((mx + 1) * int64_t(elem));
+}
+
+bool overlaps(uintptr_t alo, uintptr_t ahi, uintptr_t blo, uintptr_t bhi) { return alo < bhi && blo < ahi; }
+
+// Builds an IndexMap from per-dimension sizes and strides, dropping size-1
+// dims and merging neighbours whose strides nest for every tensor.
+template <int NT>
+sx::IndexMap<NT> make_index_map(int nd, const int64_t* dims, const int64_t (*st)[sx::kMaxRank]) {
+  sx::IndexMap<NT> m{};
+  int k = 0;
+  for (int d = 0; d < nd; ++d) {
+    if (dims[d] == 1) continue;
+    bool merge = k > 0;
+    for (int t = 0; t < NT && merge; ++t) merge = st[t][d] * dims[d] == m.st[t][k - 1];
+    if (merge) {
+      m.dim[k - 1] *= dims[d];
+      for (int t = 0; t < NT; ++t) m.st[t][k - 1] = st[t][d];
+    } else {
+      m.dim[k] = dims[d];
+      for (int t = 0; t < NT; ++t) m.st[t][k] = st[t][d];
+      ++k;
+    }
+  }
+  if (k == 0) {
+    m.dim[0] = 1;
+    for (int t = 0; t < NT; ++t) m.st[t][0] = 0;
+    k = 1;
+  }
+  m.nd = k;
+  return m;
+}
+
+sx_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SX_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------ element-scan validation
+
+struct EsPlan {
+  sx::EsParams p;
+  int64_t numel;
+};
+
+sx_status plan_element_scan(sx_body body, int rank, const int64_t* shape, int axis, int state_axis,
+                            const int64_t* initial_strides, int64_t x_width, const int64_t* x_strides,
+                            int64_t s_width, const int64_t* s_strides, EsPlan* plan) {
+  if (body != SX_BODY_TANH_AFFINE && body != SX_BODY_NORM_CAP && body != SX_BODY_MAX_PLUS)
+    return fail(SX_E_UNSUPPORTED, "element-scan: unknown body %d", int(body));
+  if (rank > sx::kMaxRank) return fail(SX_E_UNSUPPORTED, "element-scan: rank %d exceeds %d", rank, sx::kMaxRank);
+  if (rank < 1 || shape == nullptr) return fail(SX_E_DIM_001, "element-scan: sequences need at least one axis");
+  int64_t numel = 0;
+  if (!checked_numel(rank, shape, &numel))
+    return fail(SX_E_DIM_001, "element-scan: bad sequence shape %s", shape_str(rank, shape).c_str());
+  const int ax = axis < 0 ? axis + rank : axis;
+  if (ax < 0 || ax >= rank)
+    return fail(SX_E_DIM_001, "element-scan: axis %d out of range for sequences %s f32", axis,
+                shape_str(rank, shape).c_str());
+  const bool vec = state_axis != SX_STATE_SCALAR;
+  if (vec && state_axis != -1 && state_axis != rank - 1)
+    return fail(SX_E_DIM_001, "element-scan: :state-axis %d is not the last axis of %s", state_axis,
+                shape_str(rank, shape).c_str());
+  if (!vec && body == SX_BODY_NORM_CAP)
+    return fail(SX_E_DIM_001, "element-scan: the norm-cap body reduces over the state, so it needs :state-axis -1");
+  int64_t n = 1;
+  if (vec) {
+    if (rank < 2 || ax == rank - 1)
+      return fail(SX_E_DIM_001, "element-scan: :axis %d is the state axis of %s", axis, shape_str(rank, shape).c_str());
+    n = shape[rank - 1];
+    if (n < 1 || n > SX_MAX_N)
+      return fail(SX_E_DIM_001, "element-scan: state width %lld is outside 1..16", (long long)n);
+    if (x_width != 1 && x_width != n)
+      return fail(SX_E_DIM_001, "element-scan: sequence x has width %lld, state width is %lld", (long long)x_width, (long long)n);
+    if (s_width != 1 && s_width != n)
+      return fail(SX_E_DIM_001, "element-scan: second sequence has width %lld, state width is %lld", (long long)s_width, (long long)n);
+  }
+  const int64_t T = shape[ax];
+  if (T < 1)
+    return fail(SX_E_DIM_001, "element-scan: axis %d of %s has length 0; it must be at least one", axis,
+                shape_str(rank, shape).c_str());
+
+  // Per-tensor shapes and strides (elements).
+  int64_t xs[sx::kMaxRank], ss[sx::kMaxRank], is[sx::kMaxRank], os[sx::kMaxRank];
+  int64_t xshape[sx::kMaxRank], sshape[sx::kMaxRank], ishape[sx::kMaxRank];
+  for (int i = 0; i < rank; ++i) xshape[i] = sshape[i] = shape[i];
+  if (vec) { xshape[rank - 1] = x_width; sshape[rank - 1] = s_width; }
+  for (int i = 0, j = 0; i < rank; ++i)
+    if (i != ax) ishape[j++] = shape[i];
+  if (x_strides) std::copy(x_strides, x_strides + rank, xs); else contiguous_strides(rank, xshape, xs);
+  if (s_strides) std::copy(s_strides, s_strides + rank, ss); else contiguous_strides(rank, sshape, ss);
+  if (initial_strides) std::copy(initial_strides, initial_strides + rank - 1, is); else contiguous_strides(rank - 1, ishape, is);
+  contiguous_strides(rank, shape, os);
+  if (vec) {  // a width-1 sequence broadcasts over the state vector
+    if (x_width == 1) xs[rank - 1] = 0;
+    if (s_width == 1) ss[rank - 1] = 0;
+  }
+
+  sx::EsParams& p = plan->p;
+  p = sx::EsParams{};
+  p.T = T;
+  p.t_stride[sx::ES_X] = xs[ax];
+  p.t_stride[sx::ES_S] = ss[ax];
+  p.t_stride[sx::ES_INIT] = 0;
+  p.t_stride[sx::ES_OUT] = os[ax];
+  p.n = body == SX_BODY_NORM_CAP ? int(n) : 1;
+  if (body == SX_BODY_NORM_CAP) {
+    p.n_stride[sx::ES_X] = xs[rank - 1];
+    p.n_stride[sx::ES_S] = ss[rank - 1];
+    p.n_stride[sx::ES_INIT] = is[rank - 2];
+    p.n_stride[sx::ES_OUT] = 1;
+  }
+  // Lane dims: every dim but the axis (and but the state axis for NORM_CAP).
+  const int lane_end = body == SX_BODY_NORM_CAP ? rank - 1 : rank;
+  int64_t dims[sx::kMaxRank];
+  int64_t st[4][sx::kMaxRank];
+  int nd = 0;
+  for (int i = 0; i < lane_end; ++i) {
+    if (i == ax) continue;
+    dims[nd] = shape[i];
+    st[sx::ES_X][nd] = xs[i];
+    st[sx::ES_S][nd] = ss[i];
+    st[sx::ES_INIT][nd] = is[i < ax ? i : i - 1];
+    st[sx::ES_OUT][nd] = os[i];
+    ++nd;
+  }
+  p.lanes = make_index_map<4>(nd, dims, st);
+  p.num_lanes = numel / T / (body == SX_BODY_NORM_CAP ? n : 1);
+  plan->numel = numel;
+
+  // Spans for the alias check are computed by the caller once the pointers are known.
+  (void)xshape;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sx_status_name(sx_status status) {
+  switch (status) {
+    case SX_OK: return "OK";
+    case SX_E_DIM_001: return "E-DIM-001";
+    case SX_E_DIM_002: return "E-DIM-002";
+    case SX_E_DIM_003: return "E-DIM-003";
+    case SX_E_UNSUPPORTED: return "E-UNSUPPORTED";
+    case SX_E_ALIAS: return "E-ALIAS";
+    case SX_E_WORKSPACE: return "E-WORKSPACE";
+    case SX_E_DEVICE: return "E-DEVICE";
+  }
+  return "E-UNKNOWN";
+}
+
+const char* sx_last_error(void) { return g_last_error.c_str(); }
+
+const char* sx_version(void) { return "sx_scan 0.1 gfx950"; }
+
+size_t sx_element_scan_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis, int state_axis) {
+  EsPlan plan;
+  const int64_t w = 1;
+  if (plan_element_scan(body, rank, shape, axis, state_axis, nullptr, w, nullptr, w, nullptr, &plan) != SX_OK)
+    return 0;
+  return sx::element_scan_workspace(body, plan.p);
+}
+
+sx_status sx_element_scan(sx_body body, int rank, const int64_t* shape, int axis, int state_axis, int reverse,
+                          const float* initial, const int64_t* initial_strides, const float* x, int64_t x_width,
+                          const int64_t* x_strides, const float* s, int64_t s_width, const int64_t* s_strides,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  EsPlan plan;
+  sx_status st = plan_element_scan(body, rank, shape, axis, state_axis, initial_strides, x_width, x_strides,
+                                   s_width, s_strides, &plan);
+  if (st != SX_OK) return st;
+  if (plan.numel == 0) return ok();
+  if (!x) return fail(SX_E_DIM_003, "element-scan: sequence x is NULL; a tensor was expected");
+  if (!s) return fail(SX_E_DIM_003, "element-scan: the second sequence is NULL; a tensor was expected");
+  if (!initial) return fail(SX_E_DIM_003, "element-scan: initial is NULL; a tensor was expected");
+  if (!out) return fail(SX_E_DIM_003, "element-scan: out is NULL; a tensor was expected");
+
+  // Alias check: out is contiguous over the output shape.
+  const bool vec = state_axis != SX_STATE_SCALAR;
+  int64_t xshape[sx::kMaxRank], sshape[sx::kMaxRank], ishape[sx::kMaxRank];
+  int64_t xs[sx::kMaxRank], ss[sx::kMaxRank], is[sx::kMaxRank];
+  const int ax = axis < 0 ? axis + rank : axis;
+  for (int i = 0; i < rank; ++i) xshape[i] = sshape[i] = shape[i];
+  if (vec) { xshape[rank - 1] = x_width; sshape[rank - 1] = s_width; }
+  for (int i = 0, j = 0; i < rank; ++i)
+    if (i != ax) ishape[j++] = shape[i];
+  if (x_strides) std::copy(x_strides, x_strides + rank, xs); else contiguous_strides(rank, xshape, xs);
+  if (s_strides) std::copy(s_strides, s_strides + rank, ss); else contiguous_strides(rank, sshape, ss);
+  if (initial_strides) std::copy(initial_strides, initial_strides + rank - 1, is); else contiguous_strides(rank - 1, ishape, is);
+  uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + uintptr_t(plan.numel) * sizeof(float);
+  uintptr_t lo, hi;
+  span_bytes(x, rank, xshape, xs, sizeof(float), &lo, &hi);
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "element-scan: out overlaps sequence x");
+  span_bytes(s, rank, sshape, ss, sizeof(float), &lo, &hi);
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "element-scan: out overlaps the second sequence");
+  span_bytes(initial, rank - 1, ishape, is, sizeof(float), &lo, &hi);
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "element-scan: out overlaps initial");
+
+  const size_t need = sx::element_scan_workspace(body, plan.p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SX_E_WORKSPACE, "element-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+
+  plan.p.reverse = reverse ? 1 : 0;
+  plan.p.x = x;
+  plan.p.s = s;
+  plan.p.init = initial;
+  plan.p.out = out;
+  return device_status(sx::launch_element_scan(body, plan.p, static_cast<hipStream_t>(stream)),
+                       "element-scan launch");
+}
+
+// ------------------------------------------------------------------ matrix-scan
+
+static sx_status plan_matrix_scan(int a_rank, const int64_t* a_shape, const int64_t* a_strides, int b_rank,
+                                  const int64_t* b_shape, const int64_t* b_strides, int axis, sx::MsParams* p,
+                                  int64_t* out_shape, int* out_rank, int64_t* out_numel) {
+  if (a_rank > sx::kMaxRank || b_rank > sx::kMaxRank)
+    return fail(SX_E_UNSUPPORTED, "matrix-scan: rank above %d", sx::kMaxRank);
+  if (!a_shape || !b_shape || a_rank < 2 || b_rank < 2)
+    return fail(SX_E_DIM_001, "matrix-scan: a must be [.., n, n] and b [.., n, m]");
+  int64_t tmp;
+  if (!checked_numel(a_rank, a_shape, &tmp) || !checked_numel(b_rank, b_shape, &tmp))
+    return fail(SX_E_DIM_001, "matrix-scan: negative or oversized dims in a %s, b %s",
+                shape_str(a_rank, a_shape).c_str(), shape_str(b_rank, b_shape).c_str());
+  const int64_t n = a_shape[a_rank - 1];
+  if (a_shape[a_rank - 2] != n)
+    return fail(SX_E_DIM_001, "matrix-scan: a %s is not square", shape_str(a_rank, a_shape).c_str());
+  if (b_shape[b_rank - 2] != n)
+    return fail(SX_E_DIM_001, "matrix-scan: inner dims differ: a %s, b %s", shape_str(a_rank, a_shape).c_str(),
+                shape_str(b_rank, b_shape).c_str());
+  if (n > SX_MAX_N)
+    return fail(SX_E_DIM_001, "matrix-scan: n = %lld, at most 16 allowed (a %s)", (long long)n,
+                shape_str(a_rank, a_shape).c_str());
+  const int64_t m = b_shape[b_rank - 1];
+  const int la = a_rank - 2, lb = b_rank - 2, L = std::max(la, lb);
+  if (L < 1)
+    return fail(SX_E_DIM_001, "matrix-scan: no leading dim to scan along (a %s, b %s)",
+                shape_str(a_rank, a_shape).c_str(), shape_str(b_rank, b_shape).c_str());
+  if (L + 2 > sx::kMaxRank) return fail(SX_E_UNSUPPORTED, "matrix-scan: result rank above %d", sx::kMaxRank);
+  int64_t lead[sx::kMaxRank], sa[sx::kMaxRank], sb[sx::kMaxRank];
+  int64_t ast[sx::kMaxRank], bst[sx::kMaxRank];
+  if (a_strides) std::copy(a_strides, a_strides + a_rank, ast); else contiguous_strides(a_rank, a_shape, ast);
+  if (b_strides) std::copy(b_strides, b_strides + b_rank, bst); else contiguous_strides(b_rank, b_shape, bst);
+  for (int i = 0; i < L; ++i) {
+    const int ia = i - (L - la), ib = i - (L - lb);
+    const int64_t da = ia >= 0 ? a_shape[ia] : 1, db = ib >= 0 ? b_shape[ib] : 1;
+    if (da != db && da != 1 && db != 1)
+      return fail(SX_E_DIM_001, "matrix-scan: leading dims of a %s and b %s do not broadcast",
+                  shape_str(a_rank, a_shape).c_str(), shape_str(b_rank, b_shape).c_str());
+    lead[i] = da == 1 ? db : da;
+    sa[i] = (ia >= 0 && da != 1) ? ast[ia] : 0;
+    sb[i] = (ib >= 0 && db != 1) ? bst[ib] : 0;
+  }
+  const int ax = axis < 0 ? axis + L : axis;
+  if (ax < 0 || ax >= L)
+    return fail(SX_E_DIM_001, "matrix-scan: axis %d out of range for leading dims %s", axis,
+                shape_str(L, lead).c_str());
+  if ((n > 1 && (ast[a_rank - 1] != 1 || ast[a_rank - 2] != n)) ||
+      (m > 1 && bst[b_rank - 1] != 1) || (n > 1 && m > 0 && bst[b_rank - 2] != m))
+    return fail(SX_E_UNSUPPORTED, "matrix-scan: the matrix dims of a and b must be row-major contiguous");
+
+  for (int i = 0; i < L; ++i) out_shape[i] = lead[i];
+  out_shape[L] = n;
+  out_shape[L + 1] = m;
+  *out_rank = L + 2;
+  int64_t numel = 0;
+  if (!checked_numel(L + 2, out_shape, &numel)) return fail(SX_E_DIM_001, "matrix-scan: result too large");
+  *out_numel = numel;
+  if (!p) return ok();
+
+  int64_t ost[sx::kMaxRank + 2];
+  contiguous_strides(L + 2, out_shape, ost);
+  *p = sx::MsParams{};
+  p->T = lead[ax];
+  p->t_stride[sx::MS_A] = sa[ax];
+  p->t_stride[sx::MS_B] = sb[ax];
+  p->t_stride[sx::MS_OUT] = ost[ax];
+  p->n = int(n);
+  p->m = int(m);
+  int64_t dims[sx::kMaxRank];
+  int64_t st[3][sx::kMaxRank];
+  int nd = 0;
+  for (int i = 0; i < L; ++i) {
+    if (i == ax) continue;
+    dims[nd] = lead[i];
+    st[sx::MS_A][nd] = sa[i];
+    st[sx::MS_B][nd] = sb[i];
+    st[sx::MS_OUT][nd] = ost[i];
+    ++nd;
+  }
+  p->batch = make_index_map<3>(nd, dims, st);
+  p->num_batch = p->T > 0 ? numel / (p->T * std::max<int64_t>(n * m, 1)) : 0;
+  if (n * m == 0) p->num_batch = 0;
+  return ok();
+}
+
+int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                             int64_t* out_shape) {
+  int64_t shp[sx::kMaxRank + 2];
+  int r = 0;
+  int64_t numel = 0;
+  if (plan_matrix_scan(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, -1, nullptr, shp, &r, &numel) != SX_OK)
+    return -1;
+  if (out_shape) std::copy(shp, shp + r, out_shape);
+  return r;
+}
+
+size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                                      int axis) {
+  sx::MsParams p;
+  int64_t shp[sx::kMaxRank + 2];
+  int r = 0;
+  int64_t numel = 0;
+  if (plan_matrix_scan(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, &p, shp, &r, &numel) != SX_OK)
+    return 0;
+  if (numel == 0) return 0;
+  return sx::matrix_scan_workspace(p);
+}
+
+sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides, const void* a,
+                         int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b, int axis,
+                         int reverse, int projective, sx_dtype out_dtype, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (dtype != SX_F32 && dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "matrix-scan: a and b must be f32 or bf16 (dtype code %d)", int(dtype));
+  if (out_dtype != SX_F32 && out_dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "matrix-scan: out must be f32 or bf16 (dtype code %d)", int(out_dtype));
+  sx::MsParams p;
+  int64_t shp[sx::kMaxRank + 2];
+  int r = 0;
+  int64_t numel = 0;
+  sx_status st = plan_matrix_scan(a_rank, a_shape, a_strides, b_rank, b_shape, b_strides, axis, &p, shp, &r, &numel);
+  if (st != SX_OK) return st;
+  if (projective)
+    return fail(SX_E_UNSUPPORTED, "matrix-scan: :projective true is not provided by this library");
+  if (numel == 0) return ok();
+  if (!a) return fail(SX_E_DIM_003, "matrix-scan: a %s %s is NULL; a tensor was expected",
+                      shape_str(a_rank, a_shape).c_str(), dtype_name(dtype));
+  if (!b) return fail(SX_E_DIM_003, "matrix-scan: b %s %s is NULL; a tensor was expected",
+                      shape_str(b_rank, b_shape).c_str(), dtype_name(dtype));
+  if (!out) return fail(SX_E_DIM_003, "matrix-scan: out is NULL; a tensor was expected");
+
+  const size_t esz = dtype == SX_BF16 ? 2 : 4, osz = out_dtype == SX_BF16 ? 2 : 4;
+  int64_t ast[sx::kMaxRank], bst[sx::kMaxRank];
+  if (a_strides) std::copy(a_strides, a_strides + a_rank, ast); else contiguous_strides(a_rank, a_shape, ast);
+  if (b_strides) std::copy(b_strides, b_strides + b_rank, bst); else contiguous_strides(b_rank, b_shape, bst);
+  uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + uintptr_t(numel) * osz, lo, hi;
+  int64_t anumel = 0, bnumel = 0;
+  checked_numel(a_rank, a_shape, &anumel);
+  checked_numel(b_rank, b_shape, &bnumel);
+  if (anumel > 0) {
+    span_bytes(a, a_rank, a_shape, ast, esz, &lo, &hi);
+    if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "matrix-scan: out overlaps a");
+  }
+  if (bnumel > 0) {
+    span_bytes(b, b_rank, b_shape, bst, esz, &lo, &hi);
+    if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "matrix-scan: out overlaps b");
+  }
+  const size_t need = sx::matrix_scan_workspace(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SX_E_WORKSPACE, "matrix-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SX_E_WORKSPACE, "matrix-scan: workspace must be 256-byte aligned");
+
+  p.in_bf16 = dtype == SX_BF16;
+  p.out_bf16 = out_dtype == SX_BF16;
+  p.reverse = reverse ? 1 : 0;
+  p.a = a;
+  p.b = b;
+  p.out = out;
+  return device_status(sx::launch_matrix_scan(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                       "matrix-scan launch");
+}
+
+}  // extern "C"

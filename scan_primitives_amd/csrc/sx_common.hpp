@@ -1,0 +1,95 @@
+// sx_common.hpp: descriptors and small device helpers shared by the host
+// dispatch (sx_api.cpp) and the kernels (element_scan.hip, matrix_scan.hip).
+// Internal to libsx_scan.so; the public interface is include/sx_scan.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sx_scan.h"
+
+namespace sx {
+
+constexpr int kMaxRank = SX_MAX_RANK;
+constexpr int kWave = 64;
+
+// Maps a flat lane (or batch) index to one element offset per tensor.
+// Dimensions are row-major: the last one varies fastest, so consecutive
+// lanes walk the innermost dimension and loads coalesce when it is
+// contiguous. The host merges dimensions whose strides allow it, so the
+// device loop below usually runs once or twice.
+template <int NT>
+struct IndexMap {
+  int nd;
+  int64_t dim[kMaxRank];
+  int64_t st[NT][kMaxRank];
+};
+
+template <int NT>
+__device__ __forceinline__ void index_offsets(const IndexMap<NT>& m, int64_t idx, int64_t (&off)[NT]) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k) off[k] = 0;
+  for (int d = m.nd - 1; d >= 0; --d) {
+    const int64_t dd = m.dim[d];
+    const int64_t i = dd == 1 ? 0 : idx % dd;
+    idx = dd == 1 ? idx : idx / dd;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) off[k] += i * m.st[k][d];
+  }
+}
+
+// ---------------------------------------------------------------- element-scan
+
+enum EsTensor { ES_X = 0, ES_S = 1, ES_INIT = 2, ES_OUT = 3 };
+
+struct EsParams {
+  IndexMap<4> lanes;     // lane -> offsets of x, s, initial, out
+  int64_t num_lanes;     // lanes (for NORM_CAP: state vectors, each of n values)
+  int64_t T;             // trips along the scan axis (>= 1)
+  int64_t t_stride[4];   // stride along the scan axis (initial: 0)
+  int64_t n_stride[4];   // stride along the state axis (NORM_CAP only; 0 for width-1 sequences)
+  int n;                 // state width for NORM_CAP, 1 otherwise
+  int reverse;
+  const float* x;
+  const float* s;
+  const float* init;
+  float* out;
+};
+
+hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream);
+size_t element_scan_workspace(sx_body body, const EsParams& p);
+
+// ---------------------------------------------------------------- matrix-scan
+
+enum MsTensor { MS_A = 0, MS_B = 1, MS_OUT = 2 };
+
+struct MsParams {
+  IndexMap<3> batch;     // batch index (every leading index but the axis) -> offsets of a, b, out
+  int64_t num_batch;
+  int64_t T;             // steps along the axis (>= 1)
+  int64_t t_stride[3];   // element stride of one step along the axis for a, b, out
+  int n, m;              // a is n x n, b and out n x m; matrix dims are row-major contiguous
+  int in_bf16;           // a and b are bf16 (else f32)
+  int out_bf16;          // out is bf16 (else f32)
+  int reverse;
+  const void* a;
+  const void* b;
+  void* out;
+};
+
+hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t matrix_scan_workspace(const MsParams& p);
+
+// ---------------------------------------------------------------- bf16 helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// Round to nearest, ties to even. NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+}  // namespace sx

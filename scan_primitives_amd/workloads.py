@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for element-scan and matrix-scan.
+
+This module only draws random numbers (torch CPU generators, fixed seeds);
+it holds none of the scans' arithmetic. Tests, the bench and the smoke check
+build their inputs here and hand the same host tensors to the HIP library
+and to the CPU oracle.
+
+The five standard workloads follow the sizes and distributions below; the
+``make_*`` functions take other sizes for the parity tests.
+
+  tanh-affine       x [4,64,32] ~ N(0,1), decay [4,64,32] ~ U(0,1),
+                    initial [4,32] ~ N(0,1), axis 1, forward
+  norm-cap          x [8,1024,16,16] ~ N(0,1), decay [8,1024,16,1] ~ U(0.8,1),
+                    initial zeros [8,16,16], axis 1, state axis -1, forward
+  max-plus          x [64,4096,256] ~ N(0,1), cost [64,4096,256] ~ U(0,0.1),
+                    initial [64,256] ~ N(0,1), axis 1, reverse
+  matrix f32        a [32,8192,16,16] = 0.9 I + 0.01 N(0,1),
+                    b [32,8192,16,1] ~ N(0,1), f32, axis 1, forward
+  matrix bf16       a [16,16384,16,16] = 0.9 I + 0.01 N(0,1),
+                    b [16,16384,16,16] ~ N(0,1), drawn in f32 and rounded to
+                    bf16 (nearest even), axis 1, reverse
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass
+class Workload:
+    name: str
+    op: str                      # "element_scan" or "matrix_scan"
+    tensors: dict                # host tensors, in the order the op takes them
+    axis: int = 1
+    reverse: bool = False
+    body: str | None = None      # element-scan body
+    state_axis: int | None = None
+    out_dtype: torch.dtype | None = None
+    meta: dict = field(default_factory=dict)
+
+    def on(self, device) -> dict:
+        return {k: v.to(device) for k, v in self.tensors.items()}
+
+    @property
+    def out_shape(self) -> tuple:
+        t = self.tensors
+        if self.op == "element_scan":
+            x = t["x"]
+            if self.state_axis is None:
+                return tuple(x.shape)
+            return tuple(x.shape[:-1]) + (t["initial"].shape[-1],)
+        lead = torch.broadcast_shapes(t["a"].shape[:-2], t["b"].shape[:-2])
+        return tuple(lead) + tuple(t["b"].shape[-2:])
+
+    @property
+    def out_numel(self) -> int:
+        n = 1
+        for d in self.out_shape:
+            n *= d
+        return n
+
+    @property
+    def out_elem_bytes(self) -> int:
+        if self.op == "element_scan":
+            return 4
+        dt = self.out_dtype or self.tensors["b"].dtype
+        return torch.tensor([], dtype=dt).element_size()
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes the method must move: every input read once, the output written once."""
+        ins = sum(v.numel() * v.element_size() for v in self.tensors.values())
+        return ins + self.out_numel * self.out_elem_bytes
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator().manual_seed(seed)
+
+
+def make_tanh(shape=(4, 64, 32), axis=1, reverse=False, seed=1) -> Workload:
+    g = _gen(seed)
+    x = torch.randn(shape, generator=g)
+    decay = torch.rand(shape, generator=g)
+    ax = axis % len(shape)
+    initial = torch.randn(shape[:ax] + shape[ax + 1:], generator=g)
+    return Workload(f"tanh-affine {list(shape)} axis {axis}{' reverse' if reverse else ''}", "element_scan",
+                    {"initial": initial, "x": x, "s": decay}, axis=axis, reverse=reverse, body="tanh_affine")
+
+
+def make_norm_cap(B=8, T=1024, H=16, n=16, gate_width=1, axis=1, reverse=False, seed=2,
+                  zero_initial=True, x_scale=1.0) -> Workload:
+    g = _gen(seed)
+    x = x_scale * torch.randn((B, T, H, n), generator=g)
+    decay = 0.8 + 0.2 * torch.rand((B, T, H, gate_width), generator=g)
+    initial = torch.zeros((B, H, n)) if zero_initial else torch.randn((B, H, n), generator=g)
+    return Workload(f"norm-cap [{B},{T},{H},{n}] gate width {gate_width}{' reverse' if reverse else ''}",
+                    "element_scan", {"initial": initial, "x": x, "s": decay}, axis=axis, reverse=reverse,
+                    body="norm_cap", state_axis=-1)
+
+
+def make_max_plus(shape=(64, 4096, 256), axis=1, reverse=True, seed=3) -> Workload:
+    g = _gen(seed)
+    x = torch.randn(shape, generator=g)
+    cost = 0.1 * torch.rand(shape, generator=g)
+    ax = axis % len(shape)
+    initial = torch.randn(shape[:ax] + shape[ax + 1:], generator=g)
+    return Workload(f"max-plus {list(shape)} axis {axis}{' reverse' if reverse else ''}", "element_scan",
+                    {"initial": initial, "x": x, "s": cost}, axis=axis, reverse=reverse, body="max_plus")
+
+
+def make_matrix(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, reverse=False, seed=4,
+                noise=0.01, out_dtype=None) -> Workload:
+    g = _gen(seed)
+    eye = torch.eye(n)
+    a = 0.9 * eye + noise * torch.randn((B, T, n, n), generator=g)
+    b = torch.randn((B, T, n, m), generator=g)
+    a, b = a.to(dtype), b.to(dtype)
+    name = f"matrix-scan {str(dtype).replace('torch.', '')} [{B},{T}] n={n} m={m}{' reverse' if reverse else ''}"
+    return Workload(name, "matrix_scan", {"a": a, "b": b}, axis=axis, reverse=reverse, out_dtype=out_dtype)
+
+
+def standard_workloads(which=None) -> list[Workload]:
+    """The five standard workloads, in order (or those whose index is in ``which``)."""
+    makers = [
+        lambda: make_tanh(),
+        lambda: make_norm_cap(),
+        lambda: make_max_plus(),
+        lambda: make_matrix(32, 8192, 16, 1, torch.float32, reverse=False, seed=4),
+        lambda: make_matrix(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5),
+    ]
+    idx = range(len(makers)) if which is None else which
+    return [makers[i]() for i in idx]
+

@@ -1,0 +1,200 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before any device work.
+
+No call here passes arguments the library would accept, so nothing reaches
+the GPU (there is none in the build container).
+"""
+
+import ctypes
+import pathlib
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import scan_primitives_amd as sx
+from scan_primitives_amd import _binding as B
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "sx_scan.h"
+
+FAKE = 1 << 40  # a plausible device address; never dereferenced by a rejected call
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for required in ("sx_element_scan", "sx_matrix_scan", "sx_element_scan_workspace_bytes",
+                     "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_status_name",
+                     "sx_last_error", "sx_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in sx_scan.h but not exported"
+
+
+def test_status_names_and_version(lib):
+    assert lib.sx_status_name(0) == b"OK"
+    assert lib.sx_status_name(1) == b"E-DIM-001"
+    assert lib.sx_status_name(2) == b"E-DIM-002"
+    assert lib.sx_status_name(3) == b"E-DIM-003"
+    assert b"gfx950" in lib.sx_version()
+
+
+def _es(lib, body=2, shape=(4, 8, 3), axis=1, state_axis=B.SX_STATE_SCALAR, x=FAKE, s=FAKE + 4096,
+        init=FAKE + 8192, out=FAKE + (1 << 20), x_width=None, s_width=None, rank=None):
+    shape = list(shape)
+    r = len(shape) if rank is None else rank
+    xw = (shape[-1] if shape else 1) if x_width is None else x_width
+    sw = (shape[-1] if shape else 1) if s_width is None else s_width
+    st = lib.sx_element_scan(body, r, B.i64_array(shape), axis, state_axis, 0, init, None, x, xw, None, s, sw,
+                             None, out, None, 0, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(axis=3), B.SX_E_DIM_001),
+    (dict(axis=-4), B.SX_E_DIM_001),
+    (dict(shape=(4, 0, 3)), B.SX_E_DIM_001),                        # empty scan axis
+    (dict(body=1), B.SX_E_DIM_001),                                 # norm-cap needs a vector state
+    (dict(body=1, shape=(2, 5, 17), state_axis=-1), B.SX_E_DIM_001),  # state width above 16
+    (dict(body=1, shape=(2, 5, 16), state_axis=-1, x_width=3), B.SX_E_DIM_001),
+    (dict(body=1, shape=(2, 5, 16), state_axis=-1, s_width=4), B.SX_E_DIM_001),
+    (dict(body=1, shape=(2, 5, 16), state_axis=0), B.SX_E_DIM_001),    # only the last axis is a state axis
+    (dict(body=1, shape=(2, 5, 16), state_axis=-1, axis=2), B.SX_E_DIM_001),  # axis is the state axis
+    (dict(x=None), B.SX_E_DIM_003),
+    (dict(s=None), B.SX_E_DIM_003),
+    (dict(init=None), B.SX_E_DIM_003),
+    (dict(out=None), B.SX_E_DIM_003),
+    (dict(out=FAKE + 16), B.SX_E_ALIAS),                            # out overlaps x
+    (dict(body=9), B.SX_E_UNSUPPORTED),
+    (dict(shape=(1,) * 9), B.SX_E_UNSUPPORTED),
+    (dict(shape=(), rank=0), B.SX_E_DIM_001),
+])
+def test_element_scan_rejects_on_host(lib, kwargs, code):
+    st, msg = _es(lib, **kwargs)
+    assert st == code, (st, msg)
+    assert msg.startswith(f"error[{B._STATUS_NAMES[code]}]")
+
+
+def test_element_scan_error_message_names_shapes(lib):
+    st, msg = _es(lib, axis=5)
+    assert "[4, 8, 3]" in msg and "axis 5" in msg
+
+
+def test_element_scan_zero_lanes_is_a_no_op(lib):
+    # [0, 6, 3] along axis 1 has no lanes: nothing to launch, nothing to check on the device
+    st, _ = _es(lib, shape=(0, 6, 3), x=None, s=None, init=None, out=None)
+    assert st == B.SX_OK
+
+
+def test_element_scan_workspace_query(lib):
+    assert lib.sx_element_scan_workspace_bytes(2, 3, B.i64_array([4, 8, 3]), 1, B.SX_STATE_SCALAR) >= 0
+    assert lib.sx_element_scan_workspace_bytes(2, 3, B.i64_array([4, 8, 3]), 7, B.SX_STATE_SCALAR) == 0
+
+
+def _ms(lib, a_shape=(2, 5, 4, 4), b_shape=(2, 5, 4, 3), dtype=B.SX_F32, out_dtype=B.SX_F32, axis=1, projective=0,
+        a=FAKE, b=FAKE + (1 << 20), out=FAKE + (1 << 22), a_strides=None):
+    st = lib.sx_matrix_scan(dtype, len(a_shape), B.i64_array(a_shape),
+                            B.i64_array(a_strides) if a_strides else None, a, len(b_shape), B.i64_array(b_shape),
+                            None, b, axis, 0, projective, out_dtype, out, None, 0, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(a_shape=(2, 5, 17, 17), b_shape=(2, 5, 17, 1)), B.SX_E_DIM_001),  # n above 16
+    (dict(a_shape=(2, 5, 4, 3)), B.SX_E_DIM_001),                           # a not square
+    (dict(b_shape=(2, 5, 5, 3)), B.SX_E_DIM_001),                           # inner dims differ
+    (dict(b_shape=(3, 5, 4, 3)), B.SX_E_DIM_001),                           # leading dims do not broadcast
+    (dict(axis=2), B.SX_E_DIM_001),
+    (dict(axis=-3), B.SX_E_DIM_001),
+    (dict(a_shape=(4, 4), b_shape=(4, 3)), B.SX_E_DIM_001),                 # no leading dim to scan
+    (dict(dtype=5), B.SX_E_DIM_002),
+    (dict(out_dtype=3), B.SX_E_DIM_002),
+    (dict(a=None), B.SX_E_DIM_003),
+    (dict(b=None), B.SX_E_DIM_003),
+    (dict(out=None), B.SX_E_DIM_003),
+    (dict(projective=1), B.SX_E_UNSUPPORTED),
+    (dict(a_strides=(80, 16, 1, 4)), B.SX_E_UNSUPPORTED),                    # transposed matrix dims
+    (dict(out=FAKE + 64), B.SX_E_ALIAS),
+])
+def test_matrix_scan_rejects_on_host(lib, kwargs, code):
+    st, msg = _ms(lib, **kwargs)
+    assert st == code, (st, msg)
+
+
+def test_matrix_scan_empty_is_a_no_op(lib):
+    st, _ = _ms(lib, a_shape=(2, 0, 4, 4), b_shape=(2, 0, 4, 3), a=None, b=None, out=None)
+    assert st == B.SX_OK
+
+
+def test_matrix_scan_out_shape_broadcasts(lib):
+    out = B.i64_array([0] * 10)
+    r = lib.sx_matrix_scan_out_shape(3, B.i64_array([7, 4, 4]), 4, B.i64_array([2, 7, 4, 3]), out)
+    assert r == 4 and list(out[:4]) == [2, 7, 4, 3]
+    r = lib.sx_matrix_scan_out_shape(4, B.i64_array([3, 1, 4, 4]), 3, B.i64_array([5, 4, 1]), out)
+    assert r == 4 and list(out[:4]) == [3, 5, 4, 1]
+    assert lib.sx_matrix_scan_out_shape(3, B.i64_array([2, 4, 4]), 3, B.i64_array([3, 4, 1]), out) == -1
+
+
+def test_matrix_scan_workspace_query_is_host_only(lib):
+    ws = lib.sx_matrix_scan_workspace_bytes(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1)
+    assert ws >= 0
+    assert lib.sx_matrix_scan_workspace_bytes(3, B.i64_array([2, 4, 4]), 3, B.i64_array([2, 5, 1]), 0) == 0
+
+
+def test_binding_refuses_host_tensors_and_bad_dtypes():
+    x = torch.zeros(2, 3, 4)
+    with pytest.raises(sx.SxError) as e:
+        sx.element_scan("max_plus", torch.zeros(2, 4), [x, x], axis=1)
+    assert e.value.name == "E-UNSUPPORTED"
+    with pytest.raises(sx.SxError) as e:
+        sx.matrix_scan(torch.zeros(2, 3, 3), torch.zeros(2, 3, 1, dtype=torch.float64))
+    assert e.value.code in (B.SX_E_UNSUPPORTED, B.SX_E_DIM_002)
+    with pytest.raises(sx.SxError):
+        sx.element_scan("no_such_body", torch.zeros(2, 4), [x, x])
+    with pytest.raises(sx.SxError) as e:
+        sx.element_scan("max_plus", torch.zeros(2, 4), [x, x, x], axis=1)
+    assert e.value.name == "E-DIM-001"
+
+
+def test_workloads_describe_the_standard_configurations():
+    from scan_primitives_amd import workloads as W
+    w = W.make_tanh()
+    assert w.out_shape == (4, 64, 32) and w.algorithmic_bytes == 98816
+    w = W.make_norm_cap(B=2, T=8)
+    assert w.out_shape == (2, 8, 16, 16)
+    w = W.make_matrix(2, 8, 16, 16, torch.bfloat16)
+    assert w.tensors["a"].dtype == torch.bfloat16
+    # the draws are seeded: the same call gives the same tensors
+    assert torch.equal(W.make_tanh().tensors["x"], W.make_tanh().tensors["x"])
+    np.testing.assert_array_equal(W.make_max_plus((2, 8, 4)).tensors["s"].numpy() >= 0, True)
+
+
+def test_algorithmic_bytes_of_the_large_workloads():
+    # full sizes, computed from shapes alone (no tensors are drawn here)
+    sizes = {
+        "norm-cap": (8 * 1024 * 16 * 16 * 4 * 2 + 8 * 1024 * 16 * 4 + 8 * 16 * 16 * 4, 17309696),
+        "max-plus": (64 * 4096 * 256 * 4 * 3 + 64 * 256 * 4, 805371904),
+        "matrix f32": (32 * 8192 * (256 + 16 + 16) * 4, 301989888),
+        "matrix bf16": (16 * 16384 * (256 + 256 + 256) * 2, 402653184),
+    }
+    for name, (got, want) in sizes.items():
+        assert got == want, name
+
+
+def test_fake_pointer_constant_is_not_null():
+    assert ctypes.c_void_p(FAKE).value == FAKE

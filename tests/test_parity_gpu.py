@@ -1,0 +1,206 @@
+"""Parity of the HIP library with the CPU oracle, element by element.
+
+Every case draws seeded inputs from ``scan_primitives_amd.workloads``, runs
+the C ABI (through the Python binding) on the GPU and the float64 oracle on
+the CPU, and compares:
+
+* element-scan (f32): |gpu - ref| <= 1e-5 + 1e-5 |ref| for every element;
+* matrix-scan: ||gpu[t] - ref[t]||_F <= tol * max(||ref[t]||_F, the RMS state
+  norm of the same scan) for every state, tol = 1e-4 for f32 operands and
+  2e-2 for bf16 operands.
+
+Sizes span several tiles with a ragged tail; the five standard workloads run
+at full size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_primitives_amd as sx
+from scan_primitives_amd import workloads as W
+from tests.helpers import (MS_TOL_BF16, MS_TOL_F32, assert_element_close, assert_matrix_close, run_gpu,
+                           run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _announce(w):
+    print(f"\n[case] {w.name}", flush=True)
+
+
+# ------------------------------------------------------------------ element-scan
+
+
+@pytest.mark.parametrize("shape,axis,reverse", [
+    ((3, 37, 19), 1, False),
+    ((3, 37, 19), 1, True),
+    ((41, 5, 3), 0, False),
+    ((2, 3, 130), -1, True),
+    ((1, 1, 1), 1, False),
+    ((5, 1, 7), 1, True),
+    ((64,), 0, False),
+])
+def test_tanh_small(shape, axis, reverse):
+    w = W.make_tanh(shape, axis=axis, reverse=reverse, seed=100 + len(shape))
+    _announce(w)
+    assert_element_close(run_gpu(w, DEV), run_oracle(w))
+
+
+@pytest.mark.parametrize("shape,axis,reverse", [
+    ((3, 200, 19), 1, True),
+    ((3, 200, 19), 1, False),
+    ((257, 3, 5), 0, True),
+    ((2, 9, 1000), -1, False),
+])
+def test_max_plus_small(shape, axis, reverse):
+    w = W.make_max_plus(shape, axis=axis, reverse=reverse, seed=110)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert_element_close(got, run_oracle(w))
+
+
+@pytest.mark.parametrize("B,T,H,n,gate,reverse", [
+    (2, 45, 5, 16, 1, False),
+    (2, 45, 5, 16, 16, True),
+    (3, 33, 2, 5, 1, True),
+    (1, 70, 3, 1, 1, False),
+    (2, 17, 9, 16, 1, False),
+])
+def test_norm_cap_small(B, T, H, n, gate, reverse):
+    w = W.make_norm_cap(B, T, H, n, gate_width=gate, reverse=reverse, seed=120, zero_initial=False)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    ref = run_oracle(w)
+    assert_element_close(got, ref)
+    assert float(torch.linalg.vector_norm(got, dim=-1).max()) <= 1 + 1e-5
+
+
+def test_element_scan_strided_and_broadcast_operands():
+    # x as a transposed view, decay broadcast along the width (stride 0), initial non-contiguous
+    g = torch.Generator().manual_seed(130)
+    xt = torch.randn(19, 3, 50, generator=g)            # [width, batch, time]
+    x = xt.permute(1, 2, 0)                              # [3, 50, 19], strides (50, 1, 150)
+    decay = torch.rand(3, 50, 1, generator=g).expand(3, 50, 19)
+    init = torch.randn(19, 3, generator=g).t()           # [3, 19] transposed
+    ref = oracle.element_scan("tanh_affine", init.numpy(), [x.numpy(), decay.numpy()], axis=1)
+    got = sx.element_scan("tanh_affine", init.to(DEV), [x.to(DEV), decay.to(DEV)], axis=1)
+    assert_element_close(got, ref)
+
+
+def test_vector_state_elementwise_bodies():
+    g = torch.Generator().manual_seed(131)
+    x = torch.randn(4, 60, 3, 7, generator=g)
+    c = 0.1 * torch.rand(4, 60, 3, 1, generator=g)
+    init = torch.randn(4, 3, 7, generator=g)
+    for body in ("max_plus", "tanh_affine"):
+        ref = oracle.element_scan(body, init.numpy(), [x.numpy(), c.numpy()], axis=1, state_axis=-1, reverse=True)
+        got = sx.element_scan(body, init.to(DEV), [x.to(DEV), c.to(DEV)], axis=1, state_axis=-1, reverse=True)
+        assert_element_close(got, ref)
+
+
+def test_max_plus_matches_float32_serial_evaluation():
+    # Subtract and maximum are correctly rounded, so a float32 evaluation in any
+    # order that keeps each lane's trips serial agrees with the float32 oracle to
+    # within the reassociation of the cost sums; report how close it is.
+    w = W.make_max_plus((4, 300, 64), seed=132)
+    got = run_gpu(w, DEV).cpu().numpy()
+    ref32 = run_oracle(w, dtype=np.float32)
+    err = np.abs(got.astype(np.float64) - ref32.astype(np.float64))
+    print(f"max-plus vs float32 oracle: {int((err == 0).sum())} of {err.size} bit-identical, max err {err.max():.3e}")
+    assert err.max() <= 1e-5 * (1 + np.abs(ref32).max())
+
+
+def test_element_scan_errors_on_device_tensors():
+    x = torch.zeros(2, 0, 3, device=DEV)
+    with pytest.raises(sx.SxError) as e:
+        sx.element_scan("max_plus", torch.zeros(2, 3, device=DEV), [x, x], axis=1)
+    assert e.value.name == "E-DIM-001"
+    x = torch.zeros(2, 4, 3, device=DEV)
+    with pytest.raises(sx.SxError) as e:
+        sx.element_scan("max_plus", torch.zeros(2, 3, device=DEV), [x, x.double()], axis=1)
+    assert e.value.name == "E-DIM-002"
+
+
+# ------------------------------------------------------------------ matrix-scan
+
+
+@pytest.mark.parametrize("B,T,n,m,reverse", [
+    (3, 65, 16, 1, False),
+    (3, 65, 16, 1, True),
+    (2, 64, 16, 16, False),
+    (2, 63, 16, 17, True),
+    (4, 129, 3, 3, False),
+    (2, 300, 1, 1, True),
+    (1, 1, 16, 16, False),
+    (5, 2, 7, 16, True),
+])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_matrix_small(B, T, n, m, reverse, dtype):
+    w = W.make_matrix(B, T, n, m, dtype, reverse=reverse, seed=140 + n + m)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert got.dtype == dtype
+    assert_matrix_close(got, run_oracle(w), MS_TOL_F32 if dtype == torch.float32 else MS_TOL_BF16)
+
+
+def test_matrix_bf16_in_f32_out():
+    w = W.make_matrix(2, 100, 16, 4, torch.bfloat16, reverse=True, seed=150, out_dtype=torch.float32)
+    got = run_gpu(w, DEV)
+    assert got.dtype == torch.float32
+    # compute is f32 on exactly widened inputs, so the f32 bar applies to an f32 result
+    assert_matrix_close(got, run_oracle(w), MS_TOL_F32)
+
+
+def test_matrix_broadcast_leading_dims_and_negative_axis():
+    g = torch.Generator().manual_seed(151)
+    a = 0.9 * torch.eye(5) + 0.05 * torch.randn(1, 40, 5, 5, generator=g)  # shared across the batch
+    b = torch.randn(3, 40, 5, 2, generator=g)
+    ref = oracle.matrix_scan(a.numpy(), b.numpy(), axis=-1)
+    got = sx.matrix_scan(a.to(DEV), b.to(DEV), axis=-1)
+    assert got.shape == b.shape
+    assert_matrix_close(got, ref, MS_TOL_F32, axis=1)
+    # time-invariant a: a has no time axis and broadcasts over it (stride 0)
+    a2 = 0.5 * torch.randn(3, 1, 5, 5, generator=g)
+    ref = oracle.matrix_scan(a2.numpy(), b.numpy(), axis=1)
+    got = sx.matrix_scan(a2.to(DEV), b.to(DEV), axis=1)
+    assert_matrix_close(got, ref, MS_TOL_F32)
+
+
+def test_matrix_scan_closed_forms_on_device():
+    g = torch.Generator().manual_seed(152)
+    b = torch.randn(2, 77, 4, 3, generator=g)
+    got = sx.matrix_scan(torch.zeros(2, 77, 4, 4, device=DEV), b.to(DEV), axis=1)
+    assert torch.equal(got.cpu(), b)                          # a = 0 gives b
+    eye = torch.eye(4).expand(2, 77, 4, 4)
+    got = sx.matrix_scan(eye.to(DEV), b.to(DEV), axis=1)
+    np.testing.assert_allclose(got.cpu().numpy(), np.cumsum(b.numpy().astype(np.float64), axis=1),
+                               rtol=1e-5, atol=1e-4)           # a = I gives a prefix sum
+
+
+def test_matrix_scan_empty_and_errors():
+    out = sx.matrix_scan(torch.zeros(2, 0, 3, 3, device=DEV), torch.zeros(2, 0, 3, 1, device=DEV), axis=1)
+    assert out.shape == (2, 0, 3, 1)
+    with pytest.raises(sx.SxError) as e:
+        sx.matrix_scan(torch.zeros(2, 4, 17, 17, device=DEV), torch.zeros(2, 4, 17, 1, device=DEV), axis=1)
+    assert e.value.name == "E-DIM-001"
+
+
+# ------------------------------------------------------------------ the standard workloads at full size
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_standard_workload_full_size(idx):
+    (w,) = W.standard_workloads([idx])
+    _announce(w)
+    got = run_gpu(w, DEV)
+    torch.cuda.synchronize()
+    ref = run_oracle(w)
+    if w.op == "element_scan":
+        assert_element_close(got, ref)
+    else:
+        tol = MS_TOL_F32 if w.tensors["a"].dtype == torch.float32 else MS_TOL_BF16
+        assert_matrix_close(got, ref, tol)
