@@ -35,7 +35,7 @@ def hipcc_path() -> str:
 
 
 def build_command(out_path: str = LIB_PATH) -> list[str]:
-    cmd = [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+    cmd = [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-shared", "-fPIC",
            "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, "-o", out_path]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     return cmd
