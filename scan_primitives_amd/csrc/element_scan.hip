@@ -16,6 +16,17 @@
 //   es_normcap_row_kernel  one 16-thread DPP row per lane, one state
 //                          component per thread; |y|^2 is reduced across the
 //                          row with DPP moves.
+//   es_maxplus_slab_kernel the max-plus body as a chunked associative scan.
+//                          A trip is the map h -> max(h - c, x); maps of that
+//                          form compose into max(h + P, Q). One workgroup of
+//                          NW waves owns 64 lanes and sweeps the scan axis in
+//                          slabs of NW*S trips: each wave summarises its S
+//                          trips into (P, Q), the summaries meet in LDS, each
+//                          wave takes its entering state by composing the
+//                          summaries before it onto the slab's carry, and
+//                          replays its trips from there. The next slab's
+//                          loads are in flight meanwhile. Inputs are read
+//                          once and no state leaves the workgroup.
 #include "sx_common.hpp"
 
 namespace sx {
@@ -197,7 +208,97 @@ __global__ __launch_bounds__(256) void es_normcap_row_kernel(const EsParams p) {
   }
 }
 
+
+template <int NW, int S>
+__global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams p) {
+  __shared__ float sP[2][NW][64];  // per slab parity: each wave's summed cost (negated)
+  __shared__ float sQ[2][NW][64];  // per slab parity: each wave's best value
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // wave-uniform: index math stays scalar
+  const int l = int(threadIdx.x) & 63;
+  const int64_t lane = int64_t(blockIdx.x) * 64 + l;
+  const bool live = lane < p.num_lanes;
+  int64_t off[4];
+  index_offsets(p.lanes, live ? lane : 0, off);
+  const int64_t T = p.T;
+  const float* xl = p.x + off[ES_X];
+  const float* cl = p.s + off[ES_S];
+  float* ol = p.out + off[ES_OUT];
+  const int64_t sx = p.t_stride[ES_X], sc = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const bool rev = p.reverse != 0;
+  float carry = p.init[off[ES_INIT]];
+
+  constexpr int64_t kSlab = int64_t(NW) * S;
+  const int64_t nslabs = (T + kSlab - 1) / kSlab;
+  const float kNegInf = -__builtin_huge_valf();
+  // Scan position q is time q (forward) or T-1-q (reverse). Positions past the
+  // end are identity trips, max(h - 0, -inf) = h. Loads always read a valid
+  // element (the position clamped to the last one; a lane past the end reads
+  // lane 0's and computes values it never stores), so no load sits behind a
+  // branch and every load of a slab is in flight at once.
+  auto time_of = [&](int64_t q) -> int64_t {
+    const int64_t qc = q < T ? q : T - 1;
+    return rev ? T - 1 - qc : qc;
+  };
+  float cx[S], cc[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int64_t q = int64_t(wave) * S + k;
+    const int64_t t = time_of(q);
+    const float xv = xl[t * sx], cv = cl[t * sc];
+    cx[k] = q < T ? xv : kNegInf;
+    cc[k] = q < T ? cv : 0.0f;
+  }
+  for (int64_t sl = 0; sl < nslabs; ++sl) {
+    const int64_t qw = sl * kSlab + int64_t(wave) * S;  // this wave's first position in the slab
+    float nx[S], nc[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {  // next slab, in flight during this one
+      const int64_t q = qw + kSlab + k;
+      const int64_t t = time_of(q);
+      const float xv = xl[t * sx], cv = cl[t * sc];
+      nx[k] = q < T ? xv : kNegInf;
+      nc[k] = q < T ? cv : 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next slab's loads issued ahead of this slab's work
+    // summary of this wave's trips: composing max(h - c, x) in scan order gives max(h + P, Q)
+    float P = 0.0f, Q = kNegInf;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      Q = fmaxf(Q - cc[k], cx[k]);
+      P = P - cc[k];
+    }
+    const int par = int(sl & 1);
+    sP[par][wave][l] = P;
+    sQ[par][wave][l] = Q;
+    __syncthreads();
+    // entering state of this wave, and the carry into the next slab (the same in every wave)
+    float h = carry, hw = carry;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w == wave) hw = h;
+      h = fmaxf(h + sP[par][w][l], sQ[par][w][l]);
+    }
+    carry = h;
+    // replay from the entering state: each trip is the serial body again
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      hw = fmaxf(hw - cc[k], cx[k]);
+      const int64_t q = qw + k;
+      if (live && q < T) ol[time_of(q) * so] = hw;
+    }
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      cx[k] = nx[k];
+      cc[k] = nc[k];
+    }
+  }
+}
 }  // namespace
+
+// The slab kernel wants about one 64-lane workgroup per CU (MI355X: 256) and
+// at least a couple of slabs along the axis; below that the lane kernel is used.
+constexpr int64_t kSlabMinLanes = 64 * 128;
+constexpr int64_t kSlabMinTrips = 512;
 
 size_t element_scan_workspace(sx_body, const EsParams&) { return 0; }
 
@@ -210,10 +311,14 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
   } else {
     const int64_t blocks = (p.num_lanes + 63) / 64;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (body == SX_BODY_TANH_AFFINE)
+    if (body == SX_BODY_TANH_AFFINE) {
       hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
-    else
+    } else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips) {
+      // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries
+      hipLaunchKernelGGL((es_maxplus_slab_kernel<16, 16>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
+    } else {
       hipLaunchKernelGGL(es_lane_kernel<SX_BODY_MAX_PLUS>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -63,6 +63,20 @@ def test_max_plus_small(shape, axis, reverse):
     assert_element_close(got, run_oracle(w))
 
 
+@pytest.mark.parametrize("shape,axis,reverse", [
+    ((33, 700, 256), 1, True),     # 8448 lanes, 700 trips: 2 full slabs and a ragged one
+    ((33, 600, 250), 1, False),    # 8250 lanes: the last 64-lane group is partial
+    ((520, 40, 17), 1, True),      # too short an axis for slabs: the lane kernel
+    ((9000, 513), 0, True),        # long axis, few lanes: the lane kernel
+    ((600, 8200), 0, False),       # axis 0 with 8200 contiguous lanes: the slab kernel
+])
+def test_max_plus_slab_path(shape, axis, reverse):
+    w = W.make_max_plus(shape, axis=axis, reverse=reverse, seed=111)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert_element_close(got, run_oracle(w))
+
+
 @pytest.mark.parametrize("B,T,H,n,gate,reverse", [
     (2, 45, 5, 16, 1, False),
     (2, 45, 5, 16, 16, True),
