@@ -157,13 +157,17 @@ __device__ __forceinline__ ARow<TIn> load_a(const TIn* ap, int n, int r, int c) 
   } else if constexpr (VEC) {
     out.u = *reinterpret_cast<const uint2*>(ap + c * 16 + 4 * r);
   } else {
+    // clamped indices: every lane loads a valid element, then zeroes what lies past n
     uint16_t h[4];
     float f[4];
+    const int row = c < n ? c : n - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool in = c < n && 4 * r + q < n;
-      if constexpr (sizeof(TIn) == 4) f[q] = in ? float(ap[c * n + 4 * r + q]) : 0.0f;
-      else h[q] = in ? uint16_t(ap[c * n + 4 * r + q]) : uint16_t(0);
+      const int col = 4 * r + q < n ? 4 * r + q : n - 1;
+      const TIn v = ap[row * n + col];
+      if constexpr (sizeof(TIn) == 4) f[q] = in ? float(v) : 0.0f;
+      else h[q] = in ? uint16_t(v) : uint16_t(0);
     }
     if constexpr (sizeof(TIn) == 4) out.v = f32x4{f[0], f[1], f[2], f[3]};
     else out.u = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
@@ -204,17 +208,46 @@ struct BCol<uint16_t> {
 
 template <typename TIn>
 __device__ __forceinline__ BCol<TIn> load_b(const TIn* bp, int n, int m, int r, int cc) {
+  // clamped indices: every lane loads a valid element, then zeroes what lies past n and m
   BCol<TIn> out;
+  const int col = cc < m ? cc : m - 1;
+  TIn v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = bp[int64_t(4 * r + q < n ? 4 * r + q : n - 1) * m + col];
   if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out.v[q] = (4 * r + q < n && cc < m) ? bp[int64_t(4 * r + q) * m + cc] : 0.0f;
+    for (int q = 0; q < 4; ++q) out.v[q] = (4 * r + q < n && cc < m) ? v[q] : 0.0f;
   } else {
     uint32_t h[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) h[q] = (4 * r + q < n && cc < m) ? uint32_t(bp[int64_t(4 * r + q) * m + cc]) : 0u;
+    for (int q = 0; q < 4; ++q) h[q] = (4 * r + q < n && cc < m) ? uint32_t(v[q]) : 0u;
     out.u = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
   }
   return out;
+}
+
+template <typename TIn>
+__device__ __forceinline__ BCol<TIn> select_b(bool keep, BCol<TIn> v) {
+  if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v.v[q] = keep ? v.v[q] : 0.0f;
+  } else {
+    v.u.x = keep ? v.u.x : 0u;
+    v.u.y = keep ? v.u.y : 0u;
+  }
+  return v;
+}
+
+template <typename TIn>
+__device__ __forceinline__ ARow<TIn> select_a(bool keep, ARow<TIn> v, ARow<TIn> other) {
+  if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v.v[q] = keep ? v.v[q] : other.v[q];
+  } else {
+    v.u.x = keep ? v.u.x : other.u.x;
+    v.u.y = keep ? v.u.y : other.u.y;
+  }
+  return v;
 }
 
 // m == 1: lane (r, c) holds b[step c][4r .. 4r+3] for the wave's 16 steps (one load per lane).
@@ -229,7 +262,10 @@ __device__ __forceinline__ f32x4 load_b_col1(const TIn* bp, int n, int r, bool v
               __uint_as_float(u.y & 0xffff0000u)};
   } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (4 * r + q < n) ? load_elem(bp + 4 * r + q) : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const float e = load_elem(bp + (4 * r + q < n ? 4 * r + q : n - 1));
+      v[q] = (4 * r + q < n) ? e : 0.0f;
+    }
   }
   return v;
 }
@@ -325,14 +361,15 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
   __shared__ uint32_t sUnit;
 
   const int tid = int(threadIdx.x);
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: index math stays scalar
+  const int lane = tid & 63;
   const int r = lane >> 4, c = lane & 15;
 
   // One counter increment per workgroup, in launch order: every unit this one
   // waits for was taken earlier by a running workgroup, so look-back progresses.
   if (tid == 0) sUnit = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const uint32_t unit = sUnit;
+  const uint32_t unit = __builtin_amdgcn_readfirstlane(sUnit);
   if (unit >= ws.num_units) return;
 
   const uint32_t num_bt = uint32_t(p.num_batch) * uint32_t(ws.col_tiles);
@@ -358,22 +395,25 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
   const int64_t t0 = p.reverse ? T - 1 - q0 : q0;  // time of scan position q0
   const bool vec_b1 = VEC && M1;                   // b[t] and out[t] are 16 contiguous, aligned values
 
-  // ---- load the wave's K steps (scan position q0 + k is time t0 +/- k)
+  // ---- load the wave's K steps (scan position q0 + k is time t0 +/- k). Steps past the end
+  // become the identity map; their loads read the last step instead, so that no load sits
+  // behind a branch and all of them are in flight together.
   ARow<TIn> A[K];
   BCol<TIn> Bv[M1 ? 1 : K];
-  f32x4 b1 = zero4();
+  const ARow<TIn> eye = identity_a<TIn>(r, c);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (q0 + k < T) A[k] = load_a<TIn, VEC>(a0 + (t0 * p.t_stride[MS_A] + k * ta), n, r, c);
-    else A[k] = identity_a<TIn>(r, c);
-    if constexpr (!M1) {
-      if (q0 + k < T) Bv[k] = load_b(b0 + (t0 * p.t_stride[MS_B] + k * tb), n, m, r, cc);
-      else Bv[k] = BCol<TIn>{};
-    }
+    const int64_t kk = q0 + k < T ? int64_t(k) : T - 1 - q0;
+    A[k] = select_a(q0 + k < T, load_a<TIn, VEC>(a0 + (t0 * p.t_stride[MS_A] + kk * ta), n, r, c), eye);
+    if constexpr (!M1) Bv[k] = select_b(q0 + k < T, load_b(b0 + (t0 * p.t_stride[MS_B] + kk * tb), n, m, r, cc));
   }
+  f32x4 b1 = zero4();
   if constexpr (M1) {
-    if (q0 + c < T) b1 = load_b_col1(b0 + (t0 * p.t_stride[MS_B] + c * tb), n, r, vec_b1);
+    const int64_t kc = q0 + c < T ? int64_t(c) : T - 1 - q0;
+    b1 = load_b_col1(b0 + (t0 * p.t_stride[MS_B] + kc * tb), n, r, vec_b1);
+    if (q0 + c >= T) b1 = zero4();
   }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first product waits on any of them
   auto bterm = [&](auto kc) -> f32x4 {
     constexpr int k = decltype(kc)::value;
     if constexpr (M1) return col0_from_lane<k>(b1, c);
