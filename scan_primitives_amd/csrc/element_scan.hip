@@ -16,6 +16,14 @@
 //   es_normcap_row_kernel  one 16-thread DPP row per lane, one state
 //                          component per thread; |y|^2 is reduced across the
 //                          row with DPP moves.
+//   es_normcap_chunk_kernel the norm-capped body split along the axis into
+//                          chunks that run at once. The body is not
+//                          associative but it contracts: a chunk starts W
+//                          trips early from h = 0, with W chosen so that the
+//                          product of per-trip Lipschitz bounds certifies the
+//                          warm-up's distance to the true state below 2^-26
+//                          (or W reaching back to the start of the axis,
+//                          which is then exact). See norm_cap_lipschitz.
 //   es_maxplus_slab_kernel the max-plus body as a chunked associative scan.
 //                          A trip is the map h -> max(h - c, x); maps of that
 //                          form compose into max(h + P, Q). One workgroup of
@@ -209,6 +217,117 @@ __global__ __launch_bounds__(256) void es_normcap_row_kernel(const EsParams p) {
 }
 
 
+// Maximum over the 16 lanes of a DPP row, every lane of the row gets it.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
+// A Lipschitz bound of one norm-capped trip h -> P(a*h + x), P the projection
+// onto the closed unit ball, over states h in that ball (every state after a
+// trip is in it). a*h moves by at most alpha = max|a_i| times |h - h'|; P is
+// nonexpansive; and when every reachable y = a*h + x has |y| >= r = |x| - alpha
+// > 1, P(y) = y/|y| moves by at most |y - y'| / r (Dunkl-Williams in an inner
+// product space: |u/|u| - v/|v|| <= 2|u - v| / (|u| + |v|)). So
+// L = alpha / max(1, |x| - alpha). Both reductions run over the whole row, so
+// every lane of the row (the inactive ones past n hold zeros) gets the same
+// bits and the row takes every decision together. Non-finite inputs give a
+// non-finite L, which never certifies.
+__device__ __forceinline__ float norm_cap_lipschitz(float x, float a) {
+  const float xn = __builtin_sqrtf(row_sum16(x * x));
+  const float al = row_max16(fabsf(a));
+  return al / fmaxf(1.0f, xn - al);
+}
+
+constexpr float kWarmupBound = 1.0f / 67108864.0f;  // 2^-26, far below f32 rounding of |h| <= 1
+
+// One DPP row (16 threads) per (lane, chunk). Positions are in scan order
+// (time T-1-q when reversed). The chunk covers positions [s, e); the row runs
+// positions [start, e) and stores [s, e), where start <= s is the warm-up
+// start certified by the walk back from s, or 0 (exact, from `initial`).
+__global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p, int64_t chunk_len, int64_t nchunks) {
+  const int64_t row = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
+  // A whole row leaves together, so no DPP read crosses into an exited row.
+  if (row >= p.num_lanes * nchunks) return;
+  const int64_t chunk = row / p.num_lanes;
+  const int64_t lane = row % p.num_lanes;
+  const int k = int(threadIdx.x & 15);
+  const bool active = k < p.n;
+  const int kk = active ? k : 0;
+  int64_t off[4];
+  index_offsets(p.lanes, lane, off);
+  const float* xl = p.x + off[ES_X] + kk * p.n_stride[ES_X];
+  const float* al = p.s + off[ES_S] + kk * p.n_stride[ES_S];
+  float* ol = p.out + off[ES_OUT] + kk * p.n_stride[ES_OUT];
+  const int64_t sx = p.t_stride[ES_X], sa = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const int64_t T = p.T;
+  const bool rev = p.reverse != 0;
+  auto time_of = [&](int64_t q) -> int64_t { return rev ? T - 1 - q : q; };
+  const int64_t s = chunk * chunk_len;
+  const int64_t e = s + chunk_len < T ? s + chunk_len : T;
+
+  // ---- walk back from s, eight positions per round, until the warm-up is certified
+  int64_t start = 0;
+  if (s > 0) {
+    float prod = 1.0f;
+    int64_t q = s - 1;
+    bool done = false;
+    while (!done) {  // row-uniform: every lane of the row computes the same bound
+      float xv[8], av[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {  // clamped, always-valid loads
+        const int64_t t = time_of(q - g >= 0 ? q - g : 0);
+        const float xr = xl[t * sx], ar = al[t * sa];
+        xv[g] = active ? xr : 0.0f;
+        av[g] = active ? ar : 0.0f;
+      }
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (!done) {
+          if (q - g < 0) {
+            start = 0;  // reached the start of the axis: run exactly from `initial`
+            done = true;
+          } else {
+            prod *= norm_cap_lipschitz(xv[g], av[g]);
+            if (prod <= kWarmupBound) {
+              start = q - g;
+              done = true;
+            }
+          }
+        }
+      }
+      q -= 8;
+    }
+  }
+
+  // ---- run [start, e): from `initial` at position 0, else from 0 (any point of the unit ball)
+  float h = 0.0f;
+  if (start == 0 && active) h = p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]];
+  constexpr int U = 8;
+  for (int64_t q0 = start; q0 < e; q0 += U) {
+    float xv[U], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = time_of(q0 + u < e ? q0 + u : e - 1);
+      const float xr = xl[t * sx], ar = al[t * sa];
+      xv[u] = active ? xr : 0.0f;
+      av[u] = active ? ar : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = q0 + u;
+      if (q < e) {  // row-uniform
+        h = norm_cap_trip(h, xv[u], av[u]);
+        if (active && q >= s) ol[time_of(q) * so] = h;
+      }
+    }
+  }
+}
+
+
 template <int NW, int S>
 __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams p) {
   __shared__ float sP[2][NW][64];  // per slab parity: each wave's summed cost (negated)
@@ -298,6 +417,12 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
 // The slab kernel wants about one 64-lane workgroup per CU (MI355X: 256) and
 // at least a couple of slabs along the axis; below that the lane kernel is used.
 constexpr int64_t kSlabMinLanes = 64 * 128;
+// Norm-cap chunking: used below kChunkMaxLanes vector lanes (where one row per
+// lane leaves most of the GPU idle), aiming at kChunkRows rows of at least
+// kChunkMinLen trips each.
+constexpr int64_t kChunkMaxLanes = 8192;
+constexpr int64_t kChunkRows = 8192;
+constexpr int64_t kChunkMinLen = 16;
 constexpr int64_t kSlabMinTrips = 512;
 
 size_t element_scan_workspace(sx_body, const EsParams&) { return 0; }
@@ -305,6 +430,17 @@ size_t element_scan_workspace(sx_body, const EsParams&) { return 0; }
 hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream) {
   if (p.num_lanes <= 0) return hipSuccess;
   if (body == SX_BODY_NORM_CAP) {
+    if (p.num_lanes < kChunkMaxLanes && p.T >= 2 * kChunkMinLen) {
+      // Few lanes: cut the axis into chunks so that about kChunkRows rows run at once.
+      int64_t nchunks = (kChunkRows + p.num_lanes - 1) / p.num_lanes;
+      int64_t len = (p.T + nchunks - 1) / nchunks;
+      if (len < kChunkMinLen) len = kChunkMinLen;
+      nchunks = (p.T + len - 1) / len;
+      const int64_t blocks = (p.num_lanes * nchunks * 16 + 255) / 256;
+      if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(es_normcap_chunk_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p, len, nchunks);
+      return hipGetLastError();
+    }
     const int64_t blocks = (p.num_lanes * 16 + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(es_normcap_row_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p);

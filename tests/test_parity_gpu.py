@@ -93,6 +93,32 @@ def test_norm_cap_small(B, T, H, n, gate, reverse):
     assert float(torch.linalg.vector_norm(got, dim=-1).max()) <= 1 + 1e-5
 
 
+@pytest.mark.parametrize("B,T,H,n,gate,reverse", [
+    (2, 300, 5, 16, 1, False),     # chunked along the axis (few lanes): ragged last chunk
+    (3, 257, 2, 5, 5, True),       # per-component gate (bound uses the largest |a|), reverse
+    (1, 1000, 3, 16, 16, False),
+])
+def test_norm_cap_chunked(B, T, H, n, gate, reverse):
+    w = W.make_norm_cap(B, T, H, n, gate_width=gate, reverse=reverse, seed=125, zero_initial=False)
+    _announce(w)
+    assert_element_close(run_gpu(w, DEV), run_oracle(w))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_norm_cap_chunked_without_contraction(reverse):
+    # decay = 1 and tiny x: no trip contracts, no warm-up can be certified, and
+    # every chunk has to run from the start of the axis; the result stays exact.
+    g = torch.Generator().manual_seed(126)
+    x = 1e-2 * torch.randn(2, 200, 3, 16, generator=g)
+    decay = torch.ones(2, 200, 3, 1)
+    init = 0.1 * torch.randn(2, 3, 16, generator=g)
+    ref = oracle.element_scan("norm_cap", init.numpy(), [x.numpy(), decay.numpy()], axis=1, state_axis=-1,
+                              reverse=reverse)
+    got = sx.element_scan("norm_cap", init.to(DEV), [x.to(DEV), decay.to(DEV)], axis=1, state_axis=-1,
+                          reverse=reverse)
+    assert_element_close(got, ref)
+
+
 def test_element_scan_strided_and_broadcast_operands():
     # x as a transposed view, decay broadcast along the width (stride 0), initial non-contiguous
     g = torch.Generator().manual_seed(130)
