@@ -1,21 +1,26 @@
 """Throughput of the scan library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 0,2,...]
-                    [--no-cpu-baseline] [--with-copy]
+                    [--no-cpu-baseline] [--with-copy] [--eager]
 
 One step runs the whole hot path once: the five standard workloads of
 ``scan_primitives_amd.workloads`` (tanh-affine, norm-cap, reverse max-plus,
 matrix-scan f32 m=1, matrix-scan bf16 m=16 reverse), each as one library
-call on inputs already resident in HBM. W untimed steps come first, then K
-timed steps bracketed by device synchronisation. Each call is also bracketed
-by HIP events on the stream the library launches on (torch's current
-stream), which gives each workload's average call duration.
+call on inputs already resident in HBM. The step is captured once in a HIP
+graph (the library launches on torch's current stream, which is the capture
+stream), so host-side launch work stays out of the timed region; W untimed
+replays come first, then K timed replays bracketed by device synchronisation.
 
-Prints ONE JSON line on stdout: the whole-job value is output elements per
-second over the timed region; ``per_config`` has each workload's
-elements/s, algorithmic GB/s and fraction of the 8 TB/s HBM peak;
-``roofline`` describes the call that takes the most time; ``cpu_baseline``
-is the CPU oracle timed on the same workloads on the host.
+Each workload's call is also timed on its own: a graph of R back-to-back
+calls (R chosen so a replay moves at least 32 MiB), replayed K times between
+two HIP events on the capture stream; the per-call time is the elapsed time
+over K * R. This gives each workload's elements/s, algorithmic GB/s and
+fraction of the 8 TB/s HBM peak.
+
+Prints ONE JSON line on stdout. ``value`` is output elements per second over
+the timed steps; ``per_config`` has each workload's figures; ``roofline``
+describes the call that takes the most time; ``cpu_baseline`` is the CPU
+oracle timed on the same workloads on the host.
 """
 
 from __future__ import annotations
@@ -23,6 +28,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import subprocess
 import sys
@@ -74,7 +80,6 @@ def measured_traffic(kernel_label: str):
 
 def cpu_baseline(workloads) -> dict:
     """Time the CPU oracle, as it stands, on the same workloads (one pass each)."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -94,7 +99,6 @@ def cpu_baseline(workloads) -> dict:
             total_elems += w.out_numel
             total_s += dt
             del host
-    _ = np  # numpy is the oracle's arithmetic
     return {"value": total_elems / total_s, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": "one pass of the float64 numpy oracle over each selected workload at full size, "
                       f"single-threaded; {total_elems} output elements in {total_s:.2f} s"}
@@ -108,7 +112,8 @@ def main() -> int:
     ap.add_argument("--only", type=str, default=None, help="comma-separated workload indices 0..4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--with-copy", action="store_true",
-                    help="also time a plain 256 MiB device copy (reference kernel for PMC byte counts)")
+                    help="also run a plain 256 MiB device copy per step (reference kernel for PMC byte counts)")
+    ap.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying graphs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -145,54 +150,79 @@ def main() -> int:
         copy_src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
         copy_dst = torch.empty_like(copy_src)
 
-    for i in range(args.warmup):
+    def one_step():
         for w, t in zip(workloads, resident):
             call(w, t)
         if copy_src is not None:
             copy_dst.copy_(copy_src)
+
+    # eager warm-up (also sizes the caching allocator), then capture
+    for _ in range(2):
+        one_step()
     torch.cuda.synchronize()
+    reps = [max(1, min(64, math.ceil((32 << 20) / w.algorithmic_bytes))) for w in workloads]
+    graphs, step_graph, keep = [], None, []
+    if not args.eager:
+        for w, t, r in zip(workloads, resident, reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                keep.append([call(w, t) for _ in range(r)])
+            graphs.append(g)
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph):
+            one_step()
+        torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)] for _ in workloads]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for j, (w, t) in enumerate(zip(workloads, resident)):
-            ev0, ev1 = events[j][s]
-            ev0.record(stream)
-            call(w, t)
-            ev1.record(stream)
-            log(f"step {s} {w.name} enqueued") if s == 0 else None
-        if copy_src is not None:
-            copy_dst.copy_(copy_src)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
+    # ---- per-workload call time: K replays of a graph of R calls, between two events
     per_config = []
-    total_elems = 0
-    for j, w in enumerate(workloads):
-        ms = [e0.elapsed_time(e1) for e0, e1 in events[j]]
-        avg_ms = sum(ms) / len(ms)
-        sec = avg_ms / 1e3
+    for j, (w, t, r) in enumerate(zip(workloads, resident, reps)):
+        def run_once():
+            if args.eager:
+                for _ in range(r):
+                    call(w, t)
+            else:
+                graphs[j].replay()
+        for _ in range(args.warmup):
+            run_once()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run_once()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / (args.steps * r)
         gbs = w.algorithmic_bytes / sec / 1e9
         per_config.append({
             "workload": w.name,
-            "call_us": round(avg_ms * 1e3, 3),
+            "call_us": round(sec * 1e6, 3),
+            "calls_per_replay": r,
             "elements_per_s": w.out_numel / sec,
             "algorithmic_bytes": w.algorithmic_bytes,
             "hbm_gbs": round(gbs, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         })
-        total_elems += w.out_numel * args.steps
-        log(f"{w.name}: {avg_ms * 1e3:.2f} us/call, {w.out_numel / sec:.3e} elements/s, {gbs:.1f} GB/s "
+        log(f"{w.name}: {sec * 1e6:.2f} us/call, {w.out_numel / sec:.3e} elements/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+
+    # ---- whole job: K steps, each one pass over every workload
+    for _ in range(args.warmup):
+        one_step() if args.eager else step_graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step() if args.eager else step_graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_elems = sum(w.out_numel for w in workloads) * args.steps
+    log(f"{args.steps} steps in {wall * 1e3:.2f} ms")
 
     dom = max(range(len(workloads)), key=lambda j: per_config[j]["call_us"])
     dw, dc = workloads[dom], per_config[dom]
-    traffic = measured_traffic(dw.name)
     roofline = {"bound": "hbm", "achieved": dc["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dc["hbm_frac"], "traffic": traffic, "kernel": dw.name,
+                "frac": dc["hbm_frac"], "traffic": measured_traffic(dw.name), "kernel": dw.name,
                 "algorithmic_bytes_per_call": dw.algorithmic_bytes}
 
     result = {
@@ -209,7 +239,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": " + ".join(w.name for w in workloads), "commit": git_sha(),
-                   "kernel_source_hash": kernel_source_hash()},
+                   "kernel_source_hash": kernel_source_hash(), "timing": "eager" if args.eager else "hip-graph"},
         "roofline": roofline,
         "per_config": per_config,
     }

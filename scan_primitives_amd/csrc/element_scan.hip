@@ -232,14 +232,17 @@ __device__ __forceinline__ float row_max16(float v) {
 // nonexpansive; and when every reachable y = a*h + x has |y| >= r = |x| - alpha
 // > 1, P(y) = y/|y| moves by at most |y - y'| / r (Dunkl-Williams in an inner
 // product space: |u/|u| - v/|v|| <= 2|u - v| / (|u| + |v|)). So
-// L = alpha / max(1, |x| - alpha). Both reductions run over the whole row, so
-// every lane of the row (the inactive ones past n hold zeros) gets the same
-// bits and the row takes every decision together. Non-finite inputs give a
+// L = alpha / max(1, |x| - alpha). The reductions run across the whole DPP
+// row (lanes past n hold zeros; a broadcast gate is read by every lane), so
+// all lanes of a row get the same bits and decide together. The hardware
+// square root and reciprocal are within 1 ulp each; the few-ulp error of the
+// product is far inside the margin between the target 2^-26 and the f32
+// rounding (about 2^-24 of |h| <= 1) it protects. Non-finite inputs give a
 // non-finite L, which never certifies.
-__device__ __forceinline__ float norm_cap_lipschitz(float x, float a) {
-  const float xn = __builtin_sqrtf(row_sum16(x * x));
-  const float al = row_max16(fabsf(a));
-  return al / fmaxf(1.0f, xn - al);
+__device__ __forceinline__ float norm_cap_lipschitz(float x, float a, bool scalar_gate) {
+  const float xn = __builtin_amdgcn_sqrtf(row_sum16(x * x));
+  const float al = scalar_gate ? fabsf(a) : row_max16(fabsf(a));
+  return al * __builtin_amdgcn_rcpf(fmaxf(1.0f, xn - al));
 }
 
 constexpr float kWarmupBound = 1.0f / 67108864.0f;  // 2^-26, far below f32 rounding of |h| <= 1
@@ -248,6 +251,12 @@ constexpr float kWarmupBound = 1.0f / 67108864.0f;  // 2^-26, far below f32 roun
 // (time T-1-q when reversed). The chunk covers positions [s, e); the row runs
 // positions [start, e) and stores [s, e), where start <= s is the warm-up
 // start certified by the walk back from s, or 0 (exact, from `initial`).
+// Fast path: chunks of at most kChunkFast trips whose warm-up certifies within
+// kWarmFast trips run entirely from one batch of loads covering
+// [s - kWarmFast, s + kChunkFast).
+constexpr int kWarmFast = 24;
+constexpr int kChunkFast = 16;
+
 __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p, int64_t chunk_len, int64_t nchunks) {
   const int64_t row = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
   // A whole row leaves together, so no DPP read crosses into an exited row.
@@ -265,11 +274,73 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
   const int64_t sx = p.t_stride[ES_X], sa = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
   const int64_t T = p.T;
   const bool rev = p.reverse != 0;
-  auto time_of = [&](int64_t q) -> int64_t { return rev ? T - 1 - q : q; };
+  auto time_of = [&](int64_t q) -> int64_t {  // clamped into [0, T): loads always read a valid element
+    q = q < 0 ? 0 : (q >= T ? T - 1 : q);
+    return rev ? T - 1 - q : q;
+  };
   const int64_t s = chunk * chunk_len;
   const int64_t e = s + chunk_len < T ? s + chunk_len : T;
+  const float h0 = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
+  const bool scalar_gate = p.n_stride[ES_S] == 0;  // a width-one gate: every lane reads the same value
 
-  // ---- walk back from s, eight positions per round, until the warm-up is certified
+  if (chunk_len <= kChunkFast) {
+    // ---- one batch of loads: buffer slot i holds position s - kWarmFast + i
+    constexpr int kSlots = kWarmFast + kChunkFast;
+    float xv[kSlots], av[kSlots];
+    {
+      const int64_t q_first = s - kWarmFast;
+      const int64_t dq = rev ? -1 : 1;
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i) {
+        const int64_t t = time_of(q_first + i);
+        (void)dq;
+        const float xr = xl[t * sx], ar = al[t * sa];
+        xv[i] = active ? xr : 0.0f;
+        av[i] = active || scalar_gate ? ar : 0.0f;
+      }
+    }
+    // walk back from s - 1 (slot kWarmFast - 1) while the bound is above the target;
+    // the per-trip bounds do not depend on h, so all of them are formed first
+    int first = -1;  // slot of the certified warm-up start
+    bool exact = false;
+    if (s == 0) {
+      first = kWarmFast;
+      exact = true;
+    } else {
+      float lip[kWarmFast];
+#pragma unroll
+      for (int i = 0; i < kWarmFast; ++i) lip[i] = norm_cap_lipschitz(xv[i], av[i], scalar_gate);
+      float prod = 1.0f;
+#pragma unroll
+      for (int i = kWarmFast - 1; i >= 0; --i) {
+        if (first < 0) {  // row-uniform
+          if (s - kWarmFast + i < 0) {
+            first = i + 1;  // reached the start of the axis
+            exact = true;
+          } else {
+            prod *= lip[i];
+            if (prod <= kWarmupBound) first = i;
+          }
+        }
+      }
+    }
+    if (first >= 0) {
+      float h = exact ? h0 : 0.0f;
+      float* op = ol + time_of(s) * so;
+      const int64_t dout = rev ? -so : so;
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i) {
+        const int64_t q = s - kWarmFast + i;
+        if (i >= first && q < e) {  // row-uniform
+          h = norm_cap_trip(h, xv[i], av[i]);
+          if (i >= kWarmFast && active) op[(i - kWarmFast) * dout] = h;
+        }
+      }
+      return;
+    }
+  }
+
+  // ---- general path: walk back eight positions per round until certified, then run forward
   int64_t start = 0;
   if (s > 0) {
     float prod = 1.0f;
@@ -278,11 +349,11 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
     while (!done) {  // row-uniform: every lane of the row computes the same bound
       float xv[8], av[8];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {  // clamped, always-valid loads
-        const int64_t t = time_of(q - g >= 0 ? q - g : 0);
+      for (int g = 0; g < 8; ++g) {
+        const int64_t t = time_of(q - g);
         const float xr = xl[t * sx], ar = al[t * sa];
         xv[g] = active ? xr : 0.0f;
-        av[g] = active ? ar : 0.0f;
+        av[g] = active || scalar_gate ? ar : 0.0f;
       }
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
@@ -291,7 +362,7 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
             start = 0;  // reached the start of the axis: run exactly from `initial`
             done = true;
           } else {
-            prod *= norm_cap_lipschitz(xv[g], av[g]);
+            prod *= norm_cap_lipschitz(xv[g], av[g], scalar_gate);
             if (prod <= kWarmupBound) {
               start = q - g;
               done = true;
@@ -302,10 +373,7 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
       q -= 8;
     }
   }
-
-  // ---- run [start, e): from `initial` at position 0, else from 0 (any point of the unit ball)
-  float h = 0.0f;
-  if (start == 0 && active) h = p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]];
+  float h = start == 0 ? h0 : 0.0f;  // from `initial` at position 0, else from 0 (in the unit ball)
   constexpr int U = 8;
   for (int64_t q0 = start; q0 < e; q0 += U) {
     float xv[U], av[U];
@@ -326,7 +394,6 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
     }
   }
 }
-
 
 template <int NW, int S>
 __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams p) {
