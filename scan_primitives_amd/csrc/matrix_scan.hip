@@ -29,6 +29,7 @@
 // row c: one 16-byte load) and X[4r + q][c], which is exactly register q of
 // the previous result. So a chain h <- a[t] @ h + b[t] feeds each result
 // straight back as the next B operand, with no data movement between steps.
+#include <algorithm>
 #include <utility>
 
 #include "sx_common.hpp"
@@ -528,14 +529,368 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
   }(std::make_integer_sequence<int, K>{});
 }
 
+// ------------------------------------------------------------------ pipelined kernel
+//
+// ms_pipe_kernel runs the same unit scheme as ms_unit_kernel (8 waves x 16
+// steps per unit, wave maps composed by a leader, decoupled look-back) but
+// keeps the memory system busy across units: each workgroup stays resident
+// and takes units one after another, and while it computes one unit from
+// registers the inputs of its next unit stream from HBM straight into LDS
+// (global_load_lds, no registers held). When the unit ends, the staged
+// inputs move from LDS into registers and the copy of the unit after that
+// starts at once.
+//
+// Layout choices that make every LDS read linear (conflict-free):
+//   a (f32):  the 16-byte piece a[c][4r..4r+3] that lane (r, c) reads sits
+//             at slot 16 r + c of the step's 1 KB block;
+//   a (bf16): the 16-byte piece a[c][8p..8p+7] sits at slot c + 16 p of the
+//             step's 512-byte block, and lane (r, c) reads its half r % 2
+//             of slot c + 16 (r / 2);
+//   b:        the same two patterns, with rows of b (m = 16 tiles) or the
+//             16 steps of one wave (m = 1) in place of the rows of a.
+// For m a multiple of 16 (bf16 only) b is staged row by row and read back in
+// result-register order (rows 4r..4r+3 of column c, four 2-byte reads); the
+// output goes the other way through the wave's own map slots in LDS, so that
+// every lane stores 16 contiguous bytes of one row.
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// Lane i's 16 bytes at src land in LDS at dst + 16 i (dst is the same for the
+// whole wave). The copy is counted by vmcnt until its bytes are in LDS.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)dst, 16, 0, 0);
+}
+
+template <typename TIn, bool M1>
+struct PipeStage {
+  static constexpr int kA = 16 * 16 * int(sizeof(TIn));                // one a[t]
+  static constexpr int kB = M1 ? 16 * int(sizeof(TIn)) : kA;           // one b[t] (a 16-column tile)
+  static constexpr int kWave = 16 * (kA + kB);                         // one wave's 16 steps
+  static constexpr int kPiecesA = sizeof(TIn) == 4 ? 16 : 8;           // 1 KB copies of a
+  static constexpr int kPieces = kPiecesA + (M1 ? 1 : 8);              // ... and of b
+};
+
+// Where one wave's 16 steps of a unit live.
+struct PipeGeo {
+  uint32_t chunk, bt;
+  int ct;
+  int64_t q0;  // scan position of the wave's first step
+  int64_t t0;  // its time index
+  int64_t off[3];
+};
+
+__device__ __forceinline__ PipeGeo pipe_geo(const MsParams& p, const MsUnitWs& ws, uint32_t unit, int wave, int kUnit) {
+  PipeGeo g;
+  const uint32_t num_bt = uint32_t(p.num_batch) * uint32_t(ws.col_tiles);
+  g.chunk = unit / num_bt;
+  g.bt = unit % num_bt;
+  g.ct = int(g.bt % uint32_t(ws.col_tiles));
+  index_offsets(p.batch, int64_t(g.bt / uint32_t(ws.col_tiles)), g.off);
+  g.q0 = int64_t(g.chunk) * kUnit + int64_t(wave) * 16;
+  g.t0 = p.reverse ? p.T - 1 - g.q0 : g.q0;
+  return g;
+}
+
+// Workgroup barrier that orders LDS traffic only. __syncthreads would also wait
+// for this wave's copies into LDS still in flight (they write LDS), which must
+// keep streaming across the barrier; every stage is read only after a barrier
+// that follows its copies' vmcnt waits.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One wave's 16 steps of a (and of b's tile) are copied into its LDS stage by
+// kPieces copy instructions of 1 KB (the bf16 m = 1 b piece is 512 bytes).
+// Piece i of the stage of the wave whose steps start at g.q0 is started here.
+// Steps past the end read the last step instead (they become identity steps
+// when the stage is read), so every source address is valid.
+template <typename TIn, bool M1>
+__device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g, char* st, int lane, int i) {
+  using S = PipeStage<TIn, M1>;
+  const TIn* a0 = static_cast<const TIn*>(p.a) + g.off[MS_A] + g.t0 * p.t_stride[MS_A];
+  const TIn* b0 = static_cast<const TIn*>(p.b) + g.off[MS_B] + g.t0 * p.t_stride[MS_B];
+  const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
+  const int64_t tb = p.reverse ? -p.t_stride[MS_B] : p.t_stride[MS_B];
+  const int64_t T = p.T, q0 = g.q0;
+  auto clamp = [&](int k) -> int64_t { return q0 + k < T ? int64_t(k) : T - 1 - q0; };
+  if (i < S::kPiecesA) {
+    if constexpr (sizeof(TIn) == 4) {  // step i; lane 16 r + c takes a[c][4r..4r+3]
+      copy16_to_lds(a0 + clamp(i) * ta + (lane & 15) * 16 + 4 * (lane >> 4), st + i * S::kA);
+    } else {  // steps 2i, 2i+1; lane takes a[c][8p..8p+7] for slot c + 16 p of its step
+      copy16_to_lds(a0 + clamp(2 * i + (lane >> 5)) * ta + (lane & 15) * 16 + 8 * ((lane >> 4) & 1),
+                    st + i * 2 * S::kA);
+    }
+    return;
+  }
+  char* sb = st + 16 * S::kA;
+  const int c = lane & 15;
+  if constexpr (M1) {  // one piece: b of all 16 steps, step c at slot c (+ 16 r or + 16 p)
+    if constexpr (sizeof(TIn) == 4) copy16_to_lds(b0 + clamp(c) * tb + 4 * (lane >> 4), sb);
+    else if (lane < 32) copy16_to_lds(b0 + clamp(c) * tb + 8 * (lane >> 4), sb);
+  } else {  // steps 2j, 2j+1 of the tile: b[c][ct*16 + 8p ..] for slot c + 16 p
+    const int j = i - S::kPiecesA;
+    copy16_to_lds(b0 + clamp(2 * j + (lane >> 5)) * tb + int64_t(c) * p.m + g.ct * 16 + 8 * ((lane >> 4) & 1),
+                  sb + j * 2 * S::kB);
+  }
+}
+
+// The copies for one unit: wave w >= 1 starts all pieces of its own stage and
+// its share of wave 0's (wave 0, the leader, keeps no copy in flight: its
+// look-back waits on vmcnt). A barrier after everyone's vmcnt wait makes all
+// stages readable.
+template <int NW, typename TIn, bool M1>
+__device__ __forceinline__ void stage_unit(const MsParams& p, const MsUnitWs& ws, uint32_t unit, int wave, int lane,
+                                           char (*stage)[PipeStage<TIn, M1>::kWave]) {
+  using S = PipeStage<TIn, M1>;
+  if (wave == 0) return;
+  const PipeGeo g = pipe_geo(p, ws, unit, wave, NW * 16);
+#pragma unroll
+  for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, &stage[wave][0], lane, i);
+  const PipeGeo g0 = pipe_geo(p, ws, unit, 0, NW * 16);
+  for (int i = wave - 1; i < S::kPieces; i += NW - 1) stage_piece<TIn, M1>(p, g0, &stage[0][0], lane, i);
+}
+
+template <int NW, typename TIn, typename TOut, bool M1>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void ms_pipe_kernel(const MsParams p, const MsUnitWs ws) {
+  constexpr int K = 16, kUnit = NW * K;
+  using S = PipeStage<TIn, M1>;
+  __shared__ __attribute__((aligned(16))) char sStage[NW][S::kWave];
+  __shared__ __attribute__((aligned(16))) float sP[NW][256];
+  __shared__ __attribute__((aligned(16))) float sL[NW][256];
+  __shared__ float sX[256];
+  __shared__ uint32_t sId[3];
+
+  const int tid = int(threadIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane >> 4, c = lane & 15;
+  const int n = p.n, m = p.m;
+  const int64_t T = p.T;
+  char* st = &sStage[wave][0];
+  const ARow<TIn> eye = identity_a<TIn>(r, c);
+
+  // Unit ids come from one counter in take order; a workgroup takes each id two
+  // units before it computes it (one unit staged in LDS, one announced), so
+  // every unit a look-back waits for was taken earlier by a running workgroup,
+  // and the smallest unfinished unit is always some workgroup's current one.
+  if (tid == 0) {
+    sId[0] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sId[1] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  uint32_t unit = __builtin_amdgcn_readfirstlane(sId[0]);
+  uint32_t next = __builtin_amdgcn_readfirstlane(sId[1]);
+  static_assert(NW >= 2, "wave 0's stage is filled by the other waves");
+  if (unit < ws.num_units) stage_unit<NW, TIn, M1>(p, ws, unit, wave, lane, sStage);
+
+  for (int it = 0; unit < ws.num_units; ++it) {
+    if (tid == 0)
+      sId[(it + 2) % 3] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const PipeGeo g = pipe_geo(p, ws, unit, wave, kUnit);
+    const bool live = c < min(16, m - g.ct * 16);
+
+    // ---- this wave's 16 steps: LDS stage -> registers, then start staging the next unit
+    __builtin_amdgcn_s_waitcnt(0);  // the copies this wave started have landed ...
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    lds_barrier();                  // (0) ... and so have everyone's
+    ARow<TIn> A[K];
+    BCol<TIn> Bv[M1 ? 1 : K];
+    f32x4 b1 = zero4();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if constexpr (sizeof(TIn) == 4) A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
+      else A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+      A[k] = select_a(g.q0 + k < T, A[k], eye);
+      if constexpr (!M1) {
+        // b[4r + v][c] sits in slot (4r + v) + 16 (c / 8), at byte 2 (c % 8); rows are 16 bytes apart
+        const uint16_t* bp = reinterpret_cast<const uint16_t*>(st + 16 * S::kA + k * S::kB + 16 * (4 * r + 16 * (c >> 3)) + 2 * (c & 7));
+        const bool in = g.q0 + k < T;
+        Bv[k].u = make_uint2(in ? uint32_t(bp[0]) | (uint32_t(bp[8]) << 16) : 0u,
+                             in ? uint32_t(bp[16]) | (uint32_t(bp[24]) << 16) : 0u);
+      }
+    }
+    if constexpr (M1) {
+      if constexpr (sizeof(TIn) == 4) {
+        b1 = *reinterpret_cast<const f32x4*>(st + 16 * S::kA + lane * 16);
+      } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(st + 16 * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+        b1 = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+      }
+      if (g.q0 + c >= T) b1 = zero4();
+    }
+
+    auto bterm = [&](auto kc) -> f32x4 {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (M1) return col0_from_lane<k>(b1, c);
+      else return Bv[k].get();
+    };
+
+    // ---- the wave's map: P = a[last] ... a[first], L = the scan of its steps from h = 0
+    f32x4 P = identity_d(r, c), L = zero4();
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      ((P = mfma_16x16x16(A[ks].get(), P, zero4()), L = mfma_16x16x16(A[ks].get(), L, bterm(std::integral_constant<int, ks>{}))), ...);
+    }(std::make_integer_sequence<int, K>{});
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sP[wave][(4 * r + v) * 16 + c] = P[v];
+    *reinterpret_cast<f32x4*>(&sL[wave][lane * 4]) = L;
+    lds_barrier();  // (1) wave maps in LDS, every stage read; sId[(it + 2) % 3] announced
+    const uint32_t after_next = __builtin_amdgcn_readfirstlane(sId[(it + 2) % 3]);
+    // the next unit's inputs stream in while the leader works and the unit is replayed
+    if (next < ws.num_units) stage_unit<NW, TIn, M1>(p, ws, next, wave, lane, sStage);
+
+    const uint32_t slot = g.bt * ws.chunks + g.chunk;
+    if (wave == 0) {
+      const uint32_t base = g.bt * ws.chunks;
+      int hi = int(g.chunk) - 1;
+      auto scan_flags = [&]() -> uint32_t {
+        const int cand = hi - lane;
+        return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      };
+      uint32_t f = g.chunk > 0 ? scan_flags() : 0u;  // in flight while the unit's map is composed
+      f32x4 G = identity_d(r, c), GL = zero4();
+      for (int i = 0; i < NW; ++i) {
+        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[i][c * 16 + 4 * r]);
+        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[i][lane * 4]);
+        G = mfma_16x16x16(Pa, G, zero4());
+        GL = mfma_16x16x16(Pa, GL, Li);
+      }
+      const f32x4 GA = to_a_operand(sX, G, r, c);
+      f32x4 h_in = zero4();
+      if (g.chunk > 0) {
+        // the aggregate goes out first, so that later units need not wait for this one
+        dev_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
+        if (live) dev_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+        raise_flag(ws.flags + slot, kFlagAggregate, lane);  // its wait also completes the window's loads
+        // nearest earlier unit whose leaving state is published, with every unit in
+        // between at least aggregated
+        int j = 0;
+        uint32_t spins = 0;
+        for (;;) {
+          const uint64_t inc = __ballot(hi - lane >= 0 && f == kFlagInclusive);
+          const uint64_t none = __ballot(hi - lane >= 0 && f == 0);
+          if (inc != 0) {
+            const int l = __ffsll((unsigned long long)inc) - 1;
+            if ((none & ((1ull << l) - 1ull)) == 0) {
+              j = hi - l;
+              break;
+            }
+          } else if (none == 0 && hi >= 64) {
+            hi -= 64;  // 64 aggregates and no leaving state yet: look further back
+            f = scan_flags();
+            continue;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins == kSpinLimit || hi < 0) {  // never hang: record it and go on
+            if (lane == 0) __hip_atomic_store(ws.header + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            j = 0;
+            break;
+          }
+          f = scan_flags();
+        }
+        // state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, four at a time
+        if (live) h_in = dev_load4(ws.H + size_t(base + j) * 256 + lane * 4);
+        for (int i = j + 1; i < int(g.chunk); i += 4) {
+          f32x4 Pb[4], Lb[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            Pb[u] = zero4();
+            Lb[u] = zero4();
+            if (i + u < int(g.chunk)) {
+              Pb[u] = dev_load4(ws.P + size_t(base + i + u) * 256 + c * 16 + 4 * r);
+              if (live) Lb[u] = dev_load4(ws.L + size_t(base + i + u) * 256 + lane * 4);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i + u < int(g.chunk)) h_in = mfma_16x16x16(Pb[u], h_in, Lb[u]);
+        }
+      }
+      const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
+      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);  // flag raised after (3)
+      *reinterpret_cast<f32x4*>(&sX[lane * 4]) = h_in;
+    }
+    lds_barrier();  // (2) the unit's entering state in LDS
+
+    // ---- this wave's entering state: the unit's, carried through the waves before it
+    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[lane * 4]);
+    for (int i = 0; i < wave; ++i)
+      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[i][c * 16 + 4 * r]), h,
+                        *reinterpret_cast<const f32x4*>(&sL[i][lane * 4]));
+    lds_barrier();  // (3) every read of sP, sL and sX for this unit is done
+
+    if (wave == 0) raise_flag(ws.flags + slot, kFlagInclusive, lane);
+
+    // ---- replay the wave's steps, storing every h[t]
+    TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
+    const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
+    auto out_at = [&](int k) -> TOut* { return o0 + (g.t0 * p.t_stride[MS_OUT] + k * to); };
+    if constexpr (M1) {
+      [&]<int... ks>(std::integer_sequence<int, ks...>) {
+        (([&] {
+           if (g.q0 + ks < T) {
+             h = mfma_16x16x16(A[ks].get(), h, bterm(std::integral_constant<int, ks>{}));
+             if (c == 0) store_h_col1(out_at(ks), h, n, r, true);
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, K>{});
+    } else {
+      // h goes row-major through this wave's map slot (free since (3)); then each lane
+      // stores 16 contiguous bytes: one step per round for f32, two for bf16
+      constexpr int kPer = sizeof(TOut) == 4 ? 1 : 2;
+      char* xs = reinterpret_cast<char*>(&sP[wave][0]);
+      [&]<int... js>(std::integer_sequence<int, js...>) {
+        (([&] {
+           constexpr int j = js;
+#pragma unroll
+           for (int s = 0; s < kPer; ++s) {
+             const int k = j * kPer + s;
+             if (g.q0 + k < T) {
+               h = mfma_16x16x16(A[k].get(), h, Bv[k].get());
+#pragma unroll
+               for (int v = 0; v < 4; ++v) {
+                 if constexpr (sizeof(TOut) == 4) {
+                   const float e = h[v];
+                   __builtin_memcpy(xs + 4 * ((4 * r + v) * 16 + c), &e, 4);
+                 } else {
+                   const uint16_t e = f32_to_bf16_rne(h[v]);
+                   __builtin_memcpy(xs + 2 * (s * 256 + (4 * r + v) * 16 + c), &e, 2);
+                 }
+               }
+             }
+           }
+           // lane l reads 16 bytes: f32, row l / 4, columns 4 (l % 4) ..; bf16, step l / 32,
+           // row (l % 32) / 2, columns 8 (l % 2) ..
+           const int k = j * kPer + (kPer == 2 ? (lane >> 5) : 0);
+           const int row = kPer == 2 ? (lane & 31) >> 1 : lane >> 2;
+           const int col = kPer == 2 ? 8 * (lane & 1) : 4 * (lane & 3);
+           uint4 v;
+           __builtin_memcpy(&v, xs + 16 * lane, 16);
+           if (g.q0 + k < T) *reinterpret_cast<uint4*>(out_at(k) + int64_t(row) * m + g.ct * 16 + col) = v;
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, K / kPer>{});
+    }
+
+    unit = next;
+    next = after_next;
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t count) {
   const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < count) p[i] = 0u;
 }
 
-constexpr int kWaves = 8;
-constexpr int kSteps = 16;
-constexpr int kUnitSteps = kWaves * kSteps;
+constexpr int kWaves = 8;          // ms_unit_kernel: waves per workgroup
+constexpr int kSteps = 16;         // steps per wave (both kernels)
+constexpr int kPipeWaves = 4;      // ms_pipe_kernel: waves per workgroup
+constexpr int kPipeBlocksPerCU = 2;
 
 struct UnitPlan {
   int col_tiles;
@@ -543,9 +898,9 @@ struct UnitPlan {
   size_t flags_bytes, block_bytes, total;
 };
 
-UnitPlan unit_plan(const MsParams& p) {
+UnitPlan unit_plan(const MsParams& p, int unit_steps) {
   UnitPlan u{};
-  u.chunks = uint64_t((p.T + kUnitSteps - 1) / kUnitSteps);
+  u.chunks = uint64_t((p.T + unit_steps - 1) / unit_steps);
   u.col_tiles = (p.m + 15) / 16;
   u.num_units = u.chunks * uint64_t(p.num_batch) * uint64_t(u.col_tiles);
   u.flags_bytes = (u.num_units * 4 + 255) / 256 * 256;
@@ -572,9 +927,46 @@ void launch_unit_variant(const MsParams& p, const MsUnitWs& ws, bool vec, unsign
                        stream, p, ws);
 }
 
+// The pipelined kernel covers n = 16 with m = 1 (f32 or bf16 inputs) or m a
+// multiple of 16 (bf16 inputs: an f32 b tile would not fit the LDS stage), and
+// needs 16-byte aligned steps of a and b (global_load_lds moves 16-byte pieces)
+// and aligned output pieces. Everything else takes ms_unit_kernel.
+bool pipe_fits(const MsParams& p) {
+  if (p.n != 16) return false;
+  const bool m1 = p.m == 1;
+  if (!m1 && !(p.in_bf16 && p.m % 16 == 0)) return false;
+  auto aligned = [&](int t, const void* base, int64_t elem, int64_t to) {
+    if (reinterpret_cast<uintptr_t>(base) % uintptr_t(to) != 0 || (p.t_stride[t] * elem) % to != 0) return false;
+    for (int d = 0; d < p.batch.nd; ++d)
+      if ((p.batch.st[t][d] * elem) % to != 0) return false;
+    return true;
+  };
+  const int64_t si = p.in_bf16 ? 2 : 4, so = p.out_bf16 ? 2 : 4;
+  return aligned(MS_A, p.a, si, 16) && aligned(MS_B, p.b, si, 16) && aligned(MS_OUT, p.out, so, m1 ? 4 * so : 16);
+}
+
+// Compute units of the current device (one resident pipelined workgroup each).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+template <typename TIn, typename TOut>
+void launch_pipe_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
+  if constexpr (sizeof(TIn) == 2)
+    hipLaunchKernelGGL((ms_pipe_kernel<kPipeWaves, TIn, TOut, false>), dim3(blocks), dim3(kPipeWaves * 64), 0, stream, p, ws);
+}
+
 template <typename TIn, typename TOut>
 hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream) {
-  const UnitPlan up = unit_plan(p);
+  const bool pipe = pipe_fits(p);
+  const UnitPlan up = unit_plan(p, pipe ? kPipeWaves * kSteps : kWaves * kSteps);
   char* base = static_cast<char*>(workspace);
   MsUnitWs ws;
   ws.header = reinterpret_cast<uint32_t*>(base);
@@ -602,6 +994,13 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
     for (int d = 0; d < p.batch.nd && vec; ++d)
       vec = (p.batch.st[MS_B][d] * int64_t(sizeof(TIn))) % va == 0 && (p.batch.st[MS_OUT][d] * int64_t(sizeof(TOut))) % vo == 0;
   }
+  if (pipe) {
+    const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(kPipeBlocksPerCU) * device_cus()));
+    if (m1)
+      hipLaunchKernelGGL((ms_pipe_kernel<kPipeWaves, TIn, TOut, true>), dim3(blocks), dim3(kPipeWaves * 64), 0, stream, p, ws);
+    else launch_pipe_tiles<TIn, TOut>(p, ws, blocks, stream);
+    return hipGetLastError();
+  }
   const unsigned blocks = unsigned(up.num_units);
   if (m1) launch_unit_variant<TIn, TOut, true>(p, ws, vec, blocks, stream);
   else launch_unit_variant<TIn, TOut, false>(p, ws, vec, blocks, stream);
@@ -612,7 +1011,11 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
 
 size_t matrix_scan_workspace(const MsParams& p) {
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return 0;
-  const UnitPlan up = unit_plan(p);
+  // Shapes only (the size is queried without dtypes or pointers): room for the
+  // pipelined kernel's shorter units whenever its shapes apply, which also
+  // covers ms_unit_kernel's longer ones.
+  const bool pipe_shape = p.n == 16 && (p.m == 1 || p.m % 16 == 0);
+  const UnitPlan up = unit_plan(p, pipe_shape ? kPipeWaves * kSteps : kWaves * kSteps);
   if (up.num_units > 0x7fffffffull) return 0;  // beyond 32-bit unit ids: the serial kernel takes it
   return up.total;
 }

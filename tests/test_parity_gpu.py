@@ -187,6 +187,47 @@ def test_matrix_small(B, T, n, m, reverse, dtype):
     assert_matrix_close(got, run_oracle(w), MS_TOL_F32 if dtype == torch.float32 else MS_TOL_BF16)
 
 
+# Shapes that take the pipelined kernel (n = 16; m = 1, or m a multiple of 16 with
+# bf16 inputs): several 16-column tiles, a last unit whose later waves lie wholly
+# past the end (700 = 5 * 128 + 60), both output types, and enough units that each
+# resident workgroup computes several of them in turn.
+@pytest.mark.parametrize("B,T,m,dtype,out,reverse", [
+    (3, 700, 32, torch.bfloat16, None, False),
+    (3, 700, 32, torch.bfloat16, None, True),
+    (2, 700, 16, torch.bfloat16, torch.float32, True),
+    (2, 333, 48, torch.bfloat16, torch.float32, False),
+    (5, 1000, 1, torch.float32, None, True),
+    (5, 1000, 1, torch.bfloat16, None, False),
+    (5, 1000, 1, torch.bfloat16, torch.float32, True),
+    (3, 77, 1, torch.float32, torch.bfloat16, False),
+    (4, 40000, 16, torch.bfloat16, None, False),
+    (2, 90000, 1, torch.float32, None, True),
+])
+def test_matrix_pipelined_shapes(B, T, m, dtype, out, reverse):
+    w = W.make_matrix(B, T, 16, m, dtype, reverse=reverse, seed=160 + m + T % 97, out_dtype=out)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert got.dtype == (out or dtype)
+    f32_bar = (out or dtype) == torch.float32
+    assert_matrix_close(got, run_oracle(w), MS_TOL_F32 if f32_bar else MS_TOL_BF16)
+
+
+@pytest.mark.parametrize("dtype,m", [(torch.float32, 1), (torch.bfloat16, 16)])
+def test_matrix_pipelined_broadcast_a(dtype, m):
+    g = torch.Generator().manual_seed(170 + m)
+    eye = torch.eye(16)
+    b = torch.randn(3, 500, 16, m, generator=g).to(dtype)
+    a = (0.9 * eye + 0.01 * torch.randn(1, 500, 16, 16, generator=g)).to(dtype)  # one a for every batch
+    ref = oracle.matrix_scan(a.float().numpy(), b.float().numpy(), axis=1)
+    got = sx.matrix_scan(a.to(DEV), b.to(DEV), axis=1)
+    tol = MS_TOL_F32 if dtype == torch.float32 else MS_TOL_BF16
+    assert_matrix_close(got, ref, tol)
+    a2 = (0.9 * eye + 0.01 * torch.randn(3, 1, 16, 16, generator=g)).to(dtype)  # constant in time
+    ref = oracle.matrix_scan(a2.float().numpy(), b.float().numpy(), axis=1, reverse=True)
+    got = sx.matrix_scan(a2.to(DEV), b.to(DEV), axis=1, reverse=True)
+    assert_matrix_close(got, ref, tol)
+
+
 def test_matrix_bf16_in_f32_out():
     w = W.make_matrix(2, 100, 16, 4, torch.bfloat16, reverse=True, seed=150, out_dtype=torch.float32)
     got = run_gpu(w, DEV)
