@@ -531,16 +531,13 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
 
 // ------------------------------------------------------------------ pipelined kernel
 //
-// ms_pipe_kernel runs the same unit scheme as ms_unit_kernel (8 waves x 16
-// steps per unit, wave maps composed by a leader, decoupled look-back) but
-// keeps the memory system busy across units: each workgroup stays resident
-// and takes units one after another, and while it computes one unit from
-// registers the inputs of its next unit stream from HBM straight into LDS
-// (global_load_lds, no registers held). When the unit ends, the staged
-// inputs move from LDS into registers and the copy of the unit after that
-// starts at once.
+// ms_lead_kernel (below) keeps the unit scheme of ms_unit_kernel (wave maps,
+// composed per unit, decoupled look-back) but overlaps everything that waits:
+// the inputs of the next unit stream into LDS while the current one is
+// computed, and a dedicated leader wave does the look-back of one unit while
+// the compute waves summarise the next.
 //
-// Layout choices that make every LDS read linear (conflict-free):
+// Layout choices that make every LDS read of a stage linear (conflict-free):
 //   a (f32):  the 16-byte piece a[c][4r..4r+3] that lane (r, c) reads sits
 //             at slot 16 r + c of the step's 1 KB block;
 //   a (bf16): the 16-byte piece a[c][8p..8p+7] sits at slot c + 16 p of the
@@ -550,8 +547,8 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
 //             16 steps of one wave (m = 1) in place of the rows of a.
 // For m a multiple of 16 (bf16 only) b is staged row by row and read back in
 // result-register order (rows 4r..4r+3 of column c, four 2-byte reads); the
-// output goes the other way through the wave's own map slots in LDS, so that
-// every lane stores 16 contiguous bytes of one row.
+// output goes the other way through a per-wave LDS slot, so that every lane
+// stores 16 contiguous bytes of one row.
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
@@ -592,17 +589,6 @@ __device__ __forceinline__ PipeGeo pipe_geo(const MsParams& p, const MsUnitWs& w
   return g;
 }
 
-// Workgroup barrier that orders LDS traffic only. __syncthreads would also wait
-// for this wave's copies into LDS still in flight (they write LDS), which must
-// keep streaming across the barrier; every stage is read only after a barrier
-// that follows its copies' vmcnt waits.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // One wave's 16 steps of a (and of b's tile) are copied into its LDS stage by
 // kPieces copy instructions of 1 KB (the bf16 m = 1 b piece is 512 bytes).
 // Piece i of the stage of the wave whose steps start at g.q0 is started here.
@@ -638,134 +624,318 @@ __device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g,
   }
 }
 
-// The copies for one unit: wave w >= 1 starts all pieces of its own stage and
-// its share of wave 0's (wave 0, the leader, keeps no copy in flight: its
-// look-back waits on vmcnt). A barrier after everyone's vmcnt wait makes all
-// stages readable.
-template <int NW, typename TIn, bool M1>
-__device__ __forceinline__ void stage_unit(const MsParams& p, const MsUnitWs& ws, uint32_t unit, int wave, int lane,
-                                           char (*stage)[PipeStage<TIn, M1>::kWave]) {
+// A compute wave's inputs for one unit, in registers: a[t] in A-operand order
+// (identity past the end) and b[t] in result-register order (zero past the end;
+// for m = 1, b of all 16 steps with step c in lane column c).
+template <typename TIn, bool M1>
+struct UnitRegs {
+  ARow<TIn> A[16];
+  BCol<TIn> Bv[M1 ? 1 : 16];
+  f32x4 b1;
+};
+
+template <typename TIn, bool M1>
+__device__ __forceinline__ void stage_to_regs(UnitRegs<TIn, M1>& R, const char* st, int64_t q0, int64_t T, int lane,
+                                              int r, int c) {
   using S = PipeStage<TIn, M1>;
-  if (wave == 0) return;
-  const PipeGeo g = pipe_geo(p, ws, unit, wave, NW * 16);
+  const ARow<TIn> eye = identity_a<TIn>(r, c);
 #pragma unroll
-  for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, &stage[wave][0], lane, i);
-  const PipeGeo g0 = pipe_geo(p, ws, unit, 0, NW * 16);
-  for (int i = wave - 1; i < S::kPieces; i += NW - 1) stage_piece<TIn, M1>(p, g0, &stage[0][0], lane, i);
+  for (int k = 0; k < 16; ++k) {
+    if constexpr (sizeof(TIn) == 4) R.A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
+    else R.A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+    R.A[k] = select_a(q0 + k < T, R.A[k], eye);
+    if constexpr (!M1) {
+      // b[4r + v][c] sits in slot (4r + v) + 16 (c / 8), at byte 2 (c % 8); rows are 16 bytes apart
+      const uint16_t* bp =
+          reinterpret_cast<const uint16_t*>(st + 16 * S::kA + k * S::kB + 16 * (4 * r + 16 * (c >> 3)) + 2 * (c & 7));
+      const bool in = q0 + k < T;
+      R.Bv[k].u = make_uint2(in ? uint32_t(bp[0]) | (uint32_t(bp[8]) << 16) : 0u,
+                             in ? uint32_t(bp[16]) | (uint32_t(bp[24]) << 16) : 0u);
+    }
+  }
+  if constexpr (M1) {
+    if constexpr (sizeof(TIn) == 4) {
+      R.b1 = *reinterpret_cast<const f32x4*>(st + 16 * S::kA + lane * 16);
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(st + 16 * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+      R.b1 = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+    }
+    if (q0 + c >= T) R.b1 = zero4();
+  }
 }
 
-template <int NW, typename TIn, typename TOut, bool M1>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void ms_pipe_kernel(const MsParams p, const MsUnitWs ws) {
-  constexpr int K = 16, kUnit = NW * K;
+template <typename TIn, bool M1, int k>
+__device__ __forceinline__ f32x4 bterm_of(const UnitRegs<TIn, M1>& R, int c) {
+  if constexpr (M1) return col0_from_lane<k>(R.b1, c);
+  else return R.Bv[k].get();
+}
+
+// The wave's map: P = a[last] ... a[first] (written row-major), L = the scan of
+// its steps from h = 0 (written in result-register order). issue(k) runs at
+// step k: it starts the copies of the next unit, spread over the steps so that
+// they never back up the memory pipeline.
+template <typename TIn, bool M1, typename Issue>
+__device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw, float* sLw, int lane, int r, int c,
+                                          Issue&& issue) {
+  f32x4 P = identity_d(r, c), L = zero4();
+  [&]<int... ks>(std::integer_sequence<int, ks...>) {
+    ((issue(ks), P = mfma_16x16x16(R.A[ks].get(), P, zero4()),
+      L = mfma_16x16x16(R.A[ks].get(), L, bterm_of<TIn, M1, ks>(R, c))),
+     ...);
+  }(std::make_integer_sequence<int, 16>{});
+#pragma unroll
+  for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = P[v];
+  *reinterpret_cast<f32x4*>(&sLw[lane * 4]) = L;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even), packed low then high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// 4 x 4 transpose inside each quad of lanes: lane j of a quad holds x[v] = M[j][v]
+// and receives M[v][j]. Two exchange levels (partner j ^ 1, then j ^ 2), each
+// taking the partner's register v ^ bit where lane and register differ in that bit.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
+  f32x4 y, z;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float pv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[v ^ 1]), 0xB1, 0xF, 0xF, false));
+    y[v] = ((j ^ v) & 1) ? pv : x[v];
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float pv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y[v ^ 2]), 0x4E, 0xF, 0xF, false));
+    z[v] = ((j ^ v) & 2) ? pv : y[v];
+  }
+  return z;
+}
+
+// Replay of one wave's 16 steps from its entering state h, storing every h[t].
+// Outputs leave registers without LDS round trips: for m = 1 each step's state
+// (lanes (r, 0)) is moved to lanes (r, step) with a DPP shift and one store per
+// lane writes all 16 steps at the end; for m = 16 a quad transpose gives each
+// lane four consecutive values of one row, stored as one piece per step.
+template <typename TIn, typename TOut, bool M1>
+__device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h, const MsParams& p, const PipeGeo& g,
+                                             int lane, int r, int c) {
+  const int64_t T = p.T;
+  const int m = p.m;
+  TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
+  const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
+  auto out_at = [&](int k) -> TOut* { return o0 + (g.t0 * p.t_stride[MS_OUT] + k * to); };
+  if constexpr (M1) {
+    f32x4 acc = zero4();  // lane (r, c) ends up with h[step c][4r .. 4r+3]
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      (([&] {
+         if (g.q0 + ks < T) {
+           h = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+#pragma unroll
+           for (int v = 0; v < 4; ++v) {
+             float x = h[v];
+             if constexpr (ks > 0)
+               x = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h[v]), 0x110 + ks, 0xF, 0xF, false));
+             acc[v] = c == ks ? x : acc[v];
+           }
+         }
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, 16>{});
+    if (g.q0 + c < T) {
+      TOut* op = out_at(c) + 4 * r;
+      if constexpr (sizeof(TOut) == 4) *reinterpret_cast<f32x4*>(op) = acc;
+      else *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    }
+  } else {
+    const int j = c & 3;
+    const int64_t row_off = int64_t(4 * r + j) * m + g.ct * 16 + 4 * (c >> 2);  // row 4r+j, columns 4(c/4)..
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      (([&] {
+         if (g.q0 + ks < T) {
+           h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+           const f32x4 t = quad_transpose(h, j);
+           TOut* op = out_at(ks) + row_off;
+           if constexpr (sizeof(TOut) == 4) *reinterpret_cast<f32x4*>(op) = t;
+           else *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]));
+         }
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, 16>{});
+  }
+}
+
+// Workgroup-local signalling through LDS words. The waves of ms_lead_kernel do
+// not meet at s_barrier: the leader and the compute waves run a unit apart.
+// A signal is published after the wave's own earlier LDS accesses have
+// completed, and a waiter reads what it waited for only after the wait.
+// The signal words are accessed with inline DS instructions: for ordinary LDS
+// accesses the compiler cannot tell them from the stages being filled by
+// global_load_lds and would first wait for every copy in flight.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t* w) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint32_t*)w));
+}
+
+__device__ __forceinline__ uint32_t lds_read_u32(const uint32_t* w) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(w)) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void lds_signal_add(uint32_t* w, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's earlier LDS accesses are done
+  if (lane == 0) asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(w)), "v"(1u) : "memory");
+}
+
+__device__ __forceinline__ void lds_signal_set(uint32_t* w, uint32_t v, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(w)), "v"(v) : "memory");
+}
+
+// Waits until *w >= target (unsigned, counts only grow).
+__device__ __forceinline__ void lds_wait_at_least(const uint32_t* w, uint32_t target) {
+  while (lds_read_u32(w) < target) __builtin_amdgcn_s_sleep(1);
+}
+
+// vmcnt(n) alone (expcnt and lgkmcnt left at their maxima), as an s_waitcnt immediate.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// ms_lead_kernel: NC compute waves, one leader wave and one loader wave per
+// workgroup; a unit is NC * 16 scan steps of one (batch, column tile).
+// Workgroups stay resident and take units one after another.
+//   - The loader streams each unit's inputs from HBM into the compute waves'
+//     LDS stages (global_load_lds, no registers held) as soon as a stage has
+//     been read, and signals when a stage has landed. It is the only wave that
+//     waits on input copies, so those waits never stall an MFMA chain.
+//   - For unit k the compute waves move their stages into registers,
+//     summarise their 16 steps each into an affine map (LDS, buffer k % 2),
+//     then replay unit k-1, whose entering state the leader has found in the
+//     meantime, storing every h[t]. Each compute wave keeps two units in
+//     registers (the one it summarises and the one it replays).
+//   - The leader composes unit k's map from the wave maps, publishes it, finds
+//     the state entering the unit by decoupled look-back over earlier units of
+//     the same (batch, tile), hands that state to the compute waves and
+//     publishes the state leaving the unit. Its round trips overlap the
+//     summary of the next unit, so a replay never waits for its own look-back.
+// The waves run a unit apart and never meet at s_barrier after the start; they
+// hand work over through LDS words.
+template <int NC, typename TIn, typename TOut, bool M1>
+__global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
+  constexpr int K = 16, kUnit = NC * K, LEADER = NC, LOADER = NC + 1;
   using S = PipeStage<TIn, M1>;
-  __shared__ __attribute__((aligned(16))) char sStage[NW][S::kWave];
-  __shared__ __attribute__((aligned(16))) float sP[NW][256];
-  __shared__ __attribute__((aligned(16))) float sL[NW][256];
-  __shared__ float sX[256];
-  __shared__ uint32_t sId[3];
+  __shared__ __attribute__((aligned(16))) char sStage[NC][S::kWave];
+  __shared__ __attribute__((aligned(16))) float sP[2][NC][256];
+  __shared__ __attribute__((aligned(16))) float sL[2][NC][256];
+  __shared__ __attribute__((aligned(16))) float sX[2][256];
+  __shared__ __attribute__((aligned(16))) float sT[256];
+  __shared__ uint32_t sId[4];
+  __shared__ uint32_t sIdCount, sSumDone, sCarryDone, sHinIt[2], sLanded[NC], sConsumed[NC];
 
   const int tid = int(threadIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane >> 4, c = lane & 15;
-  const int n = p.n, m = p.m;
   const int64_t T = p.T;
-  char* st = &sStage[wave][0];
-  const ARow<TIn> eye = identity_a<TIn>(r, c);
+  const uint32_t NU = ws.num_units;
 
-  // Unit ids come from one counter in take order; a workgroup takes each id two
-  // units before it computes it (one unit staged in LDS, one announced), so
-  // every unit a look-back waits for was taken earlier by a running workgroup,
-  // and the smallest unfinished unit is always some workgroup's current one.
   if (tid == 0) {
-    sId[0] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sId[1] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sIdCount = 0;
+    sSumDone = 0;
+    sCarryDone = 0;
+    sHinIt[0] = sHinIt[1] = 0;
+  }
+  if (tid < NC) {
+    sLanded[tid] = 0;
+    sConsumed[tid] = 0;
   }
   __syncthreads();
-  uint32_t unit = __builtin_amdgcn_readfirstlane(sId[0]);
-  uint32_t next = __builtin_amdgcn_readfirstlane(sId[1]);
-  static_assert(NW >= 2, "wave 0's stage is filled by the other waves");
-  if (unit < ws.num_units) stage_unit<NW, TIn, M1>(p, ws, unit, wave, lane, sStage);
 
-  for (int it = 0; unit < ws.num_units; ++it) {
-    if (tid == 0)
-      sId[(it + 2) % 3] = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const PipeGeo g = pipe_geo(p, ws, unit, wave, kUnit);
-    const bool live = c < min(16, m - g.ct * 16);
+  // Unit ids come from one counter in take order. The leader takes the id of
+  // unit k+2 before it works on unit k, so that the loader can stage unit k+1
+  // in time; the smallest unfinished unit is then always the one some leader
+  // is working on, whose predecessors are all done, so look-back ends.
+  auto unit_id = [&](int k) -> uint32_t {
+    lds_wait_at_least(&sIdCount, uint32_t(k) + 1);
+    return __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
+  };
 
-    // ---- this wave's 16 steps: LDS stage -> registers, then start staging the next unit
-    __builtin_amdgcn_s_waitcnt(0);  // the copies this wave started have landed ...
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    lds_barrier();                  // (0) ... and so have everyone's
-    ARow<TIn> A[K];
-    BCol<TIn> Bv[M1 ? 1 : K];
-    f32x4 b1 = zero4();
+  if (wave == LOADER) {
+    // ------------------------------------------------------------ loader
+    // Stage w of unit k is filled once compute wave w has read unit k-1 from it.
+    // Up to three stages are in flight; with only copies outstanding, vmcnt
+    // drains in issue order, so vmcnt(2 kPieces) means the oldest stage landed.
+    // The loader issues ahead of the compute waves on its SIMD: its few
+    // instructions keep the whole workgroup fed.
+    __builtin_amdgcn_s_setprio(3);
+    for (int k = 0;; ++k) {
+      const uint32_t unit = unit_id(k);
+      if (unit >= NU) break;
+      [&]<int... ws_>(std::integer_sequence<int, ws_...>) {
+        (([&] {
+           constexpr int w = ws_;
+           lds_wait_at_least(&sConsumed[w], uint32_t(k));
+           const PipeGeo g = pipe_geo(p, ws, unit, w, kUnit);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if constexpr (sizeof(TIn) == 4) A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
-      else A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
-      A[k] = select_a(g.q0 + k < T, A[k], eye);
-      if constexpr (!M1) {
-        // b[4r + v][c] sits in slot (4r + v) + 16 (c / 8), at byte 2 (c % 8); rows are 16 bytes apart
-        const uint16_t* bp = reinterpret_cast<const uint16_t*>(st + 16 * S::kA + k * S::kB + 16 * (4 * r + 16 * (c >> 3)) + 2 * (c & 7));
-        const bool in = g.q0 + k < T;
-        Bv[k].u = make_uint2(in ? uint32_t(bp[0]) | (uint32_t(bp[8]) << 16) : 0u,
-                             in ? uint32_t(bp[16]) | (uint32_t(bp[24]) << 16) : 0u);
-      }
+           for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, &sStage[w][0], lane, i);
+           if constexpr (w >= 2) {
+             __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kPieces));
+             lds_signal_set(&sLanded[w - 2], uint32_t(k) + 1, lane);
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, NC>{});
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kPieces));
+      lds_signal_set(&sLanded[NC - 2], uint32_t(k) + 1, lane);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_signal_set(&sLanded[NC - 1], uint32_t(k) + 1, lane);
     }
-    if constexpr (M1) {
-      if constexpr (sizeof(TIn) == 4) {
-        b1 = *reinterpret_cast<const f32x4*>(st + 16 * S::kA + lane * 16);
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(st + 16 * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
-        b1 = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                   __uint_as_float(u.y & 0xffff0000u)};
-      }
-      if (g.q0 + c >= T) b1 = zero4();
-    }
+    return;
+  }
 
-    auto bterm = [&](auto kc) -> f32x4 {
-      constexpr int k = decltype(kc)::value;
-      if constexpr (M1) return col0_from_lane<k>(b1, c);
-      else return Bv[k].get();
+  if (wave == LEADER) {
+    // ------------------------------------------------------------ leader
+    __builtin_amdgcn_s_setprio(2);  // its look-back is on every replay's path
+    auto take = [&](int k) {
+      uint32_t id = 0;
+      if (lane == 0) id = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      id = __builtin_amdgcn_readfirstlane(id);
+      lds_signal_set(&sId[k & 3], id, lane);
+      lds_signal_set(&sIdCount, uint32_t(k) + 1, lane);
     };
-
-    // ---- the wave's map: P = a[last] ... a[first], L = the scan of its steps from h = 0
-    f32x4 P = identity_d(r, c), L = zero4();
-    [&]<int... ks>(std::integer_sequence<int, ks...>) {
-      ((P = mfma_16x16x16(A[ks].get(), P, zero4()), L = mfma_16x16x16(A[ks].get(), L, bterm(std::integral_constant<int, ks>{}))), ...);
-    }(std::make_integer_sequence<int, K>{});
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sP[wave][(4 * r + v) * 16 + c] = P[v];
-    *reinterpret_cast<f32x4*>(&sL[wave][lane * 4]) = L;
-    lds_barrier();  // (1) wave maps in LDS, every stage read; sId[(it + 2) % 3] announced
-    const uint32_t after_next = __builtin_amdgcn_readfirstlane(sId[(it + 2) % 3]);
-    // the next unit's inputs stream in while the leader works and the unit is replayed
-    if (next < ws.num_units) stage_unit<NW, TIn, M1>(p, ws, next, wave, lane, sStage);
-
-    const uint32_t slot = g.bt * ws.chunks + g.chunk;
-    if (wave == 0) {
-      const uint32_t base = g.bt * ws.chunks;
+    take(0);
+    take(1);
+    for (int k = 0;; ++k) {
+      take(k + 2);
+      const uint32_t unit = __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
+      if (unit >= NU) break;
+      const PipeGeo g = pipe_geo(p, ws, unit, 0, kUnit);
+      const bool live = c < min(16, p.m - g.ct * 16);
+      const uint32_t base = g.bt * ws.chunks, slot = base + g.chunk;
       int hi = int(g.chunk) - 1;
       auto scan_flags = [&]() -> uint32_t {
         const int cand = hi - lane;
         return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       };
-      uint32_t f = g.chunk > 0 ? scan_flags() : 0u;  // in flight while the unit's map is composed
+      lds_wait_at_least(&sSumDone, uint32_t(NC) * uint32_t(k + 1));  // the wave maps of unit k are in LDS
       f32x4 G = identity_d(r, c), GL = zero4();
-      for (int i = 0; i < NW; ++i) {
-        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[i][c * 16 + 4 * r]);
-        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[i][lane * 4]);
+      for (int i = 0; i < NC; ++i) {
+        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[k & 1][i][c * 16 + 4 * r]);
+        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[k & 1][i][lane * 4]);
         G = mfma_16x16x16(Pa, G, zero4());
         GL = mfma_16x16x16(Pa, GL, Li);
       }
-      const f32x4 GA = to_a_operand(sX, G, r, c);
+      const f32x4 GA = to_a_operand(sT, G, r, c);
       f32x4 h_in = zero4();
       if (g.chunk > 0) {
-        // the aggregate goes out first, so that later units need not wait for this one
+        // the aggregate goes out first, so that later units need not wait for this one;
+        // the first look-back window is read while its stores complete
         dev_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
         if (live) dev_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
-        raise_flag(ws.flags + slot, kFlagAggregate, lane);  // its wait also completes the window's loads
+        uint32_t f = scan_flags();
+        raise_flag(ws.flags + slot, kFlagAggregate, lane);  // waits for the stores (and the window)
         // nearest earlier unit whose leaving state is published, with every unit in
         // between at least aggregated
         int j = 0;
@@ -792,12 +962,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           }
           f = scan_flags();
         }
-        // state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, four at a time
+        // state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, eight at a time
         if (live) h_in = dev_load4(ws.H + size_t(base + j) * 256 + lane * 4);
-        for (int i = j + 1; i < int(g.chunk); i += 4) {
-          f32x4 Pb[4], Lb[4];
+        for (int i = j + 1; i < int(g.chunk); i += 8) {
+          f32x4 Pb[8], Lb[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < 8; ++u) {
             Pb[u] = zero4();
             Lb[u] = zero4();
             if (i + u < int(g.chunk)) {
@@ -806,79 +976,62 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 8; ++u)
             if (i + u < int(g.chunk)) h_in = mfma_16x16x16(Pb[u], h_in, Lb[u]);
         }
       }
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
-      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);  // flag raised after (3)
-      *reinterpret_cast<f32x4*>(&sX[lane * 4]) = h_in;
+      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      // hand the entering state over once the replay of unit k-2 (same slot) has read its own
+      lds_wait_at_least(&sCarryDone, k >= 2 ? uint32_t(NC) * uint32_t(k - 1) : 0u);
+      *reinterpret_cast<f32x4*>(&sX[k & 1][lane * 4]) = h_in;
+      lds_signal_set(&sHinIt[k & 1], uint32_t(k) + 1, lane);
+      raise_flag(ws.flags + slot, kFlagInclusive, lane);
     }
-    lds_barrier();  // (2) the unit's entering state in LDS
+    return;
+  }
 
-    // ---- this wave's entering state: the unit's, carried through the waves before it
-    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[lane * 4]);
+  // -------------------------------------------------------------- compute waves
+  const char* st = &sStage[wave][0];
+  UnitRegs<TIn, M1> RA, RB;
+  PipeGeo gA, gB;
+
+  // Unit k: stage -> Rc, summarise unit k. Returns false (doing nothing) when there is no unit k.
+  auto step = [&](UnitRegs<TIn, M1>& Rc, PipeGeo& gc, int k) -> bool {
+    const uint32_t unit = unit_id(k);
+    if (unit >= NU) return false;
+    gc = pipe_geo(p, ws, unit, wave, kUnit);
+    lds_wait_at_least(&sLanded[wave], uint32_t(k) + 1);
+    stage_to_regs<TIn, M1>(Rc, st, gc.q0, T, lane, r, c);
+    lds_signal_set(&sConsumed[wave], uint32_t(k) + 1, lane);  // (waits for the stage reads first)
+    // map buffer k % 2 held unit k-2's maps: every wave's carry of unit k-2 is done
+    lds_wait_at_least(&sCarryDone, k >= 2 ? uint32_t(NC) * uint32_t(k - 1) : 0u);
+    summarize<TIn, M1>(Rc, &sP[k & 1][wave][0], &sL[k & 1][wave][0], lane, r, c, [](int) {});
+    lds_signal_add(&sSumDone, lane);
+    return true;
+  };
+  // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.
+  auto finish = [&](const UnitRegs<TIn, M1>& R, const PipeGeo& g, int k) {
+    lds_wait_at_least(&sHinIt[k & 1], uint32_t(k) + 1);
+    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[k & 1][lane * 4]);
     for (int i = 0; i < wave; ++i)
-      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[i][c * 16 + 4 * r]), h,
-                        *reinterpret_cast<const f32x4*>(&sL[i][lane * 4]));
-    lds_barrier();  // (3) every read of sP, sL and sX for this unit is done
+      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[k & 1][i][c * 16 + 4 * r]), h,
+                        *reinterpret_cast<const f32x4*>(&sL[k & 1][i][lane * 4]));
+    lds_signal_add(&sCarryDone, lane);
+    replay_steps<TIn, TOut, M1>(R, h, p, g, lane, r, c);
+  };
 
-    if (wave == 0) raise_flag(ws.flags + slot, kFlagInclusive, lane);
-
-    // ---- replay the wave's steps, storing every h[t]
-    TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
-    const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
-    auto out_at = [&](int k) -> TOut* { return o0 + (g.t0 * p.t_stride[MS_OUT] + k * to); };
-    if constexpr (M1) {
-      [&]<int... ks>(std::integer_sequence<int, ks...>) {
-        (([&] {
-           if (g.q0 + ks < T) {
-             h = mfma_16x16x16(A[ks].get(), h, bterm(std::integral_constant<int, ks>{}));
-             if (c == 0) store_h_col1(out_at(ks), h, n, r, true);
-           }
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, K>{});
-    } else {
-      // h goes row-major through this wave's map slot (free since (3)); then each lane
-      // stores 16 contiguous bytes: one step per round for f32, two for bf16
-      constexpr int kPer = sizeof(TOut) == 4 ? 1 : 2;
-      char* xs = reinterpret_cast<char*>(&sP[wave][0]);
-      [&]<int... js>(std::integer_sequence<int, js...>) {
-        (([&] {
-           constexpr int j = js;
-#pragma unroll
-           for (int s = 0; s < kPer; ++s) {
-             const int k = j * kPer + s;
-             if (g.q0 + k < T) {
-               h = mfma_16x16x16(A[k].get(), h, Bv[k].get());
-#pragma unroll
-               for (int v = 0; v < 4; ++v) {
-                 if constexpr (sizeof(TOut) == 4) {
-                   const float e = h[v];
-                   __builtin_memcpy(xs + 4 * ((4 * r + v) * 16 + c), &e, 4);
-                 } else {
-                   const uint16_t e = f32_to_bf16_rne(h[v]);
-                   __builtin_memcpy(xs + 2 * (s * 256 + (4 * r + v) * 16 + c), &e, 2);
-                 }
-               }
-             }
-           }
-           // lane l reads 16 bytes: f32, row l / 4, columns 4 (l % 4) ..; bf16, step l / 32,
-           // row (l % 32) / 2, columns 8 (l % 2) ..
-           const int k = j * kPer + (kPer == 2 ? (lane >> 5) : 0);
-           const int row = kPer == 2 ? (lane & 31) >> 1 : lane >> 2;
-           const int col = kPer == 2 ? 8 * (lane & 1) : 4 * (lane & 3);
-           uint4 v;
-           __builtin_memcpy(&v, xs + 16 * lane, 16);
-           if (g.q0 + k < T) *reinterpret_cast<uint4*>(out_at(k) + int64_t(row) * m + g.ct * 16 + col) = v;
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, K / kPer>{});
+  for (int k = 0;; k += 2) {
+    if (!step(RA, gA, k)) {
+      if (k > 0) finish(RB, gB, k - 1);
+      break;
     }
-
-    unit = next;
-    next = after_next;
+    if (k > 0) finish(RB, gB, k - 1);
+    if (!step(RB, gB, k + 1)) {
+      finish(RA, gA, k);
+      break;
+    }
+    finish(RA, gA, k);
   }
 }
 
@@ -889,8 +1042,7 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count) {
 
 constexpr int kWaves = 8;          // ms_unit_kernel: waves per workgroup
 constexpr int kSteps = 16;         // steps per wave (both kernels)
-constexpr int kPipeWaves = 4;      // ms_pipe_kernel: waves per workgroup
-constexpr int kPipeBlocksPerCU = 2;
+constexpr int kLeadCompute = 6;    // ms_lead_kernel: compute waves per workgroup (plus leader and loader)
 
 struct UnitPlan {
   int col_tiles;
@@ -958,15 +1110,16 @@ int device_cus() {
 }
 
 template <typename TIn, typename TOut>
-void launch_pipe_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
+void launch_lead_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
   if constexpr (sizeof(TIn) == 2)
-    hipLaunchKernelGGL((ms_pipe_kernel<kPipeWaves, TIn, TOut, false>), dim3(blocks), dim3(kPipeWaves * 64), 0, stream, p, ws);
+    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false>), dim3(blocks), dim3((kLeadCompute + 2) * 64), 0,
+                       stream, p, ws);
 }
 
 template <typename TIn, typename TOut>
 hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream) {
   const bool pipe = pipe_fits(p);
-  const UnitPlan up = unit_plan(p, pipe ? kPipeWaves * kSteps : kWaves * kSteps);
+  const UnitPlan up = unit_plan(p, pipe ? kLeadCompute * kSteps : kWaves * kSteps);
   char* base = static_cast<char*>(workspace);
   MsUnitWs ws;
   ws.header = reinterpret_cast<uint32_t*>(base);
@@ -995,10 +1148,11 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
       vec = (p.batch.st[MS_B][d] * int64_t(sizeof(TIn))) % va == 0 && (p.batch.st[MS_OUT][d] * int64_t(sizeof(TOut))) % vo == 0;
   }
   if (pipe) {
-    const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(kPipeBlocksPerCU) * device_cus()));
+    const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cus())));
     if (m1)
-      hipLaunchKernelGGL((ms_pipe_kernel<kPipeWaves, TIn, TOut, true>), dim3(blocks), dim3(kPipeWaves * 64), 0, stream, p, ws);
-    else launch_pipe_tiles<TIn, TOut>(p, ws, blocks, stream);
+      hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true>), dim3(blocks), dim3((kLeadCompute + 2) * 64), 0,
+                         stream, p, ws);
+    else launch_lead_tiles<TIn, TOut>(p, ws, blocks, stream);
     return hipGetLastError();
   }
   const unsigned blocks = unsigned(up.num_units);
@@ -1015,7 +1169,7 @@ size_t matrix_scan_workspace(const MsParams& p) {
   // pipelined kernel's shorter units whenever its shapes apply, which also
   // covers ms_unit_kernel's longer ones.
   const bool pipe_shape = p.n == 16 && (p.m == 1 || p.m % 16 == 0);
-  const UnitPlan up = unit_plan(p, pipe_shape ? kPipeWaves * kSteps : kWaves * kSteps);
+  const UnitPlan up = unit_plan(p, pipe_shape ? kLeadCompute * kSteps : kWaves * kSteps);
   if (up.num_units > 0x7fffffffull) return 0;  // beyond 32-bit unit ids: the serial kernel takes it
   return up.total;
 }
