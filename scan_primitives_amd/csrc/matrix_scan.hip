@@ -5,20 +5,26 @@
 // matrix product a step, computed in f32 (bf16 operands widen exactly);
 // :reverse runs from the end, h[t] = a[t] @ h[t+1] + b[t] from h[T] = 0.
 //
-// Kernels here:
-//   ms_chunk_kernel   the single-pass chunked scan. The scan axis is cut into
-//                     chunks of K steps; one wave owns one (batch, 16-column
-//                     tile of m, chunk) unit. It keeps the chunk's a and b in
-//                     registers, composes the chunk's affine map (A, B) with
-//                     MFMA, publishes it, takes the state entering the chunk
-//                     from its predecessors by decoupled look-back, and
-//                     replays the chunk from that state with MFMA, storing
-//                     every h[t]. Inputs are read from HBM once.
+// Kernels here (all single pass: inputs are read from HBM once):
+//   ms_lead_kernel    the pipelined scan for n = 16 (m = 1, or bf16 with m a
+//                     multiple of 16). Persistent workgroups of six compute
+//                     waves, a leader wave and a loader wave take units of 96
+//                     scan steps of one (batch, 16-column tile) from a counter.
+//                     The loader copies a unit's a and b straight into LDS;
+//                     each compute wave summarises its 16 steps into an affine
+//                     map with MFMA; the leader composes the unit's map,
+//                     publishes it, finds the state entering the unit by
+//                     decoupled look-back over earlier units, and hands it
+//                     back; the compute waves replay their steps from it,
+//                     storing every h[t].
+//   ms_unit_kernel    the same scan with one workgroup of eight waves per unit
+//                     of 128 steps and inputs loaded into registers; it takes
+//                     every shape and alignment the pipelined kernel does not.
 //   ms_serial_kernel  one 256-thread block per (batch, 16-column tile of m):
 //                     thread (i, j) owns h[i][j]; every step stages a[t] in
 //                     LDS and forms row i of a[t] @ h with a k-ordered FMA
 //                     chain. Serial in time; used when the look-back state
-//                     would not fit the chunked kernel's 32-bit unit ids.
+//                     would not fit 32-bit unit ids.
 //
 // MFMA mapping (v_mfma_f32_16x16x4_f32, wave64; lane l = 16 r + c, r = 0..3):
 //   A operand  lane (r, c) gives A[c][k], B operand gives B[k][c], for the
@@ -559,6 +565,12 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)dst, 16, 0, 0);
 }
 
+// The same with the LDS destination as a byte address (no generic-pointer
+// conversion, hence no null test, on the copy path).
+__device__ __forceinline__ void copy16_to_lds_at(const void* src, uint32_t lds_byte) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)(uintptr_t)lds_byte, 16, 0, 0);
+}
+
 template <typename TIn, bool M1>
 struct PipeStage {
   static constexpr int kA = 16 * 16 * int(sizeof(TIn));                // one a[t]
@@ -583,7 +595,13 @@ __device__ __forceinline__ PipeGeo pipe_geo(const MsParams& p, const MsUnitWs& w
   g.chunk = unit / num_bt;
   g.bt = unit % num_bt;
   g.ct = int(g.bt % uint32_t(ws.col_tiles));
-  index_offsets(p.batch, int64_t(g.bt / uint32_t(ws.col_tiles)), g.off);
+  const uint32_t batch = g.bt / uint32_t(ws.col_tiles);
+  if (p.batch.nd == 1) {  // one leading dimension (the usual case): no 64-bit divisions
+#pragma unroll
+    for (int t = 0; t < 3; ++t) g.off[t] = int64_t(batch) * p.batch.st[t][0];
+  } else {
+    index_offsets(p.batch, int64_t(batch), g.off);
+  }
   g.q0 = int64_t(g.chunk) * kUnit + int64_t(wave) * 16;
   g.t0 = p.reverse ? p.T - 1 - g.q0 : g.q0;
   return g;
@@ -621,6 +639,44 @@ __device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g,
     const int j = i - S::kPiecesA;
     copy16_to_lds(b0 + clamp(2 * j + (lane >> 5)) * tb + int64_t(c) * p.m + g.ct * 16 + 8 * ((lane >> 4) & 1),
                   sb + j * 2 * S::kB);
+  }
+}
+
+// All pieces of one wave's stage. When the wave's 16 steps all lie inside the
+// scan (every unit but the last) the sources advance by a fixed stride from
+// per-lane offsets computed once: the loader's issue rate is bound by its own
+// instruction latency, so the clamped per-piece addressing is kept for the
+// last unit only.
+template <typename TIn, bool M1>
+__device__ __forceinline__ void stage_wave(const MsParams& p, const PipeGeo& g, char* st, uint32_t st_lds, int lane) {
+  using S = PipeStage<TIn, M1>;
+  if (g.q0 + 16 > p.T) {
+#pragma unroll
+    for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, st, lane, i);
+    return;
+  }
+  const TIn* a0 = static_cast<const TIn*>(p.a) + g.off[MS_A] + g.t0 * p.t_stride[MS_A];
+  const TIn* b0 = static_cast<const TIn*>(p.b) + g.off[MS_B] + g.t0 * p.t_stride[MS_B];
+  const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
+  const int64_t tb = p.reverse ? -p.t_stride[MS_B] : p.t_stride[MS_B];
+  const int c = lane & 15;
+  if constexpr (sizeof(TIn) == 4) {
+    const TIn* src = a0 + c * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < S::kPiecesA; ++i) copy16_to_lds_at(src + i * ta, st_lds + i * S::kA);
+  } else {
+    const TIn* src = a0 + (lane >> 5) * ta + c * 16 + 8 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int i = 0; i < S::kPiecesA; ++i) copy16_to_lds_at(src + 2 * i * ta, st_lds + i * 2 * S::kA);
+  }
+  const uint32_t sb = st_lds + 16 * S::kA;
+  if constexpr (M1) {
+    if constexpr (sizeof(TIn) == 4) copy16_to_lds_at(b0 + c * tb + 4 * (lane >> 4), sb);
+    else if (lane < 32) copy16_to_lds_at(b0 + c * tb + 8 * (lane >> 4), sb);
+  } else {
+    const TIn* src = b0 + (lane >> 5) * tb + int64_t(c) * p.m + g.ct * 16 + 8 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) copy16_to_lds_at(src + 2 * j * tb, sb + j * 2 * S::kB);
   }
 }
 
@@ -821,21 +877,37 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     publishes the state leaving the unit. Its round trips overlap the
 //     summary of the next unit, so a replay never waits for its own look-back.
 // The waves run a unit apart and never meet at s_barrier after the start; they
-// hand work over through LDS words.
+// hand work over through LDS words. A counter that several waves raise only
+// says "all of unit k are in" if no wave can add for a later unit first. A
+// compute wave summarises unit k >= 2 only after every wave's carry of unit
+// k-2, which each wave makes after summarising unit k-1; so the carry count
+// is unambiguous. The summary counts are kept per map buffer (k % 2): unit 1
+// has no carry to wait for, and with one shared count a fast wave's unit-1
+// summary could stand in for a slow wave's unit-0 summary not yet written.
+//
+// Placement: wave i runs on SIMD i % 4, and a wave that shares a SIMD with a
+// wave running MFMA chains gets few issue slots (measured: a copy-issuing wave
+// falls from 6.6 to 0.9 TB/s). So the six compute waves are waves 0, 1, 2, 4,
+// 5, 6 (SIMDs 0-2, two each) and the leader (wave 3) and the loader (wave 7)
+// share SIMD 3, where no MFMA chain runs.
 template <int NC, typename TIn, typename TOut, bool M1>
-__global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
-  constexpr int K = 16, kUnit = NC * K, LEADER = NC, LOADER = NC + 1;
+__global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
+  static_assert(NC == 6, "compute waves fill SIMDs 0-2, two each");
+  constexpr int K = 16, kUnit = NC * K, LEADER = 3, LOADER = 7;
   using S = PipeStage<TIn, M1>;
+  static_assert(3 * S::kPieces <= 63, "the loader keeps up to three stages in flight");
   __shared__ __attribute__((aligned(16))) char sStage[NC][S::kWave];
   __shared__ __attribute__((aligned(16))) float sP[2][NC][256];
   __shared__ __attribute__((aligned(16))) float sL[2][NC][256];
   __shared__ __attribute__((aligned(16))) float sX[2][256];
   __shared__ __attribute__((aligned(16))) float sT[256];
   __shared__ uint32_t sId[4];
-  __shared__ uint32_t sIdCount, sSumDone, sCarryDone, sHinIt[2], sLanded[NC], sConsumed[NC];
+  __shared__ uint32_t sIdCount, sSumDone[2], sCarryDone, sHinIt[2], sLanded[NC], sConsumed[NC];
 
   const int tid = int(threadIdx.x);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // compute waves are numbered 0..NC-1 in unit step order
+  const int wave = hw_wave < LEADER ? hw_wave : hw_wave - 1;
   const int lane = tid & 63;
   const int r = lane >> 4, c = lane & 15;
   const int64_t T = p.T;
@@ -843,7 +915,7 @@ __global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p
 
   if (tid == 0) {
     sIdCount = 0;
-    sSumDone = 0;
+    sSumDone[0] = sSumDone[1] = 0;
     sCarryDone = 0;
     sHinIt[0] = sHinIt[1] = 0;
   }
@@ -862,40 +934,51 @@ __global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p
     return __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
   };
 
-  if (wave == LOADER) {
+  if (hw_wave == LOADER) {
     // ------------------------------------------------------------ loader
-    // Stage w of unit k is filled once compute wave w has read unit k-1 from it.
-    // Up to three stages are in flight; with only copies outstanding, vmcnt
-    // drains in issue order, so vmcnt(2 kPieces) means the oldest stage landed.
-    // The loader issues ahead of the compute waves on its SIMD: its few
-    // instructions keep the whole workgroup fed.
-    __builtin_amdgcn_s_setprio(3);
+    const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const uint32_t*>(&sStage[0][0])));
+    // Stage w of unit k is filled once compute wave w has read unit k-1 from it,
+    // in whatever order the compute waves free their stages. Landings are
+    // confirmed with vmcnt(0), which relies on no ordering among the copies:
+    // whenever three stages are in flight or there is nothing to issue, the
+    // loader waits for all of them and signals them all. (Signalling the
+    // oldest stage alone with a partial vmcnt wait measured no faster.)
     for (int k = 0;; ++k) {
       const uint32_t unit = unit_id(k);
       if (unit >= NU) break;
-      [&]<int... ws_>(std::integer_sequence<int, ws_...>) {
-        (([&] {
-           constexpr int w = ws_;
-           lds_wait_at_least(&sConsumed[w], uint32_t(k));
-           const PipeGeo g = pipe_geo(p, ws, unit, w, kUnit);
-#pragma unroll
-           for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, &sStage[w][0], lane, i);
-           if constexpr (w >= 2) {
-             __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kPieces));
-             lds_signal_set(&sLanded[w - 2], uint32_t(k) + 1, lane);
-           }
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, NC>{});
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kPieces));
-      lds_signal_set(&sLanded[NC - 2], uint32_t(k) + 1, lane);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      lds_signal_set(&sLanded[NC - 1], uint32_t(k) + 1, lane);
+      uint32_t issued = 0, pending = 0;  // stages started / started but not yet signalled
+      int n_issued = 0, n_pending = 0;
+      auto flush = [&]() {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        for (int w = 0; w < NC; ++w)
+          if ((pending >> w) & 1u) lds_signal_set(&sLanded[w], uint32_t(k) + 1, lane);
+        pending = 0;
+        n_pending = 0;
+      };
+      while (n_issued < NC) {
+        bool progress = false;
+        for (int w = 0; w < NC; ++w) {
+          if ((issued >> w) & 1u) continue;
+          if (lds_read_u32(&sConsumed[w]) < uint32_t(k)) continue;
+          if (n_pending == 3) flush();
+          stage_wave<TIn, M1>(p, pipe_geo(p, ws, unit, w, kUnit), &sStage[w][0], stage_lds + w * S::kWave, lane);
+          pending |= 1u << w;
+          ++n_pending;
+          issued |= 1u << w;
+          ++n_issued;
+          progress = true;
+        }
+        if (!progress) {
+          if (n_pending > 0) flush();
+          else __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      if (n_pending > 0) flush();
     }
     return;
   }
 
-  if (wave == LEADER) {
+  if (hw_wave == LEADER) {
     // ------------------------------------------------------------ leader
     __builtin_amdgcn_s_setprio(2);  // its look-back is on every replay's path
     auto take = [&](int k) {
@@ -919,7 +1002,7 @@ __global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p
         const int cand = hi - lane;
         return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       };
-      lds_wait_at_least(&sSumDone, uint32_t(NC) * uint32_t(k + 1));  // the wave maps of unit k are in LDS
+      lds_wait_at_least(&sSumDone[k & 1], uint32_t(NC) * uint32_t(k / 2 + 1));  // the wave maps of unit k are in LDS
       f32x4 G = identity_d(r, c), GL = zero4();
       for (int i = 0; i < NC; ++i) {
         const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[k & 1][i][c * 16 + 4 * r]);
@@ -1007,7 +1090,7 @@ __global__ __launch_bounds__((NC + 2) * 64) void ms_lead_kernel(const MsParams p
     // map buffer k % 2 held unit k-2's maps: every wave's carry of unit k-2 is done
     lds_wait_at_least(&sCarryDone, k >= 2 ? uint32_t(NC) * uint32_t(k - 1) : 0u);
     summarize<TIn, M1>(Rc, &sP[k & 1][wave][0], &sL[k & 1][wave][0], lane, r, c, [](int) {});
-    lds_signal_add(&sSumDone, lane);
+    lds_signal_add(&sSumDone[k & 1], lane);
     return true;
   };
   // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.
@@ -1112,8 +1195,7 @@ int device_cus() {
 template <typename TIn, typename TOut>
 void launch_lead_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
   if constexpr (sizeof(TIn) == 2)
-    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false>), dim3(blocks), dim3((kLeadCompute + 2) * 64), 0,
-                       stream, p, ws);
+    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false>), dim3(blocks), dim3(512), 0, stream, p, ws);
 }
 
 template <typename TIn, typename TOut>
@@ -1150,8 +1232,7 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
   if (pipe) {
     const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cus())));
     if (m1)
-      hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true>), dim3(blocks), dim3((kLeadCompute + 2) * 64), 0,
-                         stream, p, ws);
+      hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true>), dim3(blocks), dim3(512), 0, stream, p, ws);
     else launch_lead_tiles<TIn, TOut>(p, ws, blocks, stream);
     return hipGetLastError();
   }

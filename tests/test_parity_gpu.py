@@ -228,6 +228,76 @@ def test_matrix_pipelined_broadcast_a(dtype, m):
     assert_matrix_close(got, ref, tol)
 
 
+# The pipelined kernel hands staged inputs and look-back state between waves and
+# workgroups; a handoff made too early shows up only now and then (it did: a
+# stage signalled before its last copy landed). Repeated calls, each on a
+# workspace refilled with random bytes, are checked one by one.
+@pytest.mark.parametrize("idx", [3, 4])
+def test_matrix_repeated_calls_dirty_workspace(idx):
+    from scan_primitives_amd import _binding as Bd
+    (w,) = W.standard_workloads([idx])
+    _announce(w)
+    t = w.on(DEV)
+    a, b = t["a"], t["b"]
+    ref = run_oracle(w)
+    lib = Bd.load_library()
+    i64 = Bd.i64_array
+    ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), i64(a.shape), b.dim(), i64(b.shape), w.axis)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(b)
+    code = Bd._DTYPES[a.dtype]
+    tol = MS_TOL_F32 if a.dtype == torch.float32 else MS_TOL_BF16
+    for rep in range(6):
+        ws.random_(0, 256)
+        st = lib.sx_matrix_scan(code, a.dim(), i64(a.shape), i64(a.stride()), a.data_ptr(), b.dim(), i64(b.shape),
+                                i64(b.stride()), b.data_ptr(), w.axis, 1 if w.reverse else 0, 0, code, out.data_ptr(),
+                                ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
+        assert st == 0, lib.sx_last_error()
+        torch.cuda.synchronize()
+        assert int(ws[4:8].view(torch.int32).item()) == 0, "a look-back hit its spin limit"
+        assert_matrix_close(out, ref, tol)
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_matrix_step_residual_repeated_calls(idx):
+    """Every stored state must follow from its predecessor by one step of the
+    recurrence: r[t] = h[t] - (a[t] @ h[t-1] + b[t]) (h[t+1] for :reverse).
+    The residual locates an error where it enters (a state handed across a
+    unit boundary shows up at that step alone), whereas a comparison with the
+    oracle sees it only if the products downstream do not damp it below the
+    tolerance. Twenty calls on a dirty workspace; the bar is the storage
+    rounding of h (bf16 keeps 8 bits), relative to the RMS state norm."""
+    from scan_primitives_amd import _binding as Bd
+    (w,) = W.standard_workloads([idx])
+    _announce(w)
+    assert w.axis == 1
+    t = w.on(DEV)
+    a, b = t["a"], t["b"]
+    af, bf = a.float(), b.float()
+    lib = Bd.load_library()
+    i64 = Bd.i64_array
+    ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), i64(a.shape), b.dim(), i64(b.shape), w.axis)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(b)
+    code = Bd._DTYPES[a.dtype]
+    bar = 1e-4 if out.dtype == torch.float32 else 1.5e-2
+    for rep in range(20):
+        ws.random_(0, 256)
+        st = lib.sx_matrix_scan(code, a.dim(), i64(a.shape), i64(a.stride()), a.data_ptr(), b.dim(), i64(b.shape),
+                                i64(b.stride()), b.data_ptr(), w.axis, 1 if w.reverse else 0, 0, code, out.data_ptr(),
+                                ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
+        assert st == 0, lib.sx_last_error()
+        h = out.float()
+        zero = torch.zeros_like(h[:, :1])
+        prev = torch.cat([h[:, 1:], zero], dim=1) if w.reverse else torch.cat([zero, h[:, :-1]], dim=1)
+        res = (h - (torch.matmul(af, prev) + bf)).flatten(2).norm(dim=-1)
+        scale = h.flatten(2).norm(dim=-1).pow(2).mean(dim=1, keepdim=True).sqrt()
+        rel = res / scale
+        worst = int(torch.argmax(rel).item())
+        assert rel.max().item() <= bar, (f"call {rep}: residual {rel.max().item():.3g} at (batch, t) = "
+                                         f"{divmod(worst, rel.shape[1])}")
+
+
 def test_matrix_bf16_in_f32_out():
     w = W.make_matrix(2, 100, 16, 4, torch.bfloat16, reverse=True, seed=150, out_dtype=torch.float32)
     got = run_gpu(w, DEV)
