@@ -12,9 +12,10 @@ stream), so host-side launch work stays out of the timed region; W untimed
 replays come first, then K timed replays bracketed by device synchronisation.
 
 Each workload's call is also timed on its own: a graph of R back-to-back
-calls (R chosen so a replay moves at least 32 MiB), replayed K times between
-two HIP events on the capture stream; the per-call time is the elapsed time
-over K * R. This gives each workload's elements/s, algorithmic GB/s and
+calls (R >= 16, and enough calls that a replay moves at least 32 MiB, up to
+64), replayed K times between two HIP events on the capture stream; the
+per-call time is the elapsed time over K * R, so the few microseconds a graph
+launch costs are spread over R calls. This gives each workload's elements/s, algorithmic GB/s and
 fraction of the 8 TB/s HBM peak.
 
 Prints ONE JSON line on stdout. ``value`` is output elements per second over
@@ -160,7 +161,7 @@ def main() -> int:
     for _ in range(2):
         one_step()
     torch.cuda.synchronize()
-    reps = [max(1, min(64, math.ceil((32 << 20) / w.algorithmic_bytes))) for w in workloads]
+    reps = [max(16, min(64, math.ceil((32 << 20) / w.algorithmic_bytes))) for w in workloads]
     graphs, step_graph, keep = [], None, []
     if not args.eager:
         for w, t, r in zip(workloads, resident, reps):
