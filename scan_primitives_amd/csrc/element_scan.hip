@@ -86,8 +86,8 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   if (full > 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      cx[u] = xp[u * dx];
-      cs[u] = sp[u * ds];
+      cx[u] = ld_stream(xp + u * dx);
+      cs[u] = ld_stream(sp + u * ds);
     }
   }
   for (int64_t t = 0; t < full; t += U) {
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        nx[u] = xp[(U + u) * dx];
-        ns[u] = sp[(U + u) * ds];
+        nx[u] = ld_stream(xp + (U + u) * dx);
+        ns[u] = ld_stream(sp + (U + u) * ds);
       }
     }
 #pragma unroll
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     }
   }
   for (int64_t t = full; t < T; ++t) {
-    h = elementwise_body<BODY>(h, *xp, *sp);
+    h = elementwise_body<BODY>(h, ld_stream(xp), ld_stream(sp));
     *op = h;
     xp += dx;
     sp += ds;
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
   for (int k = 0; k < S; ++k) {
     const int64_t q = int64_t(wave) * S + k;
     const int64_t t = time_of(q);
-    const float xv = xl[t * sx], cv = cl[t * sc];
+    const float xv = ld_stream(xl + t * sx), cv = ld_stream(cl + t * sc);
     cx[k] = q < T ? xv : kNegInf;
     cc[k] = q < T ? cv : 0.0f;
   }
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
     for (int k = 0; k < S; ++k) {  // next slab, in flight during this one
       const int64_t q = qw + kSlab + k;
       const int64_t t = time_of(q);
-      const float xv = xl[t * sx], cv = cl[t * sc];
+      const float xv = ld_stream(xl + t * sx), cv = ld_stream(cl + t * sc);
       nx[k] = q < T ? xv : kNegInf;
       nc[k] = q < T ? cv : 0.0f;
     }
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
     for (int k = 0; k < S; ++k) {
       hw = fmaxf(hw - cc[k], cx[k]);
       const int64_t q = qw + k;
-      if (live && q < T) ol[time_of(q) * so] = hw;
+      if (live && q < T) st_stream(ol + time_of(q) * so, hw);
     }
 #pragma unroll
     for (int k = 0; k < S; ++k) {

