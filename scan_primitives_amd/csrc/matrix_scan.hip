@@ -1184,18 +1184,6 @@ bool pipe_fits(const MsParams& p) {
   return aligned(MS_A, p.a, si, 16) && aligned(MS_B, p.b, si, 16) && aligned(MS_OUT, p.out, so, m1 ? 4 * so : 16);
 }
 
-// Compute units of the current device (one resident pipelined workgroup each).
-int device_cus() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (dev < 64) cached[dev] = cus;
-  return cus;
-}
-
 template <typename TIn, typename TOut>
 void launch_lead_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
   if constexpr (sizeof(TIn) == 2)
@@ -1234,7 +1222,7 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
       vec = (p.batch.st[MS_B][d] * int64_t(sizeof(TIn))) % va == 0 && (p.batch.st[MS_OUT][d] * int64_t(sizeof(TOut))) % vo == 0;
   }
   if (pipe) {
-    const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cus())));
+    const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cu_count())));
     if (m1)
       hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true>), dim3(blocks), dim3(512), 0, stream, p, ws);
     else launch_lead_tiles<TIn, TOut>(p, ws, blocks, stream);

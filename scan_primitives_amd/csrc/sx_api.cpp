@@ -14,6 +14,21 @@
 
 #include "sx_common.hpp"
 
+namespace sx {
+
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+}  // namespace sx
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -277,6 +292,8 @@ sx_status sx_element_scan(sx_body body, int rank, const int64_t* shape, int axis
   const size_t need = sx::element_scan_workspace(body, plan.p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(SX_E_WORKSPACE, "element-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SX_E_WORKSPACE, "element-scan: workspace must be 256-byte aligned");
 
   plan.p.reverse = reverse ? 1 : 0;
   plan.p.x = x;

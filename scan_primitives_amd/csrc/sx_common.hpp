@@ -38,6 +38,10 @@ __device__ __forceinline__ void index_offsets(const IndexMap<NT>& m, int64_t idx
   }
 }
 
+// Compute units of the current device (the persistent kernels keep one or two
+// workgroups resident on each); cached per device.
+int device_cu_count();
+
 // ---------------------------------------------------------------- element-scan
 
 enum EsTensor { ES_X = 0, ES_S = 1, ES_INIT = 2, ES_OUT = 3 };

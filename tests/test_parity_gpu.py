@@ -64,7 +64,6 @@ def test_max_plus_small(shape, axis, reverse):
 
 
 @pytest.mark.parametrize("shape,axis,reverse", [
-    ((33, 700, 256), 1, True),     # 8448 lanes, 700 trips: 2 full slabs and a ragged one
     ((33, 600, 250), 1, False),    # 8250 lanes: the last 64-lane group is partial
     ((520, 40, 17), 1, True),      # too short an axis for slabs: the lane kernel
     ((9000, 513), 0, True),        # long axis, few lanes: the lane kernel
@@ -75,6 +74,39 @@ def test_max_plus_slab_path(shape, axis, reverse):
     _announce(w)
     got = run_gpu(w, DEV)
     assert_element_close(got, run_oracle(w))
+
+
+@pytest.mark.parametrize("shape,axis,reverse", [
+    ((33, 700, 256), 1, True),     # 8448 lanes, 700 trips: the slab kernel, 2 full slabs and a ragged one
+    ((3, 1000, 512), 1, False),    # below 8192 lanes the lane kernel runs: two rows of lanes per batch
+    ((1, 200, 256), 1, False),     # one row of lanes
+    ((2, 128, 768), 1, True),      # a short axis
+    ((4, 5000, 256), 1, True),     # a long axis
+    ((300, 1024), 0, False),       # axis 0: the lanes are the contiguous last dim
+])
+def test_max_plus_rows_path(shape, axis, reverse):
+    """Lanes along a contiguous last dim, with ragged axis lengths."""
+    w = W.make_max_plus(shape, axis=axis, reverse=reverse, seed=112)
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert_element_close(got, run_oracle(w))
+
+
+def test_max_plus_rows_strided_views():
+    """Padded rows, a strided initial, and a view shifted by one element."""
+    g = torch.Generator().manual_seed(113)
+    xb = torch.randn(5, 300, 320, generator=g)
+    cb = 0.1 * torch.rand(5, 300, 320, generator=g)
+    ib = torch.randn(256, 5, generator=g)
+    x, c, init = xb[:, :, :256], cb[:, :, :256], ib.t()  # init [5, 256] with strides (1, 5)
+    ref = oracle.element_scan("max_plus", init.numpy(), [x.numpy(), c.numpy()], axis=1, reverse=True)
+    got = sx.element_scan("max_plus", init.to(DEV), [xb.to(DEV)[:, :, :256], cb.to(DEV)[:, :, :256]], axis=1,
+                          reverse=True)
+    assert_element_close(got, ref)
+    x1, c1 = xb[:, :, 1:257], cb[:, :, 1:257]
+    ref = oracle.element_scan("max_plus", init.numpy(), [x1.numpy(), c1.numpy()], axis=1, reverse=False)
+    got = sx.element_scan("max_plus", init.to(DEV), [xb.to(DEV)[:, :, 1:257], cb.to(DEV)[:, :, 1:257]], axis=1)
+    assert_element_close(got, ref)
 
 
 @pytest.mark.parametrize("B,T,H,n,gate,reverse", [
