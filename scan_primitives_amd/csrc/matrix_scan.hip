@@ -788,23 +788,45 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
   TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
   const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
   auto out_at = [&](int k) -> TOut* { return o0 + (g.t0 * p.t_stride[MS_OUT] + k * to); };
+  // Every unit but the last has all 16 steps inside the scan. For those the
+  // steps carry no test and are software-pipelined: step k's MFMA chain is
+  // issued from h[k-1], then h[k-1]'s output work (gather or transpose,
+  // packing, store), which needs no MFMA result still in flight, runs while
+  // that chain executes.
+  const bool full = g.q0 + 16 <= T;
   if constexpr (M1) {
     f32x4 acc = zero4();  // lane (r, c) ends up with h[step c][4r .. 4r+3]
-    [&]<int... ks>(std::integer_sequence<int, ks...>) {
-      (([&] {
-         if (g.q0 + ks < T) {
-           h = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+    auto gather = [&](auto ks_c, const f32x4& hv) {  // h[ks] (lanes (r, 0)) into column ks
+      constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
-           for (int v = 0; v < 4; ++v) {
-             float x = h[v];
-             if constexpr (ks > 0)
-               x = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h[v]), 0x110 + ks, 0xF, 0xF, false));
-             acc[v] = c == ks ? x : acc[v];
+      for (int v = 0; v < 4; ++v) {
+        float x = hv[v];
+        if constexpr (ks > 0)
+          x = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hv[v]), 0x110 + ks, 0xF, 0xF, false));
+        acc[v] = c == ks ? x : acc[v];
+      }
+    };
+    if (full) {
+      [&]<int... ks>(std::integer_sequence<int, ks...>) {
+        (([&] {
+           const f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+           if constexpr (ks > 0) gather(std::integral_constant<int, ks - 1>{}, h);
+           h = hn;
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, 16>{});
+      gather(std::integral_constant<int, 15>{}, h);
+    } else {
+      [&]<int... ks>(std::integer_sequence<int, ks...>) {
+        (([&] {
+           if (g.q0 + ks < T) {
+             h = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+             gather(std::integral_constant<int, ks>{}, h);
            }
-         }
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, 16>{});
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, 16>{});
+    }
     if (g.q0 + c < T) {
       TOut* op = out_at(c) + 4 * r;
       if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), acc);
@@ -813,18 +835,33 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
   } else {
     const int j = c & 3;
     const int64_t row_off = int64_t(4 * r + j) * m + g.ct * 16 + 4 * (c >> 2);  // row 4r+j, columns 4(c/4)..
-    [&]<int... ks>(std::integer_sequence<int, ks...>) {
-      (([&] {
-         if (g.q0 + ks < T) {
-           h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
-           const f32x4 t = quad_transpose(h, j);
-           TOut* op = out_at(ks) + row_off;
-           if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), t);
-           else st_stream(reinterpret_cast<u32x2*>(op), u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])});
-         }
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, 16>{});
+    auto emit = [&](int ks, const f32x4& hv) {  // h[ks] to memory, four consecutive values of one row per lane
+      const f32x4 t = quad_transpose(hv, j);
+      TOut* op = out_at(ks) + row_off;
+      if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), t);
+      else st_stream(reinterpret_cast<u32x2*>(op), u32x2{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])});
+    };
+    if (full) {
+      [&]<int... ks>(std::integer_sequence<int, ks...>) {
+        (([&] {
+           const f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+           if constexpr (ks > 0) emit(ks - 1, h);
+           h = hn;
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, 16>{});
+      emit(15, h);
+    } else {
+      [&]<int... ks>(std::integer_sequence<int, ks...>) {
+        (([&] {
+           if (g.q0 + ks < T) {
+             h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+             emit(ks, h);
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, 16>{});
+    }
   }
 }
 
@@ -871,7 +908,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     been read, and signals when a stage has landed. It is the only wave that
 //     waits on input copies, so those waits never stall an MFMA chain.
 //   - For unit k the compute waves move their stages into registers,
-//     summarise their 16 steps each into an affine map (LDS, buffer k % 2),
+//     summarise their 16 steps each into an affine map (LDS, slot k % 4),
 //     then replay unit k-1, whose entering state the leader has found in the
 //     meantime, storing every h[t]. Each compute wave keeps two units in
 //     registers (the one it summarises and the one it replays).
@@ -881,13 +918,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     publishes the state leaving the unit. Its round trips overlap the
 //     summary of the next unit, so a replay never waits for its own look-back.
 // The waves run a unit apart and never meet at s_barrier after the start; they
-// hand work over through LDS words. A counter that several waves raise only
-// says "all of unit k are in" if no wave can add for a later unit first. A
-// compute wave summarises unit k >= 2 only after every wave's carry of unit
-// k-2, which each wave makes after summarising unit k-1; so the carry count
-// is unambiguous. The summary counts are kept per map buffer (k % 2): unit 1
-// has no carry to wait for, and with one shared count a fast wave's unit-1
-// summary could stand in for a slow wave's unit-0 summary not yet written.
+// hand work over through LDS words. Per-unit LDS slots rotate over four
+// units, and so do the counters that guard them: a counter that several
+// waves raise only says "all of unit k are in" if no wave can add for a later
+// unit on the same counter first. A compute wave summarises unit k into slot
+// k % 4 only after every wave's carry of unit k-4 out of that slot; each wave
+// carries its units in order and summarises unit k+1 before it carries unit
+// k. So when any wave adds its summary or carry of unit k+4 to slot k % 4,
+// every wave has already added its summary and carry of unit k there. (With
+// one shared summary count, a fast wave's unit-1 summary, which has no carry
+// to wait for, once stood in for a slow wave's unit-0 summary not yet written.)
 //
 // Placement: wave i runs on SIMD i % 4, and a wave that shares a SIMD with a
 // wave running MFMA chains gets few issue slots (measured: a copy-issuing wave
@@ -901,12 +941,16 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   using S = PipeStage<TIn, M1>;
   static_assert(3 * S::kPieces <= 63, "the loader keeps up to three stages in flight");
   __shared__ __attribute__((aligned(16))) char sStage[NC][S::kWave];
-  __shared__ __attribute__((aligned(16))) float sP[2][NC][256];
-  __shared__ __attribute__((aligned(16))) float sL[2][NC][256];
-  __shared__ __attribute__((aligned(16))) float sX[2][256];
+  // Per-unit LDS slots (wave maps, entering state and their signals) rotate
+  // over kBufs units, so that a wave can run up to kBufs - 2 units ahead of
+  // the slowest wave's carry before it has to wait.
+  constexpr int kBufs = 4;
+  __shared__ __attribute__((aligned(16))) float sP[kBufs][NC][256];
+  __shared__ __attribute__((aligned(16))) float sL[kBufs][NC][256];
+  __shared__ __attribute__((aligned(16))) float sX[kBufs][256];
   __shared__ __attribute__((aligned(16))) float sT[256];
   __shared__ uint32_t sId[4];
-  __shared__ uint32_t sIdCount, sSumDone[2], sCarryDone, sHinIt[2], sLanded[NC], sConsumed[NC];
+  __shared__ uint32_t sIdCount, sSumDone[kBufs], sCarryDone[kBufs], sHinIt[kBufs], sLanded[NC], sConsumed[NC];
 
   const int tid = int(threadIdx.x);
   const int hw_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -919,9 +963,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
 
   if (tid == 0) {
     sIdCount = 0;
-    sSumDone[0] = sSumDone[1] = 0;
-    sCarryDone = 0;
-    sHinIt[0] = sHinIt[1] = 0;
+    for (int b = 0; b < kBufs; ++b) sSumDone[b] = sCarryDone[b] = sHinIt[b] = 0;
   }
   if (tid < NC) {
     sLanded[tid] = 0;
@@ -1006,11 +1048,12 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
         const int cand = hi - lane;
         return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       };
-      lds_wait_at_least(&sSumDone[k & 1], uint32_t(NC) * uint32_t(k / 2 + 1));  // the wave maps of unit k are in LDS
+      const int kb = k % kBufs;
+      lds_wait_at_least(&sSumDone[kb], uint32_t(NC) * uint32_t(k / kBufs + 1));  // the wave maps of unit k are in LDS
       f32x4 G = identity_d(r, c), GL = zero4();
       for (int i = 0; i < NC; ++i) {
-        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[k & 1][i][c * 16 + 4 * r]);
-        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[k & 1][i][lane * 4]);
+        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]);
+        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]);
         G = mfma_16x16x16(Pa, G, zero4());
         GL = mfma_16x16x16(Pa, GL, Li);
       }
@@ -1070,9 +1113,9 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
       if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
       // hand the entering state over once the replay of unit k-2 (same slot) has read its own
-      lds_wait_at_least(&sCarryDone, k >= 2 ? uint32_t(NC) * uint32_t(k - 1) : 0u);
-      *reinterpret_cast<f32x4*>(&sX[k & 1][lane * 4]) = h_in;
-      lds_signal_set(&sHinIt[k & 1], uint32_t(k) + 1, lane);
+      lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
+      *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
+      lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
       raise_flag(ws.flags + slot, kFlagInclusive, lane);
     }
     return;
@@ -1091,20 +1134,21 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     lds_wait_at_least(&sLanded[wave], uint32_t(k) + 1);
     stage_to_regs<TIn, M1>(Rc, st, gc.q0, T, lane, r, c);
     lds_signal_set(&sConsumed[wave], uint32_t(k) + 1, lane);  // (waits for the stage reads first)
-    // map buffer k % 2 held unit k-2's maps: every wave's carry of unit k-2 is done
-    lds_wait_at_least(&sCarryDone, k >= 2 ? uint32_t(NC) * uint32_t(k - 1) : 0u);
-    summarize<TIn, M1>(Rc, &sP[k & 1][wave][0], &sL[k & 1][wave][0], lane, r, c, [](int) {});
-    lds_signal_add(&sSumDone[k & 1], lane);
+    const int kb = k % kBufs;
+    lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
+    summarize<TIn, M1>(Rc, &sP[kb][wave][0], &sL[kb][wave][0], lane, r, c, [](int) {});
+    lds_signal_add(&sSumDone[kb], lane);
     return true;
   };
   // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.
   auto finish = [&](const UnitRegs<TIn, M1>& R, const PipeGeo& g, int k) {
-    lds_wait_at_least(&sHinIt[k & 1], uint32_t(k) + 1);
-    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[k & 1][lane * 4]);
+    const int kb = k % kBufs;
+    lds_wait_at_least(&sHinIt[kb], uint32_t(k) + 1);
+    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[kb][lane * 4]);
     for (int i = 0; i < wave; ++i)
-      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[k & 1][i][c * 16 + 4 * r]), h,
-                        *reinterpret_cast<const f32x4*>(&sL[k & 1][i][lane * 4]));
-    lds_signal_add(&sCarryDone, lane);
+      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]), h,
+                        *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]));
+    lds_signal_add(&sCarryDone[kb], lane);
     replay_steps<TIn, TOut, M1>(R, h, p, g, lane, r, c);
   };
 
