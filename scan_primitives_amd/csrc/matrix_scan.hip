@@ -560,6 +560,11 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
 
+// The LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t* w) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint32_t*)w));
+}
+
 // Cache policy of the input copies: non-temporal (each input is read once).
 constexpr int kCopyPolicy = 2;
 
@@ -687,6 +692,9 @@ __device__ __forceinline__ void stage_wave(const MsParams& p, const PipeGeo& g, 
 // A compute wave's inputs for one unit, in registers: a[t] in A-operand order
 // (identity past the end) and b[t] in result-register order (zero past the end;
 // for m = 1, b of all 16 steps with step c in lane column c).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
 template <typename TIn, bool M1>
 struct UnitRegs {
   ARow<TIn> A[16];
@@ -699,18 +707,26 @@ __device__ __forceinline__ void stage_to_regs(UnitRegs<TIn, M1>& R, const char* 
                                               int r, int c) {
   using S = PipeStage<TIn, M1>;
   const ARow<TIn> eye = identity_a<TIn>(r, c);
+  // bf16 b tiles: element (R, C) of a step's tile sits at byte 256 (C / 8) + 16 R + 2 (C % 8).
+  // A transposing LDS read (ds_read_b64_tr_b16) gives lane (r, c) the column piece b[4r .. 4r+3][c]
+  // in one instruction: within each 16-lane row, the 8-byte pieces that lanes 4q .. 4q+3 supply form
+  // row q of a 4 x 16 block, and lane j receives column j of that block. So lane (r, c) supplies
+  // b[4r + c/4][4 (c%4) .. 4 (c%4) + 3].
+  static_assert(M1 || sizeof(TIn) == 2, "the pipelined kernel stages 16-column b tiles for bf16 only");
+  uint32_t b_lds = 0;
+  if constexpr (!M1)
+    b_lds = lds_addr(reinterpret_cast<const uint32_t*>(st + 16 * S::kA)) + 256 * ((c & 3) >> 1) + 16 * (4 * r + (c >> 2)) +
+            8 * (c & 1);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     if constexpr (sizeof(TIn) == 4) R.A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
     else R.A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
     R.A[k] = select_a(q0 + k < T, R.A[k], eye);
     if constexpr (!M1) {
-      // b[4r + v][c] sits in slot (4r + v) + 16 (c / 8), at byte 2 (c % 8); rows are 16 bytes apart
-      const uint16_t* bp =
-          reinterpret_cast<const uint16_t*>(st + 16 * S::kA + k * S::kB + 16 * (4 * r + 16 * (c >> 3)) + 2 * (c & 7));
       const bool in = q0 + k < T;
-      R.Bv[k].u = make_uint2(in ? uint32_t(bp[0]) | (uint32_t(bp[8]) << 16) : 0u,
-                             in ? uint32_t(bp[16]) | (uint32_t(bp[24]) << 16) : 0u);
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4_ptr>(uintptr_t(b_lds + k * S::kB)));
+      R.Bv[k].u = make_uint2(in ? uint32_t(uint16_t(v[0])) | (uint32_t(uint16_t(v[1])) << 16) : 0u,
+                             in ? uint32_t(uint16_t(v[2])) | (uint32_t(uint16_t(v[3])) << 16) : 0u);
     }
   }
   if constexpr (M1) {
@@ -872,9 +888,6 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
 // The signal words are accessed with inline DS instructions: for ordinary LDS
 // accesses the compiler cannot tell them from the stages being filled by
 // global_load_lds and would first wait for every copy in flight.
-__device__ __forceinline__ uint32_t lds_addr(const uint32_t* w) {
-  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint32_t*)w));
-}
 
 __device__ __forceinline__ uint32_t lds_read_u32(const uint32_t* w) {
   uint32_t v;
