@@ -925,7 +925,9 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     then replay unit k-1, whose entering state the leader has found in the
 //     meantime, storing every h[t]. Each compute wave keeps two units in
 //     registers (the one it summarises and the one it replays).
-//   - The leader composes unit k's map from the wave maps, publishes it, finds
+//   - The leader composes unit k's map from the wave maps (leaving in wave i's
+//     slot the composition of maps 0 .. i, so that every wave carries the
+//     entering state in one step), publishes it, finds
 //     the state entering the unit by decoupled look-back over earlier units of
 //     the same (batch, tile), hands that state to the compute waves and
 //     publishes the state leaving the unit. Its round trips overlap the
@@ -1063,12 +1065,20 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       };
       const int kb = k % kBufs;
       lds_wait_at_least(&sSumDone[kb], uint32_t(NC) * uint32_t(k / kBufs + 1));  // the wave maps of unit k are in LDS
+      // Compose the wave maps in step order. Slot i is overwritten with the
+      // composition of maps 0 .. i, so that wave i+1 carries the unit's
+      // entering state over all the waves before it with one map.
       f32x4 G = identity_d(r, c), GL = zero4();
       for (int i = 0; i < NC; ++i) {
         const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]);
         const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]);
         G = mfma_16x16x16(Pa, G, zero4());
         GL = mfma_16x16x16(Pa, GL, Li);
+        if (i + 1 < NC) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sP[kb][i][(4 * r + v) * 16 + c] = G[v];
+          *reinterpret_cast<f32x4*>(&sL[kb][i][lane * 4]) = GL;
+        }
       }
       const f32x4 GA = to_a_operand(sT, G, r, c);
       f32x4 h_in = zero4();
@@ -1158,9 +1168,9 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     const int kb = k % kBufs;
     lds_wait_at_least(&sHinIt[kb], uint32_t(k) + 1);
     f32x4 h = *reinterpret_cast<const f32x4*>(&sX[kb][lane * 4]);
-    for (int i = 0; i < wave; ++i)
-      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]), h,
-                        *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]));
+    if (wave > 0)  // slot wave-1 holds the composition of the maps of waves 0 .. wave-1
+      h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][wave - 1][c * 16 + 4 * r]), h,
+                        *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]));
     lds_signal_add(&sCarryDone[kb], lane);
     replay_steps<TIn, TOut, M1>(R, h, p, g, lane, r, c);
   };
