@@ -934,15 +934,17 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     summary of the next unit, so a replay never waits for its own look-back.
 // The waves run a unit apart and never meet at s_barrier after the start; they
 // hand work over through LDS words. Per-unit LDS slots rotate over four
-// units, and so do the counters that guard them: a counter that several
-// waves raise only says "all of unit k are in" if no wave can add for a later
-// unit on the same counter first. A compute wave summarises unit k into slot
-// k % 4 only after every wave's carry of unit k-4 out of that slot; each wave
-// carries its units in order and summarises unit k+1 before it carries unit
-// k. So when any wave adds its summary or carry of unit k+4 to slot k % 4,
-// every wave has already added its summary and carry of unit k there. (With
-// one shared summary count, a fast wave's unit-1 summary, which has no carry
-// to wait for, once stood in for a slow wave's unit-0 summary not yet written.)
+// units. Each compute wave announces its summary of unit k in a word of its
+// own (set to k + 1), so the leader composes wave i's map as soon as it is
+// in. The carry counts that guard slot reuse are kept per slot: a count that
+// several waves raise only says "all of unit k are in" if no wave can add for
+// a later unit on the same count first. A compute wave summarises unit k into
+// slot k % 4 only after every wave's carry of unit k-4 out of that slot; each
+// wave carries its units in order and summarises unit k+1 before it carries
+// unit k. So when any wave adds its carry of unit k+4 to slot k % 4, every
+// wave has already added its carry of unit k there. (With one shared summary
+// count, a fast wave's unit-1 summary, which has no carry to wait for, once
+// stood in for a slow wave's unit-0 summary not yet written.)
 //
 // Placement: wave i runs on SIMD i % 4, and a wave that shares a SIMD with a
 // wave running MFMA chains gets few issue slots (measured: a copy-issuing wave
@@ -965,7 +967,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   __shared__ __attribute__((aligned(16))) float sX[kBufs][256];
   __shared__ __attribute__((aligned(16))) float sT[256];
   __shared__ uint32_t sId[4];
-  __shared__ uint32_t sIdCount, sSumDone[kBufs], sCarryDone[kBufs], sHinIt[kBufs], sLanded[NC], sConsumed[NC];
+  __shared__ uint32_t sIdCount, sSumDone[NC], sCarryDone[kBufs], sHinIt[kBufs], sLanded[NC], sConsumed[NC];
 
   const int tid = int(threadIdx.x);
   const int hw_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -978,9 +980,10 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
 
   if (tid == 0) {
     sIdCount = 0;
-    for (int b = 0; b < kBufs; ++b) sSumDone[b] = sCarryDone[b] = sHinIt[b] = 0;
+    for (int b = 0; b < kBufs; ++b) sCarryDone[b] = sHinIt[b] = 0;
   }
   if (tid < NC) {
+    sSumDone[tid] = 0;
     sLanded[tid] = 0;
     sConsumed[tid] = 0;
   }
@@ -1064,12 +1067,12 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
         return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       };
       const int kb = k % kBufs;
-      lds_wait_at_least(&sSumDone[kb], uint32_t(NC) * uint32_t(k / kBufs + 1));  // the wave maps of unit k are in LDS
       // Compose the wave maps in step order. Slot i is overwritten with the
       // composition of maps 0 .. i, so that wave i+1 carries the unit's
       // entering state over all the waves before it with one map.
       f32x4 G = identity_d(r, c), GL = zero4();
       for (int i = 0; i < NC; ++i) {
+        lds_wait_at_least(&sSumDone[i], uint32_t(k) + 1);  // wave i's map of unit k is in LDS
         const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]);
         const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]);
         G = mfma_16x16x16(Pa, G, zero4());
@@ -1160,7 +1163,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     const int kb = k % kBufs;
     lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
     summarize<TIn, M1>(Rc, &sP[kb][wave][0], &sL[kb][wave][0], lane, r, c, [](int) {});
-    lds_signal_add(&sSumDone[kb], lane);
+    lds_signal_set(&sSumDone[wave], uint32_t(k) + 1, lane);
     return true;
   };
   // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.
