@@ -35,6 +35,8 @@
 //                          replays its trips from there. The next slab's
 //                          loads are in flight meanwhile. Inputs are read
 //                          once and no state leaves the workgroup.
+#include <utility>
+
 #include "sx_common.hpp"
 
 namespace sx {
@@ -123,6 +125,12 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     sp += ds;
     op += dout;
   }
+}
+
+// Lane N of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
 }
 
 // DPP move within a 16-lane row; CTRL is the gfx9 dpp_ctrl encoding.
@@ -257,6 +265,7 @@ constexpr float kWarmupBound = 1.0f / 67108864.0f;  // 2^-26, far below f32 roun
 constexpr int kWarmFast = 24;
 constexpr int kChunkFast = 16;
 
+template <bool SCALAR_GATE>
 __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p, int64_t chunk_len, int64_t nchunks) {
   const int64_t row = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
   // A whole row leaves together, so no DPP read crosses into an exited row.
@@ -281,63 +290,81 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
   const int64_t s = chunk * chunk_len;
   const int64_t e = s + chunk_len < T ? s + chunk_len : T;
   const float h0 = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
-  const bool scalar_gate = p.n_stride[ES_S] == 0;  // a width-one gate: every lane reads the same value
+  constexpr bool scalar_gate = SCALAR_GATE;  // a width-one gate: every lane reads the same value
 
   if (chunk_len <= kChunkFast) {
-    // ---- one batch of loads: buffer slot i holds position s - kWarmFast + i
-    constexpr int kSlots = kWarmFast + kChunkFast;
-    float xv[kSlots], av[kSlots];
-    {
+    // ---- one batch of loads: buffer slot i holds position s - kWarmFast + i.
+    // A width-one gate is the same for the whole row, so the row keeps one copy:
+    // lane j of the row holds slot 16 g + j in register g, and a trip takes it
+    // with a row broadcast. That keeps the kernel at two waves per SIMD.
+    auto fast = [&](auto scalar_c) -> bool {
+      constexpr bool kScalar = decltype(scalar_c)::value;
+      constexpr int kSlots = kWarmFast + kChunkFast;
+      constexpr int kGateRegs = kScalar ? (kSlots + 15) / 16 : kSlots;
       const int64_t q_first = s - kWarmFast;
-      const int64_t dq = rev ? -1 : 1;
+      float xv[kSlots], gv[kGateRegs];
 #pragma unroll
       for (int i = 0; i < kSlots; ++i) {
-        const int64_t t = time_of(q_first + i);
-        (void)dq;
-        const float xr = xl[t * sx], ar = al[t * sa];
+        const float xr = xl[time_of(q_first + i) * sx];
         xv[i] = active ? xr : 0.0f;
-        av[i] = active || scalar_gate ? ar : 0.0f;
       }
-    }
-    // walk back from s - 1 (slot kWarmFast - 1) while the bound is above the target;
-    // the per-trip bounds do not depend on h, so all of them are formed first
-    int first = -1;  // slot of the certified warm-up start
-    bool exact = false;
-    if (s == 0) {
-      first = kWarmFast;
-      exact = true;
-    } else {
-      float lip[kWarmFast];
 #pragma unroll
-      for (int i = 0; i < kWarmFast; ++i) lip[i] = norm_cap_lipschitz(xv[i], av[i], scalar_gate);
-      float prod = 1.0f;
+      for (int g = 0; g < kGateRegs; ++g) {
+        if constexpr (kScalar) {
+          gv[g] = al[time_of(q_first + 16 * g + k) * sa];
+        } else {
+          const float ar = al[time_of(q_first + g) * sa];
+          gv[g] = active ? ar : 0.0f;
+        }
+      }
+      auto gate = [&](auto i_c) -> float {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (kScalar) return row_bcast<i % 16>(gv[i / 16]);
+        else return gv[i];
+      };
+      // walk back from s - 1 (slot kWarmFast - 1) while the bound is above the target
+      int first = -1;  // slot of the certified warm-up start
+      bool exact = false;
+      if (s == 0) {
+        first = kWarmFast;
+        exact = true;
+      } else {
+        // the per-trip bounds do not depend on h: form them all at once, then walk
+        float lip[kWarmFast];
+        [&]<int... is>(std::integer_sequence<int, is...>) {
+          ((lip[is] = norm_cap_lipschitz(xv[is], gate(std::integral_constant<int, is>{}), kScalar)), ...);
+        }(std::make_integer_sequence<int, kWarmFast>{});
+        float prod = 1.0f;
 #pragma unroll
-      for (int i = kWarmFast - 1; i >= 0; --i) {
-        if (first < 0) {  // row-uniform
-          if (s - kWarmFast + i < 0) {
-            first = i + 1;  // reached the start of the axis
-            exact = true;
-          } else {
-            prod *= lip[i];
-            if (prod <= kWarmupBound) first = i;
+        for (int i = kWarmFast - 1; i >= 0; --i) {
+          if (first < 0) {  // row-uniform
+            if (s - kWarmFast + i < 0) {
+              first = i + 1;  // reached the start of the axis
+              exact = true;
+            } else {
+              prod *= lip[i];
+              if (prod <= kWarmupBound) first = i;
+            }
           }
         }
       }
-    }
-    if (first >= 0) {
+      if (first < 0) return false;
       float h = exact ? h0 : 0.0f;
       float* op = ol + time_of(s) * so;
       const int64_t dout = rev ? -so : so;
-#pragma unroll
-      for (int i = 0; i < kSlots; ++i) {
-        const int64_t q = s - kWarmFast + i;
-        if (i >= first && q < e) {  // row-uniform
-          h = norm_cap_trip(h, xv[i], av[i]);
-          if (i >= kWarmFast && active) op[(i - kWarmFast) * dout] = h;
-        }
-      }
-      return;
-    }
+      [&]<int... is>(std::integer_sequence<int, is...>) {
+        (([&] {
+           const int64_t q = s - kWarmFast + is;
+           if (is >= first && q < e) {  // row-uniform
+             h = norm_cap_trip(h, xv[is], gate(std::integral_constant<int, is>{}));
+             if (is >= kWarmFast && active) op[(is - kWarmFast) * dout] = h;
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, kSlots>{});
+      return true;
+    };
+    if (fast(std::integral_constant<bool, SCALAR_GATE>{})) return;
   }
 
   // ---- general path: walk back eight positions per round until certified, then run forward
@@ -505,7 +532,10 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
       nchunks = (p.T + len - 1) / len;
       const int64_t blocks = (p.num_lanes * nchunks * 16 + 255) / 256;
       if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL(es_normcap_chunk_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p, len, nchunks);
+      if (p.n_stride[ES_S] == 0)  // a width-one gate
+        hipLaunchKernelGGL(es_normcap_chunk_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, stream, p, len, nchunks);
+      else
+        hipLaunchKernelGGL(es_normcap_chunk_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, stream, p, len, nchunks);
       return hipGetLastError();
     }
     const int64_t blocks = (p.num_lanes * 16 + 255) / 256;
