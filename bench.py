@@ -79,29 +79,33 @@ def measured_traffic(kernel_label: str):
     return None if entry is None else entry.get("bytes")
 
 
-def cpu_baseline(workloads) -> dict:
-    """Time the CPU oracle, as it stands, on the same workloads (one pass each)."""
+def cpu_baseline(workloads, min_seconds: float = 10.0) -> dict:
+    """Time the CPU oracle, as it stands, on the same workloads: whole passes
+    over every workload at full size, repeated until at least ``min_seconds``
+    of oracle time have been spent (one pass takes well under a second)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    total_elems, total_s = 0, 0.0
+    total_elems, total_s, passes = 0, 0.0, 0
+    hosts = [{k: v.float().numpy() for k, v in w.tensors.items()} for w in workloads]
     with threadpool_limits(limits=1):
-        for w in workloads:
-            host = {k: v.float().numpy() for k, v in w.tensors.items()}
-            t0 = time.perf_counter()
-            if w.op == "element_scan":
-                oracle.element_scan(w.body, host["initial"], [host["x"], host["s"]], axis=w.axis,
-                                    state_axis=w.state_axis, reverse=w.reverse)
-            else:
-                oracle.matrix_scan(host["a"], host["b"], axis=w.axis, reverse=w.reverse)
-            dt = time.perf_counter() - t0
-            log(f"cpu oracle {w.name}: {dt:.3f} s")
-            total_elems += w.out_numel
-            total_s += dt
-            del host
+        while passes == 0 or total_s < min_seconds:
+            for w, host in zip(workloads, hosts):
+                t0 = time.perf_counter()
+                if w.op == "element_scan":
+                    oracle.element_scan(w.body, host["initial"], [host["x"], host["s"]], axis=w.axis,
+                                        state_axis=w.state_axis, reverse=w.reverse)
+                else:
+                    oracle.matrix_scan(host["a"], host["b"], axis=w.axis, reverse=w.reverse)
+                dt = time.perf_counter() - t0
+                if passes == 0:
+                    log(f"cpu oracle {w.name}: {dt:.3f} s")
+                total_elems += w.out_numel
+                total_s += dt
+            passes += 1
     return {"value": total_elems / total_s, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": "one pass of the float64 numpy oracle over each selected workload at full size, "
+            "sample": f"{passes} passes of the float64 numpy oracle over every selected workload at full size, "
                       f"single-threaded; {total_elems} output elements in {total_s:.2f} s"}
 
 
