@@ -1138,7 +1138,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       }
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
       if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
-      // hand the entering state over once the replay of unit k-2 (same slot) has read its own
+      // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
       *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
       lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
