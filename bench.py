@@ -15,7 +15,9 @@ Each workload's call is also timed on its own: a graph of R back-to-back
 calls (R >= 16, and enough calls that a replay moves at least 32 MiB, up to
 64), replayed K times between two HIP events on the capture stream; the
 per-call time is the elapsed time over K * R, so the few microseconds a graph
-launch costs are spread over R calls. This gives each workload's elements/s, algorithmic GB/s and
+launch costs are spread over R calls. A cold figure follows: the median of
+single calls, each after a 512 MiB write that evicts the last-level cache
+(256 MB), timed between HIP events (it includes the launch). This gives each workload's elements/s, algorithmic GB/s and
 fraction of the 8 TB/s HBM peak.
 
 Prints ONE JSON line on stdout. ``value`` is output elements per second over
@@ -211,6 +213,26 @@ def main() -> int:
         })
         log(f"{w.name}: {sec * 1e6:.2f} us/call, {w.out_numel / sec:.3e} elements/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
+
+    # ---- the same calls cold: before each one, a 512 MiB write evicts the 256 MB last-level cache
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+    for j, (w, t) in enumerate(zip(workloads, resident)):
+        times = []
+        for _ in range(max(args.steps, 20)):
+            flush.fill_(float(j))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(w, t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        times.sort()
+        sec = times[len(times) // 2]
+        gbs = w.algorithmic_bytes / sec / 1e9
+        per_config[j]["call_us_cold"] = round(sec * 1e6, 3)
+        per_config[j]["hbm_frac_cold"] = round(gbs / HBM_PEAK_GBS, 4)
+        log(f"{w.name} (cold, median of {len(times)} single calls): {sec * 1e6:.2f} us/call, {gbs:.1f} GB/s")
+    del flush
 
     # ---- whole job: K steps, each one pass over every workload
     for _ in range(args.warmup):
