@@ -31,6 +31,10 @@ Sources, all from the SexpGPU documentation pages:
   "matrix-scan" section: ``h[t] = a[t] @ h[t-1] + b[t]`` from ``h = 0``,
   ``:reverse`` running from the end, NumPy broadcasting of the leading dims,
   ``:axis`` counted among the leading dims, result in ``b``'s shape.
+* "Tensor operations", the "matrix-scan" section, on the prelude's
+  ``linear-scan``: the same recurrence over one-by-one matrices, taking ``a``
+  and ``b`` (numbers included) broadcast to one shape; ``cumsum`` is built on
+  it, which makes it the linear scan with ``a = 1``.
 
 Readings where the pages leave a point open (each is listed with its reason
 in the design notes of the repository):
@@ -54,7 +58,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["element_scan", "matrix_scan", "BODIES"]
+__all__ = ["element_scan", "matrix_scan", "linear_scan", "cumsum", "BODIES"]
 
 
 # --- element-scan bodies ----------------------------------------------------
@@ -194,3 +198,41 @@ def matrix_scan(a, b, axis=0, reverse=False, dtype=np.float64):
         h = a_t[t] @ h + b_t[t]
         out[t] = h
     return np.moveaxis(out, 0, ax)
+
+
+def linear_scan(a, b, axis=0, reverse=False, dtype=np.float64):
+    """Run a linear scan the plain way: one multiply-add per step, every
+    position of the broadcast shape outside ``axis`` its own recurrence.
+
+    ``a`` and ``b`` are numbers or arrays broadcast (NumPy rules) to one
+    shape, in which ``axis`` counts. Forward: ``h[t] = a[t] * h[t-1] + b[t]``
+    from ``h[-1] = 0``; reverse: ``h[t] = a[t] * h[t+1] + b[t]`` from
+    ``h[T] = 0``. The result has the broadcast shape.
+
+    Follows "Tensor operations", the "matrix-scan" section: the matrix
+    recurrence over one-by-one matrices, operands broadcast to one shape.
+    """
+    a = np.asarray(a, dtype=dtype)
+    b = np.asarray(b, dtype=dtype)
+    shape = np.broadcast_shapes(a.shape, b.shape)
+    if len(shape) < 1:
+        raise ValueError("linear_scan: the operands broadcast to a number; there is no axis to scan")
+    ax = axis + len(shape) if axis < 0 else axis
+    if not 0 <= ax < len(shape):
+        raise ValueError(f"linear_scan: axis {axis} out of range for rank {len(shape)}")
+    a_t = np.moveaxis(np.broadcast_to(a, shape), ax, 0)
+    b_t = np.moveaxis(np.broadcast_to(b, shape), ax, 0)
+    T = shape[ax]
+    out = np.empty((T,) + b_t.shape[1:], dtype=dtype)
+    h = np.zeros(b_t.shape[1:], dtype=dtype)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        h = a_t[t] * h + b_t[t]
+        out[t] = h
+    return np.moveaxis(out, 0, ax)
+
+
+def cumsum(x, axis=0, reverse=False, dtype=np.float64):
+    """Running sum along ``axis`` (from the end when ``reverse``): the linear
+    scan with ``a = 1``, as the "matrix-scan" section builds cumsum on it."""
+    return linear_scan(1.0, x, axis=axis, reverse=reverse, dtype=dtype)

@@ -135,3 +135,60 @@ def test_unmutated_oracle_passes_the_same_pins():
     for body in ES_PINS:
         assert not _some_pin_fails(ES_PINS[body])
     assert not _some_pin_fails(MS_PINS)
+
+
+_real_ls = oracle.linear_scan
+
+
+def _ls_a_shifted(a, b, axis=0, reverse=False, dtype=np.float64):
+    # uses a[t-1] at step t
+    shape = np.broadcast_shapes(np.shape(a), np.shape(b))
+    a_b = np.broadcast_to(np.asarray(a, dtype=np.float64), shape)
+    return _real_ls(np.roll(a_b, 1, axis=axis % len(shape)), b, axis, reverse, dtype)
+
+
+def _ls_swapped(a, b, axis=0, reverse=False, dtype=np.float64):
+    return _real_ls(b, a, axis, reverse, dtype)
+
+
+def _ls_wrong_direction(a, b, axis=0, reverse=False, dtype=np.float64):
+    return _real_ls(a, b, axis, not reverse, dtype)
+
+
+def _ls_starts_from_b0_twice(a, b, axis=0, reverse=False, dtype=np.float64):
+    out = _real_ls(a, b, axis, reverse, dtype)
+    shape = np.broadcast_shapes(np.shape(a), np.shape(b))
+    b_b = np.broadcast_to(np.asarray(b, dtype=np.float64), shape)
+    return out + np.take(b_b, [-1 if reverse else 0], axis=axis % len(shape))
+
+
+def _ls_adds_a(a, b, axis=0, reverse=False, dtype=np.float64):
+    # h + a instead of a * h: the number broadcast still shapes the result
+    shape = np.broadcast_shapes(np.shape(a), np.shape(b))
+    a_b = np.moveaxis(np.broadcast_to(np.asarray(a, dtype=np.float64), shape), axis % len(shape), 0)
+    b_b = np.moveaxis(np.broadcast_to(np.asarray(b, dtype=np.float64), shape), axis % len(shape), 0)
+    h = np.zeros(a_b.shape[1:])
+    out = np.empty_like(b_b)
+    for t in (range(len(b_b) - 1, -1, -1) if reverse else range(len(b_b))):
+        h = a_b[t] + h + b_b[t]
+        out[t] = h
+    return np.moveaxis(out, 0, axis % len(shape))
+
+
+LS_PINS = [
+    (pins.test_linear_scan_product_sum, {"reverse": False}),
+    (pins.test_linear_scan_product_sum, {"reverse": True}),
+    (pins.test_linear_scan_inverse_problem, {"reverse": False}),
+    (pins.test_linear_scan_inverse_problem, {"reverse": True}),
+    (pins.test_linear_scan_geometric_series, {}),
+]
+
+
+@pytest.mark.parametrize("mutant", [_ls_a_shifted, _ls_swapped, _ls_wrong_direction, _ls_starts_from_b0_twice, _ls_adds_a])
+def test_linear_scan_mutants_are_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "linear_scan", mutant)
+    assert _some_pin_fails(LS_PINS), f"no linear-scan pin caught {mutant.__name__}"
+
+
+def test_unmutated_linear_scan_passes_its_pins():
+    assert not _some_pin_fails(LS_PINS)

@@ -432,3 +432,99 @@ def test_matrix_scan_scalar_closed_form():
     out = oracle.matrix_scan(a.reshape(T, 1, 1), b.reshape(T, 1, 1))[:, 0, 0]
     ref = [sum(math.prod(a[s + 1: t + 1]) * b[s] for s in range(t + 1)) for t in range(T)]
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+# --- linear-scan and cumsum ----------------------------------------------------
+# "Tensor operations", the "matrix-scan" section: linear-scan is the matrix
+# recurrence over one-by-one matrices, operands broadcast to one shape; cumsum
+# is built on it (a = 1).
+
+
+@pytest.mark.parametrize("axis,reverse", [(0, False), (1, False), (1, True), (-1, True)])
+def test_linear_scan_unit_a_is_cumsum(axis, reverse):
+    x = _rng(60).standard_normal((4, 7, 5))
+    ref = np.flip(np.cumsum(np.flip(x, axis), axis=axis), axis) if reverse else np.cumsum(x, axis=axis)
+    np.testing.assert_allclose(oracle.cumsum(x, axis=axis, reverse=reverse), ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.linear_scan(1.0, x, axis=axis, reverse=reverse), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_linear_scan_zero_a_is_b():
+    b = _rng(61).standard_normal((3, 9, 2))
+    np.testing.assert_array_equal(oracle.linear_scan(np.zeros((3, 9, 2)), b, axis=1), b)
+    np.testing.assert_array_equal(oracle.linear_scan(0.0, b, axis=1, reverse=True), b)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_linear_scan_product_sum(reverse):
+    # Closed form: h[t] = sum over s up to t of (a[s+1] ... a[t]) b[s]
+    # (reverse: s from t up, with the product a[t] ... a[s-1]).
+    r = _rng(62)
+    T = 7
+    a = r.uniform(-1.5, 1.5, (T, 3))
+    b = r.standard_normal((T, 3))
+    out = oracle.linear_scan(a, b, axis=0, reverse=reverse)
+    ref = np.zeros((T, 3))
+    for t in range(T):
+        srcs = range(t, T) if reverse else range(t + 1)
+        for s in srcs:
+            between = range(t, s) if reverse else range(s + 1, t + 1)
+            coeff = np.ones(3)
+            for q in between:
+                coeff = coeff * a[q]
+            ref[t] += coeff * b[s]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_scan_geometric_series():
+    # constant a and b: h[t] = b (1 - a^(t+1)) / (1 - a)
+    a, b, T = 0.7, 1.3, 20
+    out = oracle.linear_scan(a, np.full(T, b), axis=0)
+    t = np.arange(T)
+    np.testing.assert_allclose(out, b * (1 - a ** (t + 1)) / (1 - a), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_linear_scan_inverse_problem(reverse):
+    # pick the states, solve each step for its b, scan, get the states back
+    r = _rng(63)
+    T = 11
+    h = r.standard_normal((2, T, 3))
+    a = r.uniform(-2, 2, (2, T, 3))
+    prev = np.zeros_like(h)
+    if reverse:
+        prev[:, :-1] = h[:, 1:]
+    else:
+        prev[:, 1:] = h[:, :-1]
+    b = h - a * prev
+    np.testing.assert_allclose(oracle.linear_scan(a, b, axis=1, reverse=reverse), h, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_scan_broadcast_operands():
+    r = _rng(64)
+    a_row = r.uniform(0.5, 1.0, (1, 6, 1))       # one gate per step, shared by every lane
+    b = r.standard_normal((4, 6, 3))
+    ref = oracle.linear_scan(np.broadcast_to(a_row, b.shape).copy(), b, axis=1)
+    np.testing.assert_array_equal(oracle.linear_scan(a_row, b, axis=1), ref)
+    # a number and an array: the result takes the array's shape
+    assert oracle.linear_scan(0.5, b, axis=-2).shape == b.shape
+
+
+def test_linear_scan_first_a_unused_forward_last_unused_reverse():
+    r = _rng(65)
+    a = r.standard_normal((9, 2))
+    b = r.standard_normal((9, 2))
+    a2 = a.copy()
+    a2[0] = 1e6
+    np.testing.assert_array_equal(oracle.linear_scan(a, b), oracle.linear_scan(a2, b))
+    a3 = a.copy()
+    a3[-1] = 1e6
+    np.testing.assert_array_equal(oracle.linear_scan(a, b, reverse=True), oracle.linear_scan(a3, b, reverse=True))
+
+
+def test_linear_scan_empty_axis_and_numbers():
+    out = oracle.linear_scan(np.ones((3, 0, 2)), np.ones((3, 0, 2)), axis=1)
+    assert out.shape == (3, 0, 2)
+    with pytest.raises(ValueError):
+        oracle.linear_scan(1.0, 2.0)  # two numbers: no axis to scan
+    with pytest.raises(ValueError):
+        oracle.linear_scan(np.ones(4), np.ones(4), axis=1)
