@@ -1,7 +1,7 @@
 """Throughput of the scan library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 0,2,...]
-                    [--no-cpu-baseline] [--with-copy] [--eager]
+                    [--no-cpu-baseline] [--with-copy] [--eager] [--no-extra]
 
 One step runs the whole hot path once: the five standard workloads of
 ``scan_primitives_amd.workloads`` (tanh-affine, norm-cap, reverse max-plus,
@@ -19,6 +19,10 @@ launch costs are spread over R calls. A cold figure follows: the median of
 single calls, each after a 512 MiB write that evicts the last-level cache
 (256 MB), timed between HIP events (it includes the launch). This gives each workload's elements/s, algorithmic GB/s and
 fraction of the 8 TB/s HBM peak.
+
+linear-scan and cumsum ([64,4096,256] f32 along axis 1) are timed the same
+two ways and reported in ``per_config`` with ``"in_step": false``; they are
+not part of the step or of ``value`` (``--no-extra`` skips them).
 
 Prints ONE JSON line on stdout. ``value`` is output elements per second over
 the timed steps; ``per_config`` has each workload's figures; ``roofline``
@@ -121,6 +125,8 @@ def main() -> int:
     ap.add_argument("--with-copy", action="store_true",
                     help="also run a plain 256 MiB device copy per step (reference kernel for PMC byte counts)")
     ap.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying graphs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the linear-scan and cumsum calls timed beside the step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,14 +148,19 @@ def main() -> int:
 
     which = None if args.only is None else [int(i) for i in args.only.split(",")]
     workloads = W.standard_workloads(which)
-    log("generated inputs: " + "; ".join(w.name for w in workloads))
+    extras = [] if args.no_extra else W.extra_workloads()
+    log("generated inputs: " + "; ".join(w.name for w in workloads + extras))
     resident = [w.on(dev) for w in workloads]
+    resident_extra = [w.on(dev) for w in extras]
     torch.cuda.synchronize()
 
     def call(w, t):
         if w.op == "element_scan":
             return sx.element_scan(w.body, t["initial"], [t["x"], t["s"]], axis=w.axis, state_axis=w.state_axis,
                                    reverse=w.reverse)
+        if w.op == "linear_scan":
+            return sx.linear_scan(t["a"] if "a" in t else w.meta["a_number"], t["b"], axis=w.axis,
+                                  reverse=w.reverse, out_dtype=w.out_dtype)
         return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
 
     copy_src = copy_dst = None
@@ -166,11 +177,16 @@ def main() -> int:
     # eager warm-up (also sizes the caching allocator), then capture
     for _ in range(2):
         one_step()
+        for w, t in zip(extras, resident_extra):
+            call(w, t)
     torch.cuda.synchronize()
-    reps = [max(16, min(64, math.ceil((32 << 20) / w.algorithmic_bytes))) for w in workloads]
+    # every measured call: the step's workloads, then the extra ones (not part of the step)
+    timed = workloads + extras
+    timed_inputs = resident + resident_extra
+    reps = [max(16, min(64, math.ceil((32 << 20) / w.algorithmic_bytes))) for w in timed]
     graphs, step_graph, keep = [], None, []
     if not args.eager:
-        for w, t, r in zip(workloads, resident, reps):
+        for w, t, r in zip(timed, timed_inputs, reps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 keep.append([call(w, t) for _ in range(r)])
@@ -184,7 +200,7 @@ def main() -> int:
 
     # ---- per-workload call time: K replays of a graph of R calls, between two events
     per_config = []
-    for j, (w, t, r) in enumerate(zip(workloads, resident, reps)):
+    for j, (w, t, r) in enumerate(zip(timed, timed_inputs, reps)):
         def run_once():
             if args.eager:
                 for _ in range(r):
@@ -210,13 +226,14 @@ def main() -> int:
             "algorithmic_bytes": w.algorithmic_bytes,
             "hbm_gbs": round(gbs, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "in_step": j < len(workloads),
         })
         log(f"{w.name}: {sec * 1e6:.2f} us/call, {w.out_numel / sec:.3e} elements/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
 
     # ---- the same calls cold: before each one, a 512 MiB write evicts the 256 MB last-level cache
     flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
-    for j, (w, t) in enumerate(zip(workloads, resident)):
+    for j, (w, t) in enumerate(zip(timed, timed_inputs)):
         times = []
         for _ in range(max(args.steps, 20)):
             flush.fill_(float(j))

@@ -1,7 +1,7 @@
 /*
  * sx_scan.h: C ABI of the MI355X (gfx950) scan library, libsx_scan.so.
  *
- * Two scans, forward only, as the SexpGPU documentation pages define them:
+ * The scans of the SexpGPU documentation pages, forward passes:
  *
  *   element-scan  "Nonlinear element scans": a nonlinear recurrence run
  *                 independently at every position outside one sequence axis,
@@ -11,6 +11,8 @@
  *                 the "matrix-scan" section: h[t] = a[t] @ h[t-1] + b[t] from
  *                 h = 0, n <= 16, computed in f32, with :axis, :reverse and
  *                 broadcast leading dims.
+ *   linear-scan   the same section: matrix-scan over one-by-one matrices,
+ *                 a and b broadcast to one shape (cumsum: a = 1).
  *
  * Conventions shared by every entry point:
  *
@@ -164,6 +166,43 @@ size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_
 /* Writes the matrix-scan result shape to out_shape (room for SX_MAX_RANK + 2
  * entries) and returns its rank, or -1 for shapes that do not fit. */
 int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                             int64_t* out_shape);
+
+/*
+ * sx_linear_scan: "Tensor operations", the "matrix-scan" section, on the
+ * prelude's linear-scan: matrix-scan over one-by-one matrices, with a and b
+ * (numbers included) broadcast to one shape. cumsum is linear-scan with
+ * a = 1 (a rank-0 a holding 1).
+ *
+ * For every index outside `axis` of the broadcast shape the scalar state runs
+ *   forward  h[t] = a[t] * h[t-1] + b[t]  from h[-1] = 0  (h[0] = b[0]),
+ *   reverse  h[t] = a[t] * h[t+1] + b[t]  from h[T] = 0  (h[T-1] = b[T-1]),
+ * and out[t] = h[t]; a[0] (forward) or a[T-1] (reverse) is never read for
+ * its value. Computation is f32 for f32 and bf16 operands alike.
+ *
+ *  dtype         SX_F32 or SX_BF16, shared by a and b (else E-DIM-002).
+ *  a_*, b_*      rank (0..SX_MAX_RANK; 0 is a number, its shape may be
+ *                NULL), shape, strides (NULL = contiguous; any value,
+ *                including 0 and negative) and data. The shapes broadcast
+ *                NumPy-style (right-aligned, each dim equal or 1) to the
+ *                result shape, of rank max(a_rank, b_rank) >= 1; otherwise
+ *                E-DIM-001.
+ *  axis          the scan axis of the result shape; negative counts from the
+ *                end; out of range is E-DIM-001.
+ *  reverse       0 forward, nonzero reverse.
+ *  out_dtype     SX_F32 or SX_BF16 (rounded to nearest even on store).
+ *  out           contiguous, the broadcast shape (see sx_linear_scan_out_shape);
+ *                must not overlap a or b (SX_E_ALIAS).
+ *
+ * No workspace. A result with no elements returns SX_OK without launching.
+ */
+sx_status sx_linear_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                         const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides,
+                         const void* b, int axis, int reverse, sx_dtype out_dtype, void* out, void* stream);
+
+/* Writes the broadcast shape of a and b to out_shape (room for SX_MAX_RANK
+ * entries) and returns its rank, or -1 for shapes that do not fit. */
+int sx_linear_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
                              int64_t* out_shape);
 
 /* "E-DIM-001" etc. for a status; "OK" for SX_OK. Static storage. */

@@ -1,11 +1,11 @@
-"""MI355X-native scan primitives: element-scan and matrix-scan on gfx950.
+"""MI355X-native scan primitives: element-scan, matrix-scan and linear-scan on gfx950.
 
 The computation lives in ``libsx_scan.so`` (hand-written HIP kernels behind
 the C ABI in ``include/sx_scan.h``); this package is its Python binding.
 PyTorch provides device memory and streams.
 """
 
-from ._binding import (BODIES, SxError, element_scan, load_library, matrix_scan)
+from ._binding import BODIES, SxError, cumsum, element_scan, linear_scan, load_library, matrix_scan
 
-__all__ = ["BODIES", "SxError", "element_scan", "matrix_scan", "load_library"]
+__all__ = ["BODIES", "SxError", "element_scan", "matrix_scan", "linear_scan", "cumsum", "load_library"]
 __version__ = "0.1.0"

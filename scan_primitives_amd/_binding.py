@@ -71,6 +71,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sx_matrix_scan_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int]
     lib.sx_matrix_scan_out_shape.restype = c_int
     lib.sx_matrix_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
+    lib.sx_linear_scan.restype = c_int
+    lib.sx_linear_scan.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
+                                   c_int, c_int, c_int, vp, vp]
+    lib.sx_linear_scan_out_shape.restype = c_int
+    lib.sx_linear_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
     lib.sx_status_name.restype = ctypes.c_char_p
     lib.sx_status_name.argtypes = [c_int]
     lib.sx_last_error.restype = ctypes.c_char_p
@@ -208,6 +213,60 @@ def matrix_scan(a: torch.Tensor, b: torch.Tensor, axis: int = 0, reverse: bool =
             ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(a.device))
     _check(status)
     return out
+
+
+def linear_scan(a, b, axis: int = 0, reverse: bool = False, out_dtype=None) -> torch.Tensor:
+    """Linear scan on the GPU: ``h[t] = a[t] * h[t-1] + b[t]`` along ``axis`` from ``h = 0``.
+
+    Matrix-scan over one-by-one matrices. ``a`` and ``b`` are tensors of one
+    float dtype (f32 or bf16) or numbers, broadcast to one shape (at least one
+    of them a tensor of rank >= 1); a number takes the tensor's dtype. The
+    result has the broadcast shape and that dtype unless ``out_dtype`` says
+    otherwise. Computation is f32.
+    """
+    ta = a if isinstance(a, torch.Tensor) else None
+    tb = b if isinstance(b, torch.Tensor) else None
+    if ta is None and tb is None:
+        raise SxError(SX_E_DIM_001, "linear-scan: a and b are both numbers; there is no axis to scan along")
+    ref = tb if tb is not None else ta
+    _require_device_tensor("a" if ref is ta else "b", ref)
+    # A number becomes a rank-0 tensor on the device (a fill kernel, no host copy).
+    if ta is None:
+        ta = torch.full((), float(a), dtype=ref.dtype, device=ref.device)
+    if tb is None:
+        tb = torch.full((), float(b), dtype=ref.dtype, device=ref.device)
+    _require_device_tensor("a", ta)
+    _require_device_tensor("b", tb)
+    if ta.dtype != tb.dtype or ta.dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"linear-scan: a is {ta.dtype} and b is {tb.dtype}; one float dtype "
+                                    "(f32 or bf16) is required")
+    if ta.device != tb.device:
+        raise SxError(SX_E_UNSUPPORTED, "linear-scan: operands on different devices")
+    out_dtype = tb.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"linear-scan: out dtype {out_dtype} is not f32 or bf16")
+    lib = load_library()
+    a_shape, b_shape = i64_array(ta.shape), i64_array(tb.shape)
+    oshape = i64_array([0] * 8)
+    r = lib.sx_linear_scan_out_shape(ta.dim(), a_shape, tb.dim(), b_shape, oshape)
+    if r < 0:
+        # let the library produce the precise status and message
+        _check(lib.sx_linear_scan(_DTYPES[ta.dtype], ta.dim(), a_shape, None, None, tb.dim(), b_shape, None, None,
+                                  axis, 0, _DTYPES[out_dtype], None, None))
+        raise SxError(SX_E_DIM_001, "linear-scan: shapes do not fit")
+    out = torch.empty(tuple(oshape[:r]), dtype=out_dtype, device=ref.device)
+    with torch.cuda.device(ref.device):
+        status = lib.sx_linear_scan(
+            _DTYPES[ta.dtype], ta.dim(), a_shape, i64_array(ta.stride()), ta.data_ptr(),
+            tb.dim(), b_shape, i64_array(tb.stride()), tb.data_ptr(),
+            axis, 1 if reverse else 0, _DTYPES[out_dtype], out.data_ptr(), _stream_handle(ref.device))
+    _check(status)
+    return out
+
+
+def cumsum(x: torch.Tensor, axis: int = 0, reverse: bool = False, out_dtype=None) -> torch.Tensor:
+    """Running sum along ``axis`` (from the end when ``reverse``): linear-scan with ``a = 1``."""
+    return linear_scan(1.0, x, axis=axis, reverse=reverse, out_dtype=out_dtype)
 
 
 def _matrix_dims_contiguous(t: torch.Tensor) -> bool:

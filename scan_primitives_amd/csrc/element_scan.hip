@@ -24,11 +24,13 @@
 //                          warm-up's distance to the true state below 2^-26
 //                          (or W reaching back to the start of the axis,
 //                          which is then exact). See norm_cap_lipschitz.
-//   es_maxplus_slab_kernel the max-plus body as a chunked associative scan.
-//                          A trip is the map h -> max(h - c, x); maps of that
-//                          form compose into max(h + P, Q). One workgroup of
-//                          NW waves owns 64 lanes and sweeps the scan axis in
-//                          slabs of NW*S trips: each wave summarises its S
+//   es_slab_kernel<BODY>   max-plus (and linear-scan) as a chunked associative
+//                          scan. A max-plus trip is the map h -> max(h - c, x);
+//                          maps of that form compose into max(h + P, Q) (a
+//                          linear trip h -> a h + b composes into P h + Q).
+//                          One workgroup of NW waves owns 64 lanes and
+//                          sweeps the scan axis in slabs of NW*S trips: each
+//                          wave summarises its S
 //                          trips into (P, Q), the summaries meet in LDS, each
 //                          wave takes its entering state by composing the
 //                          summaries before it onto the slab's carry, and
@@ -55,13 +57,25 @@ template <int BODY>
 __device__ __forceinline__ float elementwise_body(float h, float x, float s) {
   if constexpr (BODY == SX_BODY_TANH_AFFINE) {
     return tanh_f32(fmaf(s, h, x));
+  } else if constexpr (BODY == kBodyLinear) {
+    return fmaf(s, h, x);  // linear-scan: a * h + b, with b as x and a as s
   } else {
     // exact: one correctly rounded subtraction and a maximum
     return fmaxf(h - s, x);
   }
 }
 
-template <int BODY>
+// Element access for the kernels linear-scan shares: f32 or bf16 (uint16_t)
+// elements, widened to f32 on load and rounded to nearest even on a bf16 store.
+__device__ __forceinline__ float ld_elem(const float* p) { return ld_stream(p); }
+__device__ __forceinline__ float ld_elem(const uint16_t* p) { return bf16_to_f32(ld_stream(p)); }
+__device__ __forceinline__ void st_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st_elem(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
+__device__ __forceinline__ void st_elem_stream(float* p, float v) { st_stream(p, v); }
+__device__ __forceinline__ void st_elem_stream(uint16_t* p, float v) { st_stream(p, f32_to_bf16_rne(v)); }
+
+// TI, TO: element types of the sequences and of out (float unless linear-scan).
+template <int BODY, typename TI = float, typename TO = float>
 __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   const int64_t lane = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (lane >= p.num_lanes) return;
@@ -69,9 +83,9 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   index_offsets(p.lanes, lane, off);
   const int64_t T = p.T;
   int64_t dx = p.t_stride[ES_X], ds = p.t_stride[ES_S], dout = p.t_stride[ES_OUT];
-  const float* xp = p.x + off[ES_X];
-  const float* sp = p.s + off[ES_S];
-  float* op = p.out + off[ES_OUT];
+  const TI* xp = reinterpret_cast<const TI*>(p.x) + off[ES_X];
+  const TI* sp = reinterpret_cast<const TI*>(p.s) + off[ES_S];
+  TO* op = reinterpret_cast<TO*>(p.out) + off[ES_OUT];
   if (p.reverse) {
     xp += (T - 1) * dx;
     sp += (T - 1) * ds;
@@ -80,7 +94,7 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     ds = -ds;
     dout = -dout;
   }
-  float h = p.init[off[ES_INIT]];
+  float h = p.init ? p.init[off[ES_INIT]] : 0.0f;  // no initial: linear-scan starts from zero
 
   constexpr int U = 8;
   const int64_t full = T / U * U;
@@ -88,8 +102,8 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   if (full > 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      cx[u] = ld_stream(xp + u * dx);
-      cs[u] = ld_stream(sp + u * ds);
+      cx[u] = ld_elem(xp + u * dx);
+      cs[u] = ld_elem(sp + u * ds);
     }
   }
   for (int64_t t = 0; t < full; t += U) {
@@ -98,14 +112,14 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     if (more) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        nx[u] = ld_stream(xp + (U + u) * dx);
-        ns[u] = ld_stream(sp + (U + u) * ds);
+        nx[u] = ld_elem(xp + (U + u) * dx);
+        ns[u] = ld_elem(sp + (U + u) * ds);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       h = elementwise_body<BODY>(h, cx[u], cs[u]);
-      op[u * dout] = h;
+      st_elem(op + u * dout, h);
     }
     xp += U * dx;
     sp += U * ds;
@@ -119,8 +133,8 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
     }
   }
   for (int64_t t = full; t < T; ++t) {
-    h = elementwise_body<BODY>(h, ld_stream(xp), ld_stream(sp));
-    *op = h;
+    h = elementwise_body<BODY>(h, ld_elem(xp), ld_elem(sp));
+    st_elem(op, h);
     xp += dx;
     sp += ds;
     op += dout;
@@ -422,10 +436,35 @@ __global__ __launch_bounds__(256) void es_normcap_chunk_kernel(const EsParams p,
   }
 }
 
-template <int NW, int S>
-__global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams p) {
-  __shared__ float sP[2][NW][64];  // per slab parity: each wave's summed cost (negated)
-  __shared__ float sQ[2][NW][64];  // per slab parity: each wave's best value
+// Trips whose maps compose in closed form. Max-plus: h -> max(h - c, x), and
+// a run of them is h -> max(h + P, Q). Linear: h -> a h + b, and a run is
+// h -> P h + Q. A trip past the end of the axis is the identity map.
+template <int BODY>
+struct SlabMap {
+  static_assert(BODY == SX_BODY_MAX_PLUS || BODY == kBodyLinear, "no closed-form composition");
+  static constexpr bool kMaxPlus = BODY == SX_BODY_MAX_PLUS;
+  __device__ static float p0() { return kMaxPlus ? 0.0f : 1.0f; }  // the identity map (P, Q)
+  __device__ static float q0() { return kMaxPlus ? -__builtin_huge_valf() : 0.0f; }
+  __device__ static float x_pad() { return kMaxPlus ? -__builtin_huge_valf() : 0.0f; }  // x (b) of an identity trip
+  __device__ static float s_pad() { return kMaxPlus ? 0.0f : 1.0f; }                     // c (a) of an identity trip
+  // the map (P, Q) followed by the trip (x, s)
+  __device__ static void fold(float& P, float& Q, float x, float s) {
+    if constexpr (kMaxPlus) {
+      Q = fmaxf(Q - s, x);
+      P = P - s;
+    } else {
+      Q = fmaf(s, Q, x);
+      P = P * s;
+    }
+  }
+  __device__ static float apply(float P, float Q, float h) { return kMaxPlus ? fmaxf(h + P, Q) : fmaf(P, h, Q); }
+};
+
+template <int BODY, int NW, int S, typename TI = float, typename TO = float>
+__global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
+  using M = SlabMap<BODY>;
+  __shared__ float sP[2][NW][64];  // per slab parity: each wave's map (P, Q)
+  __shared__ float sQ[2][NW][64];
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);  // wave-uniform: index math stays scalar
   const int l = int(threadIdx.x) & 63;
   const int64_t lane = int64_t(blockIdx.x) * 64 + l;
@@ -433,18 +472,17 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
   int64_t off[4];
   index_offsets(p.lanes, live ? lane : 0, off);
   const int64_t T = p.T;
-  const float* xl = p.x + off[ES_X];
-  const float* cl = p.s + off[ES_S];
-  float* ol = p.out + off[ES_OUT];
+  const TI* xl = reinterpret_cast<const TI*>(p.x) + off[ES_X];
+  const TI* cl = reinterpret_cast<const TI*>(p.s) + off[ES_S];
+  TO* ol = reinterpret_cast<TO*>(p.out) + off[ES_OUT];
   const int64_t sx = p.t_stride[ES_X], sc = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
   const bool rev = p.reverse != 0;
-  float carry = p.init[off[ES_INIT]];
+  float carry = p.init ? p.init[off[ES_INIT]] : 0.0f;  // no initial: linear-scan starts from zero
 
   constexpr int64_t kSlab = int64_t(NW) * S;
   const int64_t nslabs = (T + kSlab - 1) / kSlab;
-  const float kNegInf = -__builtin_huge_valf();
   // Scan position q is time q (forward) or T-1-q (reverse). Positions past the
-  // end are identity trips, max(h - 0, -inf) = h. Loads always read a valid
+  // end are identity trips. Loads always read a valid
   // element (the position clamped to the last one; a lane past the end reads
   // lane 0's and computes values it never stores), so no load sits behind a
   // branch and every load of a slab is in flight at once.
@@ -457,9 +495,9 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
   for (int k = 0; k < S; ++k) {
     const int64_t q = int64_t(wave) * S + k;
     const int64_t t = time_of(q);
-    const float xv = ld_stream(xl + t * sx), cv = ld_stream(cl + t * sc);
-    cx[k] = q < T ? xv : kNegInf;
-    cc[k] = q < T ? cv : 0.0f;
+    const float xv = ld_elem(xl + t * sx), cv = ld_elem(cl + t * sc);
+    cx[k] = q < T ? xv : M::x_pad();
+    cc[k] = q < T ? cv : M::s_pad();
   }
   for (int64_t sl = 0; sl < nslabs; ++sl) {
     const int64_t qw = sl * kSlab + int64_t(wave) * S;  // this wave's first position in the slab
@@ -468,18 +506,15 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
     for (int k = 0; k < S; ++k) {  // next slab, in flight during this one
       const int64_t q = qw + kSlab + k;
       const int64_t t = time_of(q);
-      const float xv = ld_stream(xl + t * sx), cv = ld_stream(cl + t * sc);
-      nx[k] = q < T ? xv : kNegInf;
-      nc[k] = q < T ? cv : 0.0f;
+      const float xv = ld_elem(xl + t * sx), cv = ld_elem(cl + t * sc);
+      nx[k] = q < T ? xv : M::x_pad();
+      nc[k] = q < T ? cv : M::s_pad();
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the next slab's loads issued ahead of this slab's work
-    // summary of this wave's trips: composing max(h - c, x) in scan order gives max(h + P, Q)
-    float P = 0.0f, Q = kNegInf;
+    // summary of this wave's trips: their maps composed in scan order
+    float P = M::p0(), Q = M::q0();
 #pragma unroll
-    for (int k = 0; k < S; ++k) {
-      Q = fmaxf(Q - cc[k], cx[k]);
-      P = P - cc[k];
-    }
+    for (int k = 0; k < S; ++k) M::fold(P, Q, cx[k], cc[k]);
     const int par = int(sl & 1);
     sP[par][wave][l] = P;
     sQ[par][wave][l] = Q;
@@ -489,15 +524,15 @@ __global__ __launch_bounds__(NW * 64) void es_maxplus_slab_kernel(const EsParams
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (w == wave) hw = h;
-      h = fmaxf(h + sP[par][w][l], sQ[par][w][l]);
+      h = M::apply(sP[par][w][l], sQ[par][w][l], h);
     }
     carry = h;
     // replay from the entering state: each trip is the serial body again
 #pragma unroll
     for (int k = 0; k < S; ++k) {
-      hw = fmaxf(hw - cc[k], cx[k]);
+      hw = elementwise_body<BODY>(hw, cx[k], cc[k]);
       const int64_t q = qw + k;
-      if (live && q < T) st_stream(ol + time_of(q) * so, hw);
+      if (live && q < T) st_elem_stream(ol + time_of(q) * so, hw);
     }
 #pragma unroll
     for (int k = 0; k < S; ++k) {
@@ -548,10 +583,35 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
       hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     } else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips) {
       // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries
-      hipLaunchKernelGGL((es_maxplus_slab_kernel<16, 16>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
+      hipLaunchKernelGGL((es_slab_kernel<SX_BODY_MAX_PLUS, 16, 16>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
     } else {
       hipLaunchKernelGGL(es_lane_kernel<SX_BODY_MAX_PLUS>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     }
+  }
+  return hipGetLastError();
+}
+
+namespace {
+template <typename TI, typename TO>
+void launch_linear(const EsParams& p, int64_t blocks, hipStream_t stream) {
+  if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)
+    hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 16, TI, TO>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((es_lane_kernel<kBodyLinear, TI, TO>), dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+}
+}  // namespace
+
+hipError_t launch_linear_scan(const EsParams& p, bool in_bf16, bool out_bf16, hipStream_t stream) {
+  if (p.num_lanes <= 0 || p.T <= 0) return hipSuccess;
+  const int64_t blocks = (p.num_lanes + 63) / 64;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (in_bf16) {
+    if (out_bf16) launch_linear<uint16_t, uint16_t>(p, blocks, stream);
+    else launch_linear<uint16_t, float>(p, blocks, stream);
+  } else {
+    if (out_bf16) launch_linear<float, uint16_t>(p, blocks, stream);
+    else launch_linear<float, float>(p, blocks, stream);
   }
   return hipGetLastError();
 }

@@ -467,4 +467,122 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
                        "matrix-scan launch");
 }
 
+// ------------------------------------------------------------------ linear-scan
+
+// a and b broadcast (NumPy: right-aligned, each dim equal or 1; rank 0 is a
+// number) to the result shape; the scan runs along `axis` of that shape.
+static sx_status plan_linear_scan(int a_rank, const int64_t* a_shape, const int64_t* a_strides, int b_rank,
+                                  const int64_t* b_shape, const int64_t* b_strides, int axis, sx::EsParams* p,
+                                  int64_t* out_shape, int* out_rank, int64_t* out_numel) {
+  if (a_rank > sx::kMaxRank || b_rank > sx::kMaxRank)
+    return fail(SX_E_UNSUPPORTED, "linear-scan: rank above %d", sx::kMaxRank);
+  if (a_rank < 0 || b_rank < 0 || (a_rank > 0 && !a_shape) || (b_rank > 0 && !b_shape))
+    return fail(SX_E_DIM_001, "linear-scan: invalid rank or missing shape");
+  int64_t tmp;
+  if (!checked_numel(a_rank, a_shape, &tmp) || !checked_numel(b_rank, b_shape, &tmp))
+    return fail(SX_E_DIM_001, "linear-scan: negative or oversized dims in a %s, b %s",
+                shape_str(a_rank, a_shape).c_str(), shape_str(b_rank, b_shape).c_str());
+  const int L = std::max(a_rank, b_rank);
+  if (L < 1)
+    return fail(SX_E_DIM_001, "linear-scan: a and b are both numbers; there is no axis to scan along");
+  int64_t shp[sx::kMaxRank], sa[sx::kMaxRank], sb[sx::kMaxRank];
+  int64_t ast[sx::kMaxRank], bst[sx::kMaxRank];
+  if (a_strides) std::copy(a_strides, a_strides + a_rank, ast); else contiguous_strides(a_rank, a_shape, ast);
+  if (b_strides) std::copy(b_strides, b_strides + b_rank, bst); else contiguous_strides(b_rank, b_shape, bst);
+  for (int i = 0; i < L; ++i) {
+    const int ia = i - (L - a_rank), ib = i - (L - b_rank);
+    const int64_t da = ia >= 0 ? a_shape[ia] : 1, db = ib >= 0 ? b_shape[ib] : 1;
+    if (da != db && da != 1 && db != 1)
+      return fail(SX_E_DIM_001, "linear-scan: a %s and b %s do not broadcast", shape_str(a_rank, a_shape).c_str(),
+                  shape_str(b_rank, b_shape).c_str());
+    shp[i] = da == 1 ? db : da;
+    sa[i] = (ia >= 0 && da != 1) ? ast[ia] : 0;
+    sb[i] = (ib >= 0 && db != 1) ? bst[ib] : 0;
+  }
+  const int ax = axis < 0 ? axis + L : axis;
+  if (ax < 0 || ax >= L)
+    return fail(SX_E_DIM_001, "linear-scan: axis %d out of range for shape %s", axis, shape_str(L, shp).c_str());
+  int64_t numel = 0;
+  if (!checked_numel(L, shp, &numel)) return fail(SX_E_DIM_001, "linear-scan: result too large");
+  std::copy(shp, shp + L, out_shape);
+  *out_rank = L;
+  *out_numel = numel;
+  if (!p) return ok();
+
+  int64_t ost[sx::kMaxRank];
+  contiguous_strides(L, shp, ost);
+  *p = sx::EsParams{};
+  p->T = shp[ax];
+  p->t_stride[sx::ES_X] = sb[ax];
+  p->t_stride[sx::ES_S] = sa[ax];
+  p->t_stride[sx::ES_OUT] = ost[ax];
+  p->n = 1;
+  int64_t dims[sx::kMaxRank];
+  int64_t st[4][sx::kMaxRank];
+  int nd = 0;
+  for (int i = 0; i < L; ++i) {
+    if (i == ax) continue;
+    dims[nd] = shp[i];
+    st[sx::ES_X][nd] = sb[i];
+    st[sx::ES_S][nd] = sa[i];
+    st[sx::ES_INIT][nd] = 0;
+    st[sx::ES_OUT][nd] = ost[i];
+    ++nd;
+  }
+  p->lanes = make_index_map<4>(nd, dims, st);
+  p->num_lanes = p->T > 0 ? numel / p->T : 0;
+  return ok();
+}
+
+int sx_linear_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                             int64_t* out_shape) {
+  int64_t shp[sx::kMaxRank];
+  int r = 0;
+  int64_t numel = 0;
+  if (plan_linear_scan(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, 0, nullptr, shp, &r, &numel) != SX_OK)
+    return -1;
+  if (out_shape) std::copy(shp, shp + r, out_shape);
+  return r;
+}
+
+sx_status sx_linear_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides, const void* a,
+                         int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b, int axis,
+                         int reverse, sx_dtype out_dtype, void* out, void* stream) {
+  if (dtype != SX_F32 && dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "linear-scan: a and b must be f32 or bf16 (dtype code %d)", int(dtype));
+  if (out_dtype != SX_F32 && out_dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "linear-scan: out must be f32 or bf16 (dtype code %d)", int(out_dtype));
+  sx::EsParams p;
+  int64_t shp[sx::kMaxRank];
+  int r = 0;
+  int64_t numel = 0;
+  sx_status st = plan_linear_scan(a_rank, a_shape, a_strides, b_rank, b_shape, b_strides, axis, &p, shp, &r, &numel);
+  if (st != SX_OK) return st;
+  if (numel == 0) return ok();
+  if (!a) return fail(SX_E_DIM_003, "linear-scan: a %s %s is NULL; a tensor was expected",
+                      shape_str(a_rank, a_shape).c_str(), dtype_name(dtype));
+  if (!b) return fail(SX_E_DIM_003, "linear-scan: b %s %s is NULL; a tensor was expected",
+                      shape_str(b_rank, b_shape).c_str(), dtype_name(dtype));
+  if (!out) return fail(SX_E_DIM_003, "linear-scan: out is NULL; a tensor was expected");
+
+  const size_t esz = dtype == SX_BF16 ? 2 : 4, osz = out_dtype == SX_BF16 ? 2 : 4;
+  int64_t ast[sx::kMaxRank], bst[sx::kMaxRank];
+  if (a_strides) std::copy(a_strides, a_strides + a_rank, ast); else contiguous_strides(a_rank, a_shape, ast);
+  if (b_strides) std::copy(b_strides, b_strides + b_rank, bst); else contiguous_strides(b_rank, b_shape, bst);
+  uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + uintptr_t(numel) * osz, lo, hi;
+  span_bytes(a, a_rank, a_shape, ast, esz, &lo, &hi);  // numel > 0: neither operand is empty
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "linear-scan: out overlaps a");
+  span_bytes(b, b_rank, b_shape, bst, esz, &lo, &hi);
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "linear-scan: out overlaps b");
+
+  p.reverse = reverse ? 1 : 0;
+  p.x = static_cast<const float*>(b);  // element type chosen by launch_linear_scan
+  p.s = static_cast<const float*>(a);
+  p.init = nullptr;
+  p.out = static_cast<float*>(out);
+  return device_status(sx::launch_linear_scan(p, dtype == SX_BF16, out_dtype == SX_BF16,
+                                              static_cast<hipStream_t>(stream)),
+                       "linear-scan launch");
+}
+
 }  // extern "C"

@@ -56,12 +56,20 @@ struct EsParams {
   int reverse;
   const float* x;
   const float* s;
-  const float* init;
+  const float* init;     // nullptr: every lane starts from zero (linear-scan)
   float* out;
 };
 
 hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream);
 size_t element_scan_workspace(sx_body body, const EsParams& p);
+
+// linear-scan runs on the element-scan kernels: b as the sequence x, a as the
+// second sequence s, init == nullptr (every lane starts from zero), and the
+// trip h -> a * h + b, a body of the library's own beside the public three.
+// Its x and s point at bf16 (uint16_t) elements when in_bf16, and out at bf16
+// elements when out_bf16; strides and offsets count elements either way.
+constexpr int kBodyLinear = 3;
+hipError_t launch_linear_scan(const EsParams& p, bool in_bf16, bool out_bf16, hipStream_t stream);
 
 // ---------------------------------------------------------------- matrix-scan
 

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for element-scan and matrix-scan.
+"""Seeded synthetic inputs for element-scan, matrix-scan and linear-scan.
 
 This module only draws random numbers (torch CPU generators, fixed seeds);
 it holds none of the scans' arithmetic. Tests, the bench and the smoke check
@@ -6,7 +6,9 @@ build their inputs here and hand the same host tensors to the HIP library
 and to the CPU oracle.
 
 The five standard workloads follow the sizes and distributions below; the
-``make_*`` functions take other sizes for the parity tests.
+``make_*`` functions take other sizes for the parity tests. linear-scan
+(``make_linear``) has no standard workload of its own: it is measured on the
+max-plus shape, [64,4096,256] along axis 1.
 
   tanh-affine       x [4,64,32] ~ N(0,1), decay [4,64,32] ~ U(0,1),
                     initial [4,32] ~ N(0,1), axis 1, forward
@@ -31,7 +33,7 @@ import torch
 @dataclass
 class Workload:
     name: str
-    op: str                      # "element_scan" or "matrix_scan"
+    op: str                      # "element_scan", "matrix_scan" or "linear_scan"
     tensors: dict                # host tensors, in the order the op takes them
     axis: int = 1
     reverse: bool = False
@@ -51,6 +53,8 @@ class Workload:
             if self.state_axis is None:
                 return tuple(x.shape)
             return tuple(x.shape[:-1]) + (t["initial"].shape[-1],)
+        if self.op == "linear_scan":
+            return tuple(torch.broadcast_shapes(t["b"].shape, t["a"].shape if "a" in t else ()))
         lead = torch.broadcast_shapes(t["a"].shape[:-2], t["b"].shape[:-2])
         return tuple(lead) + tuple(t["b"].shape[-2:])
 
@@ -121,6 +125,38 @@ def make_matrix(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, reverse=Fa
     return Workload(name, "matrix_scan", {"a": a, "b": b}, axis=axis, reverse=reverse, out_dtype=out_dtype)
 
 
+def make_linear(shape=(64, 4096, 256), axis=1, reverse=False, dtype=torch.float32, a_kind="decay",
+                a_shape=None, seed=6, out_dtype=None) -> Workload:
+    """linear-scan inputs: b ~ N(0,1) of ``shape``; a by ``a_kind``:
+
+    "decay"  a ~ U(0.9, 1) of ``a_shape`` (default ``shape``; a shape that
+             broadcasts against it tests broadcasting),
+    "signed" a ~ U(-1, 1) of ``a_shape``,
+    "ones"   the number 1 (cumsum),
+    "number" the number 0.95.
+    Tensors are drawn in f32 and rounded to ``dtype`` (nearest even for bf16).
+    """
+    g = _gen(seed)
+    b = torch.randn(shape, generator=g)
+    tensors, meta = {"b": b.to(dtype)}, {}
+    ash = tuple(shape) if a_shape is None else tuple(a_shape)
+    if a_kind == "decay":
+        tensors["a"] = (0.9 + 0.1 * torch.rand(ash, generator=g)).to(dtype)
+    elif a_kind == "signed":
+        tensors["a"] = (2.0 * torch.rand(ash, generator=g) - 1.0).to(dtype)
+    elif a_kind == "ones":
+        meta["a_number"] = 1.0
+    elif a_kind == "number":
+        meta["a_number"] = 0.95
+    else:
+        raise ValueError(f"unknown a_kind {a_kind!r}")
+    what = "cumsum" if a_kind == "ones" else f"linear-scan a {a_kind}"
+    name = f"{what} {str(dtype).replace('torch.', '')} {list(shape)} axis {axis}{' reverse' if reverse else ''}"
+    if a_shape is not None:
+        name += f" a {list(a_shape)}"
+    return Workload(name, "linear_scan", tensors, axis=axis, reverse=reverse, out_dtype=out_dtype, meta=meta)
+
+
 def standard_workloads(which=None) -> list[Workload]:
     """The five standard workloads, in order (or those whose index is in ``which``)."""
     makers = [
@@ -133,3 +169,8 @@ def standard_workloads(which=None) -> list[Workload]:
     idx = range(len(makers)) if which is None else which
     return [makers[i]() for i in idx]
 
+
+def extra_workloads() -> list[Workload]:
+    """linear-scan and cumsum on the max-plus shape, [64,4096,256] along axis 1,
+    f32: timed beside the step, not part of it."""
+    return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7)]

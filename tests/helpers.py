@@ -20,6 +20,9 @@ def run_gpu(w, dev):
     if w.op == "element_scan":
         return sx.element_scan(w.body, t["initial"], [t["x"], t["s"]], axis=w.axis, state_axis=w.state_axis,
                                reverse=w.reverse)
+    if w.op == "linear_scan":
+        a = t["a"] if "a" in t else w.meta["a_number"]
+        return sx.linear_scan(a, t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
     return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
 
 
@@ -29,6 +32,10 @@ def run_oracle(w, dtype=np.float64):
     if w.op == "element_scan":
         return oracle.element_scan(w.body, f(t["initial"]), [f(t["x"]), f(t["s"])], axis=w.axis,
                                    state_axis=w.state_axis, reverse=w.reverse, dtype=dtype)
+    if w.op == "linear_scan":
+        # a number takes the tensors' dtype, as the binding does
+        a = f(t["a"]) if "a" in t else f(torch.tensor(w.meta["a_number"], dtype=t["b"].dtype))
+        return oracle.linear_scan(a, f(t["b"]), axis=w.axis, reverse=w.reverse, dtype=dtype)
     return oracle.matrix_scan(f(t["a"]), f(t["b"]), axis=w.axis, reverse=w.reverse, dtype=dtype)
 
 
@@ -42,6 +49,11 @@ def assert_element_close(got: torch.Tensor, ref: np.ndarray, atol=ES_ATOL, rtol=
         idx = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{int(bad.sum())} of {err.size} elements outside {atol}+{rtol}|ref|; worst at "
                              f"{idx}: got {g[idx]!r}, ref {ref[idx]!r}, max abs err {err.max():.3e}")
+
+
+def assert_linear_close(got: torch.Tensor, ref: np.ndarray, tol: float, axis: int):
+    """linear-scan is matrix-scan over 1 x 1 matrices: the matrix-scan bar on 1 x 1 states."""
+    assert_matrix_close(got[..., None, None], ref[..., None, None], tol, axis=axis % max(ref.ndim, 1))
 
 
 def matrix_state_errors(got: torch.Tensor, ref: np.ndarray):

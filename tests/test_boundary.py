@@ -36,8 +36,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for required in ("sx_element_scan", "sx_matrix_scan", "sx_element_scan_workspace_bytes",
-                     "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_status_name",
-                     "sx_last_error", "sx_version"):
+                     "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_linear_scan",
+                     "sx_linear_scan_out_shape", "sx_status_name", "sx_last_error", "sx_version"):
         assert required in names
 
 
@@ -154,6 +154,64 @@ def test_matrix_scan_workspace_query_is_host_only(lib):
     ws = lib.sx_matrix_scan_workspace_bytes(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1)
     assert ws >= 0
     assert lib.sx_matrix_scan_workspace_bytes(3, B.i64_array([2, 4, 4]), 3, B.i64_array([2, 5, 1]), 0) == 0
+
+
+def _ls(lib, a_shape=(3, 9, 5), b_shape=(3, 9, 5), dtype=B.SX_F32, out_dtype=B.SX_F32, axis=1, a=FAKE,
+        b=FAKE + (1 << 20), out=FAKE + (1 << 22), a_strides=None, b_strides=None):
+    st = lib.sx_linear_scan(dtype, len(a_shape), B.i64_array(a_shape) if a_shape else None,
+                            B.i64_array(a_strides) if a_strides else None, a, len(b_shape),
+                            B.i64_array(b_shape) if b_shape else None, B.i64_array(b_strides) if b_strides else None,
+                            b, axis, 0, out_dtype, out, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(b_shape=(3, 8, 5)), B.SX_E_DIM_001),                 # shapes do not broadcast
+    (dict(a_shape=(2, 9, 1)), B.SX_E_DIM_001),                 # leading 2 against b's 3
+    (dict(axis=3), B.SX_E_DIM_001),
+    (dict(axis=-4), B.SX_E_DIM_001),
+    (dict(a_shape=(), b_shape=()), B.SX_E_DIM_001),            # two numbers: no axis
+    (dict(dtype=2), B.SX_E_DIM_002),
+    (dict(out_dtype=7), B.SX_E_DIM_002),
+    (dict(a=None), B.SX_E_DIM_003),
+    (dict(b=None), B.SX_E_DIM_003),
+    (dict(out=None), B.SX_E_DIM_003),
+    (dict(out=FAKE + 64), B.SX_E_ALIAS),                        # out over a
+    (dict(out=FAKE + (1 << 20) + 4), B.SX_E_ALIAS),            # out over b
+    (dict(a_shape=(1, 2, 3, 4, 5, 6, 7, 8, 9)), B.SX_E_UNSUPPORTED),
+])
+def test_linear_scan_rejects_on_host(lib, kwargs, code):
+    st, msg = _ls(lib, **kwargs)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_linear_scan_empty_is_a_no_op(lib):
+    assert _ls(lib, a_shape=(3, 0, 5), b_shape=(3, 0, 5), a=None, b=None, out=None)[0] == B.SX_OK
+    assert _ls(lib, a_shape=(), b_shape=(0, 9, 5), a=None, b=None, out=None)[0] == B.SX_OK
+
+
+def test_linear_scan_out_shape_broadcasts(lib):
+    out = B.i64_array([0] * 8)
+    assert lib.sx_linear_scan_out_shape(0, None, 3, B.i64_array([4, 6, 2]), out) == 3
+    assert list(out[:3]) == [4, 6, 2]
+    assert lib.sx_linear_scan_out_shape(2, B.i64_array([6, 1]), 3, B.i64_array([4, 1, 2]), out) == 3
+    assert list(out[:3]) == [4, 6, 2]
+    assert lib.sx_linear_scan_out_shape(1, B.i64_array([5]), 0, None, out) == 1 and out[0] == 5
+    assert lib.sx_linear_scan_out_shape(2, B.i64_array([2, 3]), 2, B.i64_array([3, 3]), out) == -1
+    assert lib.sx_linear_scan_out_shape(0, None, 0, None, out) == -1
+
+
+def test_linear_scan_binding_refuses_before_the_device():
+    with pytest.raises(sx.SxError) as e:
+        sx.linear_scan(0.5, 2.0)
+    assert e.value.name == "E-DIM-001"
+    with pytest.raises(sx.SxError) as e:
+        sx.cumsum(torch.zeros(4, 3))
+    assert e.value.name == "E-UNSUPPORTED"  # a host tensor: the library takes device tensors
+    with pytest.raises(sx.SxError) as e:
+        sx.linear_scan(torch.zeros(4, 3), [1.0, 2.0])
+    assert e.value.name in ("E-UNSUPPORTED", "E-DIM-003")
 
 
 def test_binding_refuses_host_tensors_and_bad_dtypes():
