@@ -31,6 +31,11 @@ Sources, all from the SexpGPU documentation pages:
   "matrix-scan" section: ``h[t] = a[t] @ h[t-1] + b[t]`` from ``h = 0``,
   ``:reverse`` running from the end, NumPy broadcasting of the leading dims,
   ``:axis`` counted among the leading dims, result in ``b``'s shape.
+* "Tensor operations", the "matrix-scan" section, on its gradient: the
+  same scan run backwards on the transposes of ``a``; and the "gradient"
+  section: a gradient has the shape (and dtype) of the tensor it is taken
+  with respect to, so a broadcast operand's gradient sums over the dims it
+  was broadcast along.
 * "Tensor operations", the "matrix-scan" section, on the prelude's
   ``linear-scan``: the same recurrence over one-by-one matrices, taking ``a``
   and ``b`` (numbers included) broadcast to one shape; ``cumsum`` is built on
@@ -58,7 +63,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["element_scan", "matrix_scan", "linear_scan", "cumsum", "BODIES"]
+__all__ = ["element_scan", "matrix_scan", "matrix_scan_vjp", "linear_scan", "cumsum", "BODIES"]
 
 
 # --- element-scan bodies ----------------------------------------------------
@@ -198,6 +203,66 @@ def matrix_scan(a, b, axis=0, reverse=False, dtype=np.float64):
         h = a_t[t] @ h + b_t[t]
         out[t] = h
     return np.moveaxis(out, 0, ax)
+
+
+def _sum_to_shape(x, shape):
+    """Sum ``x`` over the dims that broadcasting ``shape`` up to ``x.shape`` added or stretched."""
+    extra = x.ndim - len(shape)
+    if extra:
+        x = x.sum(axis=tuple(range(extra)))
+    stretched = tuple(i for i, d in enumerate(shape) if d == 1 and x.shape[i] != 1)
+    if stretched:
+        x = x.sum(axis=stretched, keepdims=True)
+    return x.reshape(shape)
+
+
+def matrix_scan_vjp(a, b, g, axis=0, reverse=False, dtype=np.float64):
+    """Gradient of ``sum(g * matrix_scan(a, b))`` with respect to ``a`` and ``b``.
+
+    Returns ``(grad_a, grad_b)`` in the shapes of ``a`` and ``b``; ``g`` has
+    the result's shape. Chain rule through one step ``h[t] = a[t] @ h[p] + b[t]``
+    (``p`` the step before in scan order, ``h[p] = 0`` at the first step):
+    with ``lam[t]`` the total derivative with respect to ``h[t]``,
+
+      lam[t]    = g[t] + a[s]^T @ lam[s]     (``s`` the step after t in scan
+                                             order; no second term at the last)
+      grad_b[t] = lam[t]
+      grad_a[t] = lam[t] @ h[p]^T            (zero at the first step)
+
+    so ``lam`` is the same scan run in the other direction on the transposes
+    of ``a``, one step shifted. Written as a plain loop over the steps, last
+    to first, after the forward scan above has produced ``h``.
+
+    Follows "Tensor operations", the "matrix-scan" section (its gradient) and
+    the "gradient" section (a gradient takes its operand's shape).
+    """
+    a = np.asarray(a, dtype=dtype)
+    b = np.asarray(b, dtype=dtype)
+    g = np.asarray(g, dtype=dtype)
+    h = matrix_scan(a, b, axis=axis, reverse=reverse, dtype=dtype)  # validates the operands
+    if g.shape != h.shape:
+        raise ValueError(f"matrix_scan_vjp: g has shape {g.shape}, the result has {h.shape}")
+    n, m = a.shape[-1], b.shape[-1]
+    lead = h.shape[:-2]
+    ax = axis + len(lead) if axis < 0 else axis
+    a_t = np.moveaxis(np.broadcast_to(a, lead + (n, n)), ax, 0)
+    g_t = np.moveaxis(g, ax, 0)
+    h_t = np.moveaxis(h, ax, 0)
+    T = lead[ax]
+    lam = np.empty(g_t.shape, dtype=dtype)
+    grad_a = np.zeros(a_t.shape, dtype=dtype)
+    order = list(range(T - 1, -1, -1)) if reverse else list(range(T))  # scan order of the forward pass
+    from_later = np.zeros(g_t.shape[1:], dtype=dtype)  # a[s]^T @ lam[s], s the step after
+    for i in range(T - 1, -1, -1):
+        t = order[i]
+        lam[t] = g_t[t] + from_later
+        if i > 0:
+            p = order[i - 1]
+            grad_a[t] = lam[t] @ np.swapaxes(h_t[p], -1, -2)
+        from_later = np.swapaxes(a_t[t], -1, -2) @ lam[t]
+    grad_a = _sum_to_shape(np.moveaxis(grad_a, 0, ax), a.shape)
+    grad_b = _sum_to_shape(np.moveaxis(lam, 0, ax), b.shape)
+    return grad_a, grad_b
 
 
 def linear_scan(a, b, axis=0, reverse=False, dtype=np.float64):

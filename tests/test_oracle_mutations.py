@@ -192,3 +192,68 @@ def test_linear_scan_mutants_are_caught(mutant, monkeypatch):
 
 def test_unmutated_linear_scan_passes_its_pins():
     assert not _some_pin_fails(LS_PINS)
+
+
+_real_vjp = oracle.matrix_scan_vjp
+
+
+def _vjp_mutant(kind):
+    """A copy of the gradient loop with one plausible mistake planted."""
+    def vjp(a, b, g, axis=0, reverse=False, dtype=np.float64):
+        a = np.asarray(a, dtype=dtype)
+        b = np.asarray(b, dtype=dtype)
+        g = np.asarray(g, dtype=dtype)
+        h = oracle.matrix_scan(a, b, axis=axis, reverse=reverse, dtype=dtype)
+        n = a.shape[-1]
+        lead = h.shape[:-2]
+        ax = axis % len(lead)
+        a_t = np.moveaxis(np.broadcast_to(a, lead + (n, n)), ax, 0)
+        g_t, h_t = np.moveaxis(g, ax, 0), np.moveaxis(h, ax, 0)
+        T = lead[ax]
+        lam = np.empty(g_t.shape)
+        grad_a = np.zeros(a_t.shape)
+        order = list(range(T - 1, -1, -1)) if reverse else list(range(T))
+        if kind == "wrong_direction":
+            order = order[::-1]
+        from_later = np.zeros(g_t.shape[1:])
+        for i in range(T - 1, -1, -1):
+            t = order[i]
+            lam[t] = g_t[t] + from_later if kind != "drops_g" or i == T - 1 else from_later
+            if i > 0:
+                p = order[i - 1]
+                hp = h_t[t] if kind == "uses_h_t" else h_t[p]
+                grad_a[t] = (hp @ np.swapaxes(lam[t], -1, -2) if kind == "outer_transposed"
+                             else lam[t] @ np.swapaxes(hp, -1, -2))
+            at = a_t[t] if kind == "no_transpose" else np.swapaxes(a_t[t], -1, -2)
+            if kind == "same_step_a" and i > 0:
+                at = np.swapaxes(a_t[order[i - 1]], -1, -2)
+            from_later = at @ lam[t]
+        grad_a = oracle._sum_to_shape(np.moveaxis(grad_a, 0, ax), a.shape)
+        grad_b = oracle._sum_to_shape(np.moveaxis(lam, 0, ax), b.shape)
+        return grad_a, grad_b
+    vjp.__name__ = f"vjp_{kind}"
+    return vjp
+
+
+VJP_PINS = [
+    (pins.test_matrix_scan_vjp_exact_by_unit_perturbations, {"axis": 1, "reverse": False}),
+    (pins.test_matrix_scan_vjp_exact_by_unit_perturbations, {"axis": 0, "reverse": True}),
+    (pins.test_matrix_scan_vjp_grad_b_is_the_transposed_scan_run_backwards, {"reverse": False}),
+    (pins.test_matrix_scan_vjp_scalar_closed_form, {}),
+]
+
+
+@pytest.mark.parametrize("kind", ["no_transpose", "same_step_a", "uses_h_t", "outer_transposed", "drops_g",
+                                  "wrong_direction"])
+def test_matrix_scan_vjp_mutants_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "matrix_scan_vjp", _vjp_mutant(kind))
+    assert _some_pin_fails(VJP_PINS), f"no gradient pin caught {kind}"
+
+
+def test_unmutated_vjp_passes_its_pins():
+    assert not _some_pin_fails(VJP_PINS)
+    # the planted-mistake copy without a mistake is the oracle
+    rng = np.random.default_rng(5)
+    a, b, g = rng.normal(size=(2, 5, 3, 3)), rng.normal(size=(2, 5, 3, 2)), rng.normal(size=(2, 5, 3, 2))
+    for x, y in zip(_vjp_mutant("none")(a, b, g, axis=1), _real_vjp(a, b, g, axis=1)):
+        np.testing.assert_array_equal(x, y)

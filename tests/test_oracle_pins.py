@@ -528,3 +528,101 @@ def test_linear_scan_empty_axis_and_numbers():
         oracle.linear_scan(1.0, 2.0)  # two numbers: no axis to scan
     with pytest.raises(ValueError):
         oracle.linear_scan(np.ones(4), np.ones(4), axis=1)
+
+
+# ---------------------------------------------------------------- matrix-scan gradient
+#
+# "Tensor operations", the "matrix-scan" section: the gradient is the same
+# scan run backwards on a's transposes; the "gradient" section: a gradient
+# has its operand's shape. The pins below fix the vector-Jacobian product by
+# what it is, the derivative of L = sum(g * h), without reusing its loop.
+
+
+def _loss(a, b, g, axis, reverse):
+    return float(np.sum(g * oracle.matrix_scan(a, b, axis=axis, reverse=reverse)))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("axis", [0, 1, -1])
+def test_matrix_scan_vjp_exact_by_unit_perturbations(axis, reverse):
+    # h is linear in b, and affine in each single entry of a (a step's matrix
+    # enters every product at most once), so a unit change of one entry moves
+    # L by exactly that entry's derivative: a brute-force Jacobian row each.
+    rng = _rng(71)
+    lead = (2, 4)
+    a = 0.6 * rng.normal(size=lead + (3, 3))
+    b = rng.normal(size=lead + (3, 2))
+    g = rng.normal(size=lead + (3, 2))
+    ga, gb = oracle.matrix_scan_vjp(a, b, g, axis=axis, reverse=reverse)
+    assert ga.shape == a.shape and gb.shape == b.shape
+    base = _loss(a, b, g, axis, reverse)
+    for idx in np.ndindex(*b.shape):
+        db = np.zeros_like(b)
+        db[idx] = 1.0
+        assert abs((_loss(a, b + db, g, axis, reverse) - base) - gb[idx]) < 1e-12 * (1 + abs(base))
+    for idx in np.ndindex(*a.shape):
+        da = np.zeros_like(a)
+        da[idx] = 1.0
+        assert abs((_loss(a + da, b, g, axis, reverse) - base) - ga[idx]) < 1e-11 * (1 + abs(base))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_scan_vjp_directional_derivative_with_broadcasting(reverse):
+    # a constant in time, b shared by the batch: central differences of L
+    # along random directions in the operands' own shapes
+    rng = _rng(72)
+    a = 0.3 * rng.normal(size=(3, 1, 4, 4)) + 0.5 * np.eye(4)   # broadcast over time 6 (axis 1)
+    b = rng.normal(size=(6, 4, 2))                              # broadcast over batch 3
+    g = rng.normal(size=(3, 6, 4, 2))
+    ga, gb = oracle.matrix_scan_vjp(a, b, g, axis=1, reverse=reverse)
+    assert ga.shape == a.shape and gb.shape == b.shape
+    for _ in range(3):
+        da, db = rng.normal(size=a.shape), rng.normal(size=b.shape)
+        eps = 1e-5
+        fd = (_loss(a + eps * da, b + eps * db, g, 1, reverse) - _loss(a - eps * da, b - eps * db, g, 1, reverse)) / (2 * eps)
+        an = float(np.sum(ga * da) + np.sum(gb * db))
+        assert abs(fd - an) <= 1e-7 * (1 + abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_scan_vjp_grad_b_is_the_transposed_scan_run_backwards(reverse):
+    # the page's statement, built explicitly: a'[t] = transpose of the a of the
+    # step after t in the forward order, scanned in the other direction over g
+    rng = _rng(73)
+    T = 7
+    a = 0.5 * rng.normal(size=(2, T, 5, 5))
+    b = rng.normal(size=(2, T, 5, 3))
+    g = rng.normal(size=(2, T, 5, 3))
+    _, gb = oracle.matrix_scan_vjp(a, b, g, axis=1, reverse=reverse)
+    at = np.swapaxes(a, -1, -2)
+    shifted = np.zeros_like(at)
+    if reverse:   # forward order is T-1 .. 0: the step after t is t-1
+        shifted[:, 1:] = at[:, :-1]
+    else:         # the step after t is t+1
+        shifted[:, :-1] = at[:, 1:]
+    want = oracle.matrix_scan(shifted, g, axis=1, reverse=not reverse)
+    np.testing.assert_allclose(gb, want, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_scan_vjp_first_step_a_has_zero_gradient():
+    # a at the first step multiplies h = 0, in either direction
+    rng = _rng(74)
+    a = rng.normal(size=(3, 5, 4, 4))
+    b = rng.normal(size=(3, 5, 4, 1))
+    g = rng.normal(size=(3, 5, 4, 1))
+    ga, _ = oracle.matrix_scan_vjp(a, b, g, axis=1)
+    assert np.all(ga[:, 0] == 0) and np.any(ga[:, 1] != 0)
+    ga, _ = oracle.matrix_scan_vjp(a, b, g, axis=1, reverse=True)
+    assert np.all(ga[:, -1] == 0) and np.any(ga[:, -2] != 0)
+
+
+def test_matrix_scan_vjp_scalar_closed_form():
+    # n = m = 1, T = 3 forward: h0 = b0, h1 = a1 b0 + b1, h2 = a2 a1 b0 + a2 b1 + b2
+    a = np.array([[[0.0]], [[2.0]], [[3.0]]])
+    b = np.array([[[1.0]], [[5.0]], [[7.0]]])
+    g = np.array([[[1.0]], [[10.0]], [[100.0]]])
+    ga, gb = oracle.matrix_scan_vjp(a, b, g, axis=0)
+    # dL/db0 = g0 + a1 g1 + a2 a1 g2 = 1 + 20 + 600; dL/db1 = g1 + a2 g2 = 310; dL/db2 = 100
+    assert gb[:, 0, 0].tolist() == [621.0, 310.0, 100.0]
+    # dL/da1 = (g1 + a2 g2) h0 = 310; dL/da2 = g2 h1 = 100 * 7
+    assert ga[:, 0, 0].tolist() == [0.0, 310.0, 700.0]
