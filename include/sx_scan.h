@@ -1,7 +1,7 @@
 /*
  * sx_scan.h: C ABI of the MI355X (gfx950) scan library, libsx_scan.so.
  *
- * The scans of the SexpGPU documentation pages, forward passes:
+ * The scans of the SexpGPU documentation pages:
  *
  *   element-scan  "Nonlinear element scans": a nonlinear recurrence run
  *                 independently at every position outside one sequence axis,
@@ -11,6 +11,8 @@
  *                 the "matrix-scan" section: h[t] = a[t] @ h[t-1] + b[t] from
  *                 h = 0, n <= 16, computed in f32, with :axis, :reverse and
  *                 broadcast leading dims.
+ *   matrix-scan gradient  the same section and "gradient": the adjoint scan
+ *                 in the other direction on a's transposes, then grad_a.
  *   linear-scan   the same section: matrix-scan over one-by-one matrices,
  *                 a and b broadcast to one shape (cumsum: a = 1).
  *
@@ -167,6 +169,52 @@ size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_
  * entries) and returns its rank, or -1 for shapes that do not fit. */
 int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
                              int64_t* out_shape);
+
+/*
+ * sx_matrix_scan_backward: "Tensor operations", the "matrix-scan" section (its
+ * gradient is the same scan run backwards on a's transposes) and the
+ * "gradient" section (a gradient has its operand's shape and dtype).
+ *
+ * Given the forward call's a and b shapes, its result h and the gradient g of
+ * a loss with respect to h, writes the gradients of that loss with respect to
+ * a and b. With lam[t] the adjoint of h[t] and s / p the steps after / before
+ * t in the forward scan order,
+ *   lam[t]    = g[t] + a[s]^T @ lam[s]   (no second term at the last step)
+ *   grad_b[t] = lam[t]
+ *   grad_a[t] = lam[t] @ h[p]^T        (zero at the first step, whose a
+ *                                      multiplies the zero state)
+ * summed over the dims along which a (or b) was broadcast. lam is computed in
+ * f32 by the matrix-scan kernels in the other direction.
+ *
+ *  dtype         SX_F32 or SX_BF16: the dtype of a, h and g alike.
+ *  a_*           a as passed to sx_matrix_scan (strides as there).
+ *  b_rank/shape  b's shape (b's values are not needed).
+ *  h             the forward result: contiguous, the shape
+ *                sx_matrix_scan_out_shape gives, dtype `dtype`.
+ *  g_strides, g  gradient of the result: that shape, dtype `dtype`; strides
+ *                NULL for contiguous; its two matrix dims row-major
+ *                contiguous (else SX_E_UNSUPPORTED).
+ *  axis, reverse those of the forward call.
+ *  grad_dtype    SX_F32 or SX_BF16 for grad_a and grad_b (rounded to nearest
+ *                even on store).
+ *  grad_a/grad_b contiguous, the shapes of a and b. Must not overlap any
+ *                input or each other (SX_E_ALIAS).
+ *  workspace     at least sx_matrix_scan_backward_workspace_bytes() bytes,
+ *                256-byte aligned; may be NULL when that is 0.
+ *
+ * Errors as sx_matrix_scan (E-DIM-001 shapes, E-DIM-002 dtypes, E-DIM-003 a
+ * NULL tensor that has elements). Empty operands return SX_OK; gradients of
+ * operands that have elements are written even when the result is empty
+ * (they are zero then).
+ */
+sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                                  const void* a, int b_rank, const int64_t* b_shape, const void* h,
+                                  const int64_t* g_strides, const void* g, int axis, int reverse, sx_dtype grad_dtype,
+                                  void* grad_a, void* grad_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sx_matrix_scan_backward needs (0 for invalid shapes). */
+size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank,
+                                               const int64_t* b_shape, int axis, sx_dtype grad_dtype);
 
 /*
  * sx_linear_scan: "Tensor operations", the "matrix-scan" section, on the

@@ -71,6 +71,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sx_matrix_scan_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int]
     lib.sx_matrix_scan_out_shape.restype = c_int
     lib.sx_matrix_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
+    lib.sx_matrix_scan_backward.restype = c_int
+    lib.sx_matrix_scan_backward.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, vp, _i64p, vp,
+                                            c_int, c_int, c_int, vp, vp, vp, c_size, vp]
+    lib.sx_matrix_scan_backward_workspace_bytes.restype = c_size
+    lib.sx_matrix_scan_backward_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int, c_int]
     lib.sx_linear_scan.restype = c_int
     lib.sx_linear_scan.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
                                    c_int, c_int, c_int, vp, vp]
@@ -176,8 +181,15 @@ def matrix_scan(a: torch.Tensor, b: torch.Tensor, axis: int = 0, reverse: bool =
     ``a`` is ``[..., n, n]`` and ``b`` ``[..., n, m]`` of one dtype (f32 or
     bf16); the leading dims broadcast. The result has the broadcast leading
     shape plus ``[n, m]`` and ``b``'s dtype unless ``out_dtype`` says
-    otherwise. Computation is f32.
+    otherwise. Computation is f32. When autograd records (an input requires
+    grad), the gradient runs through ``matrix_scan_backward``.
     """
+    if torch.is_grad_enabled() and any(isinstance(t, torch.Tensor) and t.requires_grad for t in (a, b)):
+        return _MatrixScanFunction.apply(a, b, axis, reverse, out_dtype, projective)
+    return _matrix_scan_forward(a, b, axis, reverse, out_dtype, projective)
+
+
+def _matrix_scan_forward(a, b, axis, reverse, out_dtype, projective) -> torch.Tensor:
     _require_device_tensor("a", a)
     _require_device_tensor("b", b)
     if a.dtype != b.dtype or a.dtype not in _DTYPES:
@@ -267,6 +279,68 @@ def linear_scan(a, b, axis: int = 0, reverse: bool = False, out_dtype=None) -> t
 def cumsum(x: torch.Tensor, axis: int = 0, reverse: bool = False, out_dtype=None) -> torch.Tensor:
     """Running sum along ``axis`` (from the end when ``reverse``): linear-scan with ``a = 1``."""
     return linear_scan(1.0, x, axis=axis, reverse=reverse, out_dtype=out_dtype)
+
+
+def matrix_scan_backward(a: torch.Tensor, b_shape, h: torch.Tensor, g: torch.Tensor, axis: int = 0,
+                         reverse: bool = False, grad_dtype=None):
+    """Gradients ``(grad_a, grad_b)`` of a loss through ``h = matrix_scan(a, b, axis, reverse)``.
+
+    ``h`` is that call's result and ``g`` the loss's gradient with respect to
+    it; ``a``, ``h`` and ``g`` share one dtype (f32 or bf16). ``grad_a`` and
+    ``grad_b`` have the shapes of ``a`` and ``b`` (summed over broadcast dims)
+    and ``grad_dtype`` (default: a's dtype). The adjoint is computed in f32.
+    """
+    for name, t in (("a", a), ("h", h), ("g", g)):
+        _require_device_tensor(name, t)
+    if not (a.dtype == h.dtype == g.dtype) or a.dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"matrix-scan gradient: a is {a.dtype}, h {h.dtype} and g {g.dtype}; one float "
+                                    "dtype (f32 or bf16) is required")
+    if not (a.device == h.device == g.device):
+        raise SxError(SX_E_UNSUPPORTED, "matrix-scan gradient: operands on different devices")
+    grad_dtype = a.dtype if grad_dtype is None else grad_dtype
+    if grad_dtype not in _DTYPES:
+        raise SxError(SX_E_DIM_002, f"matrix-scan gradient: grad dtype {grad_dtype} is not f32 or bf16")
+    b_shape = tuple(int(d) for d in b_shape)
+    if tuple(g.shape) != tuple(h.shape):
+        raise SxError(SX_E_DIM_001, f"matrix-scan gradient: g {tuple(g.shape)} and h {tuple(h.shape)} differ")
+    lib = load_library()
+    if a.dim() >= 2 and not _matrix_dims_contiguous(a):
+        a = a.contiguous()
+    if g.dim() >= 2 and not _matrix_dims_contiguous(g):
+        g = g.contiguous()
+    h = h.contiguous()
+    a_shape, bs = i64_array(a.shape), i64_array(b_shape)
+    ws_bytes = lib.sx_matrix_scan_backward_workspace_bytes(a.dim(), a_shape, len(b_shape), bs, axis,
+                                                           _DTYPES[grad_dtype])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+    grad_a = torch.empty(tuple(a.shape), dtype=grad_dtype, device=a.device)
+    grad_b = torch.empty(b_shape, dtype=grad_dtype, device=a.device)
+    with torch.cuda.device(a.device):
+        status = lib.sx_matrix_scan_backward(
+            _DTYPES[a.dtype], a.dim(), a_shape, i64_array(a.stride()), a.data_ptr(),
+            len(b_shape), bs, h.data_ptr(), i64_array(g.stride()), g.data_ptr(),
+            axis, 1 if reverse else 0, _DTYPES[grad_dtype], grad_a.data_ptr(), grad_b.data_ptr(),
+            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(a.device))
+    _check(status)
+    return grad_a, grad_b
+
+
+class _MatrixScanFunction(torch.autograd.Function):
+    """matrix_scan with its gradient from the library: saves a and the result."""
+
+    @staticmethod
+    def forward(ctx, a, b, axis, reverse, out_dtype, projective):
+        h = _matrix_scan_forward(a, b, axis, reverse, out_dtype, projective)
+        ctx.save_for_backward(a, h)
+        ctx.b_shape, ctx.b_dtype, ctx.axis, ctx.reverse = tuple(b.shape), b.dtype, axis, reverse
+        return h
+
+    @staticmethod
+    def backward(ctx, g):
+        a, h = ctx.saved_tensors
+        grad_a, grad_b = matrix_scan_backward(a, ctx.b_shape, h, g, axis=ctx.axis, reverse=ctx.reverse,
+                                              grad_dtype=ctx.b_dtype)
+        return grad_a, grad_b, None, None, None, None
 
 
 def _matrix_dims_contiguous(t: torch.Tensor) -> bool:

@@ -53,7 +53,10 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = f32_to_b
 
 // ------------------------------------------------------------------ serial kernel
 
-template <typename TIn, typename TOut>
+// ADJ (all kernels here): the step at scan position q multiplies by the
+// transpose of a at position q - 1 (position 0 at q = 0, where the state it
+// multiplies is zero). That is the adjoint recurrence of a matrix scan.
+template <typename TIn, typename TOut, bool ADJ = false>
 __global__ __launch_bounds__(256) void ms_serial_kernel(const MsParams p) {
   const int col_tiles = (p.m + 15) / 16;
   const int64_t batch = int64_t(blockIdx.x) / col_tiles;
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256) void ms_serial_kernel(const MsParams p) {
   index_offsets(p.batch, batch, off);
   const int64_t T = p.T;
   int64_t da = p.t_stride[MS_A], db = p.t_stride[MS_B], dout = p.t_stride[MS_OUT];
-  const TIn* ap = static_cast<const TIn*>(p.a) + off[MS_A] + (in_a ? i * n + j : 0);
+  const TIn* ap = static_cast<const TIn*>(p.a) + off[MS_A] + (in_a ? (ADJ ? j * n + i : i * n + j) : 0);
   const TIn* bp = static_cast<const TIn*>(p.b) + off[MS_B] + (in_h ? int64_t(i) * m + col : 0);
   TOut* op = static_cast<TOut*>(p.out) + off[MS_OUT] + (in_h ? int64_t(i) * m + col : 0);
   if (p.reverse) {
@@ -87,8 +90,9 @@ __global__ __launch_bounds__(256) void ms_serial_kernel(const MsParams p) {
   float bn = in_h ? load_elem(bp) : 0.0f;
   for (int64_t t = 0; t < T; ++t) {
     const float av = an, bv = bn;
+    const int64_t da_next = (ADJ && t == 0) ? 0 : da;  // ADJ: steps 0 and 1 both use position 0
     if (t + 1 < T) {  // next step's operands, loaded ahead of this step's product
-      an = in_a ? load_elem(ap + da) : 0.0f;
+      an = in_a ? load_elem(ap + da_next) : 0.0f;
       bn = in_h ? load_elem(bp + db) : 0.0f;
     }
     sa[i][j] = av;
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) void ms_serial_kernel(const MsParams p) {
     __syncthreads();
     sh[i][j] = acc;
     if (in_h) store_elem(op, acc);
-    ap += da;
+    ap += da_next;
     bp += db;
     op += dout;
   }
@@ -157,10 +161,25 @@ struct ARow<uint16_t> {
   }
 };
 
-template <typename TIn, bool VEC>
+template <typename TIn, bool VEC, bool ADJ = false>
 __device__ __forceinline__ ARow<TIn> load_a(const TIn* ap, int n, int r, int c) {
   ARow<TIn> out;
-  if constexpr (VEC && sizeof(TIn) == 4) {
+  if constexpr (ADJ) {
+    // row c of the transpose is column c of a: a[4r .. 4r+3][c], clamped indices, zero past n
+    uint16_t h[4];
+    float f[4];
+    const int col = c < n ? c : n - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool in = c < n && 4 * r + q < n;
+      const int row = 4 * r + q < n ? 4 * r + q : n - 1;
+      const TIn v = ap[row * n + col];
+      if constexpr (sizeof(TIn) == 4) f[q] = in ? float(v) : 0.0f;
+      else h[q] = in ? uint16_t(v) : uint16_t(0);
+    }
+    if constexpr (sizeof(TIn) == 4) out.v = f32x4{f[0], f[1], f[2], f[3]};
+    else out.u = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+  } else if constexpr (VEC && sizeof(TIn) == 4) {
     out.v = *reinterpret_cast<const f32x4*>(ap + c * 16 + 4 * r);
   } else if constexpr (VEC) {
     out.u = *reinterpret_cast<const uint2*>(ap + c * 16 + 4 * r);
@@ -360,7 +379,7 @@ __device__ __forceinline__ f32x4 to_a_operand(float* scratch, f32x4 d, int r, in
 // look-back over earlier units of the same (batch, tile), and publishes the
 // leaving state. Every wave then applies the maps of the waves before it to
 // that state and replays its K steps, storing h at every step.
-template <int NW, int K, typename TIn, typename TOut, bool VEC, bool M1>
+template <int NW, int K, typename TIn, typename TOut, bool VEC, bool M1, bool ADJ = false>
 __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, const MsUnitWs ws) {
   static_assert(K == 16, "the m == 1 path keeps one step per lane column");
   __shared__ float sP[NW][256];  // wave maps: P row-major (A-operand order readable)
@@ -412,7 +431,9 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t kk = q0 + k < T ? int64_t(k) : T - 1 - q0;
-    A[k] = select_a(q0 + k < T, load_a<TIn, VEC>(a0 + (t0 * p.t_stride[MS_A] + kk * ta), n, r, c), eye);
+    int64_t ka = kk;  // a's position, relative to q0
+    if constexpr (ADJ) ka = q0 + kk > 0 ? kk - 1 : -q0;
+    A[k] = select_a(q0 + k < T, load_a<TIn, VEC, ADJ>(a0 + (t0 * p.t_stride[MS_A] + ka * ta), n, r, c), eye);
     if constexpr (!M1) Bv[k] = select_b(q0 + k < T, load_b(b0 + (t0 * p.t_stride[MS_B] + kk * tb), n, m, r, cc));
   }
   f32x4 b1 = zero4();
@@ -621,7 +642,11 @@ __device__ __forceinline__ PipeGeo pipe_geo(const MsParams& p, const MsUnitWs& w
 // Piece i of the stage of the wave whose steps start at g.q0 is started here.
 // Steps past the end read the last step instead (they become identity steps
 // when the stage is read), so every source address is valid.
-template <typename TIn, bool M1>
+// ADJ: a's step blocks are those of positions one earlier (see ms_serial_kernel);
+// f32 blocks are laid out for a transposed read (see stage_to_regs): lane L
+// copies the piece of row 4 ((L / 4) % 4) + L / 16 at columns 4 (L % 4) ...,
+// so that LDS word 64 q + (16 r + c) holds a[4r + q][c].
+template <typename TIn, bool M1, bool ADJ>
 __device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g, char* st, int lane, int i) {
   using S = PipeStage<TIn, M1>;
   const TIn* a0 = static_cast<const TIn*>(p.a) + g.off[MS_A] + g.t0 * p.t_stride[MS_A];
@@ -630,11 +655,19 @@ __device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g,
   const int64_t tb = p.reverse ? -p.t_stride[MS_B] : p.t_stride[MS_B];
   const int64_t T = p.T, q0 = g.q0;
   auto clamp = [&](int k) -> int64_t { return q0 + k < T ? int64_t(k) : T - 1 - q0; };
+  auto clamp_a = [&](int k) -> int64_t {  // a's position for step k, relative to q0
+    const int64_t kk = clamp(k);
+    if constexpr (ADJ) return q0 + kk > 0 ? kk - 1 : -q0;
+    return kk;
+  };
   if (i < S::kPiecesA) {
-    if constexpr (sizeof(TIn) == 4) {  // step i; lane 16 r + c takes a[c][4r..4r+3]
-      copy16_to_lds(a0 + clamp(i) * ta + (lane & 15) * 16 + 4 * (lane >> 4), st + i * S::kA);
+    if constexpr (sizeof(TIn) == 4 && ADJ) {
+      copy16_to_lds(a0 + clamp_a(i) * ta + (4 * ((lane >> 2) & 3) + (lane >> 4)) * 16 + 4 * (lane & 3),
+                    st + i * S::kA);
+    } else if constexpr (sizeof(TIn) == 4) {  // step i; lane 16 r + c takes a[c][4r..4r+3]
+      copy16_to_lds(a0 + clamp_a(i) * ta + (lane & 15) * 16 + 4 * (lane >> 4), st + i * S::kA);
     } else {  // steps 2i, 2i+1; lane takes a[c][8p..8p+7] for slot c + 16 p of its step
-      copy16_to_lds(a0 + clamp(2 * i + (lane >> 5)) * ta + (lane & 15) * 16 + 8 * ((lane >> 4) & 1),
+      copy16_to_lds(a0 + clamp_a(2 * i + (lane >> 5)) * ta + (lane & 15) * 16 + 8 * ((lane >> 4) & 1),
                     st + i * 2 * S::kA);
     }
     return;
@@ -656,21 +689,22 @@ __device__ __forceinline__ void stage_piece(const MsParams& p, const PipeGeo& g,
 // per-lane offsets computed once: the loader's issue rate is bound by its own
 // instruction latency, so the clamped per-piece addressing is kept for the
 // last unit only.
-template <typename TIn, bool M1>
+template <typename TIn, bool M1, bool ADJ>
 __device__ __forceinline__ void stage_wave(const MsParams& p, const PipeGeo& g, char* st, uint32_t st_lds, int lane) {
   using S = PipeStage<TIn, M1>;
-  if (g.q0 + 16 > p.T) {
+  if (g.q0 + 16 > p.T || (ADJ && g.q0 == 0)) {
 #pragma unroll
-    for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1>(p, g, st, lane, i);
+    for (int i = 0; i < S::kPieces; ++i) stage_piece<TIn, M1, ADJ>(p, g, st, lane, i);
     return;
   }
-  const TIn* a0 = static_cast<const TIn*>(p.a) + g.off[MS_A] + g.t0 * p.t_stride[MS_A];
-  const TIn* b0 = static_cast<const TIn*>(p.b) + g.off[MS_B] + g.t0 * p.t_stride[MS_B];
   const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
   const int64_t tb = p.reverse ? -p.t_stride[MS_B] : p.t_stride[MS_B];
+  // ADJ: a from one position earlier (q0 >= 1 here)
+  const TIn* a0 = static_cast<const TIn*>(p.a) + g.off[MS_A] + g.t0 * p.t_stride[MS_A] - (ADJ ? ta : 0);
+  const TIn* b0 = static_cast<const TIn*>(p.b) + g.off[MS_B] + g.t0 * p.t_stride[MS_B];
   const int c = lane & 15;
   if constexpr (sizeof(TIn) == 4) {
-    const TIn* src = a0 + c * 16 + 4 * (lane >> 4);
+    const TIn* src = ADJ ? a0 + (4 * ((lane >> 2) & 3) + (lane >> 4)) * 16 + 4 * (lane & 3) : a0 + c * 16 + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < S::kPiecesA; ++i) copy16_to_lds_at(src + i * ta, st_lds + i * S::kA);
   } else {
@@ -702,7 +736,7 @@ struct UnitRegs {
   f32x4 b1;
 };
 
-template <typename TIn, bool M1>
+template <typename TIn, bool M1, bool ADJ>
 __device__ __forceinline__ void stage_to_regs(UnitRegs<TIn, M1>& R, const char* st, int64_t q0, int64_t T, int lane,
                                               int r, int c) {
   using S = PipeStage<TIn, M1>;
@@ -717,10 +751,25 @@ __device__ __forceinline__ void stage_to_regs(UnitRegs<TIn, M1>& R, const char* 
   if constexpr (!M1)
     b_lds = lds_addr(reinterpret_cast<const uint32_t*>(st + 16 * S::kA)) + 256 * ((c & 3) >> 1) + 16 * (4 * r + (c >> 2)) +
             8 * (c & 1);
+  // ADJ, the transpose of a: lane (r, c) needs a[4r .. 4r+3][c]. For f32 the loader laid the
+  // block out so that these are LDS words 64 q + lane (four linear reads); a bf16 block has the
+  // layout of a bf16 b tile, so the same transposing read gives the column piece.
+  const uint32_t a_lds = lds_addr(reinterpret_cast<const uint32_t*>(st)) + 256 * ((c & 3) >> 1) + 16 * (4 * r + (c >> 2)) +
+                         8 * (c & 1);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    if constexpr (sizeof(TIn) == 4) R.A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
-    else R.A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+    if constexpr (sizeof(TIn) == 4 && ADJ) {
+      const float* w = reinterpret_cast<const float*>(st + k * S::kA) + lane;
+      R.A[k].v = f32x4{w[0], w[64], w[128], w[192]};
+    } else if constexpr (sizeof(TIn) == 4) {
+      R.A[k].v = *reinterpret_cast<const f32x4*>(st + k * S::kA + lane * 16);
+    } else if constexpr (ADJ) {
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4_ptr>(uintptr_t(a_lds + k * S::kA)));
+      R.A[k].u = make_uint2(uint32_t(uint16_t(v[0])) | (uint32_t(uint16_t(v[1])) << 16),
+                            uint32_t(uint16_t(v[2])) | (uint32_t(uint16_t(v[3])) << 16));
+    } else {
+      R.A[k].u = *reinterpret_cast<const uint2*>(st + k * S::kA + 16 * (c + 16 * (r >> 1)) + 8 * (r & 1));
+    }
     R.A[k] = select_a(q0 + k < T, R.A[k], eye);
     if constexpr (!M1) {
       const bool in = q0 + k < T;
@@ -951,7 +1000,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 // falls from 6.6 to 0.9 TB/s). So the six compute waves are waves 0, 1, 2, 4,
 // 5, 6 (SIMDs 0-2, two each) and the leader (wave 3) and the loader (wave 7)
 // share SIMD 3, where no MFMA chain runs.
-template <int NC, typename TIn, typename TOut, bool M1>
+template <int NC, typename TIn, typename TOut, bool M1, bool ADJ = false>
 __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
   static_assert(NC == 6, "compute waves fill SIMDs 0-2, two each");
   constexpr int K = 16, kUnit = NC * K, LEADER = 3, LOADER = 7;
@@ -1025,7 +1074,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
           if ((issued >> w) & 1u) continue;
           if (lds_read_u32(&sConsumed[w]) < uint32_t(k)) continue;
           if (n_pending == 3) flush();
-          stage_wave<TIn, M1>(p, pipe_geo(p, ws, unit, w, kUnit), &sStage[w][0], stage_lds + w * S::kWave, lane);
+          stage_wave<TIn, M1, ADJ>(p, pipe_geo(p, ws, unit, w, kUnit), &sStage[w][0], stage_lds + w * S::kWave, lane);
           pending |= 1u << w;
           ++n_pending;
           issued |= 1u << w;
@@ -1158,7 +1207,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     if (unit >= NU) return false;
     gc = pipe_geo(p, ws, unit, wave, kUnit);
     lds_wait_at_least(&sLanded[wave], uint32_t(k) + 1);
-    stage_to_regs<TIn, M1>(Rc, st, gc.q0, T, lane, r, c);
+    stage_to_regs<TIn, M1, ADJ>(Rc, st, gc.q0, T, lane, r, c);
     lds_signal_set(&sConsumed[wave], uint32_t(k) + 1, lane);  // (waits for the stage reads first)
     const int kb = k % kBufs;
     lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
@@ -1218,17 +1267,20 @@ UnitPlan unit_plan(const MsParams& p, int unit_steps) {
   return u;
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool ADJ>
 hipError_t launch_serial(const MsParams& p, hipStream_t stream) {
   const int64_t blocks = p.num_batch * ((p.m + 15) / 16);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((ms_serial_kernel<TIn, TOut>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ms_serial_kernel<TIn, TOut, ADJ>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, bool M1>
+template <typename TIn, typename TOut, bool M1, bool ADJ>
 void launch_unit_variant(const MsParams& p, const MsUnitWs& ws, bool vec, unsigned blocks, hipStream_t stream) {
-  if (vec)
+  if (ADJ)  // the transposed loads are element loads: no vector variant
+    hipLaunchKernelGGL((ms_unit_kernel<kWaves, kSteps, TIn, TOut, false, M1, ADJ>), dim3(blocks), dim3(kWaves * 64),
+                       0, stream, p, ws);
+  else if (vec)
     hipLaunchKernelGGL((ms_unit_kernel<kWaves, kSteps, TIn, TOut, true, M1>), dim3(blocks), dim3(kWaves * 64), 0,
                        stream, p, ws);
   else
@@ -1254,13 +1306,14 @@ bool pipe_fits(const MsParams& p) {
   return aligned(MS_A, p.a, si, 16) && aligned(MS_B, p.b, si, 16) && aligned(MS_OUT, p.out, so, m1 ? 4 * so : 16);
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool ADJ>
 void launch_lead_tiles(const MsParams& p, const MsUnitWs& ws, unsigned blocks, hipStream_t stream) {
   if constexpr (sizeof(TIn) == 2)
-    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false>), dim3(blocks), dim3(512), 0, stream, p, ws);
+    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false, ADJ>), dim3(blocks), dim3(512), 0, stream, p,
+                       ws);
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool ADJ>
 hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream) {
   const bool pipe = pipe_fits(p);
   const UnitPlan up = unit_plan(p, pipe ? kLeadCompute * kSteps : kWaves * kSteps);
@@ -1294,13 +1347,14 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
   if (pipe) {
     const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cu_count())));
     if (m1)
-      hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true>), dim3(blocks), dim3(512), 0, stream, p, ws);
-    else launch_lead_tiles<TIn, TOut>(p, ws, blocks, stream);
+      hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true, ADJ>), dim3(blocks), dim3(512), 0, stream, p,
+                         ws);
+    else launch_lead_tiles<TIn, TOut, ADJ>(p, ws, blocks, stream);
     return hipGetLastError();
   }
   const unsigned blocks = unsigned(up.num_units);
-  if (m1) launch_unit_variant<TIn, TOut, true>(p, ws, vec, blocks, stream);
-  else launch_unit_variant<TIn, TOut, false>(p, ws, vec, blocks, stream);
+  if (m1) launch_unit_variant<TIn, TOut, true, ADJ>(p, ws, vec, blocks, stream);
+  else launch_unit_variant<TIn, TOut, false, ADJ>(p, ws, vec, blocks, stream);
   return hipGetLastError();
 }
 
@@ -1320,16 +1374,25 @@ size_t matrix_scan_workspace(const MsParams& p) {
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;
   const size_t need = matrix_scan_workspace(p);
-  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+  const bool chunked = need > 0 && workspace != nullptr && workspace_bytes >= need;
+  if (p.adjoint) {  // the adjoint is kept in f32
+    if (p.out_bf16) return hipErrorInvalidValue;
+    if (chunked)
+      return p.in_bf16 ? launch_chunked<uint16_t, float, true>(p, workspace, stream)
+                       : launch_chunked<float, float, true>(p, workspace, stream);
+    return p.in_bf16 ? launch_serial<uint16_t, float, true>(p, stream) : launch_serial<float, float, true>(p, stream);
+  }
+  if (chunked) {
     if (p.in_bf16)
-      return p.out_bf16 ? launch_chunked<uint16_t, uint16_t>(p, workspace, stream)
-                        : launch_chunked<uint16_t, float>(p, workspace, stream);
-    return p.out_bf16 ? launch_chunked<float, uint16_t>(p, workspace, stream)
-                      : launch_chunked<float, float>(p, workspace, stream);
+      return p.out_bf16 ? launch_chunked<uint16_t, uint16_t, false>(p, workspace, stream)
+                        : launch_chunked<uint16_t, float, false>(p, workspace, stream);
+    return p.out_bf16 ? launch_chunked<float, uint16_t, false>(p, workspace, stream)
+                      : launch_chunked<float, float, false>(p, workspace, stream);
   }
   if (p.in_bf16)
-    return p.out_bf16 ? launch_serial<uint16_t, uint16_t>(p, stream) : launch_serial<uint16_t, float>(p, stream);
-  return p.out_bf16 ? launch_serial<float, uint16_t>(p, stream) : launch_serial<float, float>(p, stream);
+    return p.out_bf16 ? launch_serial<uint16_t, uint16_t, false>(p, stream)
+                      : launch_serial<uint16_t, float, false>(p, stream);
+  return p.out_bf16 ? launch_serial<float, uint16_t, false>(p, stream) : launch_serial<float, float, false>(p, stream);
 }
 
 }  // namespace sx

@@ -467,6 +467,221 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
                        "matrix-scan launch");
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ matrix-scan gradient
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sum of a contiguous full-shape f32 tensor (rank R) down to a target shape
+// (right-aligned, each dim equal or 1): which dims are kept, which summed.
+sx::SumToParams sum_to_plan(int R, const int64_t* full, int t_rank, const int64_t* tshape) {
+  sx::SumToParams q{};
+  int64_t fst[sx::kMaxRank + 2];
+  contiguous_strides(R, full, fst);
+  q.targets = 1;
+  q.reduced = 1;
+  for (int d = 0; d < R; ++d) {
+    const int e = d - (R - t_rank);
+    const bool summed = e < 0 || (tshape[e] == 1 && full[d] != 1);
+    if (summed) {
+      q.red_dim[q.nd_red] = full[d];
+      q.red_st[q.nd_red++] = fst[d];
+      q.reduced *= full[d];
+    } else {
+      q.keep_dim[q.nd_keep] = full[d];
+      q.keep_st[q.nd_keep++] = fst[d];
+      q.targets *= full[d];
+    }
+  }
+  // slices of the summed space: at least 32 terms each, at most 64 MiB of partial sums
+  int64_t splits = std::max<int64_t>(1, std::min<int64_t>(65535, q.reduced / 32));
+  if (q.targets > 0) splits = std::max<int64_t>(1, std::min<int64_t>(splits, (int64_t(64) << 20) / 4 / q.targets));
+  q.splits = splits;
+  q.per = (q.reduced + splits - 1) / splits;
+  return q;
+}
+
+bool same_shape(int r1, const int64_t* s1, int r2, const int64_t* s2) {
+  if (r1 != r2) return false;
+  for (int i = 0; i < r1; ++i)
+    if (s1[i] != s2[i]) return false;
+  return true;
+}
+
+struct MsBackPlan {
+  sx::MsParams p;                       // the adjoint scan (b = g, out = lam)
+  int out_rank;
+  int64_t out_shape[sx::kMaxRank + 2];  // lead + [n, m]
+  int64_t out_numel, a_full_numel;
+  bool lam_direct, ga_direct;           // lam is grad_b itself; grad_a written in place
+  sx::SumToParams sum_a, sum_b;
+  size_t scan_ws, lam_off, ga_off, part_off, total;
+};
+
+sx_status plan_matrix_scan_backward(int a_rank, const int64_t* a_shape, const int64_t* a_strides, int b_rank,
+                                    const int64_t* b_shape, const int64_t* g_strides, int axis, bool grad_f32,
+                                    MsBackPlan* bp) {
+  sx::MsParams fwd;
+  int64_t numel = 0;
+  sx_status st = plan_matrix_scan(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, &fwd, bp->out_shape,
+                                  &bp->out_rank, &numel);
+  if (st != SX_OK) return st;
+  // the adjoint scan: a as given, the gradient of the result in b's place
+  int r = 0;
+  int64_t shp[sx::kMaxRank + 2];
+  st = plan_matrix_scan(a_rank, a_shape, a_strides, bp->out_rank, bp->out_shape, g_strides, axis, &bp->p, shp, &r,
+                        &bp->out_numel);
+  if (st != SX_OK) return st;
+  const int L = bp->out_rank - 2;
+  const int64_t n = bp->out_shape[L];
+  int64_t afull[sx::kMaxRank + 2];
+  std::copy(bp->out_shape, bp->out_shape + L, afull);
+  afull[L] = afull[L + 1] = n;
+  checked_numel(L + 2, afull, &bp->a_full_numel);
+  bp->lam_direct = grad_f32 && same_shape(b_rank, b_shape, bp->out_rank, bp->out_shape);
+  bp->ga_direct = same_shape(a_rank, a_shape, L + 2, afull);
+  bp->sum_a = sum_to_plan(L + 2, afull, a_rank, a_shape);
+  bp->sum_b = sum_to_plan(bp->out_rank, bp->out_shape, b_rank, b_shape);
+  bp->scan_ws = align_up(sx::matrix_scan_workspace(bp->p));
+  size_t off = bp->scan_ws;
+  bp->lam_off = off;
+  if (!bp->lam_direct) off += align_up(size_t(bp->out_numel) * 4);
+  bp->ga_off = off;
+  if (!bp->ga_direct) off += align_up(size_t(bp->a_full_numel) * 4);
+  bp->part_off = off;
+  size_t part = 0;
+  if (!bp->ga_direct) part = std::max(part, size_t(bp->sum_a.splits * bp->sum_a.targets) * 4);
+  if (!same_shape(b_rank, b_shape, bp->out_rank, bp->out_shape))
+    part = std::max(part, size_t(bp->sum_b.splits * bp->sum_b.targets) * 4);
+  bp->total = off + align_up(part);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
+                                               int axis, sx_dtype grad_dtype) {
+  MsBackPlan bp;
+  if (plan_matrix_scan_backward(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, grad_dtype == SX_F32,
+                                &bp) != SX_OK)
+    return 0;
+  return bp.total;
+}
+
+sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                                  const void* a, int b_rank, const int64_t* b_shape, const void* h,
+                                  const int64_t* g_strides, const void* g, int axis, int reverse, sx_dtype grad_dtype,
+                                  void* grad_a, void* grad_b, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SX_F32 && dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "matrix-scan gradient: a, h and g must be f32 or bf16 (dtype code %d)", int(dtype));
+  if (grad_dtype != SX_F32 && grad_dtype != SX_BF16)
+    return fail(SX_E_DIM_002, "matrix-scan gradient: gradients must be f32 or bf16 (dtype code %d)", int(grad_dtype));
+  MsBackPlan bp;
+  sx_status st = plan_matrix_scan_backward(a_rank, a_shape, a_strides, b_rank, b_shape, g_strides, axis,
+                                           grad_dtype == SX_F32, &bp);
+  if (st != SX_OK) return st;
+  int64_t a_numel = 0, b_numel = 0;
+  checked_numel(a_rank, a_shape, &a_numel);
+  checked_numel(b_rank, b_shape, &b_numel);
+  if (a_numel == 0 && b_numel == 0) return ok();
+  if (bp.out_numel > 0 || bp.a_full_numel > 0) {
+    if (!a) return fail(SX_E_DIM_003, "matrix-scan gradient: a %s %s is NULL; a tensor was expected",
+                        shape_str(a_rank, a_shape).c_str(), dtype_name(dtype));
+  }
+  if (bp.out_numel > 0) {
+    if (!h) return fail(SX_E_DIM_003, "matrix-scan gradient: the forward result h %s is NULL; a tensor was expected",
+                        shape_str(bp.out_rank, bp.out_shape).c_str());
+    if (!g) return fail(SX_E_DIM_003, "matrix-scan gradient: the result's gradient g %s is NULL; a tensor was expected",
+                        shape_str(bp.out_rank, bp.out_shape).c_str());
+  }
+  if (a_numel > 0 && !grad_a) return fail(SX_E_DIM_003, "matrix-scan gradient: grad_a is NULL; a tensor was expected");
+  if (b_numel > 0 && !grad_b) return fail(SX_E_DIM_003, "matrix-scan gradient: grad_b is NULL; a tensor was expected");
+
+  // outputs overlap no input and not each other
+  const size_t esz = dtype == SX_BF16 ? 2 : 4, gsz = grad_dtype == SX_BF16 ? 2 : 4;
+  int64_t ast[sx::kMaxRank], gst[sx::kMaxRank + 2], ost[sx::kMaxRank + 2];
+  if (a_strides) std::copy(a_strides, a_strides + a_rank, ast); else contiguous_strides(a_rank, a_shape, ast);
+  contiguous_strides(bp.out_rank, bp.out_shape, ost);
+  if (g_strides) std::copy(g_strides, g_strides + bp.out_rank, gst); else std::copy(ost, ost + bp.out_rank, gst);
+  struct Span { uintptr_t lo, hi; const char* name; };
+  Span ins[3];
+  int nin = 0;
+  uintptr_t lo, hi;
+  if (a_numel > 0) { span_bytes(a, a_rank, a_shape, ast, esz, &lo, &hi); ins[nin++] = {lo, hi, "a"}; }
+  if (bp.out_numel > 0) {
+    span_bytes(h, bp.out_rank, bp.out_shape, ost, esz, &lo, &hi); ins[nin++] = {lo, hi, "h"};
+    span_bytes(g, bp.out_rank, bp.out_shape, gst, esz, &lo, &hi); ins[nin++] = {lo, hi, "g"};
+  }
+  const uintptr_t galo = reinterpret_cast<uintptr_t>(grad_a), gahi = galo + uintptr_t(a_numel) * gsz;
+  const uintptr_t gblo = reinterpret_cast<uintptr_t>(grad_b), gbhi = gblo + uintptr_t(b_numel) * gsz;
+  for (int i = 0; i < nin; ++i) {
+    if (a_numel > 0 && overlaps(galo, gahi, ins[i].lo, ins[i].hi))
+      return fail(SX_E_ALIAS, "matrix-scan gradient: grad_a overlaps %s", ins[i].name);
+    if (b_numel > 0 && overlaps(gblo, gbhi, ins[i].lo, ins[i].hi))
+      return fail(SX_E_ALIAS, "matrix-scan gradient: grad_b overlaps %s", ins[i].name);
+  }
+  if (a_numel > 0 && b_numel > 0 && overlaps(galo, gahi, gblo, gbhi))
+    return fail(SX_E_ALIAS, "matrix-scan gradient: grad_a overlaps grad_b");
+  if (bp.total > 0 && (workspace == nullptr || workspace_bytes < bp.total))
+    return fail(SX_E_WORKSPACE, "matrix-scan gradient: workspace of %zu bytes given, %zu needed", workspace_bytes,
+                bp.total);
+  if (bp.total > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SX_E_WORKSPACE, "matrix-scan gradient: workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* lam = bp.lam_direct ? static_cast<float*>(grad_b) : reinterpret_cast<float*>(ws + bp.lam_off);
+  // 1. the adjoint: the scan in the other direction over g, on a transposed and shifted a step
+  bp.p.in_bf16 = dtype == SX_BF16;
+  bp.p.out_bf16 = 0;
+  bp.p.reverse = reverse ? 0 : 1;
+  bp.p.adjoint = 1;
+  bp.p.a = a;
+  bp.p.b = g;
+  bp.p.out = lam;
+  hipError_t e = sx::launch_matrix_scan(bp.p, ws, bp.scan_ws, s);
+  if (e != hipSuccess) return device_status(e, "matrix-scan gradient: adjoint scan launch");
+  // 2. grad_a = lam h[prev]^T per step (and grad_b = lam rounded, when that is all grad_b is)
+  const int L = bp.out_rank - 2;
+  const int ax = axis < 0 ? axis + L : axis;
+  sx::GradAParams gp{};
+  gp.steps = bp.out_numel > 0 ? bp.out_numel / (bp.out_shape[L] * bp.out_shape[L + 1])
+                              : (bp.a_full_numel > 0 ? bp.a_full_numel / (bp.out_shape[L] * bp.out_shape[L]) : 0);
+  gp.T = bp.out_shape[ax];
+  gp.inner = 1;
+  for (int i = ax + 1; i < L; ++i) gp.inner *= bp.out_shape[i];
+  gp.n = int(bp.out_shape[L]);
+  gp.m = int(bp.out_shape[L + 1]);
+  gp.reverse = reverse ? 1 : 0;
+  gp.lam = lam;
+  gp.h = h;
+  gp.grad_a = bp.ga_direct ? grad_a : static_cast<void*>(ws + bp.ga_off);
+  const bool b_full = same_shape(b_rank, b_shape, bp.out_rank, bp.out_shape);
+  gp.grad_b = (b_full && !bp.lam_direct) ? grad_b : nullptr;
+  e = sx::launch_grad_a(gp, dtype == SX_BF16, grad_dtype == SX_BF16 && bp.ga_direct, s);
+  if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_a launch");
+  // 3. sums over broadcast dims
+  if (!bp.ga_direct && a_numel > 0) {
+    bp.sum_a.src = reinterpret_cast<const float*>(ws + bp.ga_off);
+    bp.sum_a.partial = reinterpret_cast<float*>(ws + bp.part_off);
+    e = sx::launch_sum_to(bp.sum_a, grad_a, grad_dtype == SX_BF16, s);
+    if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_a sum launch");
+  }
+  if (!b_full && b_numel > 0) {
+    bp.sum_b.src = lam;
+    bp.sum_b.partial = reinterpret_cast<float*>(ws + bp.part_off);
+    e = sx::launch_sum_to(bp.sum_b, grad_b, grad_dtype == SX_BF16, s);
+    if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_b sum launch");
+  }
+  return ok();
+}
+
 // ------------------------------------------------------------------ linear-scan
 
 // a and b broadcast (NumPy: right-aligned, each dim equal or 1; rank 0 is a

@@ -84,6 +84,7 @@ struct MsParams {
   int in_bf16;           // a and b are bf16 (else f32)
   int out_bf16;          // out is bf16 (else f32)
   int reverse;
+  int adjoint;           // step q multiplies by the transpose of a at position q - 1 (the gradient's scan)
   const void* a;
   const void* b;
   void* out;
@@ -91,6 +92,36 @@ struct MsParams {
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
 size_t matrix_scan_workspace(const MsParams& p);
+
+// ---------------------------------------------------------------- matrix-scan gradient
+
+// grad_a[s] = lam[s] @ h[prev(s)]^T for every step s (a row-major index over
+// the leading dims; prev(s) is the step before s in the forward scan order),
+// zero at the first step; optionally grad_b[s] = lam[s] rounded to bf16.
+struct GradAParams {
+  int64_t steps;         // product of the leading dims
+  int64_t T, inner;      // scan axis length; product of the leading dims after it
+  int n, m;
+  int reverse;           // of the forward scan
+  const float* lam;      // contiguous, leading dims + [n, m], f32
+  const void* h;         // the forward result, contiguous, leading dims + [n, m]
+  void* grad_a;          // contiguous, leading dims + [n, n]; bf16 when grad_a_bf16, else f32
+  void* grad_b;          // nullptr, or contiguous bf16, leading dims + [n, m]
+};
+hipError_t launch_grad_a(const GradAParams& g, bool h_bf16, bool grad_a_bf16, hipStream_t stream);
+
+// out[e] = sum of src over the dims a broadcast operand was stretched along:
+// target element e (row-major over the kept dims) starts at src offset
+// decode(e, keep), and the reduced index j adds decode(j, red).
+struct SumToParams {
+  const float* src;
+  float* partial;        // splits x targets floats of workspace
+  int64_t targets, reduced, splits, per;
+  int nd_keep, nd_red;
+  int64_t keep_dim[kMaxRank + 2], keep_st[kMaxRank + 2];
+  int64_t red_dim[kMaxRank + 2], red_st[kMaxRank + 2];
+};
+hipError_t launch_sum_to(const SumToParams& p, void* out, bool out_bf16, hipStream_t stream);
 
 // ---------------------------------------------------------------- streaming loads
 

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for required in ("sx_element_scan", "sx_matrix_scan", "sx_element_scan_workspace_bytes",
                      "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_linear_scan",
-                     "sx_linear_scan_out_shape", "sx_status_name", "sx_last_error", "sx_version"):
+                     "sx_linear_scan_out_shape", "sx_matrix_scan_backward", "sx_matrix_scan_backward_workspace_bytes",
+                     "sx_status_name", "sx_last_error", "sx_version"):
         assert required in names
 
 
@@ -154,6 +155,59 @@ def test_matrix_scan_workspace_query_is_host_only(lib):
     ws = lib.sx_matrix_scan_workspace_bytes(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1)
     assert ws >= 0
     assert lib.sx_matrix_scan_workspace_bytes(3, B.i64_array([2, 4, 4]), 3, B.i64_array([2, 5, 1]), 0) == 0
+
+
+def _msb(lib, a_shape=(2, 5, 4, 4), b_shape=(2, 5, 4, 3), dtype=B.SX_F32, grad=B.SX_F32, axis=1, a=FAKE,
+         h=FAKE + (1 << 20), g=FAKE + (2 << 20), ga=FAKE + (4 << 20), gb=FAKE + (5 << 20), ws=FAKE + (8 << 20),
+         ws_bytes=1 << 30, g_strides=None):
+    st = lib.sx_matrix_scan_backward(dtype, len(a_shape), B.i64_array(a_shape), None, a, len(b_shape),
+                                     B.i64_array(b_shape), h, B.i64_array(g_strides) if g_strides else None, g, axis,
+                                     0, grad, ga, gb, ws, ws_bytes, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=4), B.SX_E_DIM_002),
+    (dict(grad=9), B.SX_E_DIM_002),
+    (dict(b_shape=(2, 5, 5, 3)), B.SX_E_DIM_001),                # inner dims differ
+    (dict(b_shape=(3, 5, 4, 3)), B.SX_E_DIM_001),                # leading dims do not broadcast
+    (dict(axis=2), B.SX_E_DIM_001),
+    (dict(a=None), B.SX_E_DIM_003),
+    (dict(h=None), B.SX_E_DIM_003),
+    (dict(g=None), B.SX_E_DIM_003),
+    (dict(ga=None), B.SX_E_DIM_003),
+    (dict(gb=None), B.SX_E_DIM_003),
+    (dict(ga=FAKE + 64), B.SX_E_ALIAS),                           # grad_a over a
+    (dict(gb=FAKE + (2 << 20) + 8), B.SX_E_ALIAS),               # grad_b over g
+    (dict(gb=FAKE + (4 << 20) + 16), B.SX_E_ALIAS),              # grad_b over grad_a
+    (dict(ws=None), B.SX_E_WORKSPACE),
+    (dict(ws_bytes=64), B.SX_E_WORKSPACE),
+    (dict(ws=FAKE + (8 << 20) + 4), B.SX_E_WORKSPACE),           # not 256-byte aligned
+    (dict(g_strides=(60, 12, 1, 4)), B.SX_E_UNSUPPORTED),        # g's matrix dims transposed
+])
+def test_matrix_scan_backward_rejects_on_host(lib, kwargs, code):
+    st, msg = _msb(lib, **kwargs)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_matrix_scan_backward_empty_is_a_no_op(lib):
+    st, _ = _msb(lib, a_shape=(2, 0, 4, 4), b_shape=(2, 0, 4, 3), a=None, h=None, g=None, ga=None, gb=None, ws=None,
+                 ws_bytes=0)
+    assert st == B.SX_OK
+
+
+def test_matrix_scan_backward_workspace_query(lib):
+    q = lib.sx_matrix_scan_backward_workspace_bytes
+    full = q(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1, B.SX_F32)
+    assert full > 0 and full % 256 == 0
+    # a broadcast over the batch needs room for the full-shape grad_a before its sum
+    shared = q(3, B.i64_array([8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1, B.SX_F32)
+    assert shared >= full + 32 * 8192 * 256 * 4
+    # bf16 gradients keep the adjoint in f32 first
+    assert q(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1, B.SX_BF16) >= \
+        full + 32 * 8192 * 16 * 4
+    assert q(3, B.i64_array([2, 4, 4]), 3, B.i64_array([2, 5, 1]), 0, B.SX_F32) == 0
 
 
 def _ls(lib, a_shape=(3, 9, 5), b_shape=(3, 9, 5), dtype=B.SX_F32, out_dtype=B.SX_F32, axis=1, a=FAKE,

@@ -1,0 +1,218 @@
+"""Parity of the HIP matrix-scan gradient with the CPU oracle's.
+
+The GPU runs the forward scan, then ``matrix_scan_backward`` on its result
+and a seeded upstream gradient g; the oracle computes the same gradients in
+float64 from the same a, b and g (``oracle.matrix_scan_vjp``). The bar is
+the matrix-scan bar on blocks: for grad_b (n x m states) and grad_a (n x n
+blocks), ||gpu - ref||_F <= tol * max(||ref||_F, RMS of the block norms of
+the same tensor), tol = 1e-4 for f32 and 2e-2 for bf16 (whose forward result
+h, rounded to bf16, enters grad_a).
+
+Shapes cover the pipelined kernel (n = 16 with m = 1, and bf16 with m = 16)
+and the per-unit kernel (n < 16, m = 3, m = 17, f32 m = 16), several units
+with a ragged last one, both directions, broadcast operands (gradients
+summed over the broadcast dims), a strided g, autograd through
+``sx.matrix_scan``, and the two matrix workloads at full size on sampled
+batch rows (a row is an exact sub-problem) plus a per-step residual check of
+the adjoint recurrence over every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_primitives_amd as sx
+from scan_primitives_amd import workloads as W
+from tests.helpers import MS_TOL_BF16, MS_TOL_F32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _blocks_close(got, ref, tol, what):
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    num = np.sqrt(np.sum((g - ref) ** 2, axis=(-2, -1)))
+    den = np.sqrt(np.sum(ref ** 2, axis=(-2, -1)))
+    if den.size == 0:
+        return
+    floor = np.sqrt(np.mean(den ** 2))
+    scale = np.maximum(den, floor)
+    bad = num > tol * scale
+    if bad.any():
+        idx = np.unravel_index(np.argmax(num / np.maximum(scale, 1e-300)), num.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {num.size} blocks outside relative {tol}; worst at {idx}: "
+                             f"{num[idx] / max(scale[idx], 1e-300):.3e}")
+
+
+def _draw(a_shape, b_shape, dtype, seed, a_scale=0.9, noise=0.05):
+    g = torch.Generator().manual_seed(seed)
+    n = a_shape[-1]
+    a = (a_scale * torch.eye(n) + noise * torch.randn(a_shape, generator=g)).to(dtype)
+    b = torch.randn(b_shape, generator=g).to(dtype)
+    return a, b, g
+
+
+def _check(a, b, axis, reverse, seed, grad_dtype=None, g_view=None):
+    dt = a.dtype
+    tol = MS_TOL_F32 if dt == torch.float32 and grad_dtype in (None, torch.float32) else MS_TOL_BF16
+    print(f"\n[case] grad a {tuple(a.shape)} b {tuple(b.shape)} {dt} axis {axis} reverse {reverse}", flush=True)
+    ad, bd = a.to(DEV), b.to(DEV)
+    h = sx.matrix_scan(ad, bd, axis=axis, reverse=reverse)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    gh = torch.randn(tuple(h.shape), generator=gen).to(dt)
+    gd = gh.to(DEV) if g_view is None else g_view(gh.to(DEV))
+    ga, gb = sx.matrix_scan_backward(ad, tuple(b.shape), h, gd, axis=axis, reverse=reverse, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    want_dt = dt if grad_dtype is None else grad_dtype
+    assert ga.dtype == want_dt and gb.dtype == want_dt
+    ra, rb = oracle.matrix_scan_vjp(a.float().numpy(), b.float().numpy(), gd.float().cpu().numpy(), axis=axis,
+                                    reverse=reverse)
+    _blocks_close(gb, rb, tol, "grad_b")
+    _blocks_close(ga, ra, tol, "grad_a")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("B,T", [(3, 700), (2, 96), (1, 97), (2, 1), (2, 2), (4, 17)])
+def test_grad_pipelined_f32_m1(B, T, reverse):
+    a, b, _ = _draw((B, T, 16, 16), (B, T, 16, 1), torch.float32, seed=31 + T)
+    _check(a, b, 1, reverse, seed=31 + T)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("B,T,m", [(2, 400, 16), (1, 130, 32)])
+def test_grad_pipelined_bf16_tiles(B, T, m, reverse):
+    a, b, _ = _draw((B, T, 16, 16), (B, T, 16, m), torch.bfloat16, seed=41 + T)
+    _check(a, b, 1, reverse, seed=41 + T)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("n,m,T,dtype", [(5, 3, 150, torch.float32), (16, 17, 140, torch.float32),
+                                         (16, 16, 200, torch.float32), (3, 1, 300, torch.bfloat16),
+                                         (1, 1, 260, torch.float32), (16, 1, 129, torch.bfloat16)])
+def test_grad_unit_kernel_shapes(n, m, T, dtype, reverse):
+    a, b, _ = _draw((2, T, n, n), (2, T, n, m), dtype, seed=51 + n + m)
+    _check(a, b, 1, reverse, seed=51 + n + m)
+
+
+def test_grad_bf16_operands_f32_gradients():
+    a, b, _ = _draw((2, 300, 16, 16), (2, 300, 16, 1), torch.bfloat16, seed=61)
+    _check(a, b, 1, False, seed=61, grad_dtype=torch.float32)
+
+
+def test_grad_f32_operands_bf16_gradients():
+    a, b, _ = _draw((2, 300, 16, 16), (2, 300, 16, 1), torch.float32, seed=62)
+    _check(a, b, 1, True, seed=62, grad_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("a_shape,b_shape,axis", [
+    ((300, 16, 16), (3, 300, 16, 1), 1),      # a shared by the batch
+    ((3, 1, 16, 16), (3, 300, 16, 1), 1),     # a constant in time
+    ((16, 16), (2, 250, 16, 1), 1),           # a one matrix for everything
+    ((3, 200, 16, 16), (200, 16, 1), 1),      # b shared by the batch
+    ((2, 100, 5, 5), (1, 100, 5, 3), -1),     # b shared, axis from the end
+    ((2, 3, 70, 4, 4), (2, 3, 70, 4, 2), 2),  # two batch dims
+    ((70, 2, 4, 4), (70, 2, 4, 2), 0),        # scan over the first leading dim
+])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_grad_broadcast_and_axes(a_shape, b_shape, axis, reverse):
+    a, b, _ = _draw(a_shape, b_shape, torch.float32, seed=71 + len(a_shape))
+    _check(a, b, axis, reverse, seed=71 + len(a_shape))
+
+
+def test_grad_bf16_broadcast_a_bf16_gradients():
+    a, b, _ = _draw((300, 16, 16), (2, 300, 16, 16), torch.bfloat16, seed=81)
+    _check(a, b, 1, False, seed=81)
+
+
+def test_grad_strided_g():
+    a, b, _ = _draw((2, 200, 16, 16), (2, 200, 16, 1), torch.float32, seed=91)
+    # g as a view: every other step of a longer tensor (leading stride 2 steps)
+    _check(a, b, 1, False, seed=91,
+           g_view=lambda g: torch.stack([g, torch.zeros_like(g)], dim=2).reshape(2, 400, 16, 1)[:, ::2])
+
+
+def test_grad_expanded_g_from_sum():
+    # loss = h.sum(): g is an expanded tensor of ones (stride 0 everywhere); the binding copies its matrix dims
+    a, b, _ = _draw((2, 150, 16, 16), (2, 150, 16, 1), torch.float32, seed=92)
+    ad, bd = a.to(DEV).requires_grad_(), b.to(DEV).requires_grad_()
+    sx.matrix_scan(ad, bd, axis=1).sum().backward()
+    ra, rb = oracle.matrix_scan_vjp(a.numpy(), b.numpy(), np.ones((2, 150, 16, 1)), axis=1)
+    _blocks_close(bd.grad, rb, MS_TOL_F32, "grad_b")
+    _blocks_close(ad.grad, ra, MS_TOL_F32, "grad_a")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_autograd_through_matrix_scan(reverse):
+    a, b, _ = _draw((2, 130, 6, 6), (2, 130, 6, 2), torch.float32, seed=93)
+    w = torch.randn((2, 130, 6, 2), generator=torch.Generator().manual_seed(94))
+    ad, bd = a.to(DEV).requires_grad_(), b.to(DEV).requires_grad_()
+    h = sx.matrix_scan(ad, bd, axis=1, reverse=reverse)
+    (h * w.to(DEV)).sum().backward()
+    ra, rb = oracle.matrix_scan_vjp(a.numpy(), b.numpy(), w.numpy(), axis=1, reverse=reverse)
+    _blocks_close(bd.grad, rb, MS_TOL_F32, "grad_b")
+    _blocks_close(ad.grad, ra, MS_TOL_F32, "grad_a")
+
+
+def test_grad_empty_and_errors():
+    a = torch.zeros((2, 0, 4, 4), device=DEV)
+    b = torch.zeros((2, 0, 4, 3), device=DEV)
+    ga, gb = sx.matrix_scan_backward(a, b.shape, b, b)
+    assert ga.shape == a.shape and gb.shape == b.shape
+    # a constant in time over an empty axis: its gradient is zero
+    a1 = torch.ones((2, 1, 4, 4), device=DEV)
+    ga, gb = sx.matrix_scan_backward(a1, (2, 0, 4, 3), b, b)
+    assert ga.shape == a1.shape and torch.count_nonzero(ga) == 0
+    x = torch.zeros((2, 5, 4, 4), device=DEV)
+    h = torch.zeros((2, 5, 4, 1), device=DEV)
+    with pytest.raises(sx.SxError) as e:
+        sx.matrix_scan_backward(x, (2, 5, 4, 1), h, h.to(torch.bfloat16))
+    assert e.value.name == "E-DIM-002"
+    with pytest.raises(sx.SxError) as e:
+        sx.matrix_scan_backward(x, (2, 5, 4, 1), h, torch.zeros((2, 5, 4, 2), device=DEV))
+    assert e.value.name == "E-DIM-001"
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_grad_standard_workload_sampled_rows_and_adjoint_residual(idx):
+    """The matrix workloads at full size: the gradient on three sampled batch
+    rows against the oracle, and the adjoint recurrence lam[t] = g[t] +
+    a[s]^T lam[s] checked step by step over every row (this is what a wrong
+    entering state anywhere in the look-back would break)."""
+    w = W.standard_workloads([idx])[0]
+    print(f"\n[case] gradient of {w.name}", flush=True)
+    t = w.on(DEV)
+    a, b = t["a"], t["b"]
+    h = sx.matrix_scan(a, b, axis=w.axis, reverse=w.reverse)
+    gen = torch.Generator().manual_seed(95)
+    g = torch.randn(tuple(h.shape), generator=gen).to(h.dtype).to(DEV)
+    grad_dtype = torch.float32  # keep the adjoint itself for the residual check
+    ga, gb = sx.matrix_scan_backward(a, tuple(b.shape), h, g, axis=w.axis, reverse=w.reverse, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    rows = [0, 7, a.shape[0] - 1]
+    tol = MS_TOL_F32 if a.dtype == torch.float32 else MS_TOL_BF16
+    for r in rows:
+        ra, rb = oracle.matrix_scan_vjp(w.tensors["a"][r].float().numpy(), w.tensors["b"][r].float().numpy(),
+                                        g[r].float().cpu().numpy(), axis=0, reverse=w.reverse)
+        _blocks_close(gb[r], rb, tol, f"grad_b row {r}")
+        _blocks_close(ga[r], ra, tol, f"grad_a row {r}")
+    # residual of the adjoint over every row (float64 on the device)
+    lam = gb.double()
+    a64 = a.double()
+    g64 = g.double()
+    if not w.reverse:   # the step after t is t + 1
+        pred = g64[:, :-1] + torch.matmul(a64[:, 1:].transpose(-1, -2).contiguous(), lam[:, 1:])
+        res, ref = lam[:, :-1] - pred, lam[:, :-1]
+        last_ok = torch.equal(lam[:, -1], g64[:, -1])
+    else:               # the step after t is t - 1
+        pred = g64[:, 1:] + torch.matmul(a64[:, :-1].transpose(-1, -2).contiguous(), lam[:, :-1])
+        res, ref = lam[:, 1:] - pred, lam[:, 1:]
+        last_ok = torch.equal(lam[:, 0], g64[:, 0])
+    assert last_ok, "the adjoint at the last step is g there"
+    num = res.pow(2).sum(dim=(-2, -1)).sqrt()
+    den = ref.pow(2).sum(dim=(-2, -1)).sqrt()
+    floor = den.pow(2).mean(dim=1, keepdim=True).sqrt()
+    rel = (num / torch.maximum(den, floor)).max().item()
+    assert rel <= 1e-4, f"adjoint residual {rel:.3e}"
