@@ -20,9 +20,10 @@ single calls, each after a 512 MiB write that evicts the last-level cache
 (256 MB), timed between HIP events (it includes the launch). This gives each workload's elements/s, algorithmic GB/s and
 fraction of the 8 TB/s HBM peak.
 
-linear-scan and cumsum ([64,4096,256] f32 along axis 1) are timed the same
-two ways and reported in ``per_config`` with ``"in_step": false``; they are
-not part of the step or of ``value`` (``--no-extra`` skips them).
+linear-scan and cumsum ([64,4096,256] f32 along axis 1) and the gradients of
+the two matrix workloads are timed the same two ways and reported in
+``per_config`` with ``"in_step": false``; they are not part of the step or
+of ``value`` (``--no-extra`` skips them).
 
 Prints ONE JSON line on stdout. ``value`` is output elements per second over
 the timed steps; ``per_config`` has each workload's figures; ``roofline``
@@ -127,7 +128,7 @@ def main() -> int:
                     help="also run a plain 256 MiB device copy per step (reference kernel for PMC byte counts)")
     ap.add_argument("--eager", action="store_true", help="launch calls directly instead of replaying graphs")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the linear-scan and cumsum calls timed beside the step")
+                    help="skip the linear-scan, cumsum and gradient calls timed beside the step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -153,6 +154,9 @@ def main() -> int:
     log("generated inputs: " + "; ".join(w.name for w in workloads + extras))
     resident = [w.on(dev) for w in workloads]
     resident_extra = [w.on(dev) for w in extras]
+    for w, t in zip(extras, resident_extra):
+        if w.op == "matrix_scan_backward":  # the forward result the gradient reads, computed once here
+            t["h"] = sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse)
     torch.cuda.synchronize()
 
     def call(w, t):
@@ -162,6 +166,9 @@ def main() -> int:
         if w.op == "linear_scan":
             return sx.linear_scan(t["a"] if "a" in t else w.meta["a_number"], t["b"], axis=w.axis,
                                   reverse=w.reverse, out_dtype=w.out_dtype)
+        if w.op == "matrix_scan_backward":
+            return sx.matrix_scan_backward(t["a"], tuple(t["b"].shape), t["h"], t["g"], axis=w.axis,
+                                           reverse=w.reverse)
         return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
 
     copy_src = copy_dst = None

@@ -10,61 +10,102 @@
 // operand broadcast over some dims has its gradient summed over them.
 //
 // Kernels here:
-//   ms_grad_a_kernel  one wave per step: lane (i, jq) forms grad_a[t][i][4jq ..
-//                     4jq+3] from row i of lam[t] and rows 4jq .. 4jq+3 of
-//                     h[p]; it also stores grad_b[t] when that is lam rounded
-//                     to bf16. Bound by HBM (a 1 KiB grad_a block per
-//                     step for n = 16).
+//   ms_grad_a_kernel  one wave per step (the grid's waves stride over the
+//                     steps). n = 16 with m = 1: an outer product, each lane
+//                     storing four consecutive values of one row; n = 16 with
+//                     16 | m: lam h^T on MFMA; other shapes element by element.
+//                     It also stores grad_b[t] when that is lam rounded to
+//                     bf16. Bound by HBM (a 1 KiB grad_a block per step for
+//                     n = 16, f32).
 //   sum_to_partial_kernel / sum_to_final_kernel
 //                     the sum over broadcast dims, in two passes (partial sums
 //                     over slices of the summed index space, then their sum in
 //                     a fixed order), so results do not depend on scheduling.
+#include <algorithm>
+
+#include "ms_mfma.hpp"
 #include "sx_common.hpp"
 
 namespace sx {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float ld_f(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st_f(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 
-// TH: element type of h; TA: of grad_a (bf16 only when it is the final result).
+// Four consecutive elements as f32 (one 16- or 8-byte load), and back.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+               __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { st_stream(reinterpret_cast<f32x4*>(p), v); }
+__device__ __forceinline__ void st4(uint16_t* p, f32x4 v) {
+  st_stream(reinterpret_cast<u32x2*>(p), u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+}
+
+// The step before step s in the forward scan order (s itself at the first step).
+__device__ __forceinline__ int64_t prev_step(const GradAParams& g, int64_t s, bool& first) {
+  const int64_t t = (s / g.inner) % g.T;
+  first = g.reverse ? t == g.T - 1 : t == 0;
+  return first ? s : (g.reverse ? s + g.inner : s - g.inner);
+}
+
+// n = 16, m = 1: grad_a[i][j] = lam[i] h[j]. Lane (i, jq), i = lane / 4, forms
+// grad_a[i][4jq .. 4jq+3] and stores it as one piece, so the wave writes the
+// step's block contiguously.
 template <typename TH, typename TA>
-__global__ __launch_bounds__(256) void ms_grad_a_kernel(const GradAParams g) {
-  const int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // the step: a row-major lead index
-  if (s >= g.steps) return;
-  const int lane = int(threadIdx.x) & 63;
+__device__ __forceinline__ void grad_a_m1(const GradAParams& g, int64_t s, int lane) {
+  const int i = lane >> 2, jq = lane & 3;
+  bool first;
+  const int64_t p = prev_step(g, s, first);
+  const float l = g.lam[s * 16 + i];
+  const f32x4 hv = ld4(static_cast<const TH*>(g.h) + p * 16 + 4 * jq);
+  const f32x4 d = first ? zero4() : l * hv;
+  st4(static_cast<TA*>(g.grad_a) + s * 256 + i * 16 + 4 * jq, d);
+  if (g.grad_b != nullptr && jq == 0) st_f(static_cast<uint16_t*>(g.grad_b) + s * 16 + i, l);
+}
+
+// n = 16, m a multiple of 16: grad_a = lam h^T, K = m, by MFMA. Lane (r, c)
+// supplies row c of lam and row c of h (columns 4r .. 4r+3 of each 16-block),
+// which are the A and X operands of lam h^T; a quad transpose of the result
+// gives each lane four consecutive values of one row to store.
+template <typename TH, typename TA>
+__device__ __forceinline__ void grad_a_tiles(const GradAParams& g, int64_t s, int lane) {
+  const int r = lane >> 4, c = lane & 15, m = g.m;
+  bool first;
+  const int64_t p = prev_step(g, s, first);
+  const float* lr = g.lam + s * 16 * m + int64_t(c) * m + 4 * r;
+  const TH* hr = static_cast<const TH*>(g.h) + p * 16 * m + int64_t(c) * m + 4 * r;
+  uint16_t* br = g.grad_b ? static_cast<uint16_t*>(g.grad_b) + s * 16 * m + int64_t(c) * m + 4 * r : nullptr;
+  f32x4 acc = zero4();
+  for (int kb = 0; kb < m; kb += 16) {
+    const f32x4 la = ld4(lr + kb);
+    acc = mfma_16x16x16(la, ld4(hr + kb), acc);
+    if (br) st4(br + kb, la);
+  }
+  const int j = c & 3;
+  const f32x4 row = quad_transpose(first ? zero4() : acc, j);  // grad_a[4r + j][4 (c / 4) ..]
+  st4(static_cast<TA*>(g.grad_a) + s * 256 + (4 * r + j) * 16 + 4 * (c >> 2), row);
+}
+
+// Any n <= 16, m: lane (i, jq) forms grad_a[i][4jq .. 4jq+3] element by element.
+template <typename TH, typename TA>
+__device__ __forceinline__ void grad_a_any(const GradAParams& g, int64_t s, int lane) {
   const int i = lane >> 2, jq = lane & 3;
   const int n = g.n, m = g.m;
-  const int64_t t = (s / g.inner) % g.T;
-  const bool first = g.reverse ? t == g.T - 1 : t == 0;
-  const int64_t prev = first ? s : (g.reverse ? s + g.inner : s - g.inner);  // always a valid step
+  bool first;
+  const int64_t p = prev_step(g, s, first);
   const float* lam = g.lam + s * int64_t(n) * m;
-  const TH* hp = static_cast<const TH*>(g.h) + prev * int64_t(n) * m;
+  const TH* hp = static_cast<const TH*>(g.h) + p * int64_t(n) * m;
   const int ic = i < n ? i : n - 1;  // clamped rows: every load is in bounds
   int jc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) jc[q] = 4 * jq + q < n ? 4 * jq + q : n - 1;
-
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  int k = 0;
-  if (m % 4 == 0 && (reinterpret_cast<uintptr_t>(g.lam) & 15) == 0) {  // rows of lam (f32) and of h in fours
-    for (; k < m; k += 4) {
-      const f32x4 l = *reinterpret_cast<const f32x4*>(lam + int64_t(ic) * m + k);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const TH* hr = hp + int64_t(jc[q]) * m + k;
-        acc[q] = fmaf(l[0], ld_f(hr), acc[q]);
-        acc[q] = fmaf(l[1], ld_f(hr + 1), acc[q]);
-        acc[q] = fmaf(l[2], ld_f(hr + 2), acc[q]);
-        acc[q] = fmaf(l[3], ld_f(hr + 3), acc[q]);
-      }
-    }
-  }
-  for (; k < m; ++k) {
+  for (int k = 0; k < m; ++k) {
     const float l = lam[int64_t(ic) * m + k];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(l, ld_f(hp + int64_t(jc[q]) * m + k), acc[q]);
@@ -78,6 +119,19 @@ __global__ __launch_bounds__(256) void ms_grad_a_kernel(const GradAParams g) {
   if (g.grad_b != nullptr && i < n) {  // grad_b = lam rounded to bf16; the row's four lanes split it
     uint16_t* gb = static_cast<uint16_t*>(g.grad_b) + s * int64_t(n) * m + int64_t(i) * m;
     for (int kk = jq; kk < m; kk += 4) st_f(gb + kk, lam[int64_t(i) * m + kk]);
+  }
+}
+
+// One wave per step, the waves of the grid striding over the steps.
+// TH: element type of h; TA: of grad_a (bf16 only when it is the final result).
+template <int PATH, typename TH, typename TA>
+__global__ __launch_bounds__(256) void ms_grad_a_kernel(const GradAParams g) {
+  const int lane = int(threadIdx.x) & 63;
+  const int64_t nw = int64_t(gridDim.x) * 4;
+  for (int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); s < g.steps; s += nw) {
+    if constexpr (PATH == 1) grad_a_m1<TH, TA>(g, s, lane);
+    else if constexpr (PATH == 2) grad_a_tiles<TH, TA>(g, s, lane);
+    else grad_a_any<TH, TA>(g, s, lane);
   }
 }
 
@@ -116,18 +170,32 @@ __global__ __launch_bounds__(256) void sum_to_final_kernel(const SumToParams p, 
 
 }  // namespace
 
+namespace {
+template <int PATH>
+void launch_grad_a_path(const GradAParams& g, bool h_bf16, bool grad_a_bf16, dim3 grid, hipStream_t stream) {
+  const dim3 block{256};
+  if (h_bf16) {
+    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, uint16_t, uint16_t>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, uint16_t, float>), grid, block, 0, stream, g);
+  } else {
+    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, float, uint16_t>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, float, float>), grid, block, 0, stream, g);
+  }
+}
+}  // namespace
+
 hipError_t launch_grad_a(const GradAParams& g, bool h_bf16, bool grad_a_bf16, hipStream_t stream) {
   if (g.steps <= 0 || g.n <= 0) return hipSuccess;
-  const int64_t blocks = (g.steps + 3) / 4;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid{unsigned(blocks)}, block{256};
-  if (h_bf16) {
-    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<uint16_t, uint16_t>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((ms_grad_a_kernel<uint16_t, float>), grid, block, 0, stream, g);
-  } else {
-    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<float, uint16_t>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((ms_grad_a_kernel<float, float>), grid, block, 0, stream, g);
-  }
+  // enough waves to fill the GPU several times over; each strides over the steps
+  const int64_t blocks = std::min<int64_t>((g.steps + 3) / 4, int64_t(device_cu_count()) * 16);
+  const dim3 grid{unsigned(blocks)};
+  // the fast paths read and write whole 16-byte (f32) or 8-byte (bf16) pieces
+  auto aligned = [](const void* q, uintptr_t a) { return q == nullptr || reinterpret_cast<uintptr_t>(q) % a == 0; };
+  const bool al = aligned(g.lam, 16) && aligned(g.h, h_bf16 ? 8 : 16) && aligned(g.grad_a, grad_a_bf16 ? 8 : 16) &&
+                  aligned(g.grad_b, 8);
+  if (g.n == 16 && g.m == 1 && al) launch_grad_a_path<1>(g, h_bf16, grad_a_bf16, grid, stream);
+  else if (g.n == 16 && g.m % 16 == 0 && al) launch_grad_a_path<2>(g, h_bf16, grad_a_bf16, grid, stream);
+  else launch_grad_a_path<0>(g, h_bf16, grad_a_bf16, grid, stream);
   return hipGetLastError();
 }
 

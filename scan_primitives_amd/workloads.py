@@ -33,7 +33,7 @@ import torch
 @dataclass
 class Workload:
     name: str
-    op: str                      # "element_scan", "matrix_scan" or "linear_scan"
+    op: str                      # "element_scan", "matrix_scan", "matrix_scan_backward" or "linear_scan"
     tensors: dict                # host tensors, in the order the op takes them
     axis: int = 1
     reverse: bool = False
@@ -55,6 +55,8 @@ class Workload:
             return tuple(x.shape[:-1]) + (t["initial"].shape[-1],)
         if self.op == "linear_scan":
             return tuple(torch.broadcast_shapes(t["b"].shape, t["a"].shape if "a" in t else ()))
+        if self.op == "matrix_scan_backward":  # the outputs are grad_a and grad_b
+            return tuple(t["a"].shape)
         lead = torch.broadcast_shapes(t["a"].shape[:-2], t["b"].shape[:-2])
         return tuple(lead) + tuple(t["b"].shape[-2:])
 
@@ -74,8 +76,16 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Bytes the method must move: every input read once, the output written once."""
-        ins = sum(v.numel() * v.element_size() for v in self.tensors.values())
+        """Bytes the method must move: every input read once, the output written once.
+
+        For the matrix-scan gradient the inputs are a, the forward result h and
+        its gradient g (g's shape and dtype are h's), and the outputs grad_a and
+        grad_b (b's values are not read)."""
+        t = self.tensors
+        if self.op == "matrix_scan_backward":
+            e = t["a"].element_size()
+            return (2 * t["a"].numel() + 2 * t["g"].numel() + t["b"].numel()) * e
+        ins = sum(v.numel() * v.element_size() for v in t.values())
         return ins + self.out_numel * self.out_elem_bytes
 
 
@@ -170,7 +180,21 @@ def standard_workloads(which=None) -> list[Workload]:
     return [makers[i]() for i in idx]
 
 
+def make_matrix_grad(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, reverse=False, seed=4) -> Workload:
+    """The gradient of a matrix workload: a and b as ``make_matrix`` draws them
+    (same seed, so the same tensors), and g ~ N(0,1) of the result's shape,
+    drawn after them in f32 and rounded to ``dtype``."""
+    w = make_matrix(B, T, n, m, dtype, axis=axis, reverse=reverse, seed=seed)
+    g = torch.randn(tuple(w.out_shape), generator=_gen(seed + 100)).to(dtype)
+    name = "gradient of " + w.name
+    return Workload(name, "matrix_scan_backward", {"a": w.tensors["a"], "b": w.tensors["b"], "g": g}, axis=axis,
+                    reverse=reverse)
+
+
 def extra_workloads() -> list[Workload]:
-    """linear-scan and cumsum on the max-plus shape, [64,4096,256] along axis 1,
-    f32: timed beside the step, not part of it."""
-    return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7)]
+    """Timed beside the step, not part of it: linear-scan and cumsum on the
+    max-plus shape, [64,4096,256] along axis 1, f32; the gradients of the two
+    matrix workloads."""
+    return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7),
+            make_matrix_grad(32, 8192, 16, 1, torch.float32, reverse=False, seed=4),
+            make_matrix_grad(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5)]
