@@ -63,7 +63,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["element_scan", "matrix_scan", "matrix_scan_vjp", "linear_scan", "cumsum", "BODIES"]
+__all__ = ["element_scan", "element_scan_vjp", "matrix_scan", "matrix_scan_vjp", "linear_scan", "cumsum",
+           "BODIES"]
 
 
 # --- element-scan bodies ----------------------------------------------------
@@ -161,6 +162,116 @@ def element_scan(body, initial, sequences, axis=0, state_axis=None,
         h = step(h, *(s[t] for s in seq_t))
         out[t] = h  # each position holds the state after its own trip
     return np.moveaxis(out, 0, ax)
+
+
+# --- element-scan gradients ------------------------------------------------
+# Each body's vector-Jacobian product at one trip: given the state it started
+# from, its sequence values, the state it produced and the adjoint lam of that
+# state, the adjoints of (incoming state, x, second sequence). Written from the
+# chain rule on the body as the page writes it.
+
+
+def _tanh_affine_vjp(h_prev, x, a, h, lam, branch):
+    # h = tanh(z), z = x + a h_prev; dtanh/dz = 1 - h^2
+    dz = lam * (1.0 - h * h)
+    return a * dz, dz, dz * h_prev
+
+
+def _norm_cap_vjp(h_prev, x, a, h, lam, capped):
+    # y = a h_prev + x; h = y when |y| <= 1, else y / |y|, whose Jacobian is
+    # (I - h h^T) / |y| (symmetric)
+    y = a * h_prev + x
+    r = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
+    dy_capped = (lam - h * np.sum(h * lam, axis=-1, keepdims=True)) / np.where(capped, r, 1.0)
+    dy = np.where(capped, dy_capped, lam)
+    return a * dy, dy, dy * h_prev
+
+
+def _max_plus_vjp(h_prev, x, c, h, lam, x_won):
+    # h = max(h_prev - c, x): the adjoint goes to the branch that gave h
+    zero = np.zeros_like(lam)
+    return np.where(x_won, zero, lam), np.where(x_won, lam, zero), np.where(x_won, zero, -lam)
+
+
+_VJP = {"tanh_affine": _tanh_affine_vjp, "norm_cap": _norm_cap_vjp, "max_plus": _max_plus_vjp}
+
+
+def _branches(body, h_prev32, x32, s32):
+    """Which branch each lane's trip took, decided in float32 from the float32
+    forward pass (the precision the scan computes in): for max-plus, x wins
+    when x >= h_prev - c (ties go to x); for norm-cap, the cap acts when
+    |y|^2 > 1 with y = a h_prev + x. None for tanh-affine, which has none."""
+    if body == "max_plus":
+        return x32 >= (h_prev32 - s32)
+    if body == "norm_cap":
+        y = s32 * h_prev32 + x32
+        return np.sum(y * y, axis=-1, keepdims=True, dtype=np.float32) > np.float32(1.0)
+    return None
+
+
+def element_scan_vjp(body, initial, sequences, g, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    """Gradient of ``sum(g * element_scan(body, initial, sequences, ...))``.
+
+    Returns ``(grad_initial, [grad_x, grad_s])`` in the shapes of ``initial``
+    and of each sequence (a width-one sequence under a vector state gets the
+    sum over the state of its broadcast gradient). With lam[t] the adjoint of
+    the state after trip t and s / p the trips after / before t in scan order,
+
+      lam[t] = g[t] + (adjoint of the incoming state from trip s's VJP)
+
+    and each trip's VJP gives its sequences' gradients; trip 0's incoming
+    adjoint is grad_initial. Values are computed in ``dtype`` (float64 by
+    default); branch decisions (max-plus's winner, norm-cap's cap) are taken
+    in float32 from a float32 forward pass, as the scan computes them.
+
+    Follows "Nonlinear element scans", introduction (the bodies) and the
+    chain rule; the pages' gradient section gives each gradient its tensor's
+    shape.
+    """
+    seqs_in = [np.asarray(s_, dtype=dtype) for s_ in sequences]
+    init = np.asarray(initial, dtype=dtype)
+    h = element_scan(body, init, seqs_in, axis=axis, state_axis=state_axis, reverse=reverse, dtype=dtype)
+    h32 = element_scan(body, np.asarray(initial, dtype=np.float32), [np.asarray(s_, dtype=np.float32) for s_ in sequences],
+                       axis=axis, state_axis=state_axis, reverse=reverse, dtype=np.float32)
+    g = np.asarray(g, dtype=dtype)
+    if g.shape != h.shape:
+        raise ValueError(f"element_scan_vjp: g has shape {g.shape}, the result has {h.shape}")
+    rank = h.ndim
+    ax = axis + rank if axis < 0 else axis
+    n = h.shape[-1]
+    wide = [np.broadcast_to(s_, s_.shape[:-1] + (n,)) if state_axis is not None else s_ for s_ in seqs_in]
+    wide32 = [w.astype(np.float32) for w in wide]
+    x_t, s_t = (np.moveaxis(w, ax, 0) for w in wide)
+    x32_t, s32_t = (np.moveaxis(w, ax, 0) for w in wide32)
+    h_t, h32_t, g_t = np.moveaxis(h, ax, 0), np.moveaxis(h32, ax, 0), np.moveaxis(g, ax, 0)
+    T = h_t.shape[0]
+    order = list(range(T - 1, -1, -1)) if reverse else list(range(T))  # scan order
+    vjp = _VJP[body]
+    gx = np.zeros(x_t.shape, dtype=dtype)
+    gs = np.zeros(s_t.shape, dtype=dtype)
+    from_later = np.zeros(h_t.shape[1:], dtype=dtype)  # adjoint reaching the state from the trip after
+    g_init = None
+    for i in range(T - 1, -1, -1):
+        t = order[i]
+        lam = g_t[t] + from_later
+        if i > 0:
+            p = order[i - 1]
+            h_prev, h_prev32 = h_t[p], h32_t[p]
+        else:
+            h_prev, h_prev32 = init, np.asarray(initial, dtype=np.float32)
+        branch = _branches(body, h_prev32, x32_t[t], s32_t[t])
+        d_prev, gx[t], gs[t] = vjp(h_prev, x_t[t], s_t[t], h_t[t], lam, branch)
+        if i > 0:
+            from_later = d_prev
+        else:
+            g_init = d_prev
+    grads = []
+    for gt, s_ in zip((gx, gs), seqs_in):
+        full = np.moveaxis(gt, 0, ax)
+        if state_axis is not None and s_.shape[-1] == 1 and n != 1:
+            full = np.sum(full, axis=-1, keepdims=True)
+        grads.append(full.reshape(s_.shape))
+    return g_init.reshape(init.shape), grads
 
 
 def matrix_scan(a, b, axis=0, reverse=False, dtype=np.float64):

@@ -257,3 +257,105 @@ def test_unmutated_vjp_passes_its_pins():
     a, b, g = rng.normal(size=(2, 5, 3, 3)), rng.normal(size=(2, 5, 3, 2)), rng.normal(size=(2, 5, 3, 2))
     for x, y in zip(_vjp_mutant("none")(a, b, g, axis=1), _real_vjp(a, b, g, axis=1)):
         np.testing.assert_array_equal(x, y)
+
+
+def _tanh_no_slope(h_prev, x, a, h, lam, branch):
+    return a * lam, lam, lam * h_prev
+
+
+def _tanh_slope_of_input(h_prev, x, a, h, lam, branch):
+    dz = lam * (1.0 - h_prev * h_prev)
+    return a * dz, dz, dz * h_prev
+
+
+def _tanh_swapped(h_prev, x, a, h, lam, branch):
+    dz = lam * (1.0 - h * h)
+    return a * dz, dz * h_prev, dz
+
+
+def _norm_cap_no_projection(h_prev, x, a, h, lam, capped):
+    y = a * h_prev + x
+    r = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
+    dy = np.where(capped, lam / r, lam)
+    return a * dy, dy, dy * h_prev
+
+
+def _norm_cap_ignores_cap(h_prev, x, a, h, lam, capped):
+    return a * lam, lam, lam * h_prev
+
+
+def _max_plus_swapped_branches(h_prev, x, c, h, lam, x_won):
+    zero = np.zeros_like(lam)
+    return np.where(x_won, lam, zero), np.where(x_won, zero, lam), np.where(x_won, -lam, zero)
+
+
+def _max_plus_cost_sign(h_prev, x, c, h, lam, x_won):
+    zero = np.zeros_like(lam)
+    return np.where(x_won, zero, lam), np.where(x_won, lam, zero), np.where(x_won, zero, lam)
+
+
+ES_VJP_MUTANTS = {
+    "tanh_no_slope": ("tanh_affine", _tanh_no_slope),
+    "tanh_slope_of_input": ("tanh_affine", _tanh_slope_of_input),
+    "tanh_swapped": ("tanh_affine", _tanh_swapped),
+    "norm_cap_no_projection": ("norm_cap", _norm_cap_no_projection),
+    "norm_cap_ignores_cap": ("norm_cap", _norm_cap_ignores_cap),
+    "max_plus_swapped_branches": ("max_plus", _max_plus_swapped_branches),
+    "max_plus_cost_sign": ("max_plus", _max_plus_cost_sign),
+}
+
+ES_VJP_PINS = {
+    "tanh_affine": [(pins.test_element_scan_vjp_central_differences, {"body": "tanh_affine", "state": None, "reverse": False}),
+                    (pins.test_tanh_affine_vjp_single_trip_and_zero_decay, {})],
+    "norm_cap": [(pins.test_element_scan_vjp_central_differences, {"body": "norm_cap", "state": 4, "reverse": True})],
+    "max_plus": [(pins.test_max_plus_vjp_exact_by_unit_perturbations, {"reverse": True})],
+}
+
+
+@pytest.mark.parametrize("name", sorted(ES_VJP_MUTANTS))
+def test_element_scan_vjp_mutants_are_caught(name, monkeypatch):
+    body, fn = ES_VJP_MUTANTS[name]
+    monkeypatch.setitem(oracle._VJP, body, fn)
+    assert _some_pin_fails(ES_VJP_PINS[body]), f"no gradient pin caught {name}"
+
+
+def _es_vjp_wrong_prev(body, initial, sequences, g, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    # every trip's incoming state taken as its own result (h[t] for h[t-1])
+    real_vjp = oracle._VJP[body]
+    def vjp(h_prev, x, a, h, lam, branch):
+        return real_vjp(h, x, a, h, lam, branch)
+    saved = oracle._VJP[body]
+    oracle._VJP[body] = vjp
+    try:
+        return _real_es_vjp(body, initial, sequences, g, axis, state_axis, reverse, dtype)
+    finally:
+        oracle._VJP[body] = saved
+
+
+def _es_vjp_wrong_direction(body, initial, sequences, g, axis=0, state_axis=None, reverse=False, dtype=np.float64):
+    return _real_es_vjp(body, initial, sequences, g, axis, state_axis, not reverse, dtype)
+
+
+_real_es_vjp = oracle.element_scan_vjp
+
+
+@pytest.mark.parametrize("mutant,body", [(_es_vjp_wrong_prev, "tanh_affine"), (_es_vjp_wrong_prev, "norm_cap"),
+                                          (_es_vjp_wrong_direction, "tanh_affine"), (_es_vjp_wrong_direction, "norm_cap"),
+                                          (_es_vjp_wrong_direction, "max_plus")])
+def test_element_scan_vjp_loop_mutants_are_caught(mutant, body, monkeypatch):
+    # (max-plus's VJP reads the incoming state only through its branch decision: see the next test)
+    monkeypatch.setattr(oracle, "element_scan_vjp", mutant)
+    assert _some_pin_fails(ES_VJP_PINS[body]), f"no {body} gradient pin caught {mutant.__name__}"
+
+
+def test_max_plus_branch_mutant_is_caught(monkeypatch):
+    real = oracle._branches
+    def wrong_sign(body, h_prev32, x32, s32):
+        return x32 >= (h_prev32 + s32) if body == "max_plus" else real(body, h_prev32, x32, s32)
+    monkeypatch.setattr(oracle, "_branches", wrong_sign)
+    assert _some_pin_fails(ES_VJP_PINS["max_plus"])
+
+
+def test_unmutated_element_scan_vjp_passes_its_pins():
+    for body in ES_VJP_PINS:
+        assert not _some_pin_fails(ES_VJP_PINS[body])

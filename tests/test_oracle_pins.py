@@ -626,3 +626,100 @@ def test_matrix_scan_vjp_scalar_closed_form():
     assert gb[:, 0, 0].tolist() == [621.0, 310.0, 100.0]
     # dL/da1 = (g1 + a2 g2) h0 = 310; dL/da2 = g2 h1 = 100 * 7
     assert ga[:, 0, 0].tolist() == [0.0, 310.0, 700.0]
+
+
+# ---------------------------------------------------------------- element-scan gradients
+#
+# The vector-Jacobian product of sum(g * element_scan(...)) fixed by what it is,
+# the derivative, without reusing the gradient loop: central differences of
+# the pinned forward oracle, exact one-sided differences where the scan is
+# piecewise linear (max-plus), and closed forms of special cases.
+
+def _es_case(body, state, rng, shape=(3, 7, 4)):
+    B, T, n = shape
+    if state is None:
+        x = rng.normal(size=shape)
+        s = rng.uniform(0.0, 0.5, size=shape) if body == "max_plus" else rng.uniform(0.2, 1.0, size=shape)
+        init = rng.normal(size=(B, n))
+    else:
+        x = 2.0 * rng.normal(size=(B, T, n))
+        s = rng.uniform(0.5, 1.0, size=(B, T, state))
+        init = 0.3 * rng.normal(size=(B, n))
+    g = rng.normal(size=(B, T, n))
+    return init, x, s, g
+
+
+def _es_loss(body, init, x, s, g, state, reverse):
+    st = None if state is None else -1
+    return float(np.sum(g * oracle.element_scan(body, init, [x, s], axis=1, state_axis=st, reverse=reverse)))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("body,state", [("tanh_affine", None), ("tanh_affine", 1), ("tanh_affine", 4),
+                                        ("norm_cap", 1), ("norm_cap", 4), ("max_plus", None), ("max_plus", 1)])
+def test_element_scan_vjp_central_differences(body, state, reverse):
+    rng = _rng(81)
+    init, x, s, g = _es_case(body, state, rng)
+    st = None if state is None else -1
+    gi, (gx, gs) = oracle.element_scan_vjp(body, init, [x, s], g, axis=1, state_axis=st, reverse=reverse)
+    assert gi.shape == init.shape and gx.shape == x.shape and gs.shape == s.shape
+    for _ in range(3):
+        di, dx, ds = rng.normal(size=init.shape), rng.normal(size=x.shape), rng.normal(size=s.shape)
+        eps = 1e-6
+        fd = (_es_loss(body, init + eps * di, x + eps * dx, s + eps * ds, g, state, reverse)
+              - _es_loss(body, init - eps * di, x - eps * dx, s - eps * ds, g, state, reverse)) / (2 * eps)
+        an = float(np.sum(gi * di) + np.sum(gx * dx) + np.sum(gs * ds))
+        assert abs(fd - an) <= 1e-6 * (1 + abs(an)), (fd, an)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_max_plus_vjp_exact_by_unit_perturbations(reverse):
+    # max-plus is piecewise linear: a perturbation small enough to change no
+    # branch moves the loss by exactly the derivative times its size
+    rng = _rng(82)
+    init, x, c, g = _es_case("max_plus", None, rng, shape=(2, 6, 3))
+    gi, (gx, gc) = oracle.element_scan_vjp("max_plus", init, [x, c], g, axis=1, reverse=reverse)
+    base = _es_loss("max_plus", init, x, c, g, None, reverse)
+    d = 2.0 ** -20
+    for arr, grad, which in ((init, gi, 0), (x, gx, 1), (c, gc, 2)):
+        for idx in np.ndindex(*arr.shape):
+            pert = [init, x, c]
+            moved = arr.copy()
+            moved[idx] += d
+            pert[which] = moved
+            got = (_es_loss("max_plus", pert[0], pert[1], pert[2], g, None, reverse) - base) / d
+            assert abs(got - grad[idx]) < 1e-6 * (1 + abs(grad[idx])), (which, idx, got, grad[idx])
+
+
+def test_tanh_affine_vjp_single_trip_and_zero_decay():
+    # one trip: h = tanh(x + a h0), so dL/dx = g (1 - h^2), dL/da = g (1 - h^2) h0, dL/dh0 = g (1 - h^2) a
+    x, a, h0, g = np.array([[0.3]]), np.array([[0.7]]), np.array([-0.4]), np.array([[2.0]])
+    gi, (gx, ga) = oracle.element_scan_vjp("tanh_affine", h0, [x, a], g, axis=0)
+    d = 2.0 * (1 - np.tanh(0.3 + 0.7 * -0.4) ** 2)
+    assert np.isclose(gx[0, 0], d) and np.isclose(ga[0, 0], d * -0.4) and np.isclose(gi[0], d * 0.7)
+    # decay 0: each trip is tanh(x) alone, so grad_x = g (1 - tanh(x)^2) and nothing reaches initial
+    rng = _rng(83)
+    x = rng.normal(size=(4, 9))
+    g = rng.normal(size=(4, 9))
+    gi, (gx, ga) = oracle.element_scan_vjp("tanh_affine", rng.normal(size=4), [x, np.zeros_like(x)], g, axis=1)
+    np.testing.assert_allclose(gx, g * (1 - np.tanh(x) ** 2), rtol=1e-14)
+    assert np.all(gi == 0)
+
+
+def test_norm_cap_vjp_uncapped_is_the_linear_scan_gradient():
+    # when the cap never acts the body is y = a h + x, a gated linear scan: its
+    # adjoint is the reverse linear scan of g with the next trip's gate
+    rng = _rng(84)
+    B, T, n = 2, 8, 5
+    x = 0.01 * rng.normal(size=(B, T, n))
+    a = rng.uniform(0.2, 0.6, size=(B, T, 1))
+    init = 0.01 * rng.normal(size=(B, n))
+    g = rng.normal(size=(B, T, n))
+    h = oracle.element_scan("norm_cap", init, [x, a], axis=1, state_axis=-1)
+    assert np.max(np.linalg.norm(h, axis=-1)) < 0.5
+    gi, (gx, ga) = oracle.element_scan_vjp("norm_cap", init, [x, a], g, axis=1, state_axis=-1)
+    shifted = np.ones((B, T, 1))
+    shifted[:, :-1] = a[:, 1:]
+    lam = oracle.linear_scan(np.broadcast_to(shifted, (B, T, n)), g, axis=1, reverse=True)
+    np.testing.assert_allclose(gx, lam, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gi, a[:, 0] * lam[:, 0], rtol=1e-12, atol=1e-12)
