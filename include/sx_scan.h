@@ -7,6 +7,8 @@
  *                 independently at every position outside one sequence axis,
  *                 with one of three fixed bodies (tanh-affine, norm-capped
  *                 vector state, max-plus), forward or reverse.
+ *   element-scan gradient  the chain rule through those bodies, trips last
+ *                 to first.
  *   matrix-scan   "Tensor operations", Operations table (matrix-scan row) and
  *                 the "matrix-scan" section: h[t] = a[t] @ h[t-1] + b[t] from
  *                 h = 0, n <= 16, computed in f32, with :axis, :reverse and
@@ -125,6 +127,49 @@ sx_status sx_element_scan(sx_body body, int rank, const int64_t* shape, int axis
  * returns 0 as well for arguments sx_element_scan would reject. */
 size_t sx_element_scan_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis,
                                        int state_axis);
+
+/*
+ * sx_element_scan_backward: gradients of an element scan. The chain rule
+ * through the bodies of "Nonlinear element scans" (introduction), with each
+ * gradient in its tensor's shape ("Tensor operations", "gradient" section).
+ *
+ * Given the forward call's arguments, its result h and the gradient g of a
+ * loss with respect to h, writes the loss's gradients with respect to
+ * initial, x and the second sequence s. The trips are taken last to first in
+ * scan order; with lam the adjoint of the state a trip produced (g there plus
+ * what the trip after passed back) and hp the state it started from:
+ *   tanh-affine  dz = lam (1 - h^2); grad_x = dz; grad_s = dz hp; to hp: s dz
+ *   norm-cap     y = s hp + x; when |y| > 1, u = y / |y| and
+ *                dy = (lam - u (u . lam)) / |y|, else dy = lam;
+ *                grad_x = dy; grad_s = dy hp; to hp: s dy
+ *   max-plus     x won (x >= hp - c; ties to x): grad_x = lam, grad_c = 0,
+ *                to hp 0; else grad_x = 0, grad_c = -lam, to hp lam
+ * grad_initial is what the first trip passes back. A width-one sequence under
+ * a vector state gets the sum over the state of its broadcast gradient. The
+ * branch decisions use f32 values computed as the forward pass does.
+ *
+ *  body .. s_strides  as for sx_element_scan, except that initial must be
+ *                contiguous (no strides argument).
+ *  h, g          the forward result and its gradient: contiguous, `shape`.
+ *  grad_initial, grad_x, grad_s
+ *                contiguous, the shapes of initial, x and s. Must not overlap
+ *                any input or each other (SX_E_ALIAS).
+ *  workspace     at least sx_element_scan_backward_workspace_bytes() bytes
+ *                (nonzero only for width-one sequences under a vector
+ *                state), 256-byte aligned; may be NULL when that is 0.
+ *
+ * Errors as sx_element_scan; E-DIM-003 for any NULL tensor.
+ */
+sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape, int axis, int state_axis,
+                                   int reverse, const float* initial, const float* x, int64_t x_width,
+                                   const int64_t* x_strides, const float* s, int64_t s_width,
+                                   const int64_t* s_strides, const float* h, const float* g, float* grad_initial,
+                                   float* grad_x, float* grad_s, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Workspace bytes sx_element_scan_backward needs (0 when none or for invalid arguments). */
+size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis,
+                                                int state_axis, int64_t x_width, int64_t s_width);
 
 /*
  * sx_matrix_scan: "Tensor operations", Operations table (matrix-scan row)

@@ -5,9 +5,9 @@ the C ABI in ``include/sx_scan.h``); this package is its Python binding.
 PyTorch provides device memory and streams.
 """
 
-from ._binding import (BODIES, SxError, cumsum, element_scan, linear_scan, load_library, matrix_scan,
-                       matrix_scan_backward)
+from ._binding import (BODIES, SxError, cumsum, element_scan, element_scan_backward, linear_scan, load_library,
+                       matrix_scan, matrix_scan_backward)
 
-__all__ = ["BODIES", "SxError", "element_scan", "matrix_scan", "matrix_scan_backward", "linear_scan", "cumsum",
-           "load_library"]
+__all__ = ["BODIES", "SxError", "element_scan", "element_scan_backward", "matrix_scan", "matrix_scan_backward",
+           "linear_scan", "cumsum", "load_library"]
 __version__ = "0.1.0"

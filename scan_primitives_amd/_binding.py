@@ -71,6 +71,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sx_matrix_scan_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int]
     lib.sx_matrix_scan_out_shape.restype = c_int
     lib.sx_matrix_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
+    lib.sx_element_scan_backward.restype = c_int
+    lib.sx_element_scan_backward.argtypes = [c_int, c_int, _i64p, c_int, c_int, c_int, vp, vp, ctypes.c_int64, _i64p,
+                                             vp, ctypes.c_int64, _i64p, vp, vp, vp, vp, vp, vp, c_size, vp]
+    lib.sx_element_scan_backward_workspace_bytes.restype = c_size
+    lib.sx_element_scan_backward_workspace_bytes.argtypes = [c_int, c_int, _i64p, c_int, c_int, ctypes.c_int64,
+                                                             ctypes.c_int64]
     lib.sx_matrix_scan_backward.restype = c_int
     lib.sx_matrix_scan_backward.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, vp, _i64p, vp,
                                             c_int, c_int, c_int, vp, vp, vp, c_size, vp]
@@ -119,8 +125,19 @@ def element_scan(body: str, initial: torch.Tensor, sequences, axis: int = 0, sta
 
     ``sequences`` is ``[x, decay]`` or ``[x, cost]`` (page order). ``state_axis``
     is ``None`` for a scalar state or ``-1`` for a vector state along the last
-    axis. Returns a new f32 tensor of the sequences' shape.
+    axis. Returns a new f32 tensor of the sequences' shape. When autograd
+    records (an input requires grad), the gradient runs through
+    ``element_scan_backward``.
     """
+    seqs = list(sequences)
+    if torch.is_grad_enabled() and any(isinstance(t, torch.Tensor) and t.requires_grad for t in [initial] + seqs):
+        if len(seqs) != 2:
+            raise SxError(SX_E_DIM_001, f"element-scan: the {body} body takes two sequences, got {len(seqs)}")
+        return _ElementScanFunction.apply(body, axis, state_axis, reverse, initial, seqs[0], seqs[1])
+    return _element_scan_forward(body, initial, seqs, axis, state_axis, reverse)
+
+
+def _element_scan_forward(body, initial, sequences, axis, state_axis, reverse) -> torch.Tensor:
     if body not in BODIES:
         raise SxError(SX_E_UNSUPPORTED, f"element-scan: unknown body {body!r}")
     seqs = list(sequences)
@@ -172,6 +189,66 @@ def element_scan(body: str, initial: torch.Tensor, sequences, axis: int = 0, sta
             _stream_handle(x.device))
     _check(status)
     return out
+
+
+def element_scan_backward(body: str, initial: torch.Tensor, sequences, h: torch.Tensor, g: torch.Tensor,
+                          axis: int = 0, state_axis=None, reverse: bool = False):
+    """Gradients ``(grad_initial, [grad_x, grad_s])`` of a loss through
+    ``h = element_scan(body, initial, sequences, axis, state_axis, reverse)``,
+    given that call's result ``h`` and the loss's gradient ``g`` with respect
+    to it. Each gradient has its tensor's shape; all are f32.
+    """
+    if body not in BODIES:
+        raise SxError(SX_E_UNSUPPORTED, f"element-scan gradient: unknown body {body!r}")
+    seqs = list(sequences)
+    if len(seqs) != 2:
+        raise SxError(SX_E_DIM_001, f"element-scan gradient: the {body} body takes two sequences, got {len(seqs)}")
+    x, s = seqs
+    for name, t in (("initial", initial), ("x", x), ("sequence 2", s), ("h", h), ("g", g)):
+        _require_device_tensor(name, t)
+        if t.dtype != torch.float32:
+            raise SxError(SX_E_DIM_002, f"element-scan gradient: {name} is {t.dtype}; element scans are f32")
+    if tuple(g.shape) != tuple(h.shape):
+        raise SxError(SX_E_DIM_001, f"element-scan gradient: g {tuple(g.shape)} and h {tuple(h.shape)} differ")
+    rank = h.dim()
+    vec = state_axis is not None
+    x_width = x.shape[-1] if vec else (h.shape[-1] if rank else 1)
+    s_width = s.shape[-1] if vec else (h.shape[-1] if rank else 1)
+    sa = state_axis if vec else SX_STATE_SCALAR
+    initial, h, g = initial.contiguous(), h.contiguous(), g.contiguous()
+    lib = load_library()
+    shape_a = i64_array(h.shape)
+    ws_bytes = lib.sx_element_scan_backward_workspace_bytes(BODIES[body], rank, shape_a, axis, sa, x_width, s_width)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=h.device) if ws_bytes else None
+    gi, gx, gs = torch.empty_like(initial), torch.empty(tuple(x.shape), dtype=torch.float32, device=h.device), \
+        torch.empty(tuple(s.shape), dtype=torch.float32, device=h.device)
+    with torch.cuda.device(h.device):
+        status = lib.sx_element_scan_backward(
+            BODIES[body], rank, shape_a, axis, sa, 1 if reverse else 0, initial.data_ptr(),
+            x.data_ptr(), x_width, i64_array(x.stride()), s.data_ptr(), s_width, i64_array(s.stride()),
+            h.data_ptr(), g.data_ptr(), gi.data_ptr(), gx.data_ptr(), gs.data_ptr(),
+            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(h.device))
+    _check(status)
+    return gi, [gx, gs]
+
+
+class _ElementScanFunction(torch.autograd.Function):
+    """element_scan with its gradient from the library: saves the inputs and the result."""
+
+    @staticmethod
+    def forward(ctx, body, axis, state_axis, reverse, initial, x, s):
+        h = _element_scan_forward(body, initial, [x, s], axis, state_axis, reverse)
+        ctx.save_for_backward(initial, x, s, h)
+        ctx.args = (body, axis, state_axis, reverse)
+        return h
+
+    @staticmethod
+    def backward(ctx, g):
+        initial, x, s, h = ctx.saved_tensors
+        body, axis, state_axis, reverse = ctx.args
+        gi, (gx, gs) = element_scan_backward(body, initial, [x, s], h, g, axis=axis, state_axis=state_axis,
+                                             reverse=reverse)
+        return None, None, None, None, gi, gx, gs
 
 
 def matrix_scan(a: torch.Tensor, b: torch.Tensor, axis: int = 0, reverse: bool = False,

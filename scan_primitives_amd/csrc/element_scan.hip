@@ -541,6 +541,242 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
     }
   }
 }
+// ------------------------------------------------------------------ gradients
+//
+// The gradient of sum(g * out) runs the trips last to first (in scan order).
+// With lam the adjoint of the state a trip produced (g there plus what the
+// trip after passed back), each trip's chain rule gives its sequences'
+// gradients and the adjoint of the state it started from, hp:
+//   tanh-affine  dz = lam (1 - h^2): grad_x = dz, grad_s = dz hp, to hp s dz
+//   max-plus     x won (x >= hp - c, ties to x): grad_x = lam, grad_c = 0, to hp 0;
+//                else grad_x = 0, grad_c = -lam, to hp lam
+//   norm-cap     y = s hp + x; capped (|y| > 1): dy = (lam - u (u . lam)) / |y|
+//                with u = y / |y|; else dy = lam: grad_x = dy, grad_s = dy hp,
+//                to hp s dy
+// For the scalar bodies the adjoint reaching hp is A lam, A = s (1 - h^2) or
+// [the carry won], and each gradient is lam times a factor of the trip's own:
+// so nu (the adjoint passed to a trip's incoming state) follows the linear
+// recurrence nu_q = A_q nu_{q+1} + A_q g_q, scanned like linear-scan, and the
+// trip's lam is g_q + nu_{q+1}. The branch decisions use f32 values as the
+// forward pass computed them.
+
+// A trip of a scalar body's gradient, reduced to what the sweep needs.
+struct VjpTrip {
+  float a;   // A: the adjoint reaching hp is a * lam
+  float g;   // g at this trip
+  float kx;  // grad_x = kx * lam
+  float ks;  // grad_s = ks * lam
+};
+
+template <int BODY>
+__device__ __forceinline__ VjpTrip vjp_trip(float h, float hp, float x, float s, float g) {
+  VjpTrip v;
+  v.g = g;
+  if constexpr (BODY == SX_BODY_TANH_AFFINE) {
+    const float d = 1.0f - h * h;
+    v.a = s * d;
+    v.kx = d;
+    v.ks = d * hp;
+  } else {
+    const bool x_won = x >= hp - s;
+    v.a = x_won ? 0.0f : 1.0f;
+    v.kx = x_won ? 1.0f : 0.0f;
+    v.ks = x_won ? 0.0f : -1.0f;
+  }
+  return v;
+}
+
+// One thread per lane, trips last to first in scan order. Forward scan
+// position q is time tq(q); the state before it is h at position q - 1
+// (initial at q = 0). Loads of a block of U trips are issued before any of
+// its trips is computed.
+template <int BODY>
+__global__ __launch_bounds__(64) void es_vjp_lane_kernel(const EsVjpParams v) {
+  const EsParams& p = v.p;
+  const int64_t lane = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (lane >= p.num_lanes) return;
+  int64_t off[4];
+  index_offsets(p.lanes, lane, off);
+  const int64_t T = p.T;
+  const int64_t sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const float* xl = p.x + off[ES_X];
+  const float* sl = p.s + off[ES_S];
+  const float* hl = v.h + off[ES_OUT];
+  const float* gl = v.g + off[ES_OUT];
+  float* gxl = v.gx + off[ES_OUT];
+  float* gsl = v.gs + off[ES_OUT];
+  const float init = p.init[off[ES_INIT]];
+  auto tq = [&](int64_t q) -> int64_t { return p.reverse ? T - 1 - q : q; };
+  constexpr int U = 8;
+  float nu = 0.0f;
+  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {  // trips q1, q1 - 1, ... (at most U of them)
+    VjpTrip tr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = q1 - u >= 0 ? q1 - u : 0;  // clamped: every load is valid
+      const int64_t t = tq(q);
+      const float hp = q > 0 ? hl[tq(q - 1) * so] : init;
+      tr[u] = vjp_trip<BODY>(hl[t * so], hp, xl[t * sx], sl[t * ss], gl[t * so]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q1 - u >= 0) {
+        const int64_t t = tq(q1 - u);
+        const float lam = tr[u].g + nu;
+        gxl[t * so] = tr[u].kx * lam;
+        gsl[t * so] = tr[u].ks * lam;
+        nu = tr[u].a * lam;
+      }
+    }
+  }
+  v.ginit[off[ES_INIT]] = nu;
+}
+
+// The scalar bodies' gradient as a chunked associative scan over the sweep
+// (the trips last to first): the adjoint map of a trip, nu -> A nu + A g,
+// composes like a linear-scan trip. One workgroup of NW waves owns 64 lanes;
+// each slab of NW*S trips is summarised per wave, the summaries meet in LDS,
+// each wave composes the ones before it onto the slab's carry, and replays
+// its trips storing both gradients. The next slab's loads are in flight
+// meanwhile. Sweep position w is scan position T - 1 - w.
+template <int BODY, int NW, int S>
+__global__ __launch_bounds__(NW * 64) void es_vjp_slab_kernel(const EsVjpParams v) {
+  const EsParams& p = v.p;
+  __shared__ float sP[2][NW][64];
+  __shared__ float sQ[2][NW][64];
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int l = int(threadIdx.x) & 63;
+  const int64_t lane = int64_t(blockIdx.x) * 64 + l;
+  const bool live = lane < p.num_lanes;
+  int64_t off[4];
+  index_offsets(p.lanes, live ? lane : 0, off);
+  const int64_t T = p.T;
+  const int64_t sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const float* xl = p.x + off[ES_X];
+  const float* sl = p.s + off[ES_S];
+  const float* hl = v.h + off[ES_OUT];
+  const float* gl = v.g + off[ES_OUT];
+  float* gxl = v.gx + off[ES_OUT];
+  float* gsl = v.gs + off[ES_OUT];
+  const float init = p.init[off[ES_INIT]];
+  // sweep position w -> time; positions past the end are clamped for loading and become identity trips
+  auto time_of = [&](int64_t w) -> int64_t {
+    const int64_t q = T - 1 - (w < T ? w : T - 1);
+    return p.reverse ? T - 1 - q : q;
+  };
+  auto load = [&](int64_t w, float (&raw)[5]) {
+    const int64_t t = time_of(w);
+    raw[0] = ld_stream(hl + t * so);
+    raw[1] = w + 1 < T ? hl[time_of(w + 1) * so] : init;  // the state before the trip
+    raw[2] = ld_stream(xl + t * sx);
+    raw[3] = ld_stream(sl + t * ss);
+    raw[4] = ld_stream(gl + t * so);
+  };
+  constexpr int64_t kSlab = int64_t(NW) * S;
+  const int64_t nslabs = (T + kSlab - 1) / kSlab;
+  float carry = 0.0f;
+  float nraw[S][5];
+#pragma unroll
+  for (int k = 0; k < S; ++k) load(int64_t(wave) * S + k, nraw[k]);
+  for (int64_t sl_i = 0; sl_i < nslabs; ++sl_i) {
+    const int64_t w0 = sl_i * kSlab + int64_t(wave) * S;
+    VjpTrip tr[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      tr[k] = vjp_trip<BODY>(nraw[k][0], nraw[k][1], nraw[k][2], nraw[k][3], nraw[k][4]);
+      if (w0 + k >= T) tr[k] = VjpTrip{1.0f, 0.0f, 0.0f, 0.0f};  // identity trip
+    }
+#pragma unroll
+    for (int k = 0; k < S; ++k) load(w0 + kSlab + k, nraw[k]);  // the next slab, in flight during this one
+    __builtin_amdgcn_sched_barrier(0);
+    float P = 1.0f, Q = 0.0f;  // this wave's trips composed: nu -> P nu + Q
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      Q = tr[k].a * (Q + tr[k].g);
+      P = P * tr[k].a;
+    }
+    const int par = int(sl_i & 1);
+    sP[par][wave][l] = P;
+    sQ[par][wave][l] = Q;
+    __syncthreads();
+    float nu = carry, nw = carry;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w == wave) nw = nu;
+      nu = fmaf(sP[par][w][l], nu, sQ[par][w][l]);
+    }
+    carry = nu;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const float lam = tr[k].g + nw;
+      if (live && w0 + k < T) {
+        const int64_t t = time_of(w0 + k);
+        st_stream(gxl + t * so, tr[k].kx * lam);
+        st_stream(gsl + t * so, tr[k].ks * lam);
+      }
+      nw = tr[k].a * lam;
+    }
+  }
+  if (live && wave == 0) v.ginit[off[ES_INIT]] = carry;
+}
+
+// Norm-cap gradient: one 16-lane DPP row per state vector, trips last to first.
+__global__ __launch_bounds__(256) void es_vjp_normcap_row_kernel(const EsVjpParams v) {
+  const EsParams& p = v.p;
+  const int64_t gtid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t lane = gtid >> 4;
+  if (lane >= p.num_lanes) return;  // a whole row leaves together
+  const int k = int(threadIdx.x & 15);
+  const bool active = k < p.n;
+  const int kk = active ? k : 0;
+  int64_t off[4];
+  index_offsets(p.lanes, lane, off);
+  const int64_t T = p.T;
+  const int64_t sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const float* xl = p.x + off[ES_X] + kk * p.n_stride[ES_X];
+  const float* sl = p.s + off[ES_S] + kk * p.n_stride[ES_S];
+  const float* hl = v.h + off[ES_OUT] + kk;
+  const float* gl = v.g + off[ES_OUT] + kk;
+  float* gxl = v.gx + off[ES_OUT] + kk;
+  float* gsl = v.gs + off[ES_OUT] + kk;
+  const float init = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
+  auto tq = [&](int64_t q) -> int64_t { return p.reverse ? T - 1 - q : q; };
+  constexpr int U = 4;
+  float nu = 0.0f;
+  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {
+    float hp[U], xv[U], sv[U], gv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = q1 - u >= 0 ? q1 - u : 0;
+      const int64_t t = tq(q);
+      const float hpv = q > 0 ? hl[tq(q - 1) * so] : init;
+      hp[u] = active ? hpv : 0.0f;
+      xv[u] = active ? xl[t * sx] : 0.0f;
+      sv[u] = active ? sl[t * ss] : 0.0f;
+      gv[u] = active ? gl[t * so] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q1 - u >= 0) {  // row-uniform
+        const float lam = gv[u] + nu;
+        const float y = fmaf(sv[u], hp[u], xv[u]);
+        const float ir = __builtin_amdgcn_rsqf(row_sum16(y * y));  // 1 / |y|, as the forward pass
+        const bool capped = ir < 1.0f;
+        const float uy = y * ir;
+        const float ul = row_sum16(uy * lam);
+        const float dy = capped ? (lam - uy * ul) * ir : lam;
+        if (active) {
+          const int64_t t = tq(q1 - u);
+          gxl[t * so] = dy;
+          gsl[t * so] = dy * hp[u];
+        }
+        nu = sv[u] * dy;
+      }
+    }
+  }
+  if (active) v.ginit[off[ES_INIT] + kk * p.n_stride[ES_INIT]] = nu;
+}
+
 }  // namespace
 
 // The slab kernel wants about one 64-lane workgroup per CU (MI355X: 256) and
@@ -612,6 +848,34 @@ hipError_t launch_linear_scan(const EsParams& p, bool in_bf16, bool out_bf16, hi
   } else {
     if (out_bf16) launch_linear<float, uint16_t>(p, blocks, stream);
     else launch_linear<float, float>(p, blocks, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipStream_t stream) {
+  const EsParams& p = v.p;
+  if (p.num_lanes <= 0 || p.T <= 0) return hipSuccess;
+  if (body == SX_BODY_NORM_CAP) {
+    const int64_t blocks = (p.num_lanes * 16 + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(es_vjp_normcap_row_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, v);
+    return hipGetLastError();
+  }
+  const int64_t blocks = (p.num_lanes + 63) / 64;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool slab = p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips;
+  if (body == SX_BODY_TANH_AFFINE) {
+    if (slab)
+      hipLaunchKernelGGL((es_vjp_slab_kernel<SX_BODY_TANH_AFFINE, 16, 8>), dim3(unsigned(blocks)), dim3(1024), 0,
+                         stream, v);
+    else
+      hipLaunchKernelGGL(es_vjp_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, v);
+  } else {
+    if (slab)
+      hipLaunchKernelGGL((es_vjp_slab_kernel<SX_BODY_MAX_PLUS, 16, 8>), dim3(unsigned(blocks)), dim3(1024), 0,
+                         stream, v);
+    else
+      hipLaunchKernelGGL(es_vjp_lane_kernel<SX_BODY_MAX_PLUS>, dim3(unsigned(blocks)), dim3(64), 0, stream, v);
   }
   return hipGetLastError();
 }

@@ -682,6 +682,119 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
   return ok();
 }
 
+// ------------------------------------------------------------------ element-scan gradient
+
+size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis, int state_axis,
+                                                int64_t x_width, int64_t s_width) {
+  EsPlan plan;
+  if (plan_element_scan(body, rank, shape, axis, state_axis, nullptr, x_width, nullptr, s_width, nullptr, &plan) !=
+      SX_OK)
+    return 0;
+  const bool vec = state_axis != SX_STATE_SCALAR;
+  const int64_t n = vec ? shape[rank - 1] : 1;
+  size_t total = 0, part = 0;
+  int64_t seq[sx::kMaxRank];
+  std::copy(shape, shape + rank, seq);
+  for (int64_t w : {x_width, s_width}) {
+    if (!vec || w != 1 || n == 1) continue;
+    total += align_up(size_t(plan.numel) * 4);  // the full-width gradient before its sum over the state
+    seq[rank - 1] = 1;
+    const sx::SumToParams q = sum_to_plan(rank, shape, rank, seq);
+    part = std::max(part, size_t(q.splits * q.targets) * 4);
+  }
+  return total + align_up(part);
+}
+
+sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape, int axis, int state_axis, int reverse,
+                                   const float* initial, const float* x, int64_t x_width, const int64_t* x_strides,
+                                   const float* s, int64_t s_width, const int64_t* s_strides, const float* h,
+                                   const float* g, float* grad_initial, float* grad_x, float* grad_s, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  EsPlan plan;
+  sx_status st = plan_element_scan(body, rank, shape, axis, state_axis, nullptr, x_width, x_strides, s_width,
+                                   s_strides, &plan);
+  if (st != SX_OK) return st;
+  if (plan.numel == 0) return ok();
+  const char* what[] = {"initial", "sequence x", "the second sequence", "the forward result h",
+                        "the result's gradient g", "grad_initial", "grad_x", "grad_s"};
+  const void* ptrs[] = {initial, x, s, h, g, grad_initial, grad_x, grad_s};
+  for (int i = 0; i < 8; ++i)
+    if (!ptrs[i]) return fail(SX_E_DIM_003, "element-scan gradient: %s is NULL; a tensor was expected", what[i]);
+  const bool vec = state_axis != SX_STATE_SCALAR;
+  const int64_t n = vec ? shape[rank - 1] : 1;
+  const int ax = axis < 0 ? axis + rank : axis;
+
+  // byte spans: inputs, then outputs (initial, h, g and every gradient are contiguous)
+  int64_t xshape[sx::kMaxRank], sshape[sx::kMaxRank], ishape[sx::kMaxRank], xs[sx::kMaxRank], ss[sx::kMaxRank];
+  int64_t is[sx::kMaxRank], os[sx::kMaxRank];
+  for (int i = 0; i < rank; ++i) xshape[i] = sshape[i] = shape[i];
+  if (vec) { xshape[rank - 1] = x_width; sshape[rank - 1] = s_width; }
+  int64_t inumel = 1;
+  for (int i = 0, j = 0; i < rank; ++i)
+    if (i != ax) inumel *= (ishape[j++] = shape[i]);
+  if (x_strides) std::copy(x_strides, x_strides + rank, xs); else contiguous_strides(rank, xshape, xs);
+  if (s_strides) std::copy(s_strides, s_strides + rank, ss); else contiguous_strides(rank, sshape, ss);
+  contiguous_strides(rank - 1, ishape, is);
+  contiguous_strides(rank, shape, os);
+  int64_t xn = 0, sn = 0;
+  checked_numel(rank, xshape, &xn);
+  checked_numel(rank, sshape, &sn);
+  uintptr_t lo[8], hi[8];
+  span_bytes(initial, rank - 1, ishape, is, 4, &lo[0], &hi[0]);
+  span_bytes(x, rank, xshape, xs, 4, &lo[1], &hi[1]);
+  span_bytes(s, rank, sshape, ss, 4, &lo[2], &hi[2]);
+  span_bytes(h, rank, shape, os, 4, &lo[3], &hi[3]);
+  span_bytes(g, rank, shape, os, 4, &lo[4], &hi[4]);
+  lo[5] = reinterpret_cast<uintptr_t>(grad_initial); hi[5] = lo[5] + uintptr_t(inumel) * 4;
+  lo[6] = reinterpret_cast<uintptr_t>(grad_x); hi[6] = lo[6] + uintptr_t(xn) * 4;
+  lo[7] = reinterpret_cast<uintptr_t>(grad_s); hi[7] = lo[7] + uintptr_t(sn) * 4;
+  for (int o = 5; o < 8; ++o)
+    for (int i = 0; i < o; ++i)
+      if (overlaps(lo[o], hi[o], lo[i], hi[i]))
+        return fail(SX_E_ALIAS, "element-scan gradient: %s overlaps %s", what[o], what[i]);
+
+  const bool x_sum = vec && x_width == 1 && n > 1, s_sum = vec && s_width == 1 && n > 1;
+  const size_t need = sx_element_scan_backward_workspace_bytes(body, rank, shape, axis, state_axis, x_width, s_width);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SX_E_WORKSPACE, "element-scan gradient: workspace of %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SX_E_WORKSPACE, "element-scan gradient: workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const size_t full = align_up(size_t(plan.numel) * 4);
+  float* gx_full = x_sum ? reinterpret_cast<float*>(ws) : grad_x;
+  float* gs_full = s_sum ? reinterpret_cast<float*>(ws + (x_sum ? full : 0)) : grad_s;
+  float* part = reinterpret_cast<float*>(ws + (x_sum ? full : 0) + (s_sum ? full : 0));
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  sx::EsVjpParams v{};
+  v.p = plan.p;
+  v.p.reverse = reverse ? 1 : 0;
+  v.p.x = x;
+  v.p.s = s;
+  v.p.init = initial;
+  v.p.out = nullptr;
+  v.h = h;
+  v.g = g;
+  v.gx = gx_full;
+  v.gs = gs_full;
+  v.ginit = grad_initial;
+  hipError_t e = sx::launch_element_scan_backward(body, v, hs);
+  if (e != hipSuccess) return device_status(e, "element-scan gradient launch");
+  int64_t seq[sx::kMaxRank];
+  std::copy(shape, shape + rank, seq);
+  seq[rank - 1] = 1;
+  for (int which = 0; which < 2; ++which) {
+    if (!(which == 0 ? x_sum : s_sum)) continue;
+    sx::SumToParams q = sum_to_plan(rank, shape, rank, seq);
+    q.src = which == 0 ? gx_full : gs_full;
+    q.partial = part;
+    e = sx::launch_sum_to(q, which == 0 ? static_cast<void*>(grad_x) : static_cast<void*>(grad_s), false, hs);
+    if (e != hipSuccess) return device_status(e, "element-scan gradient: sum over the state launch");
+  }
+  return ok();
+}
+
 // ------------------------------------------------------------------ linear-scan
 
 // a and b broadcast (NumPy: right-aligned, each dim equal or 1; rank 0 is a

@@ -63,6 +63,20 @@ struct EsParams {
 hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream);
 size_t element_scan_workspace(sx_body body, const EsParams& p);
 
+// Gradient of an element scan: p as planned for the forward call (initial
+// contiguous), h (the forward result) and g (its gradient) in out's layout;
+// gx and gs full-width gradients of the two sequences in out's layout; ginit
+// in initial's layout.
+struct EsVjpParams {
+  EsParams p;
+  const float* h;
+  const float* g;
+  float* gx;
+  float* gs;
+  float* ginit;
+};
+hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipStream_t stream);
+
 // linear-scan runs on the element-scan kernels: b as the sequence x, a as the
 // second sequence s, init == nullptr (every lane starts from zero), and the
 // trip h -> a * h + b, a body of the library's own beside the public three.

@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
     for required in ("sx_element_scan", "sx_matrix_scan", "sx_element_scan_workspace_bytes",
                      "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_linear_scan",
                      "sx_linear_scan_out_shape", "sx_matrix_scan_backward", "sx_matrix_scan_backward_workspace_bytes",
+                     "sx_element_scan_backward", "sx_element_scan_backward_workspace_bytes",
                      "sx_status_name", "sx_last_error", "sx_version"):
         assert required in names
 
@@ -208,6 +209,48 @@ def test_matrix_scan_backward_workspace_query(lib):
     assert q(4, B.i64_array([32, 8192, 16, 16]), 4, B.i64_array([32, 8192, 16, 1]), 1, B.SX_BF16) >= \
         full + 32 * 8192 * 16 * 4
     assert q(3, B.i64_array([2, 4, 4]), 3, B.i64_array([2, 5, 1]), 0, B.SX_F32) == 0
+
+
+def _esb(lib, body=2, shape=(4, 8, 3), axis=1, state_axis=B.SX_STATE_SCALAR, ptrs=None, x_width=3, s_width=3,
+         ws=None, ws_bytes=0):
+    base = {"initial": FAKE, "x": FAKE + (1 << 20), "s": FAKE + (2 << 20), "h": FAKE + (3 << 20), "g": FAKE + (4 << 20),
+            "gi": FAKE + (5 << 20), "gx": FAKE + (6 << 20), "gs": FAKE + (7 << 20)}
+    base.update(ptrs or {})
+    st = lib.sx_element_scan_backward(body, len(shape), B.i64_array(shape), axis, state_axis, 0, base["initial"],
+                                      base["x"], x_width, None, base["s"], s_width, None, base["h"], base["g"],
+                                      base["gi"], base["gx"], base["gs"], ws, ws_bytes, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(body=7), B.SX_E_UNSUPPORTED),
+    (dict(axis=3), B.SX_E_DIM_001),
+    (dict(shape=(4, 0, 3)), B.SX_E_DIM_001),                              # empty scan axis
+    (dict(body=1), B.SX_E_DIM_001),                                       # norm-cap needs a vector state
+    (dict(ptrs={"initial": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"h": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"g": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"gi": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"gx": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"gs": None}), B.SX_E_DIM_003),
+    (dict(ptrs={"gx": FAKE + (3 << 20) + 8}), B.SX_E_ALIAS),             # grad_x over h
+    (dict(ptrs={"gs": FAKE + (6 << 20) + 4}), B.SX_E_ALIAS),             # grad_s over grad_x
+    (dict(ptrs={"gi": FAKE + 4}), B.SX_E_ALIAS),                          # grad_initial over initial
+    (dict(body=1, shape=(4, 8, 3), state_axis=-1, x_width=3, s_width=1), B.SX_E_WORKSPACE),  # width-1 gate sums
+])
+def test_element_scan_backward_rejects_on_host(lib, kwargs, code):
+    st, msg = _esb(lib, **kwargs)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_element_scan_backward_workspace_query(lib):
+    q = lib.sx_element_scan_backward_workspace_bytes
+    assert q(0, 3, B.i64_array([4, 64, 32]), 1, B.SX_STATE_SCALAR, 32, 32) == 0
+    need = q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 1)
+    assert need >= 8 * 1024 * 16 * 16 * 4 and need % 256 == 0   # the width-1 gate's full-width gradient
+    assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == 0
+    assert q(2, 3, B.i64_array([4, 8, 3]), 5, B.SX_STATE_SCALAR, 3, 3) == 0  # invalid axis
 
 
 def _ls(lib, a_shape=(3, 9, 5), b_shape=(3, 9, 5), dtype=B.SX_F32, out_dtype=B.SX_F32, axis=1, a=FAKE,
