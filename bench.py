@@ -21,7 +21,7 @@ single calls, each after a 512 MiB write that evicts the last-level cache
 fraction of the 8 TB/s HBM peak.
 
 linear-scan and cumsum ([64,4096,256] f32 along axis 1) and the gradients of
-the two matrix workloads are timed the same two ways and reported in
+the five workloads are timed the same two ways and reported in
 ``per_config`` with ``"in_step": false``; they are not part of the step or
 of ``value`` (``--no-extra`` skips them).
 
@@ -154,9 +154,12 @@ def main() -> int:
     log("generated inputs: " + "; ".join(w.name for w in workloads + extras))
     resident = [w.on(dev) for w in workloads]
     resident_extra = [w.on(dev) for w in extras]
-    for w, t in zip(extras, resident_extra):
-        if w.op == "matrix_scan_backward":  # the forward result the gradient reads, computed once here
+    for w, t in zip(extras, resident_extra):  # the forward result a gradient reads, computed once here
+        if w.op == "matrix_scan_backward":
             t["h"] = sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse)
+        elif w.op == "element_scan_backward":
+            t["h"] = sx.element_scan(w.body, t["initial"], [t["x"], t["s"]], axis=w.axis, state_axis=w.state_axis,
+                                     reverse=w.reverse)
     torch.cuda.synchronize()
 
     def call(w, t):
@@ -169,6 +172,9 @@ def main() -> int:
         if w.op == "matrix_scan_backward":
             return sx.matrix_scan_backward(t["a"], tuple(t["b"].shape), t["h"], t["g"], axis=w.axis,
                                            reverse=w.reverse)
+        if w.op == "element_scan_backward":
+            return sx.element_scan_backward(w.body, t["initial"], [t["x"], t["s"]], t["h"], t["g"], axis=w.axis,
+                                            state_axis=w.state_axis, reverse=w.reverse)
         return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
 
     copy_src = copy_dst = None

@@ -607,27 +607,40 @@ __global__ __launch_bounds__(64) void es_vjp_lane_kernel(const EsVjpParams v) {
   float* gsl = v.gs + off[ES_OUT];
   const float init = p.init[off[ES_INIT]];
   auto tq = [&](int64_t q) -> int64_t { return p.reverse ? T - 1 - q : q; };
+  // blocks of U trips (q1, q1 - 1, ...), block i + 1's loads in flight while block i is computed
   constexpr int U = 8;
-  float nu = 0.0f;
-  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {  // trips q1, q1 - 1, ... (at most U of them)
-    VjpTrip tr[U];
+  struct Block {
+    float h[U], hp[U], x[U], s[U], g[U];
+  };
+  auto load = [&](int64_t q1, Block& B) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t q = q1 - u >= 0 ? q1 - u : 0;  // clamped: every load is valid
       const int64_t t = tq(q);
-      const float hp = q > 0 ? hl[tq(q - 1) * so] : init;
-      tr[u] = vjp_trip<BODY>(hl[t * so], hp, xl[t * sx], sl[t * ss], gl[t * so]);
+      B.hp[u] = hl[tq(q > 0 ? q - 1 : 0) * so];  // unconditional; initial is selected at the trip
+      B.h[u] = hl[t * so];
+      B.x[u] = xl[t * sx];
+      B.s[u] = sl[t * ss];
+      B.g[u] = gl[t * so];
     }
+  };
+  float nu = 0.0f;
+  Block cur, nxt;
+  load(T - 1, cur);
+  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {
+    load(q1 - U, nxt);  // always (clamped positions): a load behind a branch would cost a full wait
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (q1 - u >= 0) {
+        const VjpTrip tr = vjp_trip<BODY>(cur.h[u], q1 - u > 0 ? cur.hp[u] : init, cur.x[u], cur.s[u], cur.g[u]);
         const int64_t t = tq(q1 - u);
-        const float lam = tr[u].g + nu;
-        gxl[t * so] = tr[u].kx * lam;
-        gsl[t * so] = tr[u].ks * lam;
-        nu = tr[u].a * lam;
+        const float lam = tr.g + nu;
+        gxl[t * so] = tr.kx * lam;
+        gsl[t * so] = tr.ks * lam;
+        nu = tr.a * lam;
       }
     }
+    cur = nxt;
   }
   v.ginit[off[ES_INIT]] = nu;
 }
@@ -667,7 +680,8 @@ __global__ __launch_bounds__(NW * 64) void es_vjp_slab_kernel(const EsVjpParams 
   auto load = [&](int64_t w, float (&raw)[5]) {
     const int64_t t = time_of(w);
     raw[0] = ld_stream(hl + t * so);
-    raw[1] = w + 1 < T ? hl[time_of(w + 1) * so] : init;  // the state before the trip
+    const float hr = hl[time_of(w + 1) * so];  // clamped position, unconditional load
+    raw[1] = w + 1 < T ? hr : init;            // the state before the trip
     raw[2] = ld_stream(xl + t * sx);
     raw[3] = ld_stream(sl + t * ss);
     raw[4] = ld_stream(gl + t * so);
@@ -741,38 +755,55 @@ __global__ __launch_bounds__(256) void es_vjp_normcap_row_kernel(const EsVjpPara
   float* gsl = v.gs + off[ES_OUT] + kk;
   const float init = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
   auto tq = [&](int64_t q) -> int64_t { return p.reverse ? T - 1 - q : q; };
-  constexpr int U = 4;
-  float nu = 0.0f;
-  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {
-    float hp[U], xv[U], sv[U], gv[U];
+  // Blocks of U trips, last to first; block i + 1's loads are issued before block i is
+  // computed, so the trip chain does not wait on memory. Positions below 0 are clamped
+  // for loading and skipped.
+  constexpr int U = 8;  // 32 loads a block: the loads in flight stay countable by vmcnt (at most 63)
+  struct Block {  // raw loads; the selects that depend on them wait until the trip is computed
+    float hr[U], xv[U], sv[U], gv[U];
+  };
+  auto load = [&](int64_t q1, Block& B) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u) {  // clamped positions: every load is valid and none is behind a branch
       const int64_t q = q1 - u >= 0 ? q1 - u : 0;
       const int64_t t = tq(q);
-      const float hpv = q > 0 ? hl[tq(q - 1) * so] : init;
-      hp[u] = active ? hpv : 0.0f;
-      xv[u] = active ? xl[t * sx] : 0.0f;
-      sv[u] = active ? sl[t * ss] : 0.0f;
-      gv[u] = active ? gl[t * so] : 0.0f;
+      B.hr[u] = hl[tq(q > 0 ? q - 1 : 0) * so];
+      B.xv[u] = xl[t * sx];
+      B.sv[u] = sl[t * ss];
+      B.gv[u] = gl[t * so];
     }
+  };
+  float nu = 0.0f;
+  Block cur, nxt;
+  load(T - 1, cur);
+  for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {
+    load(q1 - U, nxt);  // always (clamped positions): a load behind a branch would cost a full wait
+    // What does not depend on the adjoint, for the whole block first: y, 1 / |y| (as
+    // the forward pass computes it), the cap decision and the direction u = y / |y|.
+    float ir[U], uy[U], hp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      hp[u] = q1 - u > 0 ? cur.hr[u] : init;  // the state before the trip (initial before the first)
+      const float y = active ? fmaf(cur.sv[u], hp[u], cur.xv[u]) : 0.0f;  // lanes past n hold zero
+      ir[u] = __builtin_amdgcn_rsqf(row_sum16(y * y));
+      uy[u] = y * ir[u];
+    }
+    // the adjoint chain: one row sum per trip
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (q1 - u >= 0) {  // row-uniform
-        const float lam = gv[u] + nu;
-        const float y = fmaf(sv[u], hp[u], xv[u]);
-        const float ir = __builtin_amdgcn_rsqf(row_sum16(y * y));  // 1 / |y|, as the forward pass
-        const bool capped = ir < 1.0f;
-        const float uy = y * ir;
-        const float ul = row_sum16(uy * lam);
-        const float dy = capped ? (lam - uy * ul) * ir : lam;
+        const float lam = cur.gv[u] + nu;
+        const float ul = row_sum16(uy[u] * lam);
+        const float dy = ir[u] < 1.0f ? (lam - uy[u] * ul) * ir[u] : lam;  // capped when |y| > 1
         if (active) {
           const int64_t t = tq(q1 - u);
           gxl[t * so] = dy;
           gsl[t * so] = dy * hp[u];
         }
-        nu = sv[u] * dy;
+        nu = active ? cur.sv[u] * dy : 0.0f;
       }
     }
+    cur = nxt;
   }
   if (active) v.ginit[off[ES_INIT] + kk * p.n_stride[ES_INIT]] = nu;
 }
@@ -863,7 +894,10 @@ hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipS
   }
   const int64_t blocks = (p.num_lanes + 63) / 64;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const bool slab = p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips;
+  // The gradient's slab kernel is associative in every case; with few lanes it
+  // still takes every load of a slab at once, where the lane kernel would wait
+  // on memory each block of trips.
+  const bool slab = p.T >= kSlabMinTrips || (p.num_lanes < kSlabMinLanes && p.T >= 64);
   if (body == SX_BODY_TANH_AFFINE) {
     if (slab)
       hipLaunchKernelGGL((es_vjp_slab_kernel<SX_BODY_TANH_AFFINE, 16, 8>), dim3(unsigned(blocks)), dim3(1024), 0,

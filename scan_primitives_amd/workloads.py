@@ -57,6 +57,8 @@ class Workload:
             return tuple(torch.broadcast_shapes(t["b"].shape, t["a"].shape if "a" in t else ()))
         if self.op == "matrix_scan_backward":  # the outputs are grad_a and grad_b
             return tuple(t["a"].shape)
+        if self.op == "element_scan_backward":  # the outputs are the gradients of initial, x and s
+            return tuple(t["x"].shape)
         lead = torch.broadcast_shapes(t["a"].shape[:-2], t["b"].shape[:-2])
         return tuple(lead) + tuple(t["b"].shape[-2:])
 
@@ -85,6 +87,8 @@ class Workload:
         if self.op == "matrix_scan_backward":
             e = t["a"].element_size()
             return (2 * t["a"].numel() + 2 * t["g"].numel() + t["b"].numel()) * e
+        if self.op == "element_scan_backward":  # initial, x, s, h, g read; their gradients written (f32)
+            return 4 * (2 * (t["initial"].numel() + t["x"].numel() + t["s"].numel()) + 2 * t["g"].numel())
         ins = sum(v.numel() * v.element_size() for v in t.values())
         return ins + self.out_numel * self.out_elem_bytes
 
@@ -191,10 +195,20 @@ def make_matrix_grad(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, rever
                     reverse=reverse)
 
 
+def make_element_grad(w: Workload, seed: int) -> Workload:
+    """The gradient of an element-scan workload: its tensors and g ~ N(0,1) of
+    the result's shape."""
+    g = torch.randn(tuple(w.out_shape), generator=_gen(seed))
+    return Workload("gradient of " + w.name, "element_scan_backward", dict(w.tensors, g=g), axis=w.axis,
+                    reverse=w.reverse, body=w.body, state_axis=w.state_axis)
+
+
 def extra_workloads() -> list[Workload]:
     """Timed beside the step, not part of it: linear-scan and cumsum on the
     max-plus shape, [64,4096,256] along axis 1, f32; the gradients of the two
-    matrix workloads."""
+    matrix workloads and of the three element-scan workloads."""
     return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7),
             make_matrix_grad(32, 8192, 16, 1, torch.float32, reverse=False, seed=4),
-            make_matrix_grad(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5)]
+            make_matrix_grad(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5),
+            make_element_grad(make_tanh(), seed=11), make_element_grad(make_norm_cap(), seed=12),
+            make_element_grad(make_max_plus(), seed=13)]
