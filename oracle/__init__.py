@@ -63,8 +63,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["element_scan", "element_scan_vjp", "matrix_scan", "matrix_scan_vjp", "linear_scan", "cumsum",
-           "BODIES"]
+__all__ = ["element_scan", "element_scan_vjp", "matrix_scan", "matrix_scan_projective", "matrix_scan_vjp",
+           "linear_scan", "cumsum", "BODIES"]
 
 
 # --- element-scan bodies ----------------------------------------------------
@@ -312,6 +312,48 @@ def matrix_scan(a, b, axis=0, reverse=False, dtype=np.float64):
     order = range(T - 1, -1, -1) if reverse else range(T)
     for t in order:
         h = a_t[t] @ h + b_t[t]
+        out[t] = h
+    return np.moveaxis(out, 0, ax)
+
+
+def matrix_scan_projective(a, b, axis=0, reverse=False, dtype=np.float64):
+    """matrix-scan with ``:projective true``: the plain way, one step at a time.
+
+    A running product P of the a's starts at the identity. Each step (in scan
+    order) replaces P by ``a[t] @ P``, takes m = the largest magnitude of its
+    entries, divides P by m, and sets ``h = (a[t] @ h + b[t]) / m`` (h from
+    0). A product whose entries are all zero divides by 1. Operands, axis,
+    broadcasting and result shape are those of ``matrix_scan``.
+
+    Follows "Tensor operations", the "matrix-scan" section (``:projective``).
+    """
+    a = np.asarray(a, dtype=dtype)
+    b = np.asarray(b, dtype=dtype)
+    if a.ndim < 2 or b.ndim < 2:
+        raise ValueError("matrix_scan_projective: a and b need two matrix dims")
+    n = a.shape[-1]
+    if a.shape[-2] != n or b.shape[-2] != n or n > 16:
+        raise ValueError("matrix_scan_projective: a must be [.., n, n] and b [.., n, m] with n <= 16")
+    m = b.shape[-1]
+    lead = np.broadcast_shapes(a.shape[:-2], b.shape[:-2])
+    if len(lead) < 1:
+        raise ValueError("matrix_scan_projective: the scan axis is one of the leading dims")
+    ax = axis + len(lead) if axis < 0 else axis
+    if not 0 <= ax < len(lead):
+        raise ValueError(f"matrix_scan_projective: axis {axis} out of range for leading rank {len(lead)}")
+    a_t = np.moveaxis(np.broadcast_to(a, lead + (n, n)), ax, 0)
+    b_t = np.moveaxis(np.broadcast_to(b, lead + (n, m)), ax, 0)
+    T = lead[ax]
+    out = np.empty((T,) + b_t.shape[1:], dtype=dtype)
+    h = np.zeros(b_t.shape[1:], dtype=dtype)
+    P = np.broadcast_to(np.eye(n, dtype=dtype), a_t.shape[1:]).copy()
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        P = a_t[t] @ P
+        big = np.max(np.abs(P), axis=(-2, -1), keepdims=True)
+        big = np.where(big > 0, big, 1.0)
+        P = P / big
+        h = (a_t[t] @ h + b_t[t]) / big
         out[t] = h
     return np.moveaxis(out, 0, ax)
 

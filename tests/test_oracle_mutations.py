@@ -359,3 +359,56 @@ def test_max_plus_branch_mutant_is_caught(monkeypatch):
 def test_unmutated_element_scan_vjp_passes_its_pins():
     for body in ES_VJP_PINS:
         assert not _some_pin_fails(ES_VJP_PINS[body])
+
+
+_real_proj = oracle.matrix_scan_projective
+
+
+def _proj_mutant(kind):
+    def f(a, b, axis=0, reverse=False, dtype=np.float64):
+        a = np.asarray(a, dtype=np.float64)
+        b = np.asarray(b, dtype=np.float64)
+        n = a.shape[-1]
+        lead = np.broadcast_shapes(a.shape[:-2], b.shape[:-2])
+        ax = axis % len(lead)
+        a_t = np.moveaxis(np.broadcast_to(a, lead + (n, n)), ax, 0)
+        b_t = np.moveaxis(np.broadcast_to(b, lead + b.shape[-2:]), ax, 0)
+        T = lead[ax]
+        out = np.empty(b_t.shape)
+        h = np.zeros(b_t.shape[1:])
+        P = np.broadcast_to(np.eye(n), a_t.shape[1:]).copy()
+        for t in (range(T - 1, -1, -1) if reverse else range(T)):
+            P = a_t[t] @ P if kind != "product_transposed" else P @ a_t[t]
+            big = np.max(np.abs(P), axis=(-2, -1), keepdims=True)
+            if kind == "sum_not_max":
+                big = np.sum(np.abs(P), axis=(-2, -1), keepdims=True)
+            big = np.where(big > 0, big, 1.0)
+            if kind != "product_not_normalised":
+                P = P / big
+            if kind == "b_not_divided":
+                h = a_t[t] @ h / big + b_t[t]
+            else:
+                h = (a_t[t] @ h + b_t[t]) / big
+            out[t] = h
+        return np.moveaxis(out, 0, ax)
+    f.__name__ = f"proj_{kind}"
+    return f
+
+
+PROJ_PINS = [
+    (pins.test_projective_with_b_after_first_step_zero_is_h_over_the_product_size, {"reverse": False}),
+    (pins.test_projective_scalar_multiple_of_identity_is_a_scaled_running_sum, {"c": 2.0}),
+]
+
+
+@pytest.mark.parametrize("kind", ["product_transposed", "sum_not_max", "product_not_normalised", "b_not_divided"])
+def test_projective_mutants_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "matrix_scan_projective", _proj_mutant(kind))
+    assert _some_pin_fails(PROJ_PINS), f"no projective pin caught {kind}"
+
+
+def test_unmutated_projective_passes_its_pins():
+    assert not _some_pin_fails(PROJ_PINS)
+    rng = np.random.default_rng(6)
+    a, b = rng.normal(size=(2, 7, 3, 3)), rng.normal(size=(2, 7, 3, 2))
+    np.testing.assert_allclose(_proj_mutant("none")(a, b, axis=1), _real_proj(a, b, axis=1), rtol=1e-15)

@@ -723,3 +723,76 @@ def test_norm_cap_vjp_uncapped_is_the_linear_scan_gradient():
     lam = oracle.linear_scan(np.broadcast_to(shifted, (B, T, n)), g, axis=1, reverse=True)
     np.testing.assert_allclose(gx, lam, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(gi, a[:, 0] * lam[:, 0], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- matrix-scan :projective
+#
+# "Tensor operations", the "matrix-scan" section: the running product of a,
+# from the identity, is divided by its largest magnitude after every step and
+# h by the same number; with b zero after its first step the result is h up
+# to a positive factor per step.
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_projective_with_b_after_first_step_zero_is_h_over_the_product_size(reverse):
+    # b zero after its first step: h[t] = (a[t] ... a[first+1] b[first]) / max|a[t] ... a[first]|, the
+    # true state divided by the largest entry of the true running product (written with explicit products)
+    rng = _rng(91)
+    T, n = 9, 4
+    a = 0.9 * rng.normal(size=(2, T, n, n))
+    b = np.zeros((2, T, n, 2))
+    first = T - 1 if reverse else 0
+    b[:, first] = rng.normal(size=(2, n, 2))
+    got = oracle.matrix_scan_projective(a, b, axis=1, reverse=reverse)
+    order = list(range(T - 1, -1, -1)) if reverse else list(range(T))
+    for bi in range(2):
+        prod = np.eye(n)
+        state = b[bi, first]
+        for i, t in enumerate(order):
+            prod = a[bi, t] @ prod
+            if i > 0:
+                state = a[bi, t] @ state
+            np.testing.assert_allclose(got[bi, t], state / np.max(np.abs(prod)), rtol=1e-12, atol=1e-14)
+
+
+def test_projective_result_is_h_up_to_a_positive_factor():
+    # the page's statement itself: with b zero after its first step, out[t] = c_t * matrix_scan(...)[t], c_t > 0
+    rng = _rng(92)
+    a = rng.normal(size=(3, 12, 5, 5))
+    b = np.zeros((3, 12, 5, 1))
+    b[:, 0] = rng.normal(size=(3, 5, 1))
+    got = oracle.matrix_scan_projective(a, b, axis=1)
+    true = oracle.matrix_scan(a, b, axis=1)
+    ratio = np.sum(got * true, axis=(-2, -1)) / np.sum(true * true, axis=(-2, -1))
+    assert np.all(ratio > 0)
+    np.testing.assert_allclose(got, ratio[..., None, None] * true, rtol=1e-10, atol=1e-300)
+
+
+@pytest.mark.parametrize("c", [0.5, 2.0, 3.0])
+def test_projective_scalar_multiple_of_identity_is_a_scaled_running_sum(c):
+    # a[t] = c I: the product after each step is c^k I with largest entry c^k, so every step divides by c:
+    # h[t] = h[t-1] + b[t] / c from h[0] = b[0] / c, i.e. cumsum(b) / c -- for any length, where the plain
+    # scan would overflow (c = 2 or 3 over 1500 steps is far beyond float64's range)
+    rng = _rng(93)
+    T, n = 1500, 3
+    a = np.broadcast_to(c * np.eye(n), (T, n, n))
+    b = rng.normal(size=(T, n, 2))
+    got = oracle.matrix_scan_projective(a, b, axis=0)
+    np.testing.assert_allclose(got, np.cumsum(b, axis=0) / c, rtol=1e-12, atol=1e-12)
+
+
+def test_projective_identity_a_is_plain_cumsum_and_reverse_is_flip_scan_flip():
+    rng = _rng(94)
+    b = rng.normal(size=(2, 30, 4, 3))
+    eye = np.broadcast_to(np.eye(4), (2, 30, 4, 4))
+    np.testing.assert_allclose(oracle.matrix_scan_projective(eye, b, axis=1), np.cumsum(b, axis=1), rtol=1e-13)
+    a = 0.7 * rng.normal(size=(2, 30, 4, 4))
+    fwd = oracle.matrix_scan_projective(np.flip(a, 1), np.flip(b, 1), axis=1)
+    np.testing.assert_allclose(oracle.matrix_scan_projective(a, b, axis=1, reverse=True), np.flip(fwd, 1),
+                               rtol=1e-13, atol=1e-15)
+
+
+def test_projective_zero_product_divides_by_one():
+    a = np.zeros((4, 2, 2))
+    b = np.arange(16, dtype=float).reshape(4, 2, 2)
+    np.testing.assert_array_equal(oracle.matrix_scan_projective(a, b, axis=0), b)
