@@ -20,8 +20,8 @@ single calls, each after a 512 MiB write that evicts the last-level cache
 (256 MB), timed between HIP events (it includes the launch). This gives each workload's elements/s, algorithmic GB/s and
 fraction of the 8 TB/s HBM peak.
 
-linear-scan and cumsum ([64,4096,256] f32 along axis 1) and the gradients of
-the five workloads are timed the same two ways and reported in
+linear-scan and cumsum ([64,4096,256] f32 along axis 1), the gradients of
+the five workloads and the f32 matrix workload with :projective are timed the same two ways and reported in
 ``per_config`` with ``"in_step": false``; they are not part of the step or
 of ``value`` (``--no-extra`` skips them).
 
@@ -175,7 +175,8 @@ def main() -> int:
         if w.op == "element_scan_backward":
             return sx.element_scan_backward(w.body, t["initial"], [t["x"], t["s"]], t["h"], t["g"], axis=w.axis,
                                             state_axis=w.state_axis, reverse=w.reverse)
-        return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)
+        return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype,
+                              projective=w.meta.get("projective", False))
 
     copy_src = copy_dst = None
     if args.with_copy:

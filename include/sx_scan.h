@@ -63,7 +63,7 @@ typedef enum sx_status {
   SX_E_DIM_001 = 1,     /* shapes do not fit, axis out of range, n > 16, empty element-scan axis */
   SX_E_DIM_002 = 2,     /* dtypes differ, or a dtype the operand does not allow */
   SX_E_DIM_003 = 3,     /* a tensor was expected: a required pointer is NULL */
-  SX_E_UNSUPPORTED = 4, /* well-formed but not provided: rank > 8, :projective, strided matrix dims */
+  SX_E_UNSUPPORTED = 4, /* well-formed but not provided: rank > 8, strided matrix dims */
   SX_E_ALIAS = 5,       /* `out` overlaps an input */
   SX_E_WORKSPACE = 6,   /* workspace NULL or smaller than the queried size */
   SX_E_DEVICE = 7       /* a HIP call failed; sx_last_error() carries hipGetErrorString */
@@ -191,8 +191,14 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *                have any stride, including 0. Otherwise SX_E_UNSUPPORTED.
  *  axis          the scan axis among the broadcast leading dims.
  *  reverse       0 forward, nonzero reverse.
- *  projective    must be 0: the :projective variant is not provided
- *                (SX_E_UNSUPPORTED).
+ *  projective    nonzero: the :projective variant of the same section. A
+ *                running product P of the a's, from the identity, takes each
+ *                step's a (P = a[t] @ P); m, the largest |entry| of P (1 if
+ *                P is zero), divides P and the new state:
+ *                h[t] = (a[t] @ h[prev] + b[t]) / m. The result is h up to a
+ *                positive factor per step when b is zero after its first
+ *                step, and stays in range where the plain product would
+ *                overflow. It uses no workspace and runs serially in time.
  *  out_dtype     SX_F32 or SX_BF16. The result is rounded to bf16 to nearest
  *                even on store when SX_BF16.
  *  out           contiguous, shape lead + [n, m] (see sx_matrix_scan_out_shape).

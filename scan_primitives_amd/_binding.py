@@ -410,10 +410,14 @@ class _MatrixScanFunction(torch.autograd.Function):
         h = _matrix_scan_forward(a, b, axis, reverse, out_dtype, projective)
         ctx.save_for_backward(a, h)
         ctx.b_shape, ctx.b_dtype, ctx.axis, ctx.reverse = tuple(b.shape), b.dtype, axis, reverse
+        ctx.projective = projective
         return h
 
     @staticmethod
     def backward(ctx, g):
+        if ctx.projective:  # "Tensor operations", matrix-scan: the :projective result has no gradient
+            raise SxError(SX_E_UNSUPPORTED, "matrix-scan: :projective true has no gradient; differentiating "
+                                            "through it is an error")
         a, h = ctx.saved_tensors
         grad_a, grad_b = matrix_scan_backward(a, ctx.b_shape, h, g, axis=ctx.axis, reverse=ctx.reverse,
                                               grad_dtype=ctx.b_dtype)

@@ -1204,6 +1204,82 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   }
 }
 
+// ------------------------------------------------------------------ :projective
+//
+// "Tensor operations", the "matrix-scan" section: the running product P of the
+// a's, from the identity, is divided after every step by its largest
+// magnitude m, and h by the same number: h = (a[t] h + b[t]) / m (m = 1 when P
+// is zero). One wave per (batch, 16-column tile), serial in time: P and h
+// advance by MFMA each step (P in result-register order, as h), m is the
+// maximum over the wave (lane, DPP row, then the four row leaders), and the
+// operands of the next K steps are in flight meanwhile.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Largest |entry| of a 16x16 tile held four values per lane, the same in every lane.
+__device__ __forceinline__ float wave_max_abs(f32x4 v) {
+  float x = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror: every lane holds its row's maximum
+  const int xi = __float_as_int(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(xi, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(xi, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+template <typename TIn, typename TOut, bool VEC>
+__global__ __launch_bounds__(64) void ms_projective_kernel(const MsParams p) {
+  const int lane = int(threadIdx.x);
+  const int r = lane >> 4, c = lane & 15;
+  const int col_tiles = (p.m + 15) / 16;
+  const int64_t batch = int64_t(blockIdx.x) / col_tiles;
+  const int ct = int(int64_t(blockIdx.x) % col_tiles);
+  const int n = p.n, m = p.m, cc = ct * 16 + c;
+  int64_t off[3];
+  index_offsets(p.batch, batch, off);
+  const int64_t T = p.T;
+  const int64_t t0 = p.reverse ? T - 1 : 0;  // time of scan position 0
+  const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
+  const int64_t tb = p.reverse ? -p.t_stride[MS_B] : p.t_stride[MS_B];
+  const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
+  const TIn* a0 = static_cast<const TIn*>(p.a) + off[MS_A] + t0 * p.t_stride[MS_A];
+  const TIn* b0 = static_cast<const TIn*>(p.b) + off[MS_B] + t0 * p.t_stride[MS_B];
+  TOut* o0 = static_cast<TOut*>(p.out) + off[MS_OUT] + t0 * p.t_stride[MS_OUT];
+  constexpr int K = 4;  // steps whose operands are in flight
+  ARow<TIn> A[K];
+  BCol<TIn> B[K];
+  auto load = [&](int64_t q, int u) {  // clamped position: every load is valid, none behind a branch
+    const int64_t qc = q < T ? q : T - 1;
+    A[u] = load_a<TIn, VEC>(a0 + qc * ta, n, r, c);
+    B[u] = load_b(b0 + qc * tb, n, m, r, cc);
+  };
+#pragma unroll
+  for (int u = 0; u < K; ++u) load(u, u);
+  f32x4 P = identity_d(r, c), h = zero4();
+  for (int64_t q0 = 0; q0 < T; q0 += K) {
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const int64_t q = q0 + u;
+      if (q < T) {  // wave-uniform
+        const f32x4 av = A[u].get();
+        P = mfma_16x16x16(av, P, zero4());
+        h = mfma_16x16x16(av, h, B[u].get());
+        const float big = wave_max_abs(P);
+        const float inv = big > 0.0f ? 1.0f / big : 1.0f;
+        P *= inv;
+        h *= inv;
+        store_h(o0 + q * to, h, n, m, r, cc);
+      }
+      load(q0 + u + K, u);
+    }
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t count) {
   const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < count) p[i] = 0u;
@@ -1332,6 +1408,32 @@ size_t matrix_scan_workspace(const MsParams& p) {
   const UnitPlan up = unit_plan(p, pipe_shape ? kLeadCompute * kSteps : kWaves * kSteps);
   if (up.num_units > 0x7fffffffull) return 0;  // beyond 32-bit unit ids: the serial kernel takes it
   return up.total;
+}
+
+hipError_t launch_matrix_scan_projective(const MsParams& p, hipStream_t stream) {
+  if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;
+  const int64_t blocks = p.num_batch * ((p.m + 15) / 16);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // whole 16-byte (f32) or 8-byte (bf16) rows of a for n = 16 with aligned steps
+  const int64_t va = 4 * int64_t(p.in_bf16 ? 2 : 4);
+  bool vec = p.n == 16 && reinterpret_cast<uintptr_t>(p.a) % uintptr_t(va) == 0 &&
+             (p.t_stride[MS_A] * (va / 4)) % va == 0;
+  for (int d = 0; d < p.batch.nd && vec; ++d) vec = (p.batch.st[MS_A][d] * (va / 4)) % va == 0;
+  const dim3 grid{unsigned(blocks)}, block{64};
+  auto go = [&](auto tin, auto tout) {
+    using TI = decltype(tin);
+    using TO = decltype(tout);
+    if (vec) hipLaunchKernelGGL((ms_projective_kernel<TI, TO, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((ms_projective_kernel<TI, TO, false>), grid, block, 0, stream, p);
+  };
+  if (p.in_bf16) {
+    if (p.out_bf16) go(uint16_t{}, uint16_t{});
+    else go(uint16_t{}, float{});
+  } else {
+    if (p.out_bf16) go(float{}, uint16_t{});
+    else go(float{}, float{});
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {

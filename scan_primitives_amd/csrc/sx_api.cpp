@@ -426,8 +426,6 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
   int64_t numel = 0;
   sx_status st = plan_matrix_scan(a_rank, a_shape, a_strides, b_rank, b_shape, b_strides, axis, &p, shp, &r, &numel);
   if (st != SX_OK) return st;
-  if (projective)
-    return fail(SX_E_UNSUPPORTED, "matrix-scan: :projective true is not provided by this library");
   if (numel == 0) return ok();
   if (!a) return fail(SX_E_DIM_003, "matrix-scan: a %s %s is NULL; a tensor was expected",
                       shape_str(a_rank, a_shape).c_str(), dtype_name(dtype));
@@ -450,6 +448,16 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
   if (bnumel > 0) {
     span_bytes(b, b_rank, b_shape, bst, esz, &lo, &hi);
     if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "matrix-scan: out overlaps b");
+  }
+  if (projective) {  // no workspace
+    p.in_bf16 = dtype == SX_BF16;
+    p.out_bf16 = out_dtype == SX_BF16;
+    p.reverse = reverse ? 1 : 0;
+    p.a = a;
+    p.b = b;
+    p.out = out;
+    return device_status(sx::launch_matrix_scan_projective(p, static_cast<hipStream_t>(stream)),
+                         "matrix-scan :projective launch");
   }
   const size_t need = sx::matrix_scan_workspace(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))

@@ -105,6 +105,8 @@ struct MsParams {
 };
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
+// :projective (no workspace): the running product's largest entry divides P and h every step.
+hipError_t launch_matrix_scan_projective(const MsParams& p, hipStream_t stream);
 size_t matrix_scan_workspace(const MsParams& p);
 
 // ---------------------------------------------------------------- matrix-scan gradient

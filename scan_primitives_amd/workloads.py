@@ -129,14 +129,17 @@ def make_max_plus(shape=(64, 4096, 256), axis=1, reverse=True, seed=3) -> Worklo
 
 
 def make_matrix(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, reverse=False, seed=4,
-                noise=0.01, out_dtype=None) -> Workload:
+                noise=0.01, out_dtype=None, projective=False) -> Workload:
     g = _gen(seed)
     eye = torch.eye(n)
     a = 0.9 * eye + noise * torch.randn((B, T, n, n), generator=g)
     b = torch.randn((B, T, n, m), generator=g)
     a, b = a.to(dtype), b.to(dtype)
     name = f"matrix-scan {str(dtype).replace('torch.', '')} [{B},{T}] n={n} m={m}{' reverse' if reverse else ''}"
-    return Workload(name, "matrix_scan", {"a": a, "b": b}, axis=axis, reverse=reverse, out_dtype=out_dtype)
+    if projective:
+        name = name.replace("matrix-scan", "matrix-scan :projective")
+    return Workload(name, "matrix_scan", {"a": a, "b": b}, axis=axis, reverse=reverse, out_dtype=out_dtype,
+                    meta={"projective": projective})
 
 
 def make_linear(shape=(64, 4096, 256), axis=1, reverse=False, dtype=torch.float32, a_kind="decay",
@@ -206,9 +209,11 @@ def make_element_grad(w: Workload, seed: int) -> Workload:
 def extra_workloads() -> list[Workload]:
     """Timed beside the step, not part of it: linear-scan and cumsum on the
     max-plus shape, [64,4096,256] along axis 1, f32; the gradients of the two
-    matrix workloads and of the three element-scan workloads."""
+    matrix workloads and of the three element-scan workloads; the f32 matrix
+    workload with :projective."""
     return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7),
             make_matrix_grad(32, 8192, 16, 1, torch.float32, reverse=False, seed=4),
             make_matrix_grad(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5),
             make_element_grad(make_tanh(), seed=11), make_element_grad(make_norm_cap(), seed=12),
-            make_element_grad(make_max_plus(), seed=13)]
+            make_element_grad(make_max_plus(), seed=13),
+            make_matrix(32, 8192, 16, 1, torch.float32, seed=4, projective=True)]

@@ -129,7 +129,7 @@ def _ms(lib, a_shape=(2, 5, 4, 4), b_shape=(2, 5, 4, 3), dtype=B.SX_F32, out_dty
     (dict(a=None), B.SX_E_DIM_003),
     (dict(b=None), B.SX_E_DIM_003),
     (dict(out=None), B.SX_E_DIM_003),
-    (dict(projective=1), B.SX_E_UNSUPPORTED),
+    (dict(projective=1, out=None), B.SX_E_DIM_003),                         # :projective checks the same
     (dict(a_strides=(80, 16, 1, 4)), B.SX_E_UNSUPPORTED),                    # transposed matrix dims
     (dict(out=FAKE + 64), B.SX_E_ALIAS),
 ])
