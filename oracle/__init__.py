@@ -36,6 +36,10 @@ Sources, all from the SexpGPU documentation pages:
   section: a gradient has the shape (and dtype) of the tensor it is taken
   with respect to, so a broadcast operand's gradient sums over the dims it
   was broadcast along.
+* "Tensor operations", the "table-scan" section: a deterministic automaton
+  ``state = table[previous, symbol]`` along one axis from ``start``; an
+  out-of-range symbol or reached entry is refused on the CPU and clamped on
+  the GPU (both are here; the GPU's is the default).
 * "Tensor operations", the "matrix-scan" section, on the prelude's
   ``linear-scan``: the same recurrence over one-by-one matrices, taking ``a``
   and ``b`` (numbers included) broadcast to one shape; ``cumsum`` is built on
@@ -64,7 +68,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["element_scan", "element_scan_vjp", "matrix_scan", "matrix_scan_projective", "matrix_scan_vjp",
-           "linear_scan", "cumsum", "BODIES"]
+           "linear_scan", "cumsum", "table_scan", "BODIES"]
 
 
 # --- element-scan bodies ----------------------------------------------------
@@ -416,6 +420,53 @@ def matrix_scan_vjp(a, b, g, axis=0, reverse=False, dtype=np.float64):
     grad_a = _sum_to_shape(np.moveaxis(grad_a, 0, ax), a.shape)
     grad_b = _sum_to_shape(np.moveaxis(lam, 0, ax), b.shape)
     return grad_a, grad_b
+
+
+def table_scan(table, symbols, axis=-1, start=0, clamp=True):
+    """Run a deterministic automaton the plain way, one symbol at a time.
+
+    ``table`` is ``[states, symbols]`` of integers and ``symbols`` any shape of
+    integers; along ``axis`` (the last by default) the state after each
+    symbol is ``table[previous, symbol]``, from ``start`` (0 by default).
+    Returns every state, in ``symbols``' shape (int32).
+
+    Out-of-range values: with ``clamp`` (the GPU reading) a symbol is clamped
+    into ``[0, symbols)`` and a table entry the run reaches into
+    ``[0, states)``; without it, either raises ``ValueError`` (the CPU
+    reading).
+
+    Follows "Tensor operations", the "table-scan" section.
+    """
+    table = np.asarray(table)
+    symbols = np.asarray(symbols)
+    if not (np.issubdtype(table.dtype, np.integer) and np.issubdtype(symbols.dtype, np.integer)):
+        raise TypeError("table_scan: table and symbols are integers")
+    if table.ndim != 2 or table.shape[0] < 1 or table.shape[1] < 1:
+        raise ValueError("table_scan: the table is [states, symbols] with at least one of each")
+    n_states, n_syms = table.shape
+    if symbols.ndim < 1:
+        raise ValueError("table_scan: symbols need at least one axis")
+    ax = axis + symbols.ndim if axis < 0 else axis
+    if not 0 <= ax < symbols.ndim:
+        raise ValueError(f"table_scan: axis {axis} out of range for rank {symbols.ndim}")
+    if not 0 <= start < n_states:
+        raise ValueError(f"table_scan: start {start} is not a state")
+    sym_t = np.moveaxis(symbols, ax, 0).astype(np.int64)
+    out = np.empty(sym_t.shape, dtype=np.int32)
+    state = np.full(sym_t.shape[1:], start, dtype=np.int64)
+    for t in range(sym_t.shape[0]):
+        x = sym_t[t]
+        if clamp:
+            x = np.clip(x, 0, n_syms - 1)
+        elif np.any((x < 0) | (x >= n_syms)):
+            raise ValueError("table_scan: a symbol is outside [0, symbols)")
+        state = table[state, x].astype(np.int64)
+        if clamp:
+            state = np.clip(state, 0, n_states - 1)
+        elif np.any((state < 0) | (state >= n_states)):
+            raise ValueError("table_scan: the run reached a table entry outside [0, states)")
+        out[t] = state
+    return np.moveaxis(out, 0, ax)
 
 
 def linear_scan(a, b, axis=0, reverse=False, dtype=np.float64):

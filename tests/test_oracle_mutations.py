@@ -412,3 +412,45 @@ def test_unmutated_projective_passes_its_pins():
     rng = np.random.default_rng(6)
     a, b = rng.normal(size=(2, 7, 3, 3)), rng.normal(size=(2, 7, 3, 2))
     np.testing.assert_allclose(_proj_mutant("none")(a, b, axis=1), _real_proj(a, b, axis=1), rtol=1e-15)
+
+
+_real_ts = oracle.table_scan
+
+
+def _ts_transposed(table, symbols, axis=-1, start=0, clamp=True):
+    table = np.asarray(table)
+    if table.shape[0] != table.shape[1]:
+        return _real_ts(table, symbols, axis, start, clamp)  # (only square tables can be swapped)
+    return _real_ts(table.T.copy(), symbols, axis, start, clamp)
+
+
+def _ts_state_before(table, symbols, axis=-1, start=0, clamp=True):
+    # stores the state before each symbol instead of after it
+    out = _real_ts(table, symbols, axis, start, clamp)
+    ax = axis % np.ndim(symbols)
+    shifted = np.roll(out, 1, axis=ax)
+    idx = [slice(None)] * out.ndim
+    idx[ax] = 0
+    shifted[tuple(idx)] = start
+    return shifted
+
+
+def _ts_ignores_start(table, symbols, axis=-1, start=0, clamp=True):
+    return _real_ts(table, symbols, axis, 0, clamp)
+
+
+TS_PINS = [
+    (pins.test_table_scan_parity_example_is_running_xor, {}),
+    (pins.test_table_scan_counter_mod_k_is_cumsum_mod_k, {"k": 7}),
+    (pins.test_table_scan_small_hand_run, {}),
+]
+
+
+@pytest.mark.parametrize("mutant", [_ts_transposed, _ts_state_before, _ts_ignores_start])
+def test_table_scan_mutants_are_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "table_scan", mutant)
+    assert _some_pin_fails(TS_PINS), f"no table-scan pin caught {mutant.__name__}"
+
+
+def test_unmutated_table_scan_passes_its_pins():
+    assert not _some_pin_fails(TS_PINS)

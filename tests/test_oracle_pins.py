@@ -796,3 +796,74 @@ def test_projective_zero_product_divides_by_one():
     a = np.zeros((4, 2, 2))
     b = np.arange(16, dtype=float).reshape(4, 2, 2)
     np.testing.assert_array_equal(oracle.matrix_scan_projective(a, b, axis=0), b)
+
+
+# ---------------------------------------------------------------- table-scan
+#
+# "Tensor operations", the "table-scan" section: state = table[previous, symbol]
+# along one axis from :start; the page's example is the parity automaton.
+
+
+def test_table_scan_parity_example_is_running_xor():
+    # the page's example: flip = [[0 1] [1 0]] over bits gives the parity so far
+    rng = _rng(101)
+    bits = rng.integers(0, 2, size=(5, 200)).astype(np.int32)
+    got = oracle.table_scan(np.array([[0, 1], [1, 0]], dtype=np.int32), bits)
+    np.testing.assert_array_equal(got, np.cumsum(bits, axis=-1) % 2)
+    assert got.dtype == np.int32 and got.shape == bits.shape
+
+
+@pytest.mark.parametrize("k", [3, 7, 16])
+def test_table_scan_counter_mod_k_is_cumsum_mod_k(k):
+    # table[s, x] = (s + x) mod k from start s0: the states are (s0 + running sum) mod k, along any axis
+    rng = _rng(102)
+    table = (np.arange(k)[:, None] + np.arange(k)[None, :]) % k
+    sym = rng.integers(0, k, size=(4, 30, 6)).astype(np.int32)
+    for axis in (0, 1, -1):
+        got = oracle.table_scan(table.astype(np.int32), sym, axis=axis, start=2)
+        np.testing.assert_array_equal(got, (2 + np.cumsum(sym, axis=axis)) % k)
+
+
+def test_table_scan_identity_reset_and_composition():
+    rng = _rng(103)
+    sym = rng.integers(0, 5, size=(3, 40)).astype(np.int32)
+    stay = np.repeat(np.arange(4)[:, None], 5, axis=1).astype(np.int32)   # table[s, x] = s
+    np.testing.assert_array_equal(oracle.table_scan(stay, sym, start=3), np.full(sym.shape, 3))
+    reset = np.repeat((np.arange(5) % 4)[None, :], 4, axis=0).astype(np.int32)  # table[s, x] = x mod 4
+    np.testing.assert_array_equal(oracle.table_scan(reset, sym), sym % 4)
+    # running the second half from the last state of the first half continues the run
+    table = rng.integers(0, 6, size=(6, 5)).astype(np.int32)
+    whole = oracle.table_scan(table, sym)
+    first = oracle.table_scan(table, sym[:, :17])
+    for row in range(3):
+        rest = oracle.table_scan(table, sym[row:row + 1, 17:], start=int(first[row, -1]))
+        np.testing.assert_array_equal(whole[row:row + 1, 17:], rest)
+
+
+def test_table_scan_small_hand_run():
+    # a 3-state automaton traced by hand: table rows are states, columns symbols
+    table = np.array([[1, 2], [0, 0], [2, 1]], dtype=np.int32)
+    sym = np.array([0, 1, 1, 0, 1], dtype=np.int32)
+    # from 0: t[0,0]=1, t[1,1]=0, t[0,1]=2, t[2,0]=2, t[2,1]=1
+    np.testing.assert_array_equal(oracle.table_scan(table, sym), [1, 0, 2, 2, 1])
+    # a square table that is not symmetric: rows (the state) and columns (the symbol) cannot be swapped
+    table = np.array([[1, 0, 0], [2, 2, 0], [1, 1, 1]], dtype=np.int32)
+    # from 0: t[0,1]=0, t[0,0]=1, t[1,2]=0, t[0,1]=0
+    np.testing.assert_array_equal(oracle.table_scan(table, np.array([1, 0, 2, 1], dtype=np.int32)), [0, 1, 0, 0])
+
+
+def test_table_scan_out_of_range_clamped_or_refused():
+    table = np.array([[1, 5], [0, -2]], dtype=np.int32)   # entries 5 and -2 are not states
+    sym = np.array([[0, 7, -1, 1, 1]], dtype=np.int32)
+    # clamped (GPU reading): symbols 7 -> 1, -1 -> 0; reached entries 5 -> 1, -2 -> 0
+    # from 0: t[0,0]=1; t[1,clamp 7=1]=-2 -> 0; t[0,clamp -1=0]=1; t[1,1]=-2 -> 0; t[0,1]=5 -> 1
+    np.testing.assert_array_equal(oracle.table_scan(table, sym), [[1, 0, 1, 0, 1]])
+    with pytest.raises(ValueError):
+        oracle.table_scan(table, sym, clamp=False)
+    with pytest.raises(ValueError):
+        oracle.table_scan(table, np.array([0, 1]), clamp=False)  # reaches 5 at the second symbol
+    for bad in (dict(start=2), dict(axis=1)):
+        with pytest.raises(ValueError):
+            oracle.table_scan(table, np.array([0, 1]), **bad)
+    with pytest.raises(ValueError):
+        oracle.table_scan(np.zeros((2, 0), dtype=np.int32), np.array([0]))
