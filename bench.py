@@ -21,7 +21,8 @@ single calls, each after a 512 MiB write that evicts the last-level cache
 fraction of the 8 TB/s HBM peak.
 
 linear-scan and cumsum ([64,4096,256] f32 along axis 1), the gradients of
-the five workloads and the f32 matrix workload with :projective are timed the same two ways and reported in
+the five workloads, the f32 matrix workload with :projective and table-scan
+on [4096,16384] int32 symbols are timed the same two ways and reported in
 ``per_config`` with ``"in_step": false``; they are not part of the step or
 of ``value`` (``--no-extra`` skips them).
 
@@ -172,6 +173,8 @@ def main() -> int:
         if w.op == "matrix_scan_backward":
             return sx.matrix_scan_backward(t["a"], tuple(t["b"].shape), t["h"], t["g"], axis=w.axis,
                                            reverse=w.reverse)
+        if w.op == "table_scan":
+            return sx.table_scan(t["table"], t["symbols"], axis=w.axis, start=w.meta.get("start", 0))
         if w.op == "element_scan_backward":
             return sx.element_scan_backward(w.body, t["initial"], [t["x"], t["s"]], t["h"], t["g"], axis=w.axis,
                                             state_axis=w.state_axis, reverse=w.reverse)

@@ -15,6 +15,8 @@
  *                 broadcast leading dims.
  *   matrix-scan gradient  the same section and "gradient": the adjoint scan
  *                 in the other direction on a's transposes, then grad_a.
+ *   table-scan    "Tensor operations", the "table-scan" section: a
+ *                 deterministic automaton over int32 symbols.
  *   linear-scan   the same section: matrix-scan over one-by-one matrices,
  *                 a and b broadcast to one shape (cumsum: a = 1).
  *
@@ -303,6 +305,33 @@ sx_status sx_linear_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
  * entries) and returns its rank, or -1 for shapes that do not fit. */
 int sx_linear_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
                              int64_t* out_shape);
+
+/*
+ * sx_table_scan: "Tensor operations", the "table-scan" section.
+ *
+ * Runs a deterministic automaton along `axis` of `symbols`: the state after
+ * each symbol is table[previous, symbol], from state `start`; out holds every
+ * state, in symbols' shape. A symbol outside [0, nsym) is clamped into that
+ * range, and so is a table entry the run reaches outside [0, states), as the
+ * pages' GPU backend does (their CPU backend refuses them instead). States
+ * have no gradient.
+ *
+ *  states, nsym  the table's shape [states, nsym], each at least 1 (E-DIM-001).
+ *  table         int32, row-major contiguous [states, nsym], device memory.
+ *  rank, shape, strides, symbols
+ *                int32 symbols, rank 1..SX_MAX_RANK; strides in elements (NULL
+ *                for contiguous).
+ *  axis          the scan axis; negative counts from the end (the pages'
+ *                default is -1). Out of range: E-DIM-001.
+ *  start         the first state; outside [0, states): E-DIM-001.
+ *  out           int32, contiguous, symbols' shape; must not overlap symbols
+ *                or the table (SX_E_ALIAS).
+ *
+ * No workspace. Symbols with no elements return SX_OK without launching.
+ */
+sx_status sx_table_scan(int states, int nsym, const int32_t* table, int rank, const int64_t* shape,
+                        const int64_t* strides, const int32_t* symbols, int axis, int32_t start, int32_t* out,
+                        void* stream);
 
 /* "E-DIM-001" etc. for a status; "OK" for SX_OK. Static storage. */
 const char* sx_status_name(sx_status status);

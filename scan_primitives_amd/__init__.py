@@ -1,4 +1,4 @@
-"""MI355X-native scan primitives: element-scan, matrix-scan and linear-scan on gfx950.
+"""MI355X-native scan primitives: element-scan, matrix-scan, linear-scan and table-scan on gfx950.
 
 The computation lives in ``libsx_scan.so`` (hand-written HIP kernels behind
 the C ABI in ``include/sx_scan.h``); this package is its Python binding.
@@ -6,8 +6,8 @@ PyTorch provides device memory and streams.
 """
 
 from ._binding import (BODIES, SxError, cumsum, element_scan, element_scan_backward, linear_scan, load_library,
-                       matrix_scan, matrix_scan_backward)
+                       matrix_scan, matrix_scan_backward, table_scan)
 
 __all__ = ["BODIES", "SxError", "element_scan", "element_scan_backward", "matrix_scan", "matrix_scan_backward",
-           "linear_scan", "cumsum", "load_library"]
+           "linear_scan", "cumsum", "table_scan", "load_library"]
 __version__ = "0.1.0"

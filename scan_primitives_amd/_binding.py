@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             c_int, c_int, c_int, vp, vp, vp, c_size, vp]
     lib.sx_matrix_scan_backward_workspace_bytes.restype = c_size
     lib.sx_matrix_scan_backward_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int, c_int]
+    lib.sx_table_scan.restype = c_int
+    lib.sx_table_scan.argtypes = [c_int, c_int, vp, c_int, _i64p, _i64p, vp, c_int, ctypes.c_int32, vp, vp]
     lib.sx_linear_scan.restype = c_int
     lib.sx_linear_scan.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
                                    c_int, c_int, c_int, vp, vp]
@@ -349,6 +351,31 @@ def linear_scan(a, b, axis: int = 0, reverse: bool = False, out_dtype=None) -> t
             _DTYPES[ta.dtype], ta.dim(), a_shape, i64_array(ta.stride()), ta.data_ptr(),
             tb.dim(), b_shape, i64_array(tb.stride()), tb.data_ptr(),
             axis, 1 if reverse else 0, _DTYPES[out_dtype], out.data_ptr(), _stream_handle(ref.device))
+    _check(status)
+    return out
+
+
+def table_scan(table: torch.Tensor, symbols: torch.Tensor, axis: int = -1, start: int = 0) -> torch.Tensor:
+    """Deterministic automaton on the GPU: along ``axis`` the state after each
+    symbol is ``table[previous, symbol]``, from ``start``. ``table`` is
+    ``[states, symbols]``, both int32; returns every state (int32, symbols'
+    shape). Out-of-range symbols and reached entries are clamped into range."""
+    _require_device_tensor("table", table)
+    _require_device_tensor("symbols", symbols)
+    if table.dtype != torch.int32 or symbols.dtype != torch.int32:
+        raise SxError(SX_E_DIM_002, f"table-scan: table is {table.dtype} and symbols {symbols.dtype}; both must be "
+                                    ":i32")
+    if table.dim() != 2:
+        raise SxError(SX_E_DIM_001, f"table-scan: the table must be [states symbols], got {tuple(table.shape)}")
+    if table.device != symbols.device:
+        raise SxError(SX_E_UNSUPPORTED, "table-scan: operands on different devices")
+    table = table.contiguous()
+    lib = load_library()
+    out = torch.empty(tuple(symbols.shape), dtype=torch.int32, device=symbols.device)
+    with torch.cuda.device(symbols.device):
+        status = lib.sx_table_scan(int(table.shape[0]), int(table.shape[1]), table.data_ptr(), symbols.dim(),
+                                   i64_array(symbols.shape), i64_array(symbols.stride()), symbols.data_ptr(),
+                                   axis, int(start), out.data_ptr(), _stream_handle(symbols.device))
     _check(status)
     return out
 

@@ -803,6 +803,64 @@ sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape,
   return ok();
 }
 
+// ------------------------------------------------------------------ table-scan
+
+sx_status sx_table_scan(int states, int nsym, const int32_t* table, int rank, const int64_t* shape,
+                        const int64_t* strides, const int32_t* symbols, int axis, int32_t start, int32_t* out,
+                        void* stream) {
+  if (states < 1 || nsym < 1)
+    return fail(SX_E_DIM_001, "table-scan: the table is [states symbols] with at least one of each, got [%d %d]",
+                states, nsym);
+  if (rank > sx::kMaxRank) return fail(SX_E_UNSUPPORTED, "table-scan: rank %d exceeds %d", rank, sx::kMaxRank);
+  if (rank < 1 || shape == nullptr) return fail(SX_E_DIM_001, "table-scan: symbols need at least one axis");
+  int64_t numel = 0;
+  if (!checked_numel(rank, shape, &numel))
+    return fail(SX_E_DIM_001, "table-scan: bad symbols shape %s", shape_str(rank, shape).c_str());
+  const int ax = axis < 0 ? axis + rank : axis;
+  if (ax < 0 || ax >= rank)
+    return fail(SX_E_DIM_001, "table-scan: axis %d out of range for symbols %s :i32", axis,
+                shape_str(rank, shape).c_str());
+  if (start < 0 || start >= states)
+    return fail(SX_E_DIM_001, "table-scan: :start %d is not a state of a [%d %d] table", int(start), states, nsym);
+  if (numel == 0) return ok();
+  if (!table) return fail(SX_E_DIM_003, "table-scan: table is NULL; a tensor was expected");
+  if (!symbols) return fail(SX_E_DIM_003, "table-scan: symbols is NULL; a tensor was expected");
+  if (!out) return fail(SX_E_DIM_003, "table-scan: out is NULL; a tensor was expected");
+  int64_t xs[sx::kMaxRank], os[sx::kMaxRank];
+  if (strides) std::copy(strides, strides + rank, xs); else contiguous_strides(rank, shape, xs);
+  contiguous_strides(rank, shape, os);
+  uintptr_t lo, hi;
+  const uintptr_t olo = reinterpret_cast<uintptr_t>(out), ohi = olo + uintptr_t(numel) * 4;
+  span_bytes(symbols, rank, shape, xs, 4, &lo, &hi);
+  if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "table-scan: out overlaps symbols");
+  const uintptr_t tlo = reinterpret_cast<uintptr_t>(table), thi = tlo + uintptr_t(int64_t(states) * nsym) * 4;
+  if (overlaps(olo, ohi, tlo, thi)) return fail(SX_E_ALIAS, "table-scan: out overlaps the table");
+
+  sx::TsParams p{};
+  p.T = shape[ax];
+  p.t_stride[0] = xs[ax];
+  p.t_stride[1] = os[ax];
+  int64_t dims[sx::kMaxRank];
+  int64_t st[2][sx::kMaxRank];
+  int nd = 0;
+  for (int i = 0; i < rank; ++i) {
+    if (i == ax) continue;
+    dims[nd] = shape[i];
+    st[0][nd] = xs[i];
+    st[1][nd] = os[i];
+    ++nd;
+  }
+  p.seqs = make_index_map<2>(nd, dims, st);
+  p.num_seq = numel / p.T;
+  p.states = states;
+  p.nsym = nsym;
+  p.start = start;
+  p.table = table;
+  p.symbols = symbols;
+  p.out = out;
+  return device_status(sx::launch_table_scan(p, static_cast<hipStream_t>(stream)), "table-scan launch");
+}
+
 // ------------------------------------------------------------------ linear-scan
 
 // a and b broadcast (NumPy: right-aligned, each dim equal or 1; rank 0 is a

@@ -77,6 +77,25 @@ struct EsVjpParams {
 };
 hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipStream_t stream);
 
+// ---------------------------------------------------------------- table-scan
+
+constexpr int kTsMaxSymbolsWave = 4096;   // per-symbol maps in LDS (8 bytes each) for tables of <= 16 states
+constexpr int kTsMaxTableLds = 12288;     // the serial kernel keeps a table of up to 48 KB in LDS
+
+// A sequence is every index of `symbols` but the axis (offsets of symbols, out).
+struct TsParams {
+  IndexMap<2> seqs;
+  int64_t num_seq;
+  int64_t T;             // symbols along the axis
+  int64_t t_stride[2];   // along the axis: symbols, out (elements)
+  int states, nsym;      // table is [states, nsym], row-major
+  int start;
+  const int32_t* table;
+  const int32_t* symbols;
+  int32_t* out;
+};
+hipError_t launch_table_scan(const TsParams& p, hipStream_t stream);
+
 // linear-scan runs on the element-scan kernels: b as the sequence x, a as the
 // second sequence s, init == nullptr (every lane starts from zero), and the
 // trip h -> a * h + b, a body of the library's own beside the public three.

@@ -33,7 +33,7 @@ import torch
 @dataclass
 class Workload:
     name: str
-    op: str                      # "element_scan", "matrix_scan", "matrix_scan_backward" or "linear_scan"
+    op: str                      # "element_scan", "matrix_scan", "matrix_scan_backward", "linear_scan", ...
     tensors: dict                # host tensors, in the order the op takes them
     axis: int = 1
     reverse: bool = False
@@ -59,6 +59,8 @@ class Workload:
             return tuple(t["a"].shape)
         if self.op == "element_scan_backward":  # the outputs are the gradients of initial, x and s
             return tuple(t["x"].shape)
+        if self.op == "table_scan":
+            return tuple(t["symbols"].shape)
         lead = torch.broadcast_shapes(t["a"].shape[:-2], t["b"].shape[:-2])
         return tuple(lead) + tuple(t["b"].shape[-2:])
 
@@ -71,7 +73,7 @@ class Workload:
 
     @property
     def out_elem_bytes(self) -> int:
-        if self.op == "element_scan":
+        if self.op in ("element_scan", "table_scan"):
             return 4
         dt = self.out_dtype or self.tensors["b"].dtype
         return torch.tensor([], dtype=dt).element_size()
@@ -198,6 +200,24 @@ def make_matrix_grad(B=32, T=8192, n=16, m=1, dtype=torch.float32, axis=1, rever
                     reverse=reverse)
 
 
+def make_table(kind="parity", B=4096, T=16384, axis=-1, start=0, seed=8) -> Workload:
+    """table-scan inputs, int32: "parity" is the pages' example (table
+    [[0 1] [1 0]] over bits, 0 and 1 with equal odds); "dfa16" a random
+    automaton of 16 states over 16 symbols, table entries and symbols
+    uniform."""
+    g = _gen(seed)
+    if kind == "parity":
+        table = torch.tensor([[0, 1], [1, 0]], dtype=torch.int32)
+        symbols = torch.randint(0, 2, (B, T), generator=g, dtype=torch.int32)
+    elif kind == "dfa16":
+        table = torch.randint(0, 16, (16, 16), generator=g, dtype=torch.int32)
+        symbols = torch.randint(0, 16, (B, T), generator=g, dtype=torch.int32)
+    else:
+        raise ValueError(f"unknown kind {kind!r}")
+    return Workload(f"table-scan {kind} [{B},{T}]", "table_scan", {"table": table, "symbols": symbols}, axis=axis,
+                    meta={"start": start})
+
+
 def make_element_grad(w: Workload, seed: int) -> Workload:
     """The gradient of an element-scan workload: its tensors and g ~ N(0,1) of
     the result's shape."""
@@ -210,10 +230,12 @@ def extra_workloads() -> list[Workload]:
     """Timed beside the step, not part of it: linear-scan and cumsum on the
     max-plus shape, [64,4096,256] along axis 1, f32; the gradients of the two
     matrix workloads and of the three element-scan workloads; the f32 matrix
-    workload with :projective."""
+    workload with :projective; table-scan on [4096,16384] int32 symbols (the
+    parity automaton and a random 16-state one)."""
     return [make_linear(a_kind="decay", seed=6), make_linear(a_kind="ones", seed=7),
             make_matrix_grad(32, 8192, 16, 1, torch.float32, reverse=False, seed=4),
             make_matrix_grad(16, 16384, 16, 16, torch.bfloat16, reverse=True, seed=5),
             make_element_grad(make_tanh(), seed=11), make_element_grad(make_norm_cap(), seed=12),
             make_element_grad(make_max_plus(), seed=13),
-            make_matrix(32, 8192, 16, 1, torch.float32, seed=4, projective=True)]
+            make_matrix(32, 8192, 16, 1, torch.float32, seed=4, projective=True),
+            make_table("parity", seed=8), make_table("dfa16", seed=9)]

@@ -20,6 +20,8 @@ def run_gpu(w, dev):
     if w.op == "element_scan":
         return sx.element_scan(w.body, t["initial"], [t["x"], t["s"]], axis=w.axis, state_axis=w.state_axis,
                                reverse=w.reverse)
+    if w.op == "table_scan":
+        return sx.table_scan(t["table"], t["symbols"], axis=w.axis, start=w.meta.get("start", 0))
     if w.op == "linear_scan":
         a = t["a"] if "a" in t else w.meta["a_number"]
         return sx.linear_scan(a, t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype)

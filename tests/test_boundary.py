@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
     for required in ("sx_element_scan", "sx_matrix_scan", "sx_element_scan_workspace_bytes",
                      "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_linear_scan",
                      "sx_linear_scan_out_shape", "sx_matrix_scan_backward", "sx_matrix_scan_backward_workspace_bytes",
-                     "sx_element_scan_backward", "sx_element_scan_backward_workspace_bytes",
+                     "sx_element_scan_backward", "sx_element_scan_backward_workspace_bytes", "sx_table_scan",
                      "sx_status_name", "sx_last_error", "sx_version"):
         assert required in names
 
@@ -251,6 +251,42 @@ def test_element_scan_backward_workspace_query(lib):
     assert need >= 8 * 1024 * 16 * 16 * 4 and need % 256 == 0   # the width-1 gate's full-width gradient
     assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == 0
     assert q(2, 3, B.i64_array([4, 8, 3]), 5, B.SX_STATE_SCALAR, 3, 3) == 0  # invalid axis
+
+
+def _ts(lib, states=3, nsym=4, table=FAKE, shape=(5, 9), symbols=FAKE + (1 << 20), axis=-1, start=0,
+        out=FAKE + (2 << 20)):
+    st = lib.sx_table_scan(states, nsym, table, len(shape), B.i64_array(shape), None, symbols, axis, start, out, None)
+    return st, lib.sx_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(nsym=0), B.SX_E_DIM_001),                          # a table with no symbols
+    (dict(states=0), B.SX_E_DIM_001),
+    (dict(axis=2), B.SX_E_DIM_001),
+    (dict(axis=-3), B.SX_E_DIM_001),
+    (dict(start=3), B.SX_E_DIM_001),                         # :start is not a state
+    (dict(start=-1), B.SX_E_DIM_001),
+    (dict(shape=()), B.SX_E_DIM_001),
+    (dict(table=None), B.SX_E_DIM_003),
+    (dict(symbols=None), B.SX_E_DIM_003),
+    (dict(out=None), B.SX_E_DIM_003),
+    (dict(out=FAKE + (1 << 20) + 8), B.SX_E_ALIAS),         # out over symbols
+    (dict(out=FAKE + 4), B.SX_E_ALIAS),                      # out over the table
+])
+def test_table_scan_rejects_on_host(lib, kwargs, code):
+    st, msg = _ts(lib, **kwargs)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_table_scan_empty_is_a_no_op(lib):
+    assert _ts(lib, shape=(5, 0), table=None, symbols=None, out=None)[0] == B.SX_OK
+
+
+def test_table_scan_binding_checks_dtypes():
+    with pytest.raises(sx.SxError) as e:
+        sx.table_scan(torch.zeros((2, 2), dtype=torch.int32), torch.zeros(5, dtype=torch.int32))
+    assert e.value.name == "E-UNSUPPORTED"  # host tensors
 
 
 def _ls(lib, a_shape=(3, 9, 5), b_shape=(3, 9, 5), dtype=B.SX_F32, out_dtype=B.SX_F32, axis=1, a=FAKE,
