@@ -79,7 +79,7 @@ hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipS
 
 // ---------------------------------------------------------------- table-scan
 
-constexpr int kTsMaxSymbolsWave = 4096;   // per-symbol maps in LDS (8 bytes each) for tables of <= 16 states
+constexpr int kTsMaxSymbolsWave = 2048;   // per-symbol maps in LDS (8 or 16 bytes each) for tables of <= 16 states
 constexpr int kTsMaxTableLds = 12288;     // the serial kernel keeps a table of up to 48 KB in LDS
 
 // A sequence is every index of `symbols` but the axis (offsets of symbols, out).

@@ -8,9 +8,11 @@
 //
 // Kernels here:
 //   ts_wave_kernel   tables of at most 16 states. One wave per sequence; a slab
-//                    of 64 * K steps gives each lane K consecutive steps. The
-//                    map of a step (state -> next state) is packed as sixteen
-//                    4-bit entries in a 64-bit word, one per symbol, in LDS.
+//                    of 64 * K steps gives each lane K consecutive steps
+//                    (slabs move between HBM and LDS coalesced). The
+//                    map of a step (state -> next state) is kept one byte per
+//                    state (8 or 16 bytes), one per symbol, in LDS, and maps
+//                    compose by byte gathers (v_perm_b32).
 //                    Each lane composes the maps of its K steps, a scan of the
 //                    lanes' maps (six rounds of composition over cross-lane
 //                    moves) gives each lane its entering state from the slab's
@@ -26,49 +28,112 @@
 namespace sx {
 namespace {
 
-constexpr int kTsK = 16;              // steps per lane per slab in ts_wave_kernel
-constexpr int64_t kTsSlab = 64 * kTsK;
-constexpr uint64_t kIdentityMap = 0xFEDCBA9876543210ull;  // nibble s holds s
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t nib(uint64_t m, uint32_t s) { return uint32_t(m >> (4 * s)) & 15u; }
+// A map of states (state -> next state) with one byte per state: MW 32-bit
+// words hold 4 * MW entries (MW = 2: up to 8 states, MW = 4: up to 16).
+// Entries past the table's states map to themselves and are never reached.
+template <int MW>
+struct StateMap {
+  uint32_t w[MW];
+};
 
-// The map "inner, then outer" over the first S states (the others stay fixed).
-__device__ __forceinline__ uint64_t compose(uint64_t outer, uint64_t inner, int S) {
-  uint64_t r = kIdentityMap;
-  for (int s = 0; s < S; ++s) {
-    const uint64_t img = nib(outer, nib(inner, uint32_t(s)));
-    r = (r & ~(uint64_t(15) << (4 * s))) | (img << (4 * s));
+template <int MW>
+__device__ __forceinline__ StateMap<MW> identity_map() {
+  StateMap<MW> m;
+#pragma unroll
+  for (int i = 0; i < MW; ++i) m.w[i] = 0x03020100u + 0x04040404u * uint32_t(i);
+  return m;
+}
+
+// "inner, then outer": entry s is outer[inner[s]], a byte gather. v_perm_b32
+// picks each result byte from the 8 bytes {src0 (high), src1 (low)} by the
+// selector byte (0-7). Sixteen entries take two gathers (entries 0-7 and
+// 8-15) and a byte select on bit 3 of the selector.
+template <int MW>
+__device__ __forceinline__ StateMap<MW> compose(const StateMap<MW>& outer, const StateMap<MW>& inner) {
+  StateMap<MW> r;
+  if constexpr (MW == 2) {
+    r.w[0] = __builtin_amdgcn_perm(outer.w[1], outer.w[0], inner.w[0]);
+    r.w[1] = __builtin_amdgcn_perm(outer.w[1], outer.w[0], inner.w[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sel = inner.w[j];
+      const uint32_t lo = __builtin_amdgcn_perm(outer.w[1], outer.w[0], sel & 0x07070707u);
+      const uint32_t hi = __builtin_amdgcn_perm(outer.w[3], outer.w[2], sel & 0x07070707u);
+      const uint32_t high = ((sel >> 3) & 0x01010101u) * 0xFFu;  // 0xFF in the bytes that select 8-15
+      r.w[j] = (hi & high) | (lo & ~high);
+    }
   }
   return r;
 }
 
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-  const int lo = __shfl_up(int(uint32_t(v)), d, 64);
-  const int hi = __shfl_up(int(uint32_t(v >> 32)), d, 64);
-  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+template <int MW>
+__device__ __forceinline__ uint32_t apply(const StateMap<MW>& m, uint32_t s) {  // m[s]
+  uint32_t w = m.w[0];
+#pragma unroll
+  for (int i = 1; i < MW; ++i) w = (s >> 2) == uint32_t(i) ? m.w[i] : w;
+  return (w >> (8 * (s & 3))) & 0xFFu;
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
-  return (uint64_t(hi) << 32) | lo;
+template <int MW>
+__device__ __forceinline__ StateMap<MW> shfl_up_map(const StateMap<MW>& m, int d) {
+  StateMap<MW> r;
+#pragma unroll
+  for (int i = 0; i < MW; ++i) r.w[i] = uint32_t(__shfl_up(int(m.w[i]), d, 64));
+  return r;
+}
+
+template <int MW>
+__device__ __forceinline__ StateMap<MW> readlane_map(const StateMap<MW>& m, int l) {
+  StateMap<MW> r;
+#pragma unroll
+  for (int i = 0; i < MW; ++i) r.w[i] = uint32_t(__builtin_amdgcn_readlane(int(m.w[i]), l));
+  return r;
 }
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// A slab of 64 K positions staged in LDS: position w sits at word w + 4 (w / 64).
+// Both access patterns are free of bank conflicts (K = 8 or 16): lane l
+// writing (or reading) 16 bytes at w = 256 j + 4 l for the coalesced global
+// side, and lane l reading (or writing) 16 bytes at w = K l + 4 j for its own
+// run of K positions.
+__device__ __forceinline__ int slab_word(int w) { return w + 4 * (w >> 6); }
+
+__device__ __forceinline__ void wave_lds_sync() {  // the wave's LDS writes are visible to its later reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // VEC: symbols and states are contiguous along the axis and every sequence
-// starts 16-byte aligned, so a lane moves its K steps as K/4 16-byte pieces.
-template <bool VEC>
+// starts 16-byte aligned. Full slabs then move between HBM and LDS as 16-byte
+// pieces, coalesced across the wave (lane l takes bytes 16 l + 1024 j), and
+// each lane takes its K consecutive positions from LDS.
+// K: positions per lane per slab (16 for maps of 8 bytes, 8 for 16: the step maps of a lane's run
+// are held in registers).
+template <bool VEC, int MW, int K>
 __global__ __launch_bounds__(256) void ts_wave_kernel(const TsParams p) {
-  __shared__ uint64_t sMap[kTsMaxSymbolsWave];
+  constexpr int64_t kSlab = 64 * K;
+  constexpr int kSlabWords = int(kSlab + kSlab / 16);
+  __shared__ StateMap<MW> sMap[kTsMaxSymbolsWave];
+  __shared__ __attribute__((aligned(16))) int32_t sSlab[4][VEC ? kSlabWords : 4];
   const int S = p.states, X = p.nsym;
   for (int x = int(threadIdx.x); x < X; x += 256) {  // per-symbol maps from the clamped table
-    uint64_t m = kIdentityMap;
-    for (int s = 0; s < S; ++s) {
-      const uint64_t e = uint64_t(clampi(p.table[int64_t(s) * X + x], 0, S - 1));
-      m = (m & ~(uint64_t(15) << (4 * s))) | (e << (4 * s));
+    StateMap<MW> m = identity_map<MW>();
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {  // fully unrolled: no register array indexed at run time
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int st = 4 * i + b;
+        if (st < S) {
+          const uint32_t e = uint32_t(clampi(p.table[int64_t(st) * X + x], 0, S - 1));
+          m.w[i] = (m.w[i] & ~(0xFFu << (8 * b))) | (e << (8 * b));
+        }
+      }
     }
     sMap[x] = m;
   }
@@ -81,79 +146,80 @@ __global__ __launch_bounds__(256) void ts_wave_kernel(const TsParams p) {
   const int32_t* xs = p.symbols + off[0];
   int32_t* os = p.out + off[1];
   const int64_t T = p.T, sx = p.t_stride[0], so = p.t_stride[1];
-  constexpr int K = kTsK;
-  // This lane's K symbols of the slab at q0. Full slabs (VEC): K/4 16-byte pieces, no
-  // branch. Otherwise element by element from clamped positions (past the end: the last).
-  auto load_vec = [&](int64_t q0, int32_t (&buf)[K]) {
-    const i32x4* src = reinterpret_cast<const i32x4*>(xs + q0 + int64_t(lane) * K);
-#pragma unroll
-    for (int j = 0; j < K / 4; ++j) {
-      const i32x4 v = ld_stream(src + j);
-      buf[4 * j] = v[0];
-      buf[4 * j + 1] = v[1];
-      buf[4 * j + 2] = v[2];
-      buf[4 * j + 3] = v[3];
-    }
-  };
-  auto load_any = [&](int64_t q0, int32_t (&buf)[K]) {
-    const int64_t q = q0 + int64_t(lane) * K;
-#pragma unroll
-    for (int k = 0; k < K; ++k) buf[k] = xs[(q + k < T ? q + k : T - 1) * sx];
-  };
   uint32_t carry = uint32_t(p.start);
-  // One slab: compose this lane's maps, scan them over the lanes, replay from the entering state.
-  auto slab = [&](int64_t q0, const int32_t (&cur)[K], bool full) {
-    const int64_t q = q0 + int64_t(lane) * K;
-    uint64_t mk[K];
-    uint64_t F = kIdentityMap;  // this lane's steps composed
+  // One slab: compose this lane's maps, scan them over the lanes, replay from the entering
+  // state into res. Positions past `valid` (relative to q0) are identity steps.
+  auto slab = [&](const int32_t (&cur)[K], int64_t valid_from_q, int32_t (&res)[K]) {
+    StateMap<MW> F = identity_map<MW>();  // this lane's steps composed
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      mk[k] = (full || q + k < T) ? sMap[clampi(cur[k], 0, X - 1)] : kIdentityMap;  // past the end: identity
-      F = compose(mk[k], F, S);
+      const StateMap<MW> mk = k < valid_from_q ? sMap[clampi(cur[k], 0, X - 1)] : identity_map<MW>();
+      F = compose<MW>(mk, F);
     }
-    uint64_t G = F;  // inclusive scan over the lanes: lane l ends with the maps of lanes 0..l composed
+    StateMap<MW> G = F;  // inclusive scan over the lanes: lane l ends with the maps of lanes 0..l composed
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const uint64_t below = shfl_up_u64(G, d);
-      if (lane >= d) G = compose(G, below, S);
+      const StateMap<MW> below = shfl_up_map<MW>(G, d);
+      if (lane >= d) G = compose<MW>(G, below);
     }
-    const uint64_t before = shfl_up_u64(G, 1);
-    uint32_t st = lane == 0 ? carry : nib(before, carry);
-    carry = nib(readlane_u64(G, 63), carry);
-    int32_t res[K];
+    const StateMap<MW> before = shfl_up_map<MW>(G, 1);
+    uint32_t st = lane == 0 ? carry : apply<MW>(before, carry);
+    carry = apply<MW>(readlane_map<MW>(G, 63), carry);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      st = nib(mk[k], st);
+    for (int k = 0; k < K; ++k) {  // the step maps again from LDS (keeping them would spill for 16 states)
+      if (k < valid_from_q) st = apply<MW>(sMap[clampi(cur[k], 0, X - 1)], st);
       res[k] = int32_t(st);
     }
-    if (full) {
-      i32x4* dst = reinterpret_cast<i32x4*>(os + q);
-#pragma unroll
-      for (int j = 0; j < K / 4; ++j) st_stream(dst + j, i32x4{res[4 * j], res[4 * j + 1], res[4 * j + 2], res[4 * j + 3]});
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (q + k < T) os[(q + k) * so] = res[k];
-    }
   };
-  int32_t cur[K], nxt[K];
-  const int64_t nfull = VEC ? T / kTsSlab : 0;
+  int32_t cur[K], res[K];
+  const int64_t nfull = VEC ? T / kSlab : 0;
   if (nfull > 0) {
-    load_vec(0, cur);
-    for (int64_t i = 0; i < nfull; ++i) {
-      load_vec((i + 1 < nfull ? i + 1 : i) * kTsSlab, nxt);  // the next full slab (or this one again), in flight
-      slab(i * kTsSlab, cur, true);
+    int32_t* buf = &sSlab[wave][0];
+    i32x4 raw[K / 4], nraw[K / 4];
+    auto load_slab = [&](int64_t q0, i32x4 (&r)[K / 4]) {  // coalesced: lane l, piece j at 256 j + 4 l
 #pragma unroll
-      for (int k = 0; k < K; ++k) cur[k] = nxt[k];
+      for (int j = 0; j < K / 4; ++j) r[j] = ld_stream(reinterpret_cast<const i32x4*>(xs + q0 + 256 * j + 4 * lane));
+    };
+    load_slab(0, raw);
+    for (int64_t i = 0; i < nfull; ++i) {
+      const int64_t q0 = i * kSlab;
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) *reinterpret_cast<i32x4*>(buf + slab_word(256 * j + 4 * lane)) = raw[j];
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(buf + slab_word(K * lane + 4 * j));
+        cur[4 * j] = v[0];
+        cur[4 * j + 1] = v[1];
+        cur[4 * j + 2] = v[2];
+        cur[4 * j + 3] = v[3];
+      }
+      load_slab((i + 1 < nfull ? i + 1 : i) * kSlab, nraw);  // the next full slab (or this one again), in flight
+      slab(cur, K, res);
+      wave_lds_sync();  // every lane has read its symbols before the buffer takes the states
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j)
+        *reinterpret_cast<i32x4*>(buf + slab_word(K * lane + 4 * j)) =
+            i32x4{res[4 * j], res[4 * j + 1], res[4 * j + 2], res[4 * j + 3]};
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j)
+        st_stream(reinterpret_cast<i32x4*>(os + q0 + 256 * j + 4 * lane),
+                  *reinterpret_cast<const i32x4*>(buf + slab_word(256 * j + 4 * lane)));
+      wave_lds_sync();  // the states have left the buffer before the next slab's symbols enter it
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) raw[j] = nraw[j];
     }
   }
-  int64_t q0 = nfull * kTsSlab;
-  if (q0 < T) load_any(q0, cur);
-  for (; q0 < T; q0 += kTsSlab) {
-    load_any(q0 + kTsSlab, nxt);
-    slab(q0, cur, false);
+  // the rest (or everything when not VEC): element by element from clamped positions
+  for (int64_t q0 = nfull * kSlab; q0 < T; q0 += kSlab) {
+    const int64_t q = q0 + int64_t(lane) * K;
 #pragma unroll
-    for (int k = 0; k < K; ++k) cur[k] = nxt[k];
+    for (int k = 0; k < K; ++k) cur[k] = xs[(q + k < T ? q + k : T - 1) * sx];
+    slab(cur, T - q, res);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (q + k < T) os[(q + k) * so] = res[k];
   }
 }
 
@@ -206,8 +272,14 @@ hipError_t launch_table_scan(const TsParams& p, hipStream_t stream) {
     bool vec = p.t_stride[0] == 1 && p.t_stride[1] == 1 && reinterpret_cast<uintptr_t>(p.symbols) % 16 == 0 &&
                reinterpret_cast<uintptr_t>(p.out) % 16 == 0;
     for (int d = 0; d < p.seqs.nd && vec; ++d) vec = p.seqs.st[0][d] % 4 == 0 && p.seqs.st[1][d] % 4 == 0;
-    if (vec) hipLaunchKernelGGL(ts_wave_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(ts_wave_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    const dim3 grid{unsigned(blocks)}, block{256};
+    if (p.states <= 8) {
+      if (vec) hipLaunchKernelGGL((ts_wave_kernel<true, 2, 16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((ts_wave_kernel<false, 2, 16>), grid, block, 0, stream, p);
+    } else {
+      if (vec) hipLaunchKernelGGL((ts_wave_kernel<true, 4, 8>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((ts_wave_kernel<false, 4, 8>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
   }
   const int64_t blocks = (p.num_seq + 255) / 256;

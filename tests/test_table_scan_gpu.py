@@ -2,7 +2,7 @@
 
 The oracle (``oracle.table_scan``, clamping as the pages' GPU backend does)
 runs the automaton one symbol at a time. Cases cover the wave kernel (tables
-of at most 16 states: full slabs of 1024 steps, a ragged tail, one step,
+of at most 16 states and 2048 symbols, maps of 8 or 16 bytes: full slabs of 1024 steps, a ragged tail, one step,
 strided and non-last axes, clamped symbols and entries, every start) and the
 serial kernel (larger tables, in LDS or not), and the two measured workloads
 at full size on sampled sequences (a sequence is an exact sub-problem).
@@ -42,7 +42,7 @@ def _rand(states, nsym, shape, seed, lo=None, hi=None):
     return table, symbols
 
 
-@pytest.mark.parametrize("states,nsym", [(2, 2), (3, 5), (16, 16), (16, 300), (7, 4096)])
+@pytest.mark.parametrize("states,nsym", [(2, 2), (3, 5), (8, 8), (9, 3), (16, 16), (16, 300), (7, 2048)])
 @pytest.mark.parametrize("shape", [(5, 3000), (64, 1024), (3, 1), (130, 2049), (1, 777)])
 def test_wave_kernel(states, nsym, shape):
     table, symbols = _rand(states, nsym, shape, seed=301 + states + nsym + shape[1])
@@ -82,9 +82,10 @@ def test_clamping():
     _check(table, symbols)
 
 
-@pytest.mark.parametrize("states,nsym", [(17, 8), (200, 60), (300, 100)])
+@pytest.mark.parametrize("states,nsym", [(17, 8), (200, 60), (300, 100), (5, 4096)])
 def test_serial_kernel(states, nsym):
-    # more than 16 states; the last table (30000 entries) does not fit the LDS copy
+    # more than 16 states, or more symbols than the wave kernel keeps; tables of 30000 and more entries do not
+    # fit the LDS copy
     table, symbols = _rand(states, nsym, (300, 700), seed=307 + states)
     _check(table, symbols)
 
