@@ -601,7 +601,7 @@ struct PipeStage {
 
 // Where one wave's 16 steps of a unit live.
 struct PipeGeo {
-  uint32_t chunk, bt;
+  uint32_t chunk, bt, batch;
   int ct;
   int64_t q0;  // scan position of the wave's first step
   int64_t t0;  // its time index
@@ -615,6 +615,7 @@ __device__ __forceinline__ PipeGeo pipe_geo(const MsParams& p, const MsUnitWs& w
   g.bt = unit % num_bt;
   g.ct = int(g.bt % uint32_t(ws.col_tiles));
   const uint32_t batch = g.bt / uint32_t(ws.col_tiles);
+  g.batch = batch;
   if (p.batch.nd == 1) {  // one leading dimension (the usual case): no 64-bit divisions
 #pragma unroll
     for (int t = 0; t < 3; ++t) g.off[t] = int64_t(batch) * p.batch.st[t][0];
@@ -723,7 +724,14 @@ struct UnitRegs {
   ARow<TIn> A[16];
   BCol<TIn> Bv[M1 ? 1 : 16];
   f32x4 b1;
+  float sc;  // SCALED kernels: lane c holds the factor of the wave's step c (lanes 16 r + c alike)
 };
+
+// The factor of step k, the same in every lane (a read of lane k).
+template <int k, typename R>
+__device__ __forceinline__ float step_scale(const R& regs) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(regs.sc), k));
+}
 
 template <typename TIn, bool M1, bool ADJ>
 __device__ __forceinline__ void stage_to_regs(UnitRegs<TIn, M1>& R, const char* st, int64_t q0, int64_t T, int lane,
@@ -789,13 +797,22 @@ __device__ __forceinline__ f32x4 bterm_of(const UnitRegs<TIn, M1>& R, int c) {
 // its steps from h = 0 (written in result-register order). issue(k) runs at
 // step k: it starts the copies of the next unit, spread over the steps so that
 // they never back up the memory pipeline.
-template <typename TIn, bool M1, typename Issue>
+// SCALED: each step's result is multiplied by its factor, h[t] = (a[t] h + b[t]) * s[t].
+template <typename TIn, bool M1, bool SCALED, typename Issue>
 __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw, float* sLw, int lane, int r, int c,
                                           Issue&& issue) {
   f32x4 P = identity_d(r, c), L = zero4();
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
-    ((issue(ks), P = mfma_16x16x16(R.A[ks].get(), P, zero4()),
-      L = mfma_16x16x16(R.A[ks].get(), L, bterm_of<TIn, M1, ks>(R, c))),
+    (([&] {
+       issue(ks);
+       P = mfma_16x16x16(R.A[ks].get(), P, zero4());
+       L = mfma_16x16x16(R.A[ks].get(), L, bterm_of<TIn, M1, ks>(R, c));
+       if constexpr (SCALED) {
+         const float sk = step_scale<ks>(R);
+         P *= sk;
+         L *= sk;
+       }
+     }()),
      ...);
   }(std::make_integer_sequence<int, 16>{});
 #pragma unroll
@@ -808,7 +825,7 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
 // (lanes (r, 0)) is moved to lanes (r, step) with a DPP shift and one store per
 // lane writes all 16 steps at the end; for m = 16 a quad transpose gives each
 // lane four consecutive values of one row, stored as one piece per step.
-template <typename TIn, typename TOut, bool M1>
+template <typename TIn, typename TOut, bool M1, bool SCALED>
 __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h, const MsParams& p, const PipeGeo& g,
                                              int lane, int r, int c) {
   const int64_t T = p.T;
@@ -837,7 +854,8 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
     if (full) {
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
-           const f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+           f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+           if constexpr (SCALED) hn *= step_scale<ks>(R);
            if constexpr (ks > 0) gather(std::integral_constant<int, ks - 1>{}, h);
            h = hn;
          }()),
@@ -849,6 +867,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
         (([&] {
            if (g.q0 + ks < T) {
              h = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+             if constexpr (SCALED) h *= step_scale<ks>(R);
              gather(std::integral_constant<int, ks>{}, h);
            }
          }()),
@@ -872,7 +891,8 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
     if (full) {
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
-           const f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+           f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+           if constexpr (SCALED) hn *= step_scale<ks>(R);
            if constexpr (ks > 0) emit(ks - 1, h);
            h = hn;
          }()),
@@ -884,6 +904,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
         (([&] {
            if (g.q0 + ks < T) {
              h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+             if constexpr (SCALED) h *= step_scale<ks>(R);
              emit(ks, h);
            }
          }()),
@@ -963,7 +984,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 // falls from 6.6 to 0.9 TB/s). So the six compute waves are waves 0, 1, 2, 4,
 // 5, 6 (SIMDs 0-2, two each) and the leader (wave 3) and the loader (wave 7)
 // share SIMD 3, where no MFMA chain runs.
-template <int NC, typename TIn, typename TOut, bool M1, bool ADJ = false>
+template <int NC, typename TIn, typename TOut, bool M1, bool ADJ = false, bool SCALED = false>
 __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
   static_assert(NC == 6, "compute waves fill SIMDs 0-2, two each");
   constexpr int K = 16, kUnit = NC * K, LEADER = 3, LOADER = 7;
@@ -1169,12 +1190,16 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     const uint32_t unit = unit_id(k);
     if (unit >= NU) return false;
     gc = pipe_geo(p, ws, unit, wave, kUnit);
+    if constexpr (SCALED) {  // the factors of the wave's 16 steps, loaded while the stage lands
+      const int64_t q = gc.q0 + c < T ? gc.q0 + c : T - 1;
+      Rc.sc = p.step_scale[int64_t(gc.batch) * T + (p.reverse ? T - 1 - q : q)];
+    }
     lds_wait_at_least(&sLanded[wave], uint32_t(k) + 1);
     stage_to_regs<TIn, M1, ADJ>(Rc, st, gc.q0, T, lane, r, c);
     lds_signal_set(&sConsumed[wave], uint32_t(k) + 1, lane);  // (waits for the stage reads first)
     const int kb = k % kBufs;
     lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
-    summarize<TIn, M1>(Rc, &sP[kb][wave][0], &sL[kb][wave][0], lane, r, c, [](int) {});
+    summarize<TIn, M1, SCALED>(Rc, &sP[kb][wave][0], &sL[kb][wave][0], lane, r, c, [](int) {});
     lds_signal_set(&sSumDone[wave], uint32_t(k) + 1, lane);
     return true;
   };
@@ -1187,7 +1212,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][wave - 1][c * 16 + 4 * r]), h,
                         *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]));
     lds_signal_add(&sCarryDone[kb], lane);
-    replay_steps<TIn, TOut, M1>(R, h, p, g, lane, r, c);
+    replay_steps<TIn, TOut, M1, SCALED>(R, h, p, g, lane, r, c);
   };
 
   for (int k = 0;; k += 2) {
@@ -1274,6 +1299,94 @@ __global__ __launch_bounds__(64) void ms_projective_kernel(const MsParams p) {
         P *= inv;
         h *= inv;
         store_h(o0 + q * to, h, n, m, r, cc);
+      }
+      load(q0 + u + K, u);
+    }
+  }
+}
+
+// :projective in parallel. In exact arithmetic the factor of step t is 1/m_t
+// with m_t = max|a[t] P'|, P' the product of every a before t (in scan order)
+// divided by its largest entry; with the factors known, h is an ordinary
+// matrix-scan of a[t] s[t] and b[t] s[t]. Two passes give the factors, one
+// wave per (batch, chunk of kProjChunk steps):
+//   ms_proj_chunk_kernel  the chunk's product (later steps on the left),
+//                         divided by its largest entry after every step so
+//                         that it stays in range; stored row-major.
+//   ms_proj_scale_kernel  the products of the chunks before this one composed
+//                         in scan order (again divided after every product),
+//                         then this chunk's steps from there, each storing the
+//                         factor of its step (1 where the product is zero).
+// The pipelined kernel with SCALED then runs the scan.
+constexpr int kProjChunk = 96;
+
+template <typename TIn, bool VEC>
+__global__ __launch_bounds__(64) void ms_proj_chunk_kernel(const MsParams p, float* prod, int64_t chunks) {
+  const int lane = int(threadIdx.x), r = lane >> 4, c = lane & 15;
+  const int64_t batch = int64_t(blockIdx.x) / chunks, ch = int64_t(blockIdx.x) % chunks;
+  int64_t off[3];
+  index_offsets(p.batch, batch, off);
+  const int64_t T = p.T;
+  const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
+  const TIn* a0 = static_cast<const TIn*>(p.a) + off[MS_A] + (p.reverse ? T - 1 : 0) * p.t_stride[MS_A];
+  const int64_t q_begin = ch * kProjChunk, q_end = q_begin + kProjChunk < T ? q_begin + kProjChunk : T;
+  constexpr int K = 4;  // steps whose operands are in flight
+  ARow<TIn> A[K];
+  auto load = [&](int64_t q, int u) { A[u] = load_a<TIn, VEC>(a0 + (q < q_end ? q : q_end - 1) * ta, p.n, r, c); };
+#pragma unroll
+  for (int u = 0; u < K; ++u) load(q_begin + u, u);
+  f32x4 P = identity_d(r, c);
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += K) {
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      if (q0 + u < q_end) {  // wave-uniform
+        P = mfma_16x16x16(A[u].get(), P, zero4());
+        const float big = wave_max_abs(P);
+        P *= big > 0.0f ? 1.0f / big : 1.0f;
+      }
+      load(q0 + u + K, u);
+    }
+  }
+  float* dst = prod + (batch * chunks + ch) * 256;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) dst[(4 * r + v) * 16 + c] = P[v];
+}
+
+template <typename TIn, bool VEC>
+__global__ __launch_bounds__(64) void ms_proj_scale_kernel(const MsParams p, const float* prod, float* step_scale,
+                                                           int64_t chunks) {
+  const int lane = int(threadIdx.x), r = lane >> 4, c = lane & 15;
+  const int64_t batch = int64_t(blockIdx.x) / chunks, ch = int64_t(blockIdx.x) % chunks;
+  int64_t off[3];
+  index_offsets(p.batch, batch, off);
+  const int64_t T = p.T;
+  // the chunks before this one, in scan order
+  f32x4 P = identity_d(r, c);
+  const float* pb = prod + batch * chunks * 256;
+  for (int64_t j = 0; j < ch; ++j) {
+    P = mfma_16x16x16(*reinterpret_cast<const f32x4*>(pb + j * 256 + c * 16 + 4 * r), P, zero4());
+    const float big = wave_max_abs(P);
+    P *= big > 0.0f ? 1.0f / big : 1.0f;
+  }
+  const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
+  const TIn* a0 = static_cast<const TIn*>(p.a) + off[MS_A] + (p.reverse ? T - 1 : 0) * p.t_stride[MS_A];
+  const int64_t q_begin = ch * kProjChunk, q_end = q_begin + kProjChunk < T ? q_begin + kProjChunk : T;
+  float* sc = step_scale + batch * T;
+  constexpr int K = 4;
+  ARow<TIn> A[K];
+  auto load = [&](int64_t q, int u) { A[u] = load_a<TIn, VEC>(a0 + (q < q_end ? q : q_end - 1) * ta, p.n, r, c); };
+#pragma unroll
+  for (int u = 0; u < K; ++u) load(q_begin + u, u);
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += K) {
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      const int64_t q = q0 + u;
+      if (q < q_end) {  // wave-uniform
+        P = mfma_16x16x16(A[u].get(), P, zero4());
+        const float big = wave_max_abs(P);
+        const float inv = big > 0.0f ? 1.0f / big : 1.0f;
+        P *= inv;
+        if (lane == 0) sc[p.reverse ? T - 1 - q : q] = inv;
       }
       load(q0 + u + K, u);
     }
@@ -1397,10 +1510,23 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
   return hipGetLastError();
 }
 
-}  // namespace
+// Room :projective's two passes take after the scan's own workspace: the chunk
+// products and the factor of every step.
+struct ProjPlan {
+  int64_t chunks;
+  size_t prod_off, scale_off, total;
+};
 
-size_t matrix_scan_workspace(const MsParams& p) {
-  if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return 0;
+ProjPlan proj_plan(const MsParams& p, size_t scan_bytes) {
+  ProjPlan q{};
+  q.chunks = (p.T + kProjChunk - 1) / kProjChunk;
+  q.prod_off = (scan_bytes + 255) / 256 * 256;
+  q.scale_off = q.prod_off + size_t(p.num_batch) * size_t(q.chunks) * 256 * sizeof(float);
+  q.total = q.scale_off + (size_t(p.num_batch) * size_t(p.T) * sizeof(float) + 255) / 256 * 256;
+  return q;
+}
+
+size_t scan_workspace(const MsParams& p) {
   // Shapes only (the size is queried without dtypes or pointers): room for the
   // pipelined kernel's shorter units whenever its shapes apply, which also
   // covers ms_unit_kernel's longer ones.
@@ -1410,8 +1536,77 @@ size_t matrix_scan_workspace(const MsParams& p) {
   return up.total;
 }
 
-hipError_t launch_matrix_scan_projective(const MsParams& p, hipStream_t stream) {
+}  // namespace
+
+size_t matrix_scan_workspace(const MsParams& p) {
+  if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return 0;
+  const size_t scan = scan_workspace(p);
+  if (scan == 0) return 0;
+  // with room for :projective's passes where the pipelined kernel runs them (n = 16)
+  return p.n == 16 ? proj_plan(p, scan).total : scan;
+}
+
+namespace {
+
+template <typename TIn, typename TOut>
+hipError_t launch_projective_passes(const MsParams& p0, void* workspace, hipStream_t stream) {
+  const size_t scan = scan_workspace(p0);
+  const ProjPlan pp = proj_plan(p0, scan);
+  char* base = static_cast<char*>(workspace);
+  float* prod = reinterpret_cast<float*>(base + pp.prod_off);
+  float* scale = reinterpret_cast<float*>(base + pp.scale_off);
+  MsParams p = p0;
+  p.step_scale = scale;
+  const int64_t waves = p.num_batch * pp.chunks;
+  if (waves > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int64_t va = 4 * int64_t(sizeof(TIn));
+  bool vec = reinterpret_cast<uintptr_t>(p.a) % uintptr_t(va) == 0 && (p.t_stride[MS_A] * int64_t(sizeof(TIn))) % va == 0;
+  for (int d = 0; d < p.batch.nd && vec; ++d) vec = (p.batch.st[MS_A][d] * int64_t(sizeof(TIn))) % va == 0;
+  const dim3 grid{unsigned(waves)}, block{64};
+  if (vec) {
+    hipLaunchKernelGGL((ms_proj_chunk_kernel<TIn, true>), grid, block, 0, stream, p, prod, pp.chunks);
+    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, true>), grid, block, 0, stream, p, prod, scale, pp.chunks);
+  } else {
+    hipLaunchKernelGGL((ms_proj_chunk_kernel<TIn, false>), grid, block, 0, stream, p, prod, pp.chunks);
+    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, false>), grid, block, 0, stream, p, prod, scale, pp.chunks);
+  }
+  // the scan of a[t] s[t], b[t] s[t]: the pipelined kernel with its factors
+  const UnitPlan up = unit_plan(p, kLeadCompute * kSteps);
+  MsUnitWs ws;
+  ws.header = reinterpret_cast<uint32_t*>(base);
+  ws.flags = reinterpret_cast<uint32_t*>(base + 256);
+  ws.P = reinterpret_cast<float*>(base + 256 + up.flags_bytes);
+  ws.L = ws.P + up.num_units * 256;
+  ws.H = ws.L + up.num_units * 256;
+  ws.num_units = uint32_t(up.num_units);
+  ws.chunks = uint32_t(up.chunks);
+  ws.col_tiles = up.col_tiles;
+  const size_t words = (256 + up.flags_bytes) / 4;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((words + 255) / 256)), dim3(256), 0, stream, ws.header, words);
+  const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cu_count())));
+  if (p.m == 1)
+    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true, false, true>), dim3(blocks), dim3(512), 0, stream,
+                       p, ws);
+  else if constexpr (sizeof(TIn) == 2)
+    hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, false, false, true>), dim3(blocks), dim3(512), 0,
+                       stream, p, ws);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;
+  // In parallel where the pipelined kernel takes the shape and the workspace has room for it all.
+  const size_t scan = scan_workspace(p);
+  if (pipe_fits(p) && scan > 0 && workspace != nullptr && workspace_bytes >= proj_plan(p, scan).total) {
+    if (p.in_bf16)
+      return p.out_bf16 ? launch_projective_passes<uint16_t, uint16_t>(p, workspace, stream)
+                        : launch_projective_passes<uint16_t, float>(p, workspace, stream);
+    return p.out_bf16 ? launch_projective_passes<float, uint16_t>(p, workspace, stream)
+                      : launch_projective_passes<float, float>(p, workspace, stream);
+  }
   const int64_t blocks = p.num_batch * ((p.m + 15) / 16);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   // whole 16-byte (f32) or 8-byte (bf16) rows of a for n = 16 with aligned steps

@@ -449,21 +449,22 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
     span_bytes(b, b_rank, b_shape, bst, esz, &lo, &hi);
     if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "matrix-scan: out overlaps b");
   }
-  if (projective) {  // no workspace
+  const size_t need = sx::matrix_scan_workspace(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(SX_E_WORKSPACE, "matrix-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SX_E_WORKSPACE, "matrix-scan: workspace must be 256-byte aligned");
+  if (projective) {
     p.in_bf16 = dtype == SX_BF16;
     p.out_bf16 = out_dtype == SX_BF16;
     p.reverse = reverse ? 1 : 0;
     p.a = a;
     p.b = b;
     p.out = out;
-    return device_status(sx::launch_matrix_scan_projective(p, static_cast<hipStream_t>(stream)),
-                         "matrix-scan :projective launch");
+    return device_status(
+        sx::launch_matrix_scan_projective(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+        "matrix-scan :projective launch");
   }
-  const size_t need = sx::matrix_scan_workspace(p);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(SX_E_WORKSPACE, "matrix-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(SX_E_WORKSPACE, "matrix-scan: workspace must be 256-byte aligned");
 
   p.in_bf16 = dtype == SX_BF16;
   p.out_bf16 = out_dtype == SX_BF16;

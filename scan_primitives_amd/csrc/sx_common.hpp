@@ -118,14 +118,17 @@ struct MsParams {
   int out_bf16;          // out is bf16 (else f32)
   int reverse;
   int adjoint;           // step q multiplies by the transpose of a at position q - 1 (the gradient's scan)
+  const float* step_scale;  // :projective's second pass: h[t] = (a[t] h + b[t]) * step_scale[batch * T + t]
   const void* a;
   const void* b;
   void* out;
 };
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
-// :projective (no workspace): the running product's largest entry divides P and h every step.
-hipError_t launch_matrix_scan_projective(const MsParams& p, hipStream_t stream);
+// :projective: the running product's largest entry divides P and h every step. In parallel (two passes
+// for the factors, then the pipelined scan) when the shape and the workspace allow, else serially.
+hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 size_t matrix_scan_workspace(const MsParams& p);
 
 // ---------------------------------------------------------------- matrix-scan gradient
