@@ -157,8 +157,11 @@ size_t sx_element_scan_workspace_bytes(sx_body body, int rank, const int64_t* sh
  *                contiguous, the shapes of initial, x and s. Must not overlap
  *                any input or each other (SX_E_ALIAS).
  *  workspace     at least sx_element_scan_backward_workspace_bytes() bytes
- *                (nonzero only for width-one sequences under a vector
- *                state), 256-byte aligned; may be NULL when that is 0.
+ *                (nonzero for width-one sequences under a vector state with
+ *                tanh-affine or max-plus, and for norm-cap with fewer than
+ *                8192 state vectors and at least 32 trips, which splits the
+ *                axis), 256-byte aligned; may be NULL when that is 0. The
+ *                call overwrites it.
  *
  * Errors as sx_element_scan; E-DIM-003 for any NULL tensor.
  */

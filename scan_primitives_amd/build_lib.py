@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsx_scan.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["sx_api.cpp", "element_scan.hip", "matrix_scan.hip", "matrix_scan_grad.hip", "table_scan.hip"]
+SOURCES = ["sx_api.cpp", "element_scan.hip", "normcap_quad.hip", "matrix_scan.hip", "matrix_scan_grad.hip",
+           "table_scan.hip"]
 ARCH = "gfx950"
 
 # Packed FP32 (v_pk_*_f32) stays off for all device code: the kernels are

@@ -37,6 +37,7 @@
 //                          replays its trips from there. The next slab's
 //                          loads are in flight meanwhile. Inputs are read
 //                          once and no state leaves the workgroup.
+#include <algorithm>
 #include <utility>
 
 #include "sx_common.hpp"
@@ -734,7 +735,54 @@ __global__ __launch_bounds__(NW * 64) void es_vjp_slab_kernel(const EsVjpParams 
   if (live && wave == 0) v.ginit[off[ES_INIT]] = carry;
 }
 
-// Norm-cap gradient: one 16-lane DPP row per state vector, trips last to first.
+// Norm-cap gradient. A trip starting from hp with y = s hp + x passes back
+// dy = (lam - u (u . lam)) / |y| when |y| > 1 (u = y / |y|), else dy = lam,
+// where lam is the trip's upstream gradient plus what the next trip passed
+// back; grad_x = dy, grad_s = dy hp, and s dy goes on to the trip before. A
+// width-one sequence under the vector state gets the sum over the row of its
+// gradient, taken here by a row reduction (lanes past n contribute zero).
+struct NcOut {
+  float* gx;
+  float* gs;
+  int64_t gx_step, gs_step;  // elements per trip
+  bool gx_sum, gs_sum;
+  bool active;
+  int k;
+  // where this row's gradients go: full width in out's layout, or one value per trip
+  __device__ NcOut(const EsVjpParams& v, const int64_t* off, int k_, bool active_) : active(active_), k(k_) {
+    const EsParams& p = v.p;
+    const int64_t so = p.t_stride[ES_OUT];
+    const int kk = active ? k : 0;
+    gx_sum = v.gx_sum != 0;
+    gs_sum = v.gs_sum != 0;
+    // out is contiguous with the state last, so its offsets are multiples of n
+    gx = gx_sum ? v.gx + off[ES_OUT] / p.n : v.gx + off[ES_OUT] + kk;
+    gs = gs_sum ? v.gs + off[ES_OUT] / p.n : v.gs + off[ES_OUT] + kk;
+    gx_step = gx_sum ? so / p.n : so;
+    gs_step = gs_sum ? so / p.n : so;
+  }
+  __device__ __forceinline__ void store(int64_t t, float dy, float hp) const {
+    const float d = active ? dy : 0.0f, dh = active ? dy * hp : 0.0f;
+    const float sx = gx_sum ? row_sum16(d) : d;  // uniform branches
+    const float ss = gs_sum ? row_sum16(dh) : dh;
+    if (gx_sum ? k == 0 : active) gx[t * gx_step] = sx;
+    if (gs_sum ? k == 0 : active) gs[t * gs_step] = ss;
+  }
+};
+
+// The trip's backward step; nu carries what goes on to the trip before.
+__device__ __forceinline__ float nc_back_trip(float hp, float x, float s, float g, float& nu, bool active) {
+  const float y = active ? fmaf(s, hp, x) : 0.0f;  // lanes past n hold zero
+  const float ir = __builtin_amdgcn_rsqf(row_sum16(y * y));
+  const float uy = y * ir;
+  const float lam = g + nu;
+  const float ul = row_sum16(uy * lam);
+  const float dy = ir < 1.0f ? (lam - uy * ul) * ir : lam;  // capped when |y| > 1
+  nu = active ? s * dy : 0.0f;
+  return dy;
+}
+
+// One 16-lane DPP row per state vector, trips last to first.
 __global__ __launch_bounds__(256) void es_vjp_normcap_row_kernel(const EsVjpParams v) {
   const EsParams& p = v.p;
   const int64_t gtid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -751,8 +799,7 @@ __global__ __launch_bounds__(256) void es_vjp_normcap_row_kernel(const EsVjpPara
   const float* sl = p.s + off[ES_S] + kk * p.n_stride[ES_S];
   const float* hl = v.h + off[ES_OUT] + kk;
   const float* gl = v.g + off[ES_OUT] + kk;
-  float* gxl = v.gx + off[ES_OUT] + kk;
-  float* gsl = v.gs + off[ES_OUT] + kk;
+  const NcOut out(v, off, k, active);
   const float init = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
   auto tq = [&](int64_t q) -> int64_t { return p.reverse ? T - 1 - q : q; };
   // Blocks of U trips, last to first; block i + 1's loads are issued before block i is
@@ -778,34 +825,219 @@ __global__ __launch_bounds__(256) void es_vjp_normcap_row_kernel(const EsVjpPara
   load(T - 1, cur);
   for (int64_t q1 = T - 1; q1 >= 0; q1 -= U) {
     load(q1 - U, nxt);  // always (clamped positions): a load behind a branch would cost a full wait
-    // What does not depend on the adjoint, for the whole block first: y, 1 / |y| (as
-    // the forward pass computes it), the cap decision and the direction u = y / |y|.
-    float ir[U], uy[U], hp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      hp[u] = q1 - u > 0 ? cur.hr[u] : init;  // the state before the trip (initial before the first)
-      const float y = active ? fmaf(cur.sv[u], hp[u], cur.xv[u]) : 0.0f;  // lanes past n hold zero
-      ir[u] = __builtin_amdgcn_rsqf(row_sum16(y * y));
-      uy[u] = y * ir[u];
-    }
-    // the adjoint chain: one row sum per trip
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (q1 - u >= 0) {  // row-uniform
-        const float lam = cur.gv[u] + nu;
-        const float ul = row_sum16(uy[u] * lam);
-        const float dy = ir[u] < 1.0f ? (lam - uy[u] * ul) * ir[u] : lam;  // capped when |y| > 1
-        if (active) {
-          const int64_t t = tq(q1 - u);
-          gxl[t * so] = dy;
-          gsl[t * so] = dy * hp[u];
-        }
-        nu = active ? cur.sv[u] * dy : 0.0f;
+        const float hp = q1 - u > 0 ? cur.hr[u] : init;  // the state before the trip (initial before the first)
+        const float dy = nc_back_trip(hp, cur.xv[u], cur.sv[u], cur.gv[u], nu, active);
+        out.store(tq(q1 - u), dy, hp);
       }
     }
     cur = nxt;
   }
   if (active) v.ginit[off[ES_INIT] + kk * p.n_stride[ES_INIT]] = nu;
+}
+
+// Norm-cap gradient split along the axis. The adjoint map of a trip,
+// nu -> s (J^T nu) with J the Jacobian of the cap, has norm at most the
+// forward trip's Lipschitz bound L = alpha / max(1, |x| - alpha) (the states
+// are in the unit ball, so |y| >= |x| - alpha), and from nu = 0 before the
+// last trip the adjoint stays within B = G L* / (1 - L*) (G the largest |g|
+// of the lane, L* its largest L, when L* < 1). A chunk of the sweep may then
+// start W trips early from nu = 0: its error entering the chunk is at most
+// (product of the W bounds) * B, and W is chosen so that this is below 2^-26 G,
+// far inside the f32 rounding of the gradients (which are at least of size G
+// where g is). Lanes whose bounds reach 1 run exactly from the sweep's start.
+// The bounds of the first trip of the scan assume |initial| <= 1, which may not
+// hold; that trip only raises L* (it never lies inside a warm-up, which ends
+// before the last trip of the sweep).
+
+// Per state vector: G and L* (non-finite values become +inf: no certificate),
+// and per chunk of the sweep the product of its trips' bounds, which lets a
+// chunk find its warm-up start a whole chunk at a time. One workgroup per
+// state vector; its R rows of 16 threads (R = blockDim.x / 16) take every
+// R-th chunk, each in batches of 16 trips. bounds holds G, L* at 2 lane,
+// 2 lane + 1 and the product of chunk c at 2 num_lanes + c num_lanes + lane.
+template <bool S1>
+__global__ __launch_bounds__(1024) void es_vjp_normcap_bound_kernel(const EsVjpParams v, int64_t len,
+                                                                   int64_t nchunks) {
+  const EsParams& p = v.p;
+  const int64_t lane = blockIdx.x;
+  const int R = int(blockDim.x >> 4), r = int(threadIdx.x >> 4);
+  const int k = int(threadIdx.x & 15);
+  const bool active = k < p.n;
+  const int kk = active ? k : 0;
+  int64_t off[4];
+  index_offsets(p.lanes, lane, off);
+  const int64_t T = p.T, sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const float* xl = p.x + off[ES_X] + kk * p.n_stride[ES_X];
+  const float* sl = p.s + off[ES_S] + kk * p.n_stride[ES_S];
+  const float* gl = v.g + off[ES_OUT] + kk;
+  auto time_of_sweep = [&](int64_t w) -> int64_t {  // w in [0, T)
+    const int64_t q = T - 1 - w;
+    return p.reverse ? T - 1 - q : q;
+  };
+  float* prods = v.bounds + 2 * p.num_lanes + lane;
+  float gmax = 0.0f, lmax = 0.0f;
+  constexpr int U = 16;
+  for (int64_t c = r; c < nchunks; c += R) {  // row-uniform
+    const int64_t w_begin = c * len, w_end = w_begin + len < T ? w_begin + len : T;
+    float prod = 1.0f;
+    for (int64_t w0 = w_begin; w0 < w_end; w0 += U) {
+      float xv[U], gv[U], sv[S1 ? 1 : U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // clamped positions: every load is valid
+        const int64_t t = time_of_sweep(w0 + u < w_end ? w0 + u : w_end - 1);
+        xv[u] = xl[t * sx];
+        gv[u] = gl[t * so];
+        if constexpr (!S1) sv[u] = sl[t * ss];
+      }
+      if constexpr (S1) sv[0] = sl[time_of_sweep(w0 + k < w_end ? w0 + k : w_end - 1) * ss];  // lane k: trip w0 + k
+      [&]<int... us>(std::integer_sequence<int, us...>) {
+        (([&] {
+           constexpr int u = us;
+           if (w0 + u < w_end) {  // row-uniform
+             float a;
+             if constexpr (S1) a = row_bcast<u>(sv[0]);
+             else a = active ? sv[u] : 0.0f;
+             const float l = norm_cap_lipschitz(active ? xv[u] : 0.0f, a, S1);
+             const float ga = active ? gv[u] : 0.0f;
+             const float gn = __builtin_amdgcn_sqrtf(row_sum16(ga * ga));
+             prod *= l;
+             lmax = l <= 3.0e38f ? fmaxf(lmax, l) : __builtin_huge_valf();  // NaN counts as unbounded
+             gmax = gn <= 3.0e38f ? fmaxf(gmax, gn) : __builtin_huge_valf();
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, U>{});
+    }
+    if (k == 0) prods[c * p.num_lanes] = prod;
+  }
+  __shared__ float red[2][64];
+  if (k == 0) {
+    red[0][r] = gmax;
+    red[1][r] = lmax;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    float m = 0.0f;
+    for (int i = 0; i < R; ++i) m = fmaxf(m, red[threadIdx.x][i]);  // values are >= 0 or +inf
+    v.bounds[2 * lane + threadIdx.x] = m;
+  }
+}
+
+// One DPP row per (state vector, chunk of the sweep): the warm-up from nu = 0
+// at the start of the latest earlier chunk from which the product of the
+// chunks' bounds is below the target (or the sweep from its start), then the
+// chunk's trips storing both gradients; the chunk that ends the sweep also
+// stores grad_initial. Sweep position w is scan position T - 1 - w. The next
+// block's loads are issued before a block is computed; a width-one gate is
+// kept one trip per lane and taken by row broadcast.
+template <bool S1>
+__global__ __launch_bounds__(256) void es_vjp_normcap_chunk_kernel(const EsVjpParams v, int64_t len,
+                                                                   int64_t nchunks) {
+  const EsParams& p = v.p;
+  const int64_t row = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
+  if (row >= p.num_lanes * nchunks) return;  // whole rows
+  const int64_t chunk = row / p.num_lanes, lane = row % p.num_lanes;
+  const int k = int(threadIdx.x & 15);
+  const bool active = k < p.n;
+  const int kk = active ? k : 0;
+  int64_t off[4];
+  index_offsets(p.lanes, lane, off);
+  const int64_t T = p.T, sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
+  const float* xl = p.x + off[ES_X] + kk * p.n_stride[ES_X];
+  const float* sl = p.s + off[ES_S] + kk * p.n_stride[ES_S];
+  const float* hl = v.h + off[ES_OUT] + kk;
+  const float* gl = v.g + off[ES_OUT] + kk;
+  const NcOut out(v, off, k, active);
+  const float init = active ? p.init[off[ES_INIT] + kk * p.n_stride[ES_INIT]] : 0.0f;
+  auto time_of_sweep = [&](int64_t w) -> int64_t {  // clamped into [0, T): every load reads a valid element
+    w = w < 0 ? 0 : (w >= T ? T - 1 : w);
+    const int64_t q = T - 1 - w;
+    return p.reverse ? T - 1 - q : q;
+  };
+  const float gmax = v.bounds[2 * lane], lmax = v.bounds[2 * lane + 1];
+  const int64_t s0 = chunk * len;
+  int64_t e0 = s0 + len < T ? s0 + len : T;
+  if (!(lmax < 1.0f) || !(gmax <= 3.0e38f)) {  // row-uniform: no certificate for this lane
+    if (chunk != 0) return;  // the first chunk's row runs the lane's whole sweep exactly
+    e0 = T;
+  }
+  // ---- the warm-up start: a whole chunk at a time, four chunk products per round
+  int64_t start = 0;
+  if (s0 > 0) {  // row-uniform (a lane without a certificate has s0 = 0 here)
+    if (lmax == 0.0f || gmax == 0.0f) {
+      start = s0;  // every adjoint map or every g is zero: nu is exactly zero entering the chunk
+    } else {
+      const float target = kWarmupBound * (1.0f - lmax) / lmax;
+      const float* prods = v.bounds + 2 * p.num_lanes + lane;
+      float prod = 1.0f;
+      int64_t c = chunk - 1;
+      bool done = false;
+      while (!done) {
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pv[u] = prods[(c - u >= 0 ? c - u : 0) * p.num_lanes];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (!done) {
+            if (c - u < 0) {
+              start = 0;  // reached the sweep's start: exact from there
+              done = true;
+            } else {
+              prod *= pv[u];
+              if (prod <= target) {
+                start = (c - u) * len;
+                done = true;
+              }
+            }
+          }
+        }
+        c -= 4;
+      }
+    }
+  }
+  // ---- the sweep over [start, e0): trips before s0 only carry the adjoint
+  constexpr int U = S1 ? 16 : 8;  // loads a block: 3 U + 1 or 4 U, countable by vmcnt (at most 63)
+  struct Block {
+    float hr[U], xv[U], gv[U], sv[S1 ? 1 : U];
+  };
+  auto load = [&](int64_t w0, Block& B) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // clamped positions: none behind a branch
+      const int64_t w = w0 + u < e0 ? w0 + u : e0 - 1;
+      const int64_t t = time_of_sweep(w);
+      B.hr[u] = hl[time_of_sweep(w + 1) * so];  // the state before the trip (scan position one earlier)
+      B.xv[u] = xl[t * sx];
+      B.gv[u] = gl[t * so];
+      if constexpr (!S1) B.sv[u] = sl[t * ss];
+    }
+    if constexpr (S1) B.sv[0] = sl[time_of_sweep(w0 + k < e0 ? w0 + k : e0 - 1) * ss];  // lane k: trip w0 + k
+  };
+  float nu = 0.0f;
+  Block cur, nxt;
+  load(start, cur);
+  for (int64_t w0 = start; w0 < e0; w0 += U) {
+    load(w0 + U, nxt);  // clamped: the last round loads valid elements it does not use
+    [&]<int... us>(std::integer_sequence<int, us...>) {
+      (([&] {
+         constexpr int u = us;
+         const int64_t w = w0 + u;
+         if (w < e0) {  // row-uniform
+           const float hp = w + 1 < T ? cur.hr[u] : init;  // the first trip of the scan starts from initial
+           float sg;
+           if constexpr (S1) sg = row_bcast<u>(cur.sv[0]);
+           else sg = cur.sv[u];
+           const float dy = nc_back_trip(hp, active ? cur.xv[u] : 0.0f, sg, cur.gv[u], nu, active);
+           if (w >= s0) out.store(time_of_sweep(w), dy, hp);
+         }
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, U>{});
+    cur = nxt;
+  }
+  if (e0 == T && active) v.ginit[off[ES_INIT] + kk * p.n_stride[ES_INIT]] = nu;
 }
 
 }  // namespace
@@ -826,6 +1058,8 @@ size_t element_scan_workspace(sx_body, const EsParams&) { return 0; }
 hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream) {
   if (p.num_lanes <= 0) return hipSuccess;
   if (body == SX_BODY_NORM_CAP) {
+    // a 16-wide state in aligned memory: four components per thread (normcap_quad.hip)
+    if (normcap_quad_forward_eligible(p)) return launch_normcap_quad_forward(p, stream);
     if (p.num_lanes < kChunkMaxLanes && p.T >= 2 * kChunkMinLen) {
       // Few lanes: cut the axis into chunks so that about kChunkRows rows run at once.
       int64_t nchunks = (kChunkRows + p.num_lanes - 1) / p.num_lanes;
@@ -883,10 +1117,53 @@ hipError_t launch_linear_scan(const EsParams& p, bool in_bf16, bool out_bf16, hi
   return hipGetLastError();
 }
 
+// The norm-cap gradient's split along the axis (as the forward pass's): chunk
+// length and count, or false when one row per state vector is used.
+static bool normcap_vjp_split(const EsParams& p, int64_t* len, int64_t* nchunks) {
+  if (!(p.num_lanes > 0 && p.num_lanes < kChunkMaxLanes && p.T >= 2 * kChunkMinLen)) return false;
+  int64_t c = (kChunkRows + p.num_lanes - 1) / p.num_lanes;
+  int64_t l = (p.T + c - 1) / c;
+  if (l < kChunkMinLen) l = kChunkMinLen;
+  *len = l;
+  *nchunks = (p.T + l - 1) / l;
+  return true;
+}
+
+int64_t element_scan_backward_bound_words(sx_body body, const EsParams& p) {
+  if (body != SX_BODY_NORM_CAP) return 0;
+  // enough for either layout: the four-components-per-thread kernels (chosen at launch, by
+  // alignment) or the one-component-per-thread ones
+  int64_t len = 0, nchunks = 0, words = normcap_quad_bound_words(p);
+  if (normcap_vjp_split(p, &len, &nchunks))
+    words = std::max(words, 2 * p.num_lanes + nchunks * p.num_lanes);  // G and L* per lane, a product per chunk
+  return words;
+}
+
 hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipStream_t stream) {
   const EsParams& p = v.p;
   if (p.num_lanes <= 0 || p.T <= 0) return hipSuccess;
   if (body == SX_BODY_NORM_CAP) {
+    if (normcap_quad_eligible(v)) return launch_normcap_quad_backward(v, stream);
+    int64_t len = 0, nchunks = 0;
+    if (v.bounds != nullptr && normcap_vjp_split(p, &len, &nchunks)) {
+      // few lanes: chunks of the sweep with certified warm-ups, as the forward pass splits its axis
+      const int64_t blocks = (p.num_lanes * nchunks * 16 + 255) / 256;
+      if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+      int rows = 1;  // rows of the bound kernel's workgroup: one chunk each, at most 64
+      while (rows < 64 && rows < nchunks) rows *= 2;
+      if (p.n_stride[ES_S] == 0) {  // a width-one gate
+        hipLaunchKernelGGL(es_vjp_normcap_bound_kernel<true>, dim3(unsigned(p.num_lanes)), dim3(16 * rows), 0,
+                           stream, v, len, nchunks);
+        hipLaunchKernelGGL(es_vjp_normcap_chunk_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, stream, v, len,
+                           nchunks);
+      } else {
+        hipLaunchKernelGGL(es_vjp_normcap_bound_kernel<false>, dim3(unsigned(p.num_lanes)), dim3(16 * rows), 0,
+                           stream, v, len, nchunks);
+        hipLaunchKernelGGL(es_vjp_normcap_chunk_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, stream, v, len,
+                           nchunks);
+      }
+      return hipGetLastError();
+    }
     const int64_t blocks = (p.num_lanes * 16 + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(es_vjp_normcap_row_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, v);

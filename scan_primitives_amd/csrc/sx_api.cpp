@@ -705,13 +705,15 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
   int64_t seq[sx::kMaxRank];
   std::copy(shape, shape + rank, seq);
   for (int64_t w : {x_width, s_width}) {
-    if (!vec || w != 1 || n == 1) continue;
+    if (!vec || w != 1 || n == 1 || body == SX_BODY_NORM_CAP) continue;  // norm-cap sums in its kernels
     total += align_up(size_t(plan.numel) * 4);  // the full-width gradient before its sum over the state
     seq[rank - 1] = 1;
     const sx::SumToParams q = sum_to_plan(rank, shape, rank, seq);
     part = std::max(part, size_t(q.splits * q.targets) * 4);
   }
-  return total + align_up(part);
+  // per-lane bounds of the norm-cap gradient's split along the axis
+  const size_t bounds = size_t(sx::element_scan_backward_bound_words(body, plan.p)) * 4;
+  return total + align_up(part) + align_up(bounds);
 }
 
 sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape, int axis, int state_axis, int reverse,
@@ -762,7 +764,11 @@ sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape,
       if (overlaps(lo[o], hi[o], lo[i], hi[i]))
         return fail(SX_E_ALIAS, "element-scan gradient: %s overlaps %s", what[o], what[i]);
 
-  const bool x_sum = vec && x_width == 1 && n > 1, s_sum = vec && s_width == 1 && n > 1;
+  // width-one sequences under a vector state: norm-cap's kernels sum their gradients over the
+  // state; for the other bodies a full-width gradient goes to the workspace and is summed after
+  const bool fused = body == SX_BODY_NORM_CAP;
+  const bool x_one = vec && x_width == 1 && n > 1, s_one = vec && s_width == 1 && n > 1;
+  const bool x_sum = x_one && !fused, s_sum = s_one && !fused;
   const size_t need = sx_element_scan_backward_workspace_bytes(body, rank, shape, axis, state_axis, x_width, s_width);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(SX_E_WORKSPACE, "element-scan gradient: workspace of %zu bytes given, %zu needed", workspace_bytes,
@@ -774,6 +780,8 @@ sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape,
   float* gx_full = x_sum ? reinterpret_cast<float*>(ws) : grad_x;
   float* gs_full = s_sum ? reinterpret_cast<float*>(ws + (x_sum ? full : 0)) : grad_s;
   float* part = reinterpret_cast<float*>(ws + (x_sum ? full : 0) + (s_sum ? full : 0));
+  const size_t bounds_bytes = size_t(sx::element_scan_backward_bound_words(body, plan.p)) * 4;
+  float* bounds = bounds_bytes > 0 ? reinterpret_cast<float*>(ws + need - align_up(bounds_bytes)) : nullptr;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   sx::EsVjpParams v{};
@@ -788,6 +796,9 @@ sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape,
   v.gx = gx_full;
   v.gs = gs_full;
   v.ginit = grad_initial;
+  v.gx_sum = x_one && fused;
+  v.gs_sum = s_one && fused;
+  v.bounds = bounds;
   hipError_t e = sx::launch_element_scan_backward(body, v, hs);
   if (e != hipSuccess) return device_status(e, "element-scan gradient launch");
   int64_t seq[sx::kMaxRank];

@@ -65,8 +65,9 @@ size_t element_scan_workspace(sx_body body, const EsParams& p);
 
 // Gradient of an element scan: p as planned for the forward call (initial
 // contiguous), h (the forward result) and g (its gradient) in out's layout;
-// gx and gs full-width gradients of the two sequences in out's layout; ginit
-// in initial's layout.
+// gx and gs full-width gradients of the two sequences in out's layout (or,
+// norm-cap only, with gx_sum / gs_sum set, the width-one gradient: contiguous,
+// out's shape with the state axis of width one); ginit in initial's layout.
 struct EsVjpParams {
   EsParams p;
   const float* h;
@@ -74,8 +75,23 @@ struct EsVjpParams {
   float* gx;
   float* gs;
   float* ginit;
+  int gx_sum, gs_sum;    // norm-cap: the sequence has width one, its gradient is summed over the state
+  float* bounds;         // norm-cap with few lanes: 2 floats per lane of workspace (nullptr: serial rows)
 };
 hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipStream_t stream);
+// workspace words the norm-cap gradient's split along the axis takes
+int64_t element_scan_backward_bound_words(sx_body body, const EsParams& p);
+// The norm-capped body with four state components per thread (normcap_quad.hip):
+// n == 16, unit component strides (or width one), 16-byte alignment,
+// non-negative strides and tensors spanning fewer than 2^31 bytes.
+struct NcQuadSpans {
+  int32_t x, s, out;  // bytes from each base pointer to one past its last element
+};
+bool normcap_quad_forward_eligible(const EsParams& p);
+hipError_t launch_normcap_quad_forward(const EsParams& p, hipStream_t stream);
+bool normcap_quad_eligible(const EsVjpParams& v);
+hipError_t launch_normcap_quad_backward(const EsVjpParams& v, hipStream_t stream);
+int64_t normcap_quad_bound_words(const EsParams& p);
 
 // ---------------------------------------------------------------- table-scan
 

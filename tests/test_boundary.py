@@ -236,7 +236,8 @@ def _esb(lib, body=2, shape=(4, 8, 3), axis=1, state_axis=B.SX_STATE_SCALAR, ptr
     (dict(ptrs={"gx": FAKE + (3 << 20) + 8}), B.SX_E_ALIAS),             # grad_x over h
     (dict(ptrs={"gs": FAKE + (6 << 20) + 4}), B.SX_E_ALIAS),             # grad_s over grad_x
     (dict(ptrs={"gi": FAKE + 4}), B.SX_E_ALIAS),                          # grad_initial over initial
-    (dict(body=1, shape=(4, 8, 3), state_axis=-1, x_width=3, s_width=1), B.SX_E_WORKSPACE),  # width-1 gate sums
+    (dict(body=0, shape=(4, 8, 3), state_axis=-1, x_width=3, s_width=1), B.SX_E_WORKSPACE),  # width-1 gate sums
+    (dict(body=1, shape=(4, 64, 3), state_axis=-1, x_width=3, s_width=3), B.SX_E_WORKSPACE),  # norm-cap split
 ])
 def test_element_scan_backward_rejects_on_host(lib, kwargs, code):
     st, msg = _esb(lib, **kwargs)
@@ -247,9 +248,18 @@ def test_element_scan_backward_rejects_on_host(lib, kwargs, code):
 def test_element_scan_backward_workspace_query(lib):
     q = lib.sx_element_scan_backward_workspace_bytes
     assert q(0, 3, B.i64_array([4, 64, 32]), 1, B.SX_STATE_SCALAR, 32, 32) == 0
-    need = q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 1)
+    need = q(0, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 1)
     assert need >= 8 * 1024 * 16 * 16 * 4 and need % 256 == 0   # the width-1 gate's full-width gradient
-    assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == 0
+    # norm-cap sums a width-one gate's gradient in its kernels: only the split's bounds remain
+    # (128 state vectors, 128 chunks of 8 trips: two bounds per vector and group of chunks (8 groups)
+    # and one product per chunk and vector)
+    assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 1) == (2 * 8 + 128) * 128 * 4
+    assert q(1, 4, B.i64_array([8, 1024, 2048, 16]), 1, -1, 1, 1) == 0
+    # norm-cap with few state vectors splits the axis
+    assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == (2 * 8 + 128) * 128 * 4
+    assert q(1, 4, B.i64_array([8, 15, 16, 16]), 1, -1, 16, 16) == 0     # too few trips to split
+    assert q(1, 4, B.i64_array([8, 1024, 2048, 16]), 1, -1, 16, 16) == 0  # enough state vectors
+    assert q(0, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == 0   # tanh-affine needs none
     assert q(2, 3, B.i64_array([4, 8, 3]), 5, B.SX_STATE_SCALAR, 3, 3) == 0  # invalid axis
 
 

@@ -10,7 +10,11 @@ winner, norm-cap's cap) from the same states.
 
 The bar is that of a linear scan, which the adjoint is: |gpu - ref| <=
 1e-4 * max(|ref|, RMS of |ref| over the scan axis of the same lane, 1e-6)
-elementwise, for grad_initial (floored by its own RMS), grad_x and grad_s.
+elementwise, for grad_initial (floored by its own RMS), grad_x and grad_s. The
+gradient of a width-one sequence under a vector state is a sum over the state
+of full-width terms; its scale is also floored by the sum of those terms'
+scales (the same bar carried through the sum: where the terms cancel, f32
+keeps an error of their size, not of the result's).
 
 Separate cases run GPU forward and GPU backward end to end through autograd
 (``sx.element_scan`` with inputs that require grad), where the lane kernels'
@@ -30,16 +34,69 @@ DEV = "cuda:0"
 TOL = 1e-4
 
 
-def _close(got, ref, axis, what):
-    g = got.detach().float().cpu().numpy().astype(np.float64)
-    assert g.shape == ref.shape, (what, g.shape, ref.shape)
-    if ref.size == 0:
-        return
+def _scale(ref, axis):
+    """The per-element scale of the bar: max(|ref|, RMS of |ref| along the scan axis)."""
     if axis is None:
         floor = np.sqrt(np.mean(ref ** 2))
     else:
         floor = np.sqrt(np.mean(ref ** 2, axis=axis, keepdims=True))
-    scale = np.maximum(np.maximum(np.abs(ref), floor), 1e-6)
+    return np.maximum(np.abs(ref), floor)
+
+
+TIE = 1e-5  # |y|^2 this close to 1 (relative): the two sides' f32 sums may take the cap either way
+
+
+def _norm_cap_ties(init, x, s, axis, reverse):
+    """Decision-dependent elements of a norm-cap gradient.
+
+    Both sides decide the cap (|y|^2 > 1) in f32 from the same forward states,
+    but sum |y|^2 in different orders, so a trip whose |y|^2 is within a few
+    ulps of 1 may go either way; either result is a correct f32 evaluation.
+    The trips after it in scan order do not depend on that decision (the
+    gradient runs last to first); it and the trips before it, and
+    grad_initial, do. Returns (mask over h's shape, mask over initial's
+    shape), true where an element depends on such a near tie."""
+    x32, s32, i32 = (np.asarray(t.numpy(), dtype=np.float32) for t in (x, s, init))
+    h32 = oracle.element_scan("norm_cap", i32, [x32, s32], axis=axis, state_axis=-1, reverse=reverse,
+                              dtype=np.float32)
+    ax = axis % h32.ndim
+    n = h32.shape[-1]
+    ht = np.moveaxis(h32, ax, 0)
+    xt = np.moveaxis(np.broadcast_to(x32, x32.shape[:-1] + (n,)), ax, 0)
+    st = np.moveaxis(np.broadcast_to(s32, s32.shape[:-1] + (n,)), ax, 0)
+    T = ht.shape[0]
+    order = list(range(T - 1, -1, -1)) if reverse else list(range(T))
+    dep = np.zeros(ht.shape[:-1], dtype=bool)  # [T, lanes...]
+    hit = np.zeros(ht.shape[1:-1], dtype=bool)
+    for i in range(T - 1, -1, -1):  # last to first: a tie marks itself and every earlier trip
+        t = order[i]
+        hp = ht[order[i - 1]] if i > 0 else i32
+        y = st[t] * hp + xt[t]
+        ss = np.sum(y.astype(np.float64) ** 2, axis=-1)
+        hit |= np.abs(ss - 1.0) < TIE
+        dep[t] = hit
+    mask = np.moveaxis(np.broadcast_to(dep[..., None], ht.shape), 0, ax)
+    return mask, hit[..., None] if init.dim() == hit.ndim + 1 else hit
+
+
+def _close(got, ref, axis, what, summed_scale=None, skip=None):
+    """summed_scale: for a width-one sequence's gradient (a sum over the state of
+    full-width terms), the sum of those terms' scales, so that the bar is the
+    per-element bar carried through the sum (cancellation in the sum leaves the
+    f32 result with an error of the size of its terms, not of the result)."""
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    if ref.size == 0:
+        return
+    scale = np.maximum(_scale(ref, axis), 1e-6)
+    if summed_scale is not None:
+        scale = np.maximum(scale, summed_scale)
+    if skip is not None:  # near-tie dependent elements: either branch is correct; they must be finite
+        skip = np.broadcast_to(skip, g.shape)
+        assert np.all(np.isfinite(g[skip])), f"{what}: non-finite values where a near tie decides"
+        g, ref, scale = g[~skip], ref[~skip], scale[~skip]
+        if ref.size == 0:
+            return
     err = np.abs(g - ref)
     bad = err > TOL * scale
     if bad.any():
@@ -75,9 +132,29 @@ def _run(body, x, s, init, g, axis, state_axis, reverse):
     ri, (rx, rs) = oracle.element_scan_vjp(body, init.numpy(), [x.numpy(), s.numpy()], g.numpy(), axis=axis,
                                            state_axis=state_axis, reverse=reverse)
     ax = axis % x.dim()
-    _close(gi, ri, None, "grad_initial")
-    _close(gx, rx, ax, "grad_x")
-    _close(gs, rs, ax, "grad_s")
+    sums = [None, None]
+    if state_axis is not None and g.shape[-1] > 1 and 1 in (x.shape[-1], s.shape[-1]):
+        # width-one sequences: the full-width terms their gradients sum, from the oracle on broadcast copies
+        full = tuple(g.shape)
+        _, terms = oracle.element_scan_vjp(body, init.numpy(), [x.expand(full).numpy().copy(),
+                                           s.expand(full).numpy().copy()], g.numpy(), axis=axis,
+                                           state_axis=state_axis, reverse=reverse)
+        for i, t in enumerate((x, s)):
+            if t.shape[-1] == 1:
+                sums[i] = np.sum(_scale(terms[i], ax), axis=-1, keepdims=True)
+    skip_h, skip_i = (None, None)
+    if body == "norm_cap":
+        skip_h, skip_i = _norm_cap_ties(init, x, s, axis, reverse)
+    _close(gi, ri, None, "grad_initial", skip=skip_i)
+    _close(gx, rx, ax, "grad_x", sums[0], skip=_width(skip_h, x))
+    _close(gs, rs, ax, "grad_s", sums[1], skip=_width(skip_h, s))
+
+
+def _width(mask, t):
+    """A mask over h's shape narrowed to a width-one sequence's (any element of the state)."""
+    if mask is None or t.shape[-1] == mask.shape[-1]:
+        return mask
+    return np.any(mask, axis=-1, keepdims=True)
 
 
 def _init_and_g(shape, axis, gen, state=False):
@@ -130,6 +207,75 @@ def test_norm_cap_workload_shape():
     _run("norm_cap", x, s, init, g, 1, -1, False)
 
 
+@pytest.mark.parametrize("case", ["certified", "gate_one", "mixed", "zero_g_lane", "zero_gate", "small_x"])
+@pytest.mark.parametrize("n,sw", [(16, 1), (5, 5)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_norm_cap_split_axis(case, n, sw, reverse):
+    """Few state vectors and a long axis: the sweep is cut into chunks with certified warm-ups.
+    gate_one makes the per-trip bound reach 1 (no certificate: the lane runs exactly from the
+    sweep's start), mixed has such lanes beside certified ones, zero_g_lane a lane whose upstream
+    gradient is zero, zero_gate gates of zero (the adjoint never crosses a trip), small_x bounds
+    just under 1 (long warm-ups)."""
+    gen = torch.Generator().manual_seed(161 + n)
+    B, T, C = 2, 1500, 3
+    x = 2.0 * torch.randn((B, T, C, n), generator=gen)
+    s = 0.8 + 0.2 * torch.rand((B, T, C, sw), generator=gen)
+    g = torch.randn((B, T, C, n), generator=gen)
+    if case == "gate_one":
+        s = torch.ones_like(s)
+        x = 0.5 * x
+    elif case == "mixed":
+        s[:, :, 1] = 1.0
+        x[:, :, 1] *= 0.25
+    elif case == "zero_g_lane":
+        g[1, :, 2] = 0.0
+    elif case == "zero_gate":
+        s = torch.zeros_like(s)
+    elif case == "small_x":
+        x = 0.35 * x
+    init = 0.3 * torch.randn((B, C, n), generator=gen)
+    _run("norm_cap", x, s, init, g, 1, -1, reverse)
+
+
+@pytest.mark.parametrize("lead", [(2, 40, 4200), (3, 20, 2), (1, 33, 1)])
+@pytest.mark.parametrize("xw,sw", [(16, 1), (1, 16), (1, 1), (16, 16)])
+def test_norm_cap_width_one_sums(lead, xw, sw):
+    """Width-one x or gate under a 16-wide state, summed over the state inside the norm-cap
+    kernels: many state vectors (one row each), a short axis (one row each) and the
+    shortest split axis."""
+    x, s, full, gen = _draw("norm_cap", lead, 16, seed=171 + xw + sw, x_width=xw, s_width=sw)
+    init = 0.3 * torch.randn((lead[0], lead[2], 16), generator=gen)
+    g = torch.randn(full, generator=gen)
+    _run("norm_cap", x, s, init, g, 1, -1, False)
+
+
+@pytest.mark.parametrize("T", [20, 600])
+def test_norm_cap_unaligned_views(T):
+    """x and the gate as views whose offsets are not multiples of four elements: the
+    one-component-per-thread kernels take these (the four-per-thread ones need 16-byte
+    alignment)."""
+    gen = torch.Generator().manual_seed(181)
+    xb = 2.0 * torch.randn((3, T, 5, 17), generator=gen)
+    sb = 0.8 + 0.2 * torch.rand((3, T, 5, 17), generator=gen)
+    x, s = xb[..., 1:], sb[..., :16]
+    init = 0.3 * torch.randn((3, 5, 16), generator=gen)
+    g = torch.randn((3, T, 5, 16), generator=gen)
+    print(f"\n[case] norm_cap unaligned views T {T}", flush=True)
+    xd, sd = xb.to(DEV)[..., 1:], sb.to(DEV)[..., :16]
+    h32 = oracle.element_scan("norm_cap", init.numpy(), [x.numpy(), s.numpy()], axis=1, state_axis=-1,
+                              dtype=np.float32)
+    gi, (gx, gs) = sx.element_scan_backward("norm_cap", init.to(DEV), [xd, sd],
+                                            torch.from_numpy(np.ascontiguousarray(h32)).to(DEV), g.to(DEV),
+                                            axis=1, state_axis=-1)
+    torch.cuda.synchronize()
+    ri, (rx, rs) = oracle.element_scan_vjp("norm_cap", init.numpy(), [x.numpy(), s.numpy()], g.numpy(), axis=1,
+                                           state_axis=-1)
+    skip_h, skip_i = _norm_cap_ties(init, x, s, 1, False)
+    _close(gi, ri, None, "grad_initial", skip=skip_i)
+    _close(gx, rx, 1, "grad_x", skip=skip_h)
+    _close(gs, rs, 1, "grad_s", skip=skip_h)
+
+
 def test_max_plus_workload_sampled_lanes():
     """The reverse max-plus workload at full size, [64,4096,256]: the GPU gradient
     of every lane from the oracle's float32 forward states; the oracle gradient
@@ -175,9 +321,10 @@ def test_autograd_through_element_scan(body, state, reverse):
     (h * w.to(DEV)).sum().backward()
     ri, (rx, rs) = oracle.element_scan_vjp(body, init.numpy(), [x.numpy(), s.numpy()], w.numpy(), axis=1,
                                            state_axis=st, reverse=reverse)
-    _close(idd.grad, ri, None, "grad_initial")
-    _close(xd.grad, rx, 1, "grad_x")
-    _close(sd.grad, rs, 1, "grad_s")
+    skip_h, skip_i = _norm_cap_ties(init, x, s, 1, reverse) if body == "norm_cap" else (None, None)
+    _close(idd.grad, ri, None, "grad_initial", skip=skip_i)
+    _close(xd.grad, rx, 1, "grad_x", skip=_width(skip_h, x))
+    _close(sd.grad, rs, 1, "grad_s", skip=_width(skip_h, s))
 
 
 def test_element_grad_errors():
