@@ -49,8 +49,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
 METRIC = "scan elements/s and achieved HBM GB/s vs MI355X peak (rocprof), per config"
-KERNEL_SOURCES = ["scan_primitives_amd/csrc/element_scan.hip", "scan_primitives_amd/csrc/matrix_scan.hip",
-                  "scan_primitives_amd/csrc/matrix_scan_grad.hip"]
+KERNEL_SOURCES = ["scan_primitives_amd/csrc/element_scan.hip", "scan_primitives_amd/csrc/normcap_quad.hip",
+                  "scan_primitives_amd/csrc/matrix_scan.hip", "scan_primitives_amd/csrc/matrix_scan_grad.hip",
+                  "scan_primitives_amd/csrc/table_scan.hip"]
 
 
 def log(*a):
