@@ -240,7 +240,10 @@ int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, con
  *   grad_a[t] = lam[t] @ h[p]^T        (zero at the first step, whose a
  *                                      multiplies the zero state)
  * summed over the dims along which a (or b) was broadcast. lam is computed in
- * f32 by the matrix-scan kernels in the other direction.
+ * f32 by the matrix-scan kernels in the other direction. With bf16 gradients
+ * and b of the result's shape, lam is stored rounded into grad_b and grad_a
+ * is formed from that rounded lam (a relative change of at most 2^-9 per
+ * element of lam, inside bf16's own rounding of the result).
  *
  *  dtype         SX_F32 or SX_BF16: the dtype of a, h and g alike.
  *  a_*           a as passed to sx_matrix_scan (strides as there).

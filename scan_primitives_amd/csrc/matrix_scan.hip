@@ -1635,12 +1635,17 @@ hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspa
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;
   const size_t need = matrix_scan_workspace(p);
   const bool chunked = need > 0 && workspace != nullptr && workspace_bytes >= need;
-  if (p.adjoint) {  // the adjoint is kept in f32
-    if (p.out_bf16) return hipErrorInvalidValue;
-    if (chunked)
-      return p.in_bf16 ? launch_chunked<uint16_t, float, true>(p, workspace, stream)
-                       : launch_chunked<float, float, true>(p, workspace, stream);
-    return p.in_bf16 ? launch_serial<uint16_t, float, true>(p, stream) : launch_serial<float, float, true>(p, stream);
+  if (p.adjoint) {  // computed in f32; stored in f32, or rounded to bf16 when that is the gradient's dtype
+    if (chunked) {
+      if (p.in_bf16)
+        return p.out_bf16 ? launch_chunked<uint16_t, uint16_t, true>(p, workspace, stream)
+                          : launch_chunked<uint16_t, float, true>(p, workspace, stream);
+      return p.out_bf16 ? launch_chunked<float, uint16_t, true>(p, workspace, stream)
+                        : launch_chunked<float, float, true>(p, workspace, stream);
+    }
+    if (p.in_bf16)
+      return p.out_bf16 ? launch_serial<uint16_t, uint16_t, true>(p, stream) : launch_serial<uint16_t, float, true>(p, stream);
+    return p.out_bf16 ? launch_serial<float, uint16_t, true>(p, stream) : launch_serial<float, float, true>(p, stream);
   }
   if (chunked) {
     if (p.in_bf16)

@@ -15,8 +15,11 @@
 //                     storing four consecutive values of one row; n = 16 with
 //                     16 | m: lam h^T on MFMA; other shapes element by element.
 //                     It also stores grad_b[t] when that is lam rounded to
-//                     bf16. Bound by HBM (a 1 KiB grad_a block per step for
-//                     n = 16, f32).
+//                     bf16 from an f32 lam. When grad_b is bf16 and has the
+//                     result's shape, the scan writes lam straight into it,
+//                     rounded, and this kernel reads that rounded lam (one
+//                     bf16 stream instead of an f32 one out and back). Bound
+//                     by HBM (a 1 KiB grad_a block per step for n = 16, f32).
 //   sum_to_partial_kernel / sum_to_final_kernel
 //                     the sum over broadcast dims, in two passes (partial sums
 //                     over slices of the summed index space, then their sum in
@@ -56,12 +59,12 @@ __device__ __forceinline__ int64_t prev_step(const GradAParams& g, int64_t s, bo
 // n = 16, m = 1: grad_a[i][j] = lam[i] h[j]. Lane (i, jq), i = lane / 4, forms
 // grad_a[i][4jq .. 4jq+3] and stores it as one piece, so the wave writes the
 // step's block contiguously.
-template <typename TH, typename TA>
+template <typename TL, typename TH, typename TA>
 __device__ __forceinline__ void grad_a_m1(const GradAParams& g, int64_t s, int lane) {
   const int i = lane >> 2, jq = lane & 3;
   bool first;
   const int64_t p = prev_step(g, s, first);
-  const float l = g.lam[s * 16 + i];
+  const float l = ld_f(static_cast<const TL*>(g.lam) + s * 16 + i);
   const f32x4 hv = ld4(static_cast<const TH*>(g.h) + p * 16 + 4 * jq);
   const f32x4 d = first ? zero4() : l * hv;
   st4(static_cast<TA*>(g.grad_a) + s * 256 + i * 16 + 4 * jq, d);
@@ -72,12 +75,12 @@ __device__ __forceinline__ void grad_a_m1(const GradAParams& g, int64_t s, int l
 // supplies row c of lam and row c of h (columns 4r .. 4r+3 of each 16-block),
 // which are the A and X operands of lam h^T; a quad transpose of the result
 // gives each lane four consecutive values of one row to store.
-template <typename TH, typename TA>
+template <typename TL, typename TH, typename TA>
 __device__ __forceinline__ void grad_a_tiles(const GradAParams& g, int64_t s, int lane) {
   const int r = lane >> 4, c = lane & 15, m = g.m;
   bool first;
   const int64_t p = prev_step(g, s, first);
-  const float* lr = g.lam + s * 16 * m + int64_t(c) * m + 4 * r;
+  const TL* lr = static_cast<const TL*>(g.lam) + s * 16 * m + int64_t(c) * m + 4 * r;
   const TH* hr = static_cast<const TH*>(g.h) + p * 16 * m + int64_t(c) * m + 4 * r;
   uint16_t* br = g.grad_b ? static_cast<uint16_t*>(g.grad_b) + s * 16 * m + int64_t(c) * m + 4 * r : nullptr;
   f32x4 acc = zero4();
@@ -92,13 +95,13 @@ __device__ __forceinline__ void grad_a_tiles(const GradAParams& g, int64_t s, in
 }
 
 // Any n <= 16, m: lane (i, jq) forms grad_a[i][4jq .. 4jq+3] element by element.
-template <typename TH, typename TA>
+template <typename TL, typename TH, typename TA>
 __device__ __forceinline__ void grad_a_any(const GradAParams& g, int64_t s, int lane) {
   const int i = lane >> 2, jq = lane & 3;
   const int n = g.n, m = g.m;
   bool first;
   const int64_t p = prev_step(g, s, first);
-  const float* lam = g.lam + s * int64_t(n) * m;
+  const TL* lam = static_cast<const TL*>(g.lam) + s * int64_t(n) * m;
   const TH* hp = static_cast<const TH*>(g.h) + p * int64_t(n) * m;
   const int ic = i < n ? i : n - 1;  // clamped rows: every load is in bounds
   int jc[4];
@@ -106,7 +109,7 @@ __device__ __forceinline__ void grad_a_any(const GradAParams& g, int64_t s, int 
   for (int q = 0; q < 4; ++q) jc[q] = 4 * jq + q < n ? 4 * jq + q : n - 1;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k = 0; k < m; ++k) {
-    const float l = lam[int64_t(ic) * m + k];
+    const float l = ld_f(lam + int64_t(ic) * m + k);
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(l, ld_f(hp + int64_t(jc[q]) * m + k), acc[q]);
   }
@@ -118,20 +121,21 @@ __device__ __forceinline__ void grad_a_any(const GradAParams& g, int64_t s, int 
   }
   if (g.grad_b != nullptr && i < n) {  // grad_b = lam rounded to bf16; the row's four lanes split it
     uint16_t* gb = static_cast<uint16_t*>(g.grad_b) + s * int64_t(n) * m + int64_t(i) * m;
-    for (int kk = jq; kk < m; kk += 4) st_f(gb + kk, lam[int64_t(i) * m + kk]);
+    for (int kk = jq; kk < m; kk += 4) st_f(gb + kk, ld_f(lam + int64_t(i) * m + kk));
   }
 }
 
 // One wave per step, the waves of the grid striding over the steps.
-// TH: element type of h; TA: of grad_a (bf16 only when it is the final result).
-template <int PATH, typename TH, typename TA>
+// TL: element type of lam (bf16 when it was rounded into a bf16 grad_b);
+// TH: of h; TA: of grad_a (bf16 only when it is the final result).
+template <int PATH, typename TL, typename TH, typename TA>
 __global__ __launch_bounds__(256) void ms_grad_a_kernel(const GradAParams g) {
   const int lane = int(threadIdx.x) & 63;
   const int64_t nw = int64_t(gridDim.x) * 4;
   for (int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); s < g.steps; s += nw) {
-    if constexpr (PATH == 1) grad_a_m1<TH, TA>(g, s, lane);
-    else if constexpr (PATH == 2) grad_a_tiles<TH, TA>(g, s, lane);
-    else grad_a_any<TH, TA>(g, s, lane);
+    if constexpr (PATH == 1) grad_a_m1<TL, TH, TA>(g, s, lane);
+    else if constexpr (PATH == 2) grad_a_tiles<TL, TH, TA>(g, s, lane);
+    else grad_a_any<TL, TH, TA>(g, s, lane);
   }
 }
 
@@ -171,16 +175,21 @@ __global__ __launch_bounds__(256) void sum_to_final_kernel(const SumToParams p, 
 }  // namespace
 
 namespace {
-template <int PATH>
+template <int PATH, typename TL>
 void launch_grad_a_path(const GradAParams& g, bool h_bf16, bool grad_a_bf16, dim3 grid, hipStream_t stream) {
   const dim3 block{256};
   if (h_bf16) {
-    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, uint16_t, uint16_t>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, uint16_t, float>), grid, block, 0, stream, g);
+    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, TL, uint16_t, uint16_t>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, TL, uint16_t, float>), grid, block, 0, stream, g);
   } else {
-    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, float, uint16_t>), grid, block, 0, stream, g);
-    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, float, float>), grid, block, 0, stream, g);
+    if (grad_a_bf16) hipLaunchKernelGGL((ms_grad_a_kernel<PATH, TL, float, uint16_t>), grid, block, 0, stream, g);
+    else hipLaunchKernelGGL((ms_grad_a_kernel<PATH, TL, float, float>), grid, block, 0, stream, g);
   }
+}
+template <int PATH>
+void launch_grad_a_lam(const GradAParams& g, bool h_bf16, bool grad_a_bf16, dim3 grid, hipStream_t stream) {
+  if (g.lam_bf16) launch_grad_a_path<PATH, uint16_t>(g, h_bf16, grad_a_bf16, grid, stream);
+  else launch_grad_a_path<PATH, float>(g, h_bf16, grad_a_bf16, grid, stream);
 }
 }  // namespace
 
@@ -191,11 +200,11 @@ hipError_t launch_grad_a(const GradAParams& g, bool h_bf16, bool grad_a_bf16, hi
   const dim3 grid{unsigned(blocks)};
   // the fast paths read and write whole 16-byte (f32) or 8-byte (bf16) pieces
   auto aligned = [](const void* q, uintptr_t a) { return q == nullptr || reinterpret_cast<uintptr_t>(q) % a == 0; };
-  const bool al = aligned(g.lam, 16) && aligned(g.h, h_bf16 ? 8 : 16) && aligned(g.grad_a, grad_a_bf16 ? 8 : 16) &&
-                  aligned(g.grad_b, 8);
-  if (g.n == 16 && g.m == 1 && al) launch_grad_a_path<1>(g, h_bf16, grad_a_bf16, grid, stream);
-  else if (g.n == 16 && g.m % 16 == 0 && al) launch_grad_a_path<2>(g, h_bf16, grad_a_bf16, grid, stream);
-  else launch_grad_a_path<0>(g, h_bf16, grad_a_bf16, grid, stream);
+  const bool al = aligned(g.lam, g.lam_bf16 ? 8 : 16) && aligned(g.h, h_bf16 ? 8 : 16) &&
+                  aligned(g.grad_a, grad_a_bf16 ? 8 : 16) && aligned(g.grad_b, 8);
+  if (g.n == 16 && g.m == 1 && al) launch_grad_a_lam<1>(g, h_bf16, grad_a_bf16, grid, stream);
+  else if (g.n == 16 && g.m % 16 == 0 && al) launch_grad_a_lam<2>(g, h_bf16, grad_a_bf16, grid, stream);
+  else launch_grad_a_lam<0>(g, h_bf16, grad_a_bf16, grid, stream);
   return hipGetLastError();
 }
 

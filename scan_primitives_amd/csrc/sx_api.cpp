@@ -526,14 +526,13 @@ struct MsBackPlan {
   int out_rank;
   int64_t out_shape[sx::kMaxRank + 2];  // lead + [n, m]
   int64_t out_numel, a_full_numel;
-  bool lam_direct, ga_direct;           // lam is grad_b itself; grad_a written in place
+  bool lam_direct, ga_direct;           // lam is grad_b itself (f32, or rounded to a bf16 grad_b); grad_a in place
   sx::SumToParams sum_a, sum_b;
   size_t scan_ws, lam_off, ga_off, part_off, total;
 };
 
 sx_status plan_matrix_scan_backward(int a_rank, const int64_t* a_shape, const int64_t* a_strides, int b_rank,
-                                    const int64_t* b_shape, const int64_t* g_strides, int axis, bool grad_f32,
-                                    MsBackPlan* bp) {
+                                    const int64_t* b_shape, const int64_t* g_strides, int axis, MsBackPlan* bp) {
   sx::MsParams fwd;
   int64_t numel = 0;
   sx_status st = plan_matrix_scan(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, &fwd, bp->out_shape,
@@ -551,7 +550,9 @@ sx_status plan_matrix_scan_backward(int a_rank, const int64_t* a_shape, const in
   std::copy(bp->out_shape, bp->out_shape + L, afull);
   afull[L] = afull[L + 1] = n;
   checked_numel(L + 2, afull, &bp->a_full_numel);
-  bp->lam_direct = grad_f32 && same_shape(b_rank, b_shape, bp->out_rank, bp->out_shape);
+  // with b at the result's shape, the scan writes lam straight into grad_b: in f32, or rounded to
+  // bf16 when the gradients are bf16 (grad_a then forms lam h^T from the rounded lam)
+  bp->lam_direct = same_shape(b_rank, b_shape, bp->out_rank, bp->out_shape);
   bp->ga_direct = same_shape(a_rank, a_shape, L + 2, afull);
   bp->sum_a = sum_to_plan(L + 2, afull, a_rank, a_shape);
   bp->sum_b = sum_to_plan(bp->out_rank, bp->out_shape, b_rank, b_shape);
@@ -577,9 +578,8 @@ extern "C" {
 size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
                                                int axis, sx_dtype grad_dtype) {
   MsBackPlan bp;
-  if (plan_matrix_scan_backward(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, grad_dtype == SX_F32,
-                                &bp) != SX_OK)
-    return 0;
+  if (grad_dtype != SX_F32 && grad_dtype != SX_BF16) return 0;
+  if (plan_matrix_scan_backward(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, &bp) != SX_OK) return 0;
   return bp.total;
 }
 
@@ -592,8 +592,7 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
   if (grad_dtype != SX_F32 && grad_dtype != SX_BF16)
     return fail(SX_E_DIM_002, "matrix-scan gradient: gradients must be f32 or bf16 (dtype code %d)", int(grad_dtype));
   MsBackPlan bp;
-  sx_status st = plan_matrix_scan_backward(a_rank, a_shape, a_strides, b_rank, b_shape, g_strides, axis,
-                                           grad_dtype == SX_F32, &bp);
+  sx_status st = plan_matrix_scan_backward(a_rank, a_shape, a_strides, b_rank, b_shape, g_strides, axis, &bp);
   if (st != SX_OK) return st;
   int64_t a_numel = 0, b_numel = 0;
   checked_numel(a_rank, a_shape, &a_numel);
@@ -645,10 +644,11 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* lam = bp.lam_direct ? static_cast<float*>(grad_b) : reinterpret_cast<float*>(ws + bp.lam_off);
+  void* lam = bp.lam_direct ? grad_b : static_cast<void*>(ws + bp.lam_off);
+  const bool lam_bf16 = bp.lam_direct && grad_dtype == SX_BF16;
   // 1. the adjoint: the scan in the other direction over g, on a transposed and shifted a step
   bp.p.in_bf16 = dtype == SX_BF16;
-  bp.p.out_bf16 = 0;
+  bp.p.out_bf16 = lam_bf16 ? 1 : 0;
   bp.p.reverse = reverse ? 0 : 1;
   bp.p.adjoint = 1;
   bp.p.a = a;
@@ -669,6 +669,7 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
   gp.m = int(bp.out_shape[L + 1]);
   gp.reverse = reverse ? 1 : 0;
   gp.lam = lam;
+  gp.lam_bf16 = lam_bf16 ? 1 : 0;
   gp.h = h;
   gp.grad_a = bp.ga_direct ? grad_a : static_cast<void*>(ws + bp.ga_off);
   const bool b_full = same_shape(b_rank, b_shape, bp.out_rank, bp.out_shape);
@@ -683,7 +684,7 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
     if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_a sum launch");
   }
   if (!b_full && b_numel > 0) {
-    bp.sum_b.src = lam;
+    bp.sum_b.src = static_cast<const float*>(lam);
     bp.sum_b.partial = reinterpret_cast<float*>(ws + bp.part_off);
     e = sx::launch_sum_to(bp.sum_b, grad_b, grad_dtype == SX_BF16, s);
     if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_b sum launch");

@@ -157,7 +157,8 @@ struct GradAParams {
   int64_t T, inner;      // scan axis length; product of the leading dims after it
   int n, m;
   int reverse;           // of the forward scan
-  const float* lam;      // contiguous, leading dims + [n, m], f32
+  const void* lam;       // contiguous, leading dims + [n, m]; bf16 when lam_bf16, else f32
+  int lam_bf16;
   const void* h;         // the forward result, contiguous, leading dims + [n, m]
   void* grad_a;          // contiguous, leading dims + [n, n]; bf16 when grad_a_bf16, else f32
   void* grad_b;          // nullptr, or contiguous bf16, leading dims + [n, m]

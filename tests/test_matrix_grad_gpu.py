@@ -102,8 +102,12 @@ def test_grad_bf16_operands_f32_gradients():
     _check(a, b, 1, False, seed=61, grad_dtype=torch.float32)
 
 
-def test_grad_f32_operands_bf16_gradients():
-    a, b, _ = _draw((2, 300, 16, 16), (2, 300, 16, 1), torch.float32, seed=62)
+@pytest.mark.parametrize("n,m,dt", [(16, 1, torch.float32), (16, 16, torch.float32), (5, 3, torch.float32),
+                                    (5, 3, torch.bfloat16), (16, 32, torch.bfloat16)])
+def test_grad_bf16_gradients(n, m, dt):
+    # bf16 gradients with b at the result's shape: the adjoint is rounded into grad_b and grad_a is
+    # formed from it (one-, MFMA- and element-wise grad_a paths, f32 and bf16 h)
+    a, b, _ = _draw((2, 300, n, n), (2, 300, n, m), dt, seed=62 + n + m)
     _check(a, b, 1, True, seed=62, grad_dtype=torch.bfloat16)
 
 
