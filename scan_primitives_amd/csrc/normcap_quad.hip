@@ -460,20 +460,23 @@ __global__ __launch_bounds__(256) void nc_quad_grad_kernel(const EsVjpParams v, 
 
 // ----------------------------------------------------------------- host side
 
-// Quads in flight: about kQuadRows rows, chunks of at least kFwdMinLen
-// (forward) or kGradMinLen (gradient) trips.
-constexpr int64_t kQuadRows = 16384;
+// Quads in flight: about kFwdRows (forward) or kGradRows (gradient) rows, in
+// chunks of at least kFwdMinLen or kGradMinLen trips. Measured on [8,1024,16,16]
+// and [64,1024,16,16]: more rows help the gradient's longer per-row chains on
+// the larger shape and slow the forward there.
+constexpr int64_t kFwdRows = 16384;
+constexpr int64_t kGradRows = 32768;
 constexpr int64_t kFwdMinLen = 16;
 constexpr int64_t kGradMinLen = 8;
 constexpr int64_t kMaxSpan = int64_t(1) << 31;  // bytes a buffer resource here may cover
 
-bool split_of(const EsParams& p, int64_t min_len, int64_t* len, int64_t* nchunks) {
-  if (!(p.num_lanes > 0 && p.num_lanes < kQuadRows && p.T >= 2 * min_len)) {
+bool split_of(const EsParams& p, int64_t rows, int64_t min_len, int64_t* len, int64_t* nchunks) {
+  if (!(p.num_lanes > 0 && p.num_lanes < rows && p.T >= 2 * min_len)) {
     *len = p.T;
     *nchunks = 1;
     return false;
   }
-  const int64_t c = (kQuadRows + p.num_lanes - 1) / p.num_lanes;
+  const int64_t c = (rows + p.num_lanes - 1) / p.num_lanes;
   int64_t l = (p.T + c - 1) / c;
   if (l < min_len) l = min_len;
   *len = l;
@@ -541,7 +544,7 @@ hipError_t launch_normcap_quad_forward(const EsParams& p, hipStream_t stream) {
   NcQuadSpans sp;
   if (!spans_of(p, &sp)) return hipErrorInvalidValue;
   int64_t len = 0, nchunks = 1;
-  split_of(p, kFwdMinLen, &len, &nchunks);
+  split_of(p, kFwdRows, kFwdMinLen, &len, &nchunks);
   const int64_t blocks = (p.num_lanes * nchunks * 4 + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   by_widths(p, [&](auto x1c, auto s1c) {
@@ -566,7 +569,7 @@ hipError_t launch_normcap_quad_backward(const EsVjpParams& v, hipStream_t stream
   NcQuadSpans sp;
   if (!spans_of(p, &sp)) return hipErrorInvalidValue;
   int64_t len = 0, nchunks = 1;
-  const bool split = split_of(p, kGradMinLen, &len, &nchunks) && v.bounds != nullptr;
+  const bool split = split_of(p, kGradRows, kGradMinLen, &len, &nchunks) && v.bounds != nullptr;
   if (!split) {
     len = p.T;
     nchunks = 1;
@@ -591,7 +594,7 @@ hipError_t launch_normcap_quad_backward(const EsVjpParams& v, hipStream_t stream
 
 int64_t normcap_quad_bound_words(const EsParams& p) {
   int64_t len = 0, nchunks = 1;
-  if (!split_of(p, kGradMinLen, &len, &nchunks)) return 0;
+  if (!split_of(p, kGradRows, kGradMinLen, &len, &nchunks)) return 0;
   return 2 * kXcds * p.num_lanes + nchunks * p.num_lanes;
 }
 

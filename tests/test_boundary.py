@@ -256,11 +256,11 @@ def test_element_scan_backward_workspace_query(lib):
     # (128 state vectors, 128 chunks of 8 trips: two bounds per vector and group of chunks (8 groups)
     # and one product per chunk and vector)
     assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 1) == (2 * 8 + 128) * 128 * 4
-    assert q(1, 4, B.i64_array([8, 1024, 2048, 16]), 1, -1, 1, 1) == 0
+    assert q(1, 4, B.i64_array([8, 1024, 4096, 16]), 1, -1, 1, 1) == 0
     # norm-cap with few state vectors splits the axis
     assert q(1, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == (2 * 8 + 128) * 128 * 4
     assert q(1, 4, B.i64_array([8, 15, 16, 16]), 1, -1, 16, 16) == 0     # too few trips to split
-    assert q(1, 4, B.i64_array([8, 1024, 2048, 16]), 1, -1, 16, 16) == 0  # enough state vectors
+    assert q(1, 4, B.i64_array([8, 1024, 4096, 16]), 1, -1, 16, 16) == 0  # enough state vectors
     assert q(0, 4, B.i64_array([8, 1024, 16, 16]), 1, -1, 16, 16) == 0   # tanh-affine needs none
     assert q(2, 3, B.i64_array([4, 8, 3]), 5, B.SX_STATE_SCALAR, 3, 3) == 0  # invalid axis
 
