@@ -14,7 +14,7 @@
 //                    state (8 or 16 bytes), one per symbol, in LDS, and maps
 //                    compose by byte gathers (v_perm_b32).
 //                    Each lane composes the maps of its K steps, a scan of the
-//                    lanes' maps (six rounds of composition over cross-lane
+//                    lanes' maps (six rounds of composition over DPP lane
 //                    moves) gives each lane its entering state from the slab's
 //                    carry, and each lane replays its steps, storing every
 //                    state. The next slab's symbols are loaded meanwhile.
@@ -50,7 +50,9 @@ __device__ __forceinline__ StateMap<MW> identity_map() {
 // "inner, then outer": entry s is outer[inner[s]], a byte gather. v_perm_b32
 // picks each result byte from the 8 bytes {src0 (high), src1 (low)} by the
 // selector byte (0-7). Sixteen entries take two gathers (entries 0-7 and
-// 8-15) and a byte select on bit 3 of the selector.
+// 8-15) and a byte select on bit 3 of the selector: that bit, moved to bit 2
+// of each byte, selects byte 4 (0xFF) or byte 0 (0x00) of {~0, 0} in a third
+// gather, which gives the byte mask with full-rate instructions only.
 template <int MW>
 __device__ __forceinline__ StateMap<MW> compose(const StateMap<MW>& outer, const StateMap<MW>& inner) {
   StateMap<MW> r;
@@ -61,29 +63,54 @@ __device__ __forceinline__ StateMap<MW> compose(const StateMap<MW>& outer, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t sel = inner.w[j];
-      const uint32_t lo = __builtin_amdgcn_perm(outer.w[1], outer.w[0], sel & 0x07070707u);
-      const uint32_t hi = __builtin_amdgcn_perm(outer.w[3], outer.w[2], sel & 0x07070707u);
-      const uint32_t high = ((sel >> 3) & 0x01010101u) * 0xFFu;  // 0xFF in the bytes that select 8-15
+      const uint32_t low3 = sel & 0x07070707u;
+      const uint32_t lo = __builtin_amdgcn_perm(outer.w[1], outer.w[0], low3);
+      const uint32_t hi = __builtin_amdgcn_perm(outer.w[3], outer.w[2], low3);
+      const uint32_t high = __builtin_amdgcn_perm(0xFFFFFFFFu, 0u, (sel >> 1) & 0x04040404u);  // 0xFF where 8-15
       r.w[j] = (hi & high) | (lo & ~high);
     }
   }
   return r;
 }
 
+// m[s] by byte gathers: byte s of the map moved to byte 0 (a select chain over
+// the words is turned by the compiler into an indexed stack access).
 template <int MW>
 __device__ __forceinline__ uint32_t apply(const StateMap<MW>& m, uint32_t s) {  // m[s]
-  uint32_t w = m.w[0];
-#pragma unroll
-  for (int i = 1; i < MW; ++i) w = (s >> 2) == uint32_t(i) ? m.w[i] : w;
-  return (w >> (8 * (s & 3))) & 0xFFu;
+  if constexpr (MW == 2) {
+    return __builtin_amdgcn_perm(m.w[1], m.w[0], s) & 0xFFu;
+  } else {
+    const uint32_t lo = __builtin_amdgcn_perm(m.w[1], m.w[0], s & 7u);
+    const uint32_t hi = __builtin_amdgcn_perm(m.w[3], m.w[2], s & 7u);
+    return (s & 8u ? hi : lo) & 0xFFu;
+  }
 }
 
-template <int MW>
-__device__ __forceinline__ StateMap<MW> shfl_up_map(const StateMap<MW>& m, int d) {
+// DPP move of a map: lanes whose source lies outside what CTRL allows (or in a
+// row left out by ROW_MASK) get the identity map, which composes as a no-op.
+template <int CTRL, int ROW_MASK, int MW>
+__device__ __forceinline__ StateMap<MW> dpp_map(const StateMap<MW>& m) {
+  const StateMap<MW> id = identity_map<MW>();
   StateMap<MW> r;
 #pragma unroll
-  for (int i = 0; i < MW; ++i) r.w[i] = uint32_t(__shfl_up(int(m.w[i]), d, 64));
+  for (int i = 0; i < MW; ++i)
+    r.w[i] = uint32_t(__builtin_amdgcn_update_dpp(int(id.w[i]), int(m.w[i]), CTRL, ROW_MASK, 0xF, false));
   return r;
+}
+
+// Inclusive scan of the lanes' maps in lane order (lane l ends with the maps of
+// lanes 0..l composed, later ones outermost) with DPP moves only: shifts by 1,
+// 2, 4 and 8 within each row of 16 lanes, then lane 15 of each even row into
+// the odd row after it, then lane 31 into rows 2 and 3.
+template <int MW>
+__device__ __forceinline__ StateMap<MW> scan_maps(StateMap<MW> G) {
+  G = compose<MW>(G, dpp_map<0x111, 0xF>(G));  // row_shr:1
+  G = compose<MW>(G, dpp_map<0x112, 0xF>(G));  // row_shr:2
+  G = compose<MW>(G, dpp_map<0x114, 0xF>(G));  // row_shr:4
+  G = compose<MW>(G, dpp_map<0x118, 0xF>(G));  // row_shr:8
+  G = compose<MW>(G, dpp_map<0x142, 0xA>(G));  // row_bcast:15 into rows 1 and 3
+  G = compose<MW>(G, dpp_map<0x143, 0xC>(G));  // row_bcast:31 into rows 2 and 3
+  return G;
 }
 
 template <int MW>
@@ -113,8 +140,7 @@ __device__ __forceinline__ void wave_lds_sync() {  // the wave's LDS writes are 
 // starts 16-byte aligned. Full slabs then move between HBM and LDS as 16-byte
 // pieces, coalesced across the wave (lane l takes bytes 16 l + 1024 j), and
 // each lane takes its K consecutive positions from LDS.
-// K: positions per lane per slab (16 for maps of 8 bytes, 8 for 16: the step maps of a lane's run
-// are held in registers).
+// K: positions per lane per slab (16: the scan over the lanes is paid once per 1024 positions).
 template <bool VEC, int MW, int K>
 __global__ __launch_bounds__(256) void ts_wave_kernel(const TsParams p) {
   constexpr int64_t kSlab = 64 * K;
@@ -156,14 +182,9 @@ __global__ __launch_bounds__(256) void ts_wave_kernel(const TsParams p) {
       const StateMap<MW> mk = k < valid_from_q ? sMap[clampi(cur[k], 0, X - 1)] : identity_map<MW>();
       F = compose<MW>(mk, F);
     }
-    StateMap<MW> G = F;  // inclusive scan over the lanes: lane l ends with the maps of lanes 0..l composed
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const StateMap<MW> below = shfl_up_map<MW>(G, d);
-      if (lane >= d) G = compose<MW>(G, below);
-    }
-    const StateMap<MW> before = shfl_up_map<MW>(G, 1);
-    uint32_t st = lane == 0 ? carry : apply<MW>(before, carry);
+    const StateMap<MW> G = scan_maps<MW>(F);  // lane l: the maps of lanes 0..l composed
+    const StateMap<MW> before = dpp_map<0x138, 0xF>(G);  // wave_shr:1 (lane 0: the identity)
+    uint32_t st = apply<MW>(before, carry);
     carry = apply<MW>(readlane_map<MW>(G, 63), carry);
 #pragma unroll
     for (int k = 0; k < K; ++k) {  // the step maps again from LDS (keeping them would spill for 16 states)
@@ -277,8 +298,8 @@ hipError_t launch_table_scan(const TsParams& p, hipStream_t stream) {
       if (vec) hipLaunchKernelGGL((ts_wave_kernel<true, 2, 16>), grid, block, 0, stream, p);
       else hipLaunchKernelGGL((ts_wave_kernel<false, 2, 16>), grid, block, 0, stream, p);
     } else {
-      if (vec) hipLaunchKernelGGL((ts_wave_kernel<true, 4, 8>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((ts_wave_kernel<false, 4, 8>), grid, block, 0, stream, p);
+      if (vec) hipLaunchKernelGGL((ts_wave_kernel<true, 4, 16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((ts_wave_kernel<false, 4, 16>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
   }
