@@ -1,6 +1,8 @@
 """The library's calls inside a captured HIP graph give the eager results.
 
-The bench replays captured graphs, so every kernel path is captured here and
+The bench replays captured graphs, so every kernel path is captured here (the
+forward scans, and the calls timed beside the step: linear-scan, cumsum,
+table-scan, :projective and the gradients) and
 replayed several times, with eager calls of the same workload in between,
 and each replay's output is checked against the eager output (and the
 oracle). Element-scan kernels are deterministic, so replays must agree bit for
@@ -62,3 +64,79 @@ def test_graph_replay_matches_eager(name):
             tol = MS_TOL_F32 if w.tensors["a"].dtype == torch.float32 else MS_TOL_BF16
             assert_matrix_close(captured, ref, tol)
             assert_matrix_close(captured, eager.double().cpu().numpy(), MS_TOL_F32)
+
+
+# The calls timed beside the step: each returns a tensor or a tuple of tensors. Deterministic kernels
+# (element-scan and its gradients, linear-scan, table-scan) must replay bit for bit; matrix-scan calls
+# (look-back) are held to the matrix-scan bar against the eager result.
+def _other_cases():
+    nc = W.make_norm_cap(2, 600, 5, 16, seed=311)
+    mp = W.make_max_plus((33, 600, 256), seed=312)
+    return {
+        "linear-scan slab": (W.make_linear((33, 600, 256), a_kind="decay", seed=313), True),
+        "cumsum": (W.make_linear((9, 700, 64), a_kind="ones", seed=314), True),
+        "table-scan parity": (W.make_table("parity", 64, 3000, seed=315), True),
+        "table-scan 16 states": (W.make_table("dfa16", 64, 3000, seed=316), True),
+        "projective f32": (W.make_matrix(3, 700, 16, 1, torch.float32, seed=317, projective=True), False),
+        "matrix gradient f32 m=1": (W.make_matrix_grad(3, 400, 16, 1, torch.float32, seed=318), False),
+        "matrix gradient bf16 m=16": (W.make_matrix_grad(2, 300, 16, 16, torch.bfloat16, reverse=True, seed=319),
+                                      False),
+        "norm-cap gradient split": (W.make_element_grad(nc, seed=320), True),
+        "max-plus gradient slab": (W.make_element_grad(mp, seed=321), True),
+    }
+
+
+def _call_other(w, t, h):
+    if w.op == "linear_scan":
+        a = t["a"] if "a" in t else w.meta["a_number"]
+        return (sx.linear_scan(a, t["b"], axis=w.axis, reverse=w.reverse, out_dtype=w.out_dtype),)
+    if w.op == "table_scan":
+        return (sx.table_scan(t["table"], t["symbols"], axis=w.axis, start=w.meta.get("start", 0)),)
+    if w.op == "matrix_scan":
+        return (sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse, projective=True),)
+    if w.op == "matrix_scan_backward":
+        ga, gb = sx.matrix_scan_backward(t["a"], tuple(t["b"].shape), h, t["g"], axis=w.axis, reverse=w.reverse)
+        return ga, gb
+    gi, (gx, gs) = sx.element_scan_backward(w.body, t["initial"], [t["x"], t["s"]], h, t["g"], axis=w.axis,
+                                            state_axis=w.state_axis, reverse=w.reverse)
+    return gi, gx, gs
+
+
+def _forward_h(w, t):
+    if w.op == "matrix_scan_backward":
+        return sx.matrix_scan(t["a"], t["b"], axis=w.axis, reverse=w.reverse)
+    if w.op == "element_scan_backward":
+        return sx.element_scan(w.body, t["initial"], [t["x"], t["s"]], axis=w.axis, state_axis=w.state_axis,
+                               reverse=w.reverse)
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(_other_cases()))
+def test_graph_replay_other_calls(name):
+    w, exact = _other_cases()[name]
+    print(f"\n[case] graph replay: {w.name}", flush=True)
+    t = w.on(DEV)
+    h = _forward_h(w, t)  # the forward result a gradient takes, computed before capture
+    eager = _call_other(w, t, h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = _call_other(w, t, h)
+    for _ in range(3):
+        _call_other(w, t, h)  # eager work between replays
+        torch.cuda.synchronize()
+        for c in captured:
+            c.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(captured, eager):
+            if exact:
+                assert torch.equal(c, e)
+            else:
+                assert torch.all(torch.isfinite(c.float()))
+                tol = MS_TOL_F32 if c.dtype == torch.float32 else MS_TOL_BF16
+                ce, ee = c.double().cpu().numpy(), e.double().cpu().numpy()
+                if ce.ndim >= 3:
+                    assert_matrix_close(c, ee, tol, axis=w.axis)
+                else:
+                    assert abs(ce - ee).max() <= tol * max(abs(ee).max(), 1e-30)
