@@ -151,6 +151,48 @@ def test_norm_cap_chunked_without_contraction(reverse):
     assert_element_close(got, ref)
 
 
+@pytest.mark.parametrize("case", ["x_width_one", "both_width_one", "aligned_view", "unaligned_view",
+                                  "strided_initial", "axis0", "many_vectors", "reverse_long"])
+def test_norm_cap_layouts(case):
+    """The 16-wide norm-cap layouts: four components per thread from 16-byte aligned memory (width-one x
+    or gate, views whose offsets are multiples of four, any initial), one component per thread otherwise
+    (unaligned views), split along the axis or not (many state vectors)."""
+    g = torch.Generator().manual_seed(140)
+    B, T, H, axis, rev = 2, 300, 5, 1, False
+    xw, sw = 16, 1
+    if case == "x_width_one":
+        xw, sw = 1, 16
+    elif case == "both_width_one":
+        xw, sw = 1, 1
+    elif case == "many_vectors":
+        B, T, H = 2, 40, 8200
+    elif case == "reverse_long":
+        B, T, H, rev = 1, 2000, 3, True
+    shape = (B, T, H)
+    pad = 4 if case == "aligned_view" else (1 if case == "unaligned_view" else 0)
+    xb = 2.0 * torch.randn(shape + (xw + pad,), generator=g)
+    x = xb[..., pad:] if case == "unaligned_view" else xb[..., :xw]
+    s = 0.8 + 0.2 * torch.rand(shape + (sw,), generator=g)
+    init = 0.3 * torch.randn((B, H, 16), generator=g)
+    if case == "strided_initial":
+        init = 0.3 * torch.randn((16, H, B), generator=g).permute(2, 1, 0)  # non-contiguous, component stride H*B
+    if case == "axis0":
+        x, s = x.transpose(0, 1), s.transpose(0, 1)  # [T, B, H, .] scanned along axis 0 (strided lanes)
+        axis = 0
+    ref = oracle.element_scan("norm_cap", init.numpy(), [x.numpy(), s.numpy()], axis=axis, state_axis=-1,
+                              reverse=rev)
+    print(f"\n[case] norm-cap layout {case} x {tuple(x.shape)} s {tuple(s.shape)}", flush=True)
+    xd = xb.to(DEV)
+    xd = xd[..., pad:] if case == "unaligned_view" else xd[..., :xw]
+    sd = s.to(DEV) if case != "axis0" else s.transpose(0, 1).contiguous().to(DEV).transpose(0, 1)
+    if case == "axis0":
+        xd = xd.transpose(0, 1)
+    idev = init.to(DEV) if case != "strided_initial" else init.permute(2, 1, 0).contiguous().to(DEV).permute(2, 1, 0)
+    got = sx.element_scan("norm_cap", idev, [xd, sd], axis=axis, state_axis=-1, reverse=rev)
+    torch.cuda.synchronize()
+    assert_element_close(got, ref)
+
+
 def test_element_scan_strided_and_broadcast_operands():
     # x as a transposed view, decay broadcast along the width (stride 0), initial non-contiguous
     g = torch.Generator().manual_seed(130)
