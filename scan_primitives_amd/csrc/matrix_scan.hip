@@ -150,6 +150,13 @@ struct ARow<uint16_t> {
   }
 };
 
+// a X + C for a staged a: bf16 a on the bf16 MFMA (X split in two halves), f32 a on the f32 MFMA.
+template <typename TIn>
+__device__ __forceinline__ f32x4 mfma_a(const ARow<TIn>& a, f32x4 x, f32x4 c) {
+  if constexpr (sizeof(TIn) == 2) return mfma_16x16x16_bf16a(a.u, x, c);
+  else return mfma_16x16x16(a.v, x, c);
+}
+
 template <typename TIn, bool VEC, bool ADJ = false>
 __device__ __forceinline__ ARow<TIn> load_a(const TIn* ap, int n, int r, int c) {
   ARow<TIn> out;
@@ -805,8 +812,8 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
     (([&] {
        issue(ks);
-       P = mfma_16x16x16(R.A[ks].get(), P, zero4());
-       L = mfma_16x16x16(R.A[ks].get(), L, bterm_of<TIn, M1, ks>(R, c));
+       P = mfma_a<TIn>(R.A[ks], P, zero4());
+       L = mfma_a<TIn>(R.A[ks], L, bterm_of<TIn, M1, ks>(R, c));
        if constexpr (SCALED) {
          const float sk = step_scale<ks>(R);
          P *= sk;
@@ -854,7 +861,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
     if (full) {
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
-           f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+           f32x4 hn = mfma_a<TIn>(R.A[ks], h, bterm_of<TIn, M1, ks>(R, c));
            if constexpr (SCALED) hn *= step_scale<ks>(R);
            if constexpr (ks > 0) gather(std::integral_constant<int, ks - 1>{}, h);
            h = hn;
@@ -866,7 +873,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
            if (g.q0 + ks < T) {
-             h = mfma_16x16x16(R.A[ks].get(), h, bterm_of<TIn, M1, ks>(R, c));
+             h = mfma_a<TIn>(R.A[ks], h, bterm_of<TIn, M1, ks>(R, c));
              if constexpr (SCALED) h *= step_scale<ks>(R);
              gather(std::integral_constant<int, ks>{}, h);
            }
@@ -891,7 +898,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
     if (full) {
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
-           f32x4 hn = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+           f32x4 hn = mfma_a<TIn>(R.A[ks], h, R.Bv[ks].get());
            if constexpr (SCALED) hn *= step_scale<ks>(R);
            if constexpr (ks > 0) emit(ks - 1, h);
            h = hn;
@@ -903,7 +910,7 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
       [&]<int... ks>(std::integer_sequence<int, ks...>) {
         (([&] {
            if (g.q0 + ks < T) {
-             h = mfma_16x16x16(R.A[ks].get(), h, R.Bv[ks].get());
+             h = mfma_a<TIn>(R.A[ks], h, R.Bv[ks].get());
              if constexpr (SCALED) h *= step_scale<ks>(R);
              emit(ks, h);
            }

@@ -35,6 +35,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// D = A X + C as above, for an A given in bf16 (lane (r, c): A[c][4r .. 4r+3], two
+// per word, the lower index in the low half) and X, C in f32, on the bf16 MFMA
+// (v_mfma_f32_16x16x16_bf16, the same operand layout as the f32 16x16x4 with all
+// of K in one instruction): X is split into the bf16 of its values and the bf16
+// of what that rounding left (X - hi, exact in f32), and D = A hi + (A lo + C)
+// takes two bf16 MFMAs instead of four f32 ones. Products of bf16 values are
+// exact in f32 and the two halves carry X to about 2^-16 relative, so D is
+// within about 2^-16 |A||X| of the f32 product (the f32 path keeps X whole).
+__device__ __forceinline__ f32x4 mfma_16x16x16_bf16a(uint2 a, f32x4 x, f32x4 c) {
+  const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+  const float hx0 = __uint_as_float(h01 << 16), hx1 = __uint_as_float(h01 & 0xffff0000u);
+  const float hx2 = __uint_as_float(h23 << 16), hx3 = __uint_as_float(h23 & 0xffff0000u);
+  const uint32_t l01 = pack_bf16x2(x[0] - hx0, x[1] - hx1), l23 = pack_bf16x2(x[2] - hx2, x[3] - hx3);
+  const s16x4_t av = __builtin_bit_cast(s16x4_t, a);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, make_uint2(l01, l23)), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, make_uint2(h01, h23)), c, 0, 0, 0);
+}
+
 // 4 x 4 transpose inside each quad of lanes: lane j of a quad holds x[v] = M[j][v]
 // and receives M[v][j]. Two exchange levels (partner j ^ 1, then j ^ 2), each
 // taking the partner's register v ^ bit where lane and register differ in that bit.
