@@ -448,7 +448,7 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
   // ---- the wave's map: P = a[last] ... a[first], L = the scan of its steps from h = 0
   f32x4 P = identity_d(r, c), L = zero4();
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
-    ((P = mfma_16x16x16(A[ks].get(), P, zero4()), L = mfma_16x16x16(A[ks].get(), L, bterm(std::integral_constant<int, ks>{}))), ...);
+    ((P = mfma_a<TIn>(A[ks], P, zero4()), L = mfma_a<TIn>(A[ks], L, bterm(std::integral_constant<int, ks>{}))), ...);
   }(std::make_integer_sequence<int, K>{});
 #pragma unroll
   for (int v = 0; v < 4; ++v) sP[wave][(4 * r + v) * 16 + c] = P[v];
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
     (([&] {
        if (q0 + ks < T) {
-         h = mfma_16x16x16(A[ks].get(), h, bterm(std::integral_constant<int, ks>{}));
+         h = mfma_a<TIn>(A[ks], h, bterm(std::integral_constant<int, ks>{}));
          TOut* op = o0 + (t0 * p.t_stride[MS_OUT] + ks * to);
          if constexpr (M1) {
            if (c == 0) store_h_col1(op, h, n, r, vec_b1);
@@ -1347,7 +1347,7 @@ __global__ __launch_bounds__(64) void ms_proj_chunk_kernel(const MsParams p, flo
 #pragma unroll
     for (int u = 0; u < K; ++u) {
       if (q0 + u < q_end) {  // wave-uniform
-        P = mfma_16x16x16(A[u].get(), P, zero4());
+        P = mfma_a<TIn>(A[u], P, zero4());
         const float big = wave_max_abs(P);
         P *= big > 0.0f ? 1.0f / big : 1.0f;
       }
@@ -1389,7 +1389,7 @@ __global__ __launch_bounds__(64) void ms_proj_scale_kernel(const MsParams p, con
     for (int u = 0; u < K; ++u) {
       const int64_t q = q0 + u;
       if (q < q_end) {  // wave-uniform
-        P = mfma_16x16x16(A[u].get(), P, zero4());
+        P = mfma_a<TIn>(A[u], P, zero4());
         const float big = wave_max_abs(P);
         const float inv = big > 0.0f ? 1.0f / big : 1.0f;
         P *= inv;
