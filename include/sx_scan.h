@@ -203,7 +203,11 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *                h[t] = (a[t] @ h[prev] + b[t]) / m. The result is h up to a
  *                positive factor per step when b is zero after its first
  *                step, and stays in range where the plain product would
- *                overflow. It uses no workspace and runs serially in time.
+ *                overflow. With n = 16 and the workspace
+ *                sx_matrix_scan_workspace_bytes() reports, it runs chunked
+ *                in parallel (passes that compute every step's factor, then
+ *                the scan); with a smaller workspace (NULL included) or
+ *                other shapes it runs serially in time and uses none.
  *  out_dtype     SX_F32 or SX_BF16. The result is rounded to bf16 to nearest
  *                even on store when SX_BF16.
  *  out           contiguous, shape lead + [n, m] (see sx_matrix_scan_out_shape).

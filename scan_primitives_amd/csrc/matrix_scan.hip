@@ -1320,12 +1320,16 @@ __global__ __launch_bounds__(64) void ms_projective_kernel(const MsParams p) {
 //   ms_proj_chunk_kernel  the chunk's product (later steps on the left),
 //                         divided by its largest entry after every step so
 //                         that it stays in range; stored row-major.
-//   ms_proj_scale_kernel  the products of the chunks before this one composed
-//                         in scan order (again divided after every product),
-//                         then this chunk's steps from there, each storing the
-//                         factor of its step (1 where the product is zero).
+//   ms_proj_prefix_kernel one wave per batch: the chunk products composed in
+//                         scan order (again divided after every product),
+//                         storing the product each chunk starts from.
+//   ms_proj_scale_kernel  this chunk's steps from its starting product, each
+//                         storing the factor of its step (1 where the product
+//                         is zero).
 // The pipelined kernel with SCALED then runs the scan.
-constexpr int kProjChunk = 96;
+constexpr int kProjChunk = 128;
+constexpr int kProjAhead = 16;  // steps of a in flight in both factor passes
+static_assert(kProjChunk % kProjAhead == 0, "the factor passes unroll whole rounds of loads");
 
 template <typename TIn, bool VEC>
 __global__ __launch_bounds__(64) void ms_proj_chunk_kernel(const MsParams p, float* prod, int64_t chunks) {
@@ -1337,66 +1341,94 @@ __global__ __launch_bounds__(64) void ms_proj_chunk_kernel(const MsParams p, flo
   const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
   const TIn* a0 = static_cast<const TIn*>(p.a) + off[MS_A] + (p.reverse ? T - 1 : 0) * p.t_stride[MS_A];
   const int64_t q_begin = ch * kProjChunk, q_end = q_begin + kProjChunk < T ? q_begin + kProjChunk : T;
-  constexpr int K = 4;  // steps whose operands are in flight
+  constexpr int K = kProjAhead;  // steps whose operands are in flight
   ARow<TIn> A[K];
   auto load = [&](int64_t q, int u) { A[u] = load_a<TIn, VEC>(a0 + (q < q_end ? q : q_end - 1) * ta, p.n, r, c); };
 #pragma unroll
   for (int u = 0; u < K; ++u) load(q_begin + u, u);
   f32x4 P = identity_d(r, c);
-  for (int64_t q0 = q_begin; q0 < q_end; q0 += K) {
+  // unrolled over the whole chunk: each step waits for its own operand only (a
+  // loop here would drain every load in flight at its head). Steps past the end
+  // are computed and dropped by a select, so no load moves behind a branch.
 #pragma unroll
-    for (int u = 0; u < K; ++u) {
-      if (q0 + u < q_end) {  // wave-uniform
-        P = mfma_a<TIn>(A[u], P, zero4());
-        const float big = wave_max_abs(P);
-        P *= big > 0.0f ? 1.0f / big : 1.0f;
-      }
-      load(q0 + u + K, u);
-    }
+  for (int k = 0; k < kProjChunk; ++k) {
+    f32x4 Pn = mfma_a<TIn>(A[k % K], P, zero4());
+    const float big = wave_max_abs(Pn);
+    Pn *= big > 0.0f ? 1.0f / big : 1.0f;
+    const bool on = q_begin + k < q_end;  // wave-uniform
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P[v] = on ? Pn[v] : P[v];
+    if (k + K < kProjChunk) load(q_begin + k + K, k % K);
+    __builtin_amdgcn_sched_barrier(0);  // the load stays K steps ahead of its use
   }
   float* dst = prod + (batch * chunks + ch) * 256;
 #pragma unroll
   for (int v = 0; v < 4; ++v) dst[(4 * r + v) * 16 + c] = P[v];
 }
 
+// Chunk products are stored row-major; lane (r, c) reads row c, columns 4r..4r+3
+// (the A operand) and keeps rows 4r..4r+3 of column c of a result.
+__global__ __launch_bounds__(64) void ms_proj_prefix_kernel(const float* prod, float* entry, int64_t chunks) {
+  const int lane = int(threadIdx.x), r = lane >> 4, c = lane & 15;
+  const int64_t batch = blockIdx.x;
+  const float* pb = prod + batch * chunks * 256 + c * 16 + 4 * r;
+  float* eb = entry + batch * chunks * 256;
+  f32x4 P = identity_d(r, c);
+  constexpr int KP = 16;  // products in flight (positions past the end read chunk 0's, unused)
+  f32x4 R[KP];
+  auto load_prod = [&](int64_t j, int u) { R[u] = *reinterpret_cast<const f32x4*>(pb + (j < chunks ? j : 0) * 256); };
+#pragma unroll
+  for (int u = 0; u < KP; ++u) load_prod(u, u);
+  for (int64_t j0 = 0; j0 < chunks; j0 += KP) {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int64_t j = j0 + u;
+      if (j < chunks) {  // wave-uniform
+#pragma unroll
+        for (int v = 0; v < 4; ++v) eb[j * 256 + (4 * r + v) * 16 + c] = P[v];
+        P = mfma_16x16x16(R[u], P, zero4());
+        const float big = wave_max_abs(P);
+        P *= big > 0.0f ? 1.0f / big : 1.0f;
+      }
+      load_prod(j0 + u + KP, u);
+    }
+  }
+}
+
 template <typename TIn, bool VEC>
-__global__ __launch_bounds__(64) void ms_proj_scale_kernel(const MsParams p, const float* prod, float* step_scale,
+__global__ __launch_bounds__(64) void ms_proj_scale_kernel(const MsParams p, const float* entry, float* step_scale,
                                                            int64_t chunks) {
   const int lane = int(threadIdx.x), r = lane >> 4, c = lane & 15;
   const int64_t batch = int64_t(blockIdx.x) / chunks, ch = int64_t(blockIdx.x) % chunks;
   int64_t off[3];
   index_offsets(p.batch, batch, off);
   const int64_t T = p.T;
-  // the chunks before this one, in scan order
-  f32x4 P = identity_d(r, c);
-  const float* pb = prod + batch * chunks * 256;
-  for (int64_t j = 0; j < ch; ++j) {
-    P = mfma_16x16x16(*reinterpret_cast<const f32x4*>(pb + j * 256 + c * 16 + 4 * r), P, zero4());
-    const float big = wave_max_abs(P);
-    P *= big > 0.0f ? 1.0f / big : 1.0f;
-  }
+  // the product this chunk starts from
+  const float* eb = entry + (batch * chunks + ch) * 256;
+  f32x4 P;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) P[v] = eb[(4 * r + v) * 16 + c];
   const int64_t ta = p.reverse ? -p.t_stride[MS_A] : p.t_stride[MS_A];
   const TIn* a0 = static_cast<const TIn*>(p.a) + off[MS_A] + (p.reverse ? T - 1 : 0) * p.t_stride[MS_A];
   const int64_t q_begin = ch * kProjChunk, q_end = q_begin + kProjChunk < T ? q_begin + kProjChunk : T;
   float* sc = step_scale + batch * T;
-  constexpr int K = 4;
+  constexpr int K = kProjAhead;
   ARow<TIn> A[K];
   auto load = [&](int64_t q, int u) { A[u] = load_a<TIn, VEC>(a0 + (q < q_end ? q : q_end - 1) * ta, p.n, r, c); };
 #pragma unroll
   for (int u = 0; u < K; ++u) load(q_begin + u, u);
-  for (int64_t q0 = q_begin; q0 < q_end; q0 += K) {
 #pragma unroll
-    for (int u = 0; u < K; ++u) {
-      const int64_t q = q0 + u;
-      if (q < q_end) {  // wave-uniform
-        P = mfma_a<TIn>(A[u], P, zero4());
-        const float big = wave_max_abs(P);
-        const float inv = big > 0.0f ? 1.0f / big : 1.0f;
-        P *= inv;
-        if (lane == 0) sc[p.reverse ? T - 1 - q : q] = inv;
-      }
-      load(q0 + u + K, u);
+  for (int k = 0; k < kProjChunk; ++k) {  // unrolled, as in ms_proj_chunk_kernel
+    const int64_t q = q_begin + k;
+    if (q < q_end) {  // wave-uniform
+      P = mfma_a<TIn>(A[k % K], P, zero4());
+      const float big = wave_max_abs(P);
+      const float inv = big > 0.0f ? 1.0f / big : 1.0f;
+      P *= inv;
+      if (lane == 0) sc[p.reverse ? T - 1 - q : q] = inv;
     }
+    if (k + K < kProjChunk) load(q + K, k % K);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -1517,18 +1549,20 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
   return hipGetLastError();
 }
 
-// Room :projective's two passes take after the scan's own workspace: the chunk
-// products and the factor of every step.
+// Room :projective's factor passes take after the scan's own workspace: the
+// chunk products, the product each chunk starts from and the factor of every step.
 struct ProjPlan {
   int64_t chunks;
-  size_t prod_off, scale_off, total;
+  size_t prod_off, entry_off, scale_off, total;
 };
 
 ProjPlan proj_plan(const MsParams& p, size_t scan_bytes) {
   ProjPlan q{};
   q.chunks = (p.T + kProjChunk - 1) / kProjChunk;
+  const size_t prods = size_t(p.num_batch) * size_t(q.chunks) * 256 * sizeof(float);
   q.prod_off = (scan_bytes + 255) / 256 * 256;
-  q.scale_off = q.prod_off + size_t(p.num_batch) * size_t(q.chunks) * 256 * sizeof(float);
+  q.entry_off = q.prod_off + prods;
+  q.scale_off = q.entry_off + prods;
   q.total = q.scale_off + (size_t(p.num_batch) * size_t(p.T) * sizeof(float) + 255) / 256 * 256;
   return q;
 }
@@ -1561,6 +1595,7 @@ hipError_t launch_projective_passes(const MsParams& p0, void* workspace, hipStre
   const ProjPlan pp = proj_plan(p0, scan);
   char* base = static_cast<char*>(workspace);
   float* prod = reinterpret_cast<float*>(base + pp.prod_off);
+  float* entry = reinterpret_cast<float*>(base + pp.entry_off);
   float* scale = reinterpret_cast<float*>(base + pp.scale_off);
   MsParams p = p0;
   p.step_scale = scale;
@@ -1572,10 +1607,12 @@ hipError_t launch_projective_passes(const MsParams& p0, void* workspace, hipStre
   const dim3 grid{unsigned(waves)}, block{64};
   if (vec) {
     hipLaunchKernelGGL((ms_proj_chunk_kernel<TIn, true>), grid, block, 0, stream, p, prod, pp.chunks);
-    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, true>), grid, block, 0, stream, p, prod, scale, pp.chunks);
+    hipLaunchKernelGGL(ms_proj_prefix_kernel, dim3(unsigned(p.num_batch)), block, 0, stream, prod, entry, pp.chunks);
+    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, true>), grid, block, 0, stream, p, entry, scale, pp.chunks);
   } else {
     hipLaunchKernelGGL((ms_proj_chunk_kernel<TIn, false>), grid, block, 0, stream, p, prod, pp.chunks);
-    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, false>), grid, block, 0, stream, p, prod, scale, pp.chunks);
+    hipLaunchKernelGGL(ms_proj_prefix_kernel, dim3(unsigned(p.num_batch)), block, 0, stream, prod, entry, pp.chunks);
+    hipLaunchKernelGGL((ms_proj_scale_kernel<TIn, false>), grid, block, 0, stream, p, entry, scale, pp.chunks);
   }
   // the scan of a[t] s[t], b[t] s[t]: the pipelined kernel with its factors
   const UnitPlan up = unit_plan(p, kLeadCompute * kSteps);
