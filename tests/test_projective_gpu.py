@@ -7,7 +7,8 @@ The bar is the matrix-scan bar: ||gpu[t] - ref[t]||_F <= tol * max(||ref[t]||_F,
 RMS of the state norms of the same scan), tol = 1e-4 for f32 operands and
 2e-2 for bf16.
 
-Cases: the pipelined shapes (n = 16, m = 1 and bf16 m = 16), other n and m,
+Cases: the pipelined shapes (n = 16, m = 1 and bf16 m = 16; one long enough
+that the chunk products compose over several rounds of loads), other n and m,
 broadcast a, both directions, products that grow (a plain scan in f32 would
 overflow; the projective one stays in range), the full-size f32 matrix
 workload on sampled rows, and the refusal of a gradient.
@@ -50,7 +51,10 @@ def _check(a, b, axis, reverse):
 @pytest.mark.parametrize("B,T,n,m,dtype", [(3, 500, 16, 1, torch.float32), (2, 300, 16, 16, torch.bfloat16),
                                            (2, 200, 5, 3, torch.float32), (2, 130, 16, 17, torch.float32),
                                            (1, 1, 16, 1, torch.float32), (2, 64, 1, 1, torch.float32),
-                                           (2, 257, 16, 16, torch.float32)])
+                                           (2, 257, 16, 16, torch.float32),
+                                           # 18 chunks of 128 steps, the last ragged: the chunk products
+                                           # compose over more than one round of loads
+                                           (2, 128 * 17 + 5, 16, 1, torch.float32)])
 def test_projective_shapes(B, T, n, m, dtype, reverse):
     a, b = _draw((B, T, n, n), (B, T, n, m), dtype, seed=201 + n + m + T)
     _check(a, b, 1, reverse)
