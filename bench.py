@@ -134,7 +134,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
               "(the scans shard with no or one small exchange, see the design notes)", file=sys.stderr)
         return 2
 
