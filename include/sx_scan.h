@@ -203,11 +203,10 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *                h[t] = (a[t] @ h[prev] + b[t]) / m. The result is h up to a
  *                positive factor per step when b is zero after its first
  *                step, and stays in range where the plain product would
- *                overflow. With n = 16 and the workspace
- *                sx_matrix_scan_workspace_bytes() reports, it runs chunked
- *                in parallel (passes that compute every step's factor, then
- *                the scan); with a smaller workspace (NULL included) or
- *                other shapes it runs serially in time and uses none.
+ *                overflow. With n = 16, on the shapes the chunked scan
+ *                takes, it runs in parallel in the workspace (passes that
+ *                compute every step's factor, then the scan); on other
+ *                shapes it runs serially in time.
  *  out_dtype     SX_F32 or SX_BF16. The result is rounded to bf16 to nearest
  *                even on store when SX_BF16.
  *  out           contiguous, shape lead + [n, m] (see sx_matrix_scan_out_shape).
@@ -221,7 +220,8 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
                          const void* b, int axis, int reverse, int projective, sx_dtype out_dtype,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sx_matrix_scan needs for these shapes (0 for invalid ones). */
+/* Workspace bytes sx_matrix_scan needs for these shapes (0 for invalid ones),
+ * with or without :projective (the size covers both). */
 size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank,
                                       const int64_t* b_shape, int axis);
 
