@@ -461,7 +461,9 @@ struct SlabMap {
   __device__ static float apply(float P, float Q, float h) { return kMaxPlus ? fmaxf(h + P, Q) : fmaf(P, h, Q); }
 };
 
-template <int BODY, int NW, int S, typename TI = float, typename TO = float>
+// CS: the second sequence (c, or a) has time stride 0, so it is read once per
+// lane rather than at every trip, and a slab holds only x in registers.
+template <int BODY, int NW, int S, typename TI = float, typename TO = float, bool CS = false>
 __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
   using M = SlabMap<BODY>;
   __shared__ float sP[2][NW][64];  // per slab parity: each wave's map (P, Q)
@@ -491,31 +493,42 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
     const int64_t qc = q < T ? q : T - 1;
     return rev ? T - 1 - qc : qc;
   };
-  float cx[S], cc[S];
+  const float c_once = CS ? ld_elem(cl) : 0.0f;
+  float cx[S], cc[CS ? 1 : S];
 #pragma unroll
   for (int k = 0; k < S; ++k) {
     const int64_t q = int64_t(wave) * S + k;
     const int64_t t = time_of(q);
-    const float xv = ld_elem(xl + t * sx), cv = ld_elem(cl + t * sc);
-    cx[k] = q < T ? xv : M::x_pad();
-    cc[k] = q < T ? cv : M::s_pad();
+    cx[k] = q < T ? ld_elem(xl + t * sx) : M::x_pad();
+    if constexpr (!CS) {
+      const float cv = ld_elem(cl + t * sc);
+      cc[k] = q < T ? cv : M::s_pad();
+    }
   }
   for (int64_t sl = 0; sl < nslabs; ++sl) {
     const int64_t qw = sl * kSlab + int64_t(wave) * S;  // this wave's first position in the slab
-    float nx[S], nc[S];
+    float nx[S], nc[CS ? 1 : S];
 #pragma unroll
     for (int k = 0; k < S; ++k) {  // next slab, in flight during this one
       const int64_t q = qw + kSlab + k;
       const int64_t t = time_of(q);
-      const float xv = ld_elem(xl + t * sx), cv = ld_elem(cl + t * sc);
+      const float xv = ld_elem(xl + t * sx);
       nx[k] = q < T ? xv : M::x_pad();
-      nc[k] = q < T ? cv : M::s_pad();
+      if constexpr (!CS) {
+        const float cv = ld_elem(cl + t * sc);
+        nc[k] = q < T ? cv : M::s_pad();
+      }
     }
+    // this slab's c at trip k
+    auto c_of = [&](int k) -> float {
+      if constexpr (CS) return qw + k < T ? c_once : M::s_pad();
+      else return cc[k];
+    };
     __builtin_amdgcn_sched_barrier(0);  // keep the next slab's loads issued ahead of this slab's work
     // summary of this wave's trips: their maps composed in scan order
     float P = M::p0(), Q = M::q0();
 #pragma unroll
-    for (int k = 0; k < S; ++k) M::fold(P, Q, cx[k], cc[k]);
+    for (int k = 0; k < S; ++k) M::fold(P, Q, cx[k], c_of(k));
     const int par = int(sl & 1);
     sP[par][wave][l] = P;
     sQ[par][wave][l] = Q;
@@ -531,14 +544,14 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
     // replay from the entering state: each trip is the serial body again
 #pragma unroll
     for (int k = 0; k < S; ++k) {
-      hw = elementwise_body<BODY>(hw, cx[k], cc[k]);
+      hw = elementwise_body<BODY>(hw, cx[k], c_of(k));
       const int64_t q = qw + k;
       if (live && q < T) st_elem_stream(ol + time_of(q) * so, hw);
     }
 #pragma unroll
     for (int k = 0; k < S; ++k) {
       cx[k] = nx[k];
-      cc[k] = nc[k];
+      if constexpr (!CS) cc[k] = nc[k];
     }
   }
 }
@@ -1095,7 +1108,10 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
 namespace {
 template <typename TI, typename TO>
 void launch_linear(const EsParams& p, int64_t blocks, hipStream_t stream) {
-  if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)
+  if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips && p.t_stride[ES_S] == 0)  // a constant in time
+    hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 32, TI, TO, true>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
+                       stream, p);
+  else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)
     hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 16, TI, TO>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
                        stream, p);
   else

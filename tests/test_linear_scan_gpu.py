@@ -82,6 +82,7 @@ def test_cumsum(shape, axis, reverse):
     ((2, 777, 4163), (777, 1), 1),   # a broadcast over batch and lanes (stride 0)
     ((3, 40, 19), (3, 40, 1), 1),    # a shared by the lanes of one batch entry
     ((3, 40, 19), (19,), 1),         # a constant along the axis
+    ((2, 777, 4163), (4163,), 1),    # the same in the slab kernel: read once per lane
     ((4, 50), (1, 50), -1),
 ])
 def test_linear_broadcast_a(shape, a_shape, axis):
