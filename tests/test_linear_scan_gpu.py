@@ -105,8 +105,9 @@ def test_linear_number_b_and_tensor_a():
 
 @pytest.mark.parametrize("shape,reverse", [((3, 37, 19), False), ((2, 777, 4163), True)])
 @pytest.mark.parametrize("out_dtype", [None, torch.float32])
-def test_linear_bf16(shape, reverse, out_dtype):
-    _check(W.make_linear(shape, axis=1, reverse=reverse, dtype=torch.bfloat16, a_kind="decay", seed=17,
+@pytest.mark.parametrize("a_kind", ["decay", "ones"])  # ones: cumsum, a constant in time
+def test_linear_bf16(shape, reverse, out_dtype, a_kind):
+    _check(W.make_linear(shape, axis=1, reverse=reverse, dtype=torch.bfloat16, a_kind=a_kind, seed=17,
                          out_dtype=out_dtype))
 
 
