@@ -1315,8 +1315,8 @@ __global__ __launch_bounds__(64) void ms_projective_kernel(const MsParams p) {
 // :projective in parallel. In exact arithmetic the factor of step t is 1/m_t
 // with m_t = max|a[t] P'|, P' the product of every a before t (in scan order)
 // divided by its largest entry; with the factors known, h is an ordinary
-// matrix-scan of a[t] s[t] and b[t] s[t]. Two passes give the factors, one
-// wave per (batch, chunk of kProjChunk steps):
+// matrix-scan of a[t] s[t] and b[t] s[t]. Three passes give the factors; the
+// first and last run one wave per (batch, chunk of kProjChunk steps):
 //   ms_proj_chunk_kernel  the chunk's product (later steps on the left),
 //                         divided by its largest entry after every step so
 //                         that it stays in range; stored row-major.
