@@ -75,6 +75,7 @@ def _other_cases():
     return {
         "linear-scan slab": (W.make_linear((33, 600, 256), a_kind="decay", seed=313), True),
         "cumsum": (W.make_linear((9, 700, 64), a_kind="ones", seed=314), True),
+        "cumsum slab": (W.make_linear((2, 777, 4163), a_kind="ones", reverse=True, seed=322), True),
         "table-scan parity": (W.make_table("parity", 64, 3000, seed=315), True),
         "table-scan 16 states": (W.make_table("dfa16", 64, 3000, seed=316), True),
         "projective f32": (W.make_matrix(3, 700, 16, 1, torch.float32, seed=317, projective=True), False),
