@@ -186,8 +186,10 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  * matrices). For every other leading index the n-by-m state runs
  *   forward  h[t] = a[t] @ h[t-1] + b[t]  from h[-1] = 0  (h[0] = b[0]),
  *   reverse  h[t] = a[t] @ h[t+1] + b[t]  from h[T] = 0  (h[T-1] = b[T-1]),
- * and out[t] = h[t]. Computation is f32 for f32 and bf16 operands alike
- * (bf16 widens to f32 exactly).
+ * and out[t] = h[t]. Computation is f32 for f32 and bf16 operands alike:
+ * bf16 widens to f32 exactly, and with bf16 a each product a[t] @ h is
+ * formed exactly (h split into three bf16 parts that sum to it) and summed in
+ * f32, as with f32 operands.
  *
  *  dtype         SX_F32 or SX_BF16, shared by a and b.
  *  a_*, b_*      rank (>= 2), shape, strides (NULL = contiguous) and data.

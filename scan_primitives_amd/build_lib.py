@@ -35,27 +35,50 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build_command(out_path: str = LIB_PATH) -> list[str]:
-    cmd = [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-shared", "-fPIC",
-           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, "-o", out_path]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    return cmd
+def compile_command(src: str, obj: str) -> list[str]:
+    return [hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
+            "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always, even when one is already there) and return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = build_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def link_command(objs: list[str], out_path: str) -> list[str]:
+    return [hipcc_path(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_path, *objs]
+
+
+def _run(cmd: list[str]) -> tuple[int, list[str]]:
     proc = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag and says so; that is harmless.
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if noise not in ln]
-    if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    return proc.returncode, [ln for ln in (proc.stdout + proc.stderr).splitlines() if noise not in ln]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always, even when one is already there) and return its path.
+
+    Each source compiles to an object of its own, in parallel, under a build
+    folder next to this file; then one link step writes the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = [(src, os.path.join(objdir, os.path.splitext(src)[0] + ".o")) for src in SOURCES]
+    cmds = [compile_command(src, obj) for src, obj in jobs]
+    if verbose:
+        for cmd in cmds:
+            print(" ".join(cmd), flush=True)
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(_run, cmds))
+    errors = [(src, msgs) for (src, _), (rc, msgs) in zip(jobs, results) if rc != 0]
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(f"{src}:\n" + "\n".join(msgs) for src, msgs in errors))
+    if verbose:
+        for (src, _), (_, msgs) in zip(jobs, results):
+            if msgs:
+                print("\n".join(msgs))
+    tmp = LIB_PATH + ".tmp"
+    rc, msgs = _run(link_command([obj for _, obj in jobs], tmp))
+    if rc != 0:
+        raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

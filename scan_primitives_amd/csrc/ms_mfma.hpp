@@ -37,22 +37,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// The upper halves (bf16 patterns) of two f32 bit patterns, packed low then high.
+__device__ __forceinline__ uint32_t upper_halves(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
 // D = A X + C as above, for an A given in bf16 (lane (r, c): A[c][4r .. 4r+3], two
-// per word, the lower index in the low half) and X, C in f32, on the bf16 MFMA
-// (v_mfma_f32_16x16x16_bf16, the same operand layout as the f32 16x16x4 with all
-// of K in one instruction): X is split into the bf16 of its values and the bf16
-// of what that rounding left (X - hi, exact in f32), and D = A hi + (A lo + C)
-// takes two bf16 MFMAs instead of four f32 ones. Products of bf16 values are
-// exact in f32 and the two halves carry X to about 2^-16 relative, so D is
-// within about 2^-16 |A||X| of the f32 product (the f32 path keeps X whole).
+// per word, the lower index in the low half) and X, C in f32, with every product
+// of an entry of A and an entry of X exact: X is cut into three bf16 parts,
+// X = hi + mid + lo exactly. hi is X truncated to bf16 (its low 16 bits cleared),
+// mid the same of what is left, and what is left after that has at most eight
+// significant bits, so lo is that remainder itself. Products of bf16 values are
+// exact in f32, so the result carries the rounding of f32 sums only, as the f32
+// MFMA does. Three v_mfma_f32_16x16x16_bf16 (the f32 16x16x4's operand layout
+// with all of K in one instruction), smallest part first, each taking the last
+// one's result as its accumulator. They stay one opcode on purpose: a
+// v_mfma_f32_16x16x32_bf16 that took a 16x16x16's result as its accumulator
+// (hi and mid in one instruction) was measured to read the accumulator before
+// that result had landed, dropping the lo product.
 __device__ __forceinline__ f32x4 mfma_16x16x16_bf16a(uint2 a, f32x4 x, f32x4 c) {
-  const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
-  const float hx0 = __uint_as_float(h01 << 16), hx1 = __uint_as_float(h01 & 0xffff0000u);
-  const float hx2 = __uint_as_float(h23 << 16), hx3 = __uint_as_float(h23 & 0xffff0000u);
-  const uint32_t l01 = pack_bf16x2(x[0] - hx0, x[1] - hx1), l23 = pack_bf16x2(x[2] - hx2, x[3] - hx3);
+  uint32_t u[4], m1[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u[q] = __float_as_uint(x[q]);
+    const float r1 = x[q] - __uint_as_float(u[q] & 0xffff0000u);  // exact
+    m1[q] = __float_as_uint(r1);
+    lo[q] = __float_as_uint(r1 - __uint_as_float(m1[q] & 0xffff0000u));  // exact; low 16 bits are zero
+  }
   const s16x4_t av = __builtin_bit_cast(s16x4_t, a);
-  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, make_uint2(l01, l23)), c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, make_uint2(h01, h23)), c, 0, 0, 0);
+  const uint2 h2 = make_uint2(upper_halves(u[0], u[1]), upper_halves(u[2], u[3]));
+  const uint2 m2 = make_uint2(upper_halves(m1[0], m1[1]), upper_halves(m1[2], m1[3]));
+  const uint2 l2 = make_uint2(upper_halves(lo[0], lo[1]), upper_halves(lo[2], lo[3]));
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, l2), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, m2), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4_t, h2), c, 0, 0, 0);
 }
 
 // 4 x 4 transpose inside each quad of lanes: lane j of a quad holds x[v] = M[j][v]
