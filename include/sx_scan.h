@@ -29,8 +29,13 @@
  *    row-major contiguous. Layouts are row-major, as PyTorch's default.
  *  - The caller owns every buffer. The library keeps no pointer after it
  *    returns and allocates no device memory. Where a workspace is needed,
- *    the caller passes one of at least the queried size; its contents on
- *    entry do not matter and the library clears what it needs on the stream.
+ *    the caller passes one of at least the queried size. Element-scan
+ *    workspaces may hold anything on entry. A matrix-scan workspace (also
+ *    those of its gradient and :projective) must be zero-filled once before
+ *    its first use; every call then leaves it ready for the next one, on any
+ *    later shape, with nothing to clear in between (no extra kernel per
+ *    call). Keep it for matrix-scan calls only: other writes to its first
+ *    256 bytes invalidate it until it is zero-filled again.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *    and the call returns without waiting. Results follow stream order.
  *    Concurrent calls that share one workspace race.
@@ -213,7 +218,13 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *                even on store when SX_BF16.
  *  out           contiguous, shape lead + [n, m] (see sx_matrix_scan_out_shape).
  *  workspace     at least sx_matrix_scan_workspace_bytes() bytes, 256-byte
- *                aligned; may be NULL when that is 0.
+ *                aligned, zero-filled before its first use (see above); may
+ *                be NULL when that size is 0.
+ *
+ * Time-parallel kernels hand each chunk's entering state on through the
+ * workspace; every wait for an earlier chunk is bounded, and one that reaches
+ * its bound is recorded in the workspace, not returned here (the call is
+ * asynchronous): sx_matrix_scan_workspace_status reports it.
  *
  * An axis of length 0 (or m = 0) returns SX_OK with nothing to write.
  */
@@ -226,6 +237,22 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
  * with or without :projective (the size covers both). */
 size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank,
                                       const int64_t* b_shape, int axis);
+
+/* Waits for `stream`, then reads and clears the status a matrix-scan
+ * workspace carries ("Tensor operations", Errors: every failure is a reported
+ * code). SX_OK when every look-back of the calls on this workspace since the
+ * last check completed; SX_E_DEVICE when one gave up waiting for an earlier
+ * chunk's published state (its results are then not valid), with the reason
+ * in sx_last_error(). SX_E_DIM_003 for a NULL workspace, SX_E_WORKSPACE for
+ * one of fewer than 256 bytes. Synchronous: not for use under graph capture. */
+sx_status sx_matrix_scan_workspace_status(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bound on the polls a matrix-scan look-back makes before it gives up and
+ * records it (see sx_matrix_scan_workspace_status); 0 restores the default
+ * (2^22 polls, about a tenth of a second). Process-wide, for calls launched
+ * after it. A diagnostic: a small bound forces give-ups, so that the report
+ * path can be tested with every kernel still running to its end. */
+void sx_set_lookback_spin_limit(uint32_t limit);
 
 /* Writes the matrix-scan result shape to out_shape (room for SX_MAX_RANK + 2
  * entries) and returns its rank, or -1 for shapes that do not fit. */

@@ -89,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    c_int, c_int, c_int, vp, vp]
     lib.sx_linear_scan_out_shape.restype = c_int
     lib.sx_linear_scan_out_shape.argtypes = [c_int, _i64p, c_int, _i64p, _i64p]
+    lib.sx_matrix_scan_workspace_status.restype = c_int
+    lib.sx_matrix_scan_workspace_status.argtypes = [vp, c_size, vp]
+    lib.sx_set_lookback_spin_limit.restype = None
+    lib.sx_set_lookback_spin_limit.argtypes = [ctypes.c_uint32]
     lib.sx_status_name.restype = ctypes.c_char_p
     lib.sx_status_name.argtypes = [c_int]
     lib.sx_last_error.restype = ctypes.c_char_p
@@ -112,6 +116,70 @@ def _check(status: int) -> None:
 
 def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+# Matrix-scan workspaces. The library needs each one zero-filled once and then
+# leaves it ready for the next call, so no call clears anything. Eager calls get
+# one per (device, stream), zero-filled when allocated. Calls captured into a
+# graph get one per capture (keyed by the HIP capture id), allocated and
+# zero-filled inside that capture: every graph then starts from a zeroed
+# workspace of its own in its first replay, and no captured workspace is handed
+# to an eager call or to another graph.
+_matrix_workspaces: dict = {}
+_hip_runtime = None
+
+
+def _capture_id(stream_handle: int):
+    """The id of the capture running on the stream, or None."""
+    global _hip_runtime
+    if _hip_runtime is None:
+        # the HIP runtime torch has loaded (the same soname the library links)
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipStreamGetCaptureInfo.restype = ctypes.c_int
+        hip.hipStreamGetCaptureInfo.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int),
+                                                ctypes.POINTER(ctypes.c_ulonglong)]
+        _hip_runtime = hip
+    status, cid = ctypes.c_int(0), ctypes.c_ulonglong(0)
+    err = _hip_runtime.hipStreamGetCaptureInfo(stream_handle, ctypes.byref(status), ctypes.byref(cid))
+    if err != 0:
+        raise SxError(SX_E_DEVICE, f"hipStreamGetCaptureInfo failed with HIP error {err}")
+    return int(cid.value) if status.value == 1 else None  # 1: hipStreamCaptureStatusActive
+
+
+def _matrix_workspace(nbytes: int, device: torch.device):
+    if nbytes == 0:
+        return None
+    handle = torch.cuda.current_stream(device).cuda_stream
+    cid = _capture_id(handle) if torch.cuda.is_current_stream_capturing() else None
+    key = (device.index, handle, cid)
+    entry = _matrix_workspaces.get(key)
+    if entry is not None and entry.numel() >= nbytes:
+        return entry
+    size = (nbytes + (1 << 20) - 1) >> 20 << 20
+    if entry is not None:
+        size = max(size, entry.numel())
+    ws = torch.zeros(size, dtype=torch.uint8, device=device)
+    _matrix_workspaces[key] = ws
+    return ws
+
+
+def matrix_scan_status(device=None) -> None:
+    """Raise ``SxError`` (E-DEVICE) if a matrix-scan look-back gave up on one of
+    this device's eager workspaces since the last check, and clear what it
+    found. Waits for the streams those workspaces belong to."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    for (index, handle, cid), ws in list(_matrix_workspaces.items()):
+        if index != dev.index or cid is not None:
+            continue
+        with torch.cuda.device(dev):
+            _check(lib.sx_matrix_scan_workspace_status(ws.data_ptr(), ws.numel(), handle))
+
+
+def set_lookback_spin_limit(limit: int) -> None:
+    """Bound on the polls a matrix-scan look-back makes before it gives up and
+    records it (0 restores the default). A diagnostic for the give-up report."""
+    load_library().sx_set_lookback_spin_limit(int(limit))
 
 
 def _require_device_tensor(name: str, t) -> None:
@@ -295,13 +363,14 @@ def _matrix_scan_forward(a, b, axis, reverse, out_dtype, projective) -> torch.Te
         raise SxError(SX_E_DIM_001, "matrix-scan: shapes do not fit")
     out = torch.empty(tuple(oshape[:r]), dtype=out_dtype, device=a.device)
     ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), a_shape, b.dim(), b_shape, axis)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+    ws = _matrix_workspace(ws_bytes, a.device)
     with torch.cuda.device(a.device):
         status = lib.sx_matrix_scan(
             _DTYPES[a.dtype], a.dim(), a_shape, i64_array(a.stride()), a.data_ptr(),
             b.dim(), b_shape, i64_array(b.stride()), b.data_ptr(),
             axis, 1 if reverse else 0, 1 if projective else 0, _DTYPES[out_dtype], out.data_ptr(),
-            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(a.device))
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            _stream_handle(a.device))
     _check(status)
     return out
 
@@ -416,7 +485,7 @@ def matrix_scan_backward(a: torch.Tensor, b_shape, h: torch.Tensor, g: torch.Ten
     a_shape, bs = i64_array(a.shape), i64_array(b_shape)
     ws_bytes = lib.sx_matrix_scan_backward_workspace_bytes(a.dim(), a_shape, len(b_shape), bs, axis,
                                                            _DTYPES[grad_dtype])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+    ws = _matrix_workspace(ws_bytes, a.device)
     grad_a = torch.empty(tuple(a.shape), dtype=grad_dtype, device=a.device)
     grad_b = torch.empty(b_shape, dtype=grad_dtype, device=a.device)
     with torch.cuda.device(a.device):
@@ -424,7 +493,8 @@ def matrix_scan_backward(a: torch.Tensor, b_shape, h: torch.Tensor, g: torch.Ten
             _DTYPES[a.dtype], a.dim(), a_shape, i64_array(a.stride()), a.data_ptr(),
             len(b_shape), bs, h.data_ptr(), i64_array(g.stride()), g.data_ptr(),
             axis, 1 if reverse else 0, _DTYPES[grad_dtype], grad_a.data_ptr(), grad_b.data_ptr(),
-            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_handle(a.device))
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            _stream_handle(a.device))
     _check(status)
     return grad_a, grad_b
 

@@ -36,6 +36,7 @@
 // the previous result. So a chain h <- a[t] @ h + b[t] feeds each result
 // straight back as the next B operand, with no data movement between steps.
 #include <algorithm>
+#include <atomic>
 #include <utility>
 
 #include "ms_mfma.hpp"
@@ -109,22 +110,91 @@ __global__ __launch_bounds__(256) void ms_serial_kernel(const MsParams p) {
 
 // ------------------------------------------------------------------ chunked kernel
 
-constexpr uint32_t kFlagAggregate = 1;  // the unit's map (A, B) is published
-constexpr uint32_t kFlagInclusive = 2;  // the state leaving the unit is published
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-// Look-back state of the chunked kernel, carved out of the caller's workspace.
+// Look-back state of the chunked kernels, carved out of the caller's workspace.
 // Slot s = bt * chunks + chunk: bt is the (batch, 16-column tile) index.
+//
+// The workspace is zero-filled once by its owner; every call then leaves it
+// ready for the next one. Each call works under an epoch, one more than the
+// last call's (stored in the header, never 0): a flag counts only if it carries
+// this call's epoch (and a fixed bit pattern beside it, so that no leftover
+// value of another kind passes for one), so what earlier calls left is never
+// mistaken for this one's, and nothing needs clearing between calls. The last
+// workgroup to finish resets the unit counter and the finish count and stores
+// the epoch. A look-back that gives up (its spin limit) sets the status word,
+// which stays set until the host reads and clears it.
+//
+// A flag is raised only after the stores of what it announces have completed,
+// so a reader that sees this call's flag reads this call's values.
+constexpr uint32_t kFlagMagic = 0x5a3c0000u;  // low half of a raised flag: magic | kind
+constexpr uint32_t kFlagAggregate = 1;        // the unit's map (A, B) is published
+constexpr uint32_t kFlagInclusive = 2;        // the state leaving the unit is published
+
 struct MsUnitWs {
-  uint32_t* header;  // [0] next unit id, [1] status (nonzero: a look-back gave up)
-  uint32_t* flags;   // per slot
+  uint32_t* header;  // [0] next unit id, [1] status (nonzero: a look-back gave up), [2] epoch of the last call,
+                     // [3] workgroups of this call that have finished
+  uint64_t* flags;   // per slot: (epoch << 32) | kFlagMagic | kind
   float* P;          // per slot, the unit's A as a row-major 16x16 block
   float* L;          // per slot, the unit's B in result-register order (lane * 4 + v)
   float* H;          // per slot, the state leaving the unit, same order as L
   uint32_t num_units;
   uint32_t chunks;   // units per bt along the scan axis
   int col_tiles;     // ceil(m / 16)
+  uint32_t spin_limit;  // polls a look-back makes before it gives up
 };
+
+__device__ __forceinline__ uint32_t call_epoch(const MsUnitWs& ws) {
+  const uint32_t last = __hip_atomic_load(ws.header + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last >= 0x3fffffffu ? 1u : last + 1u;
+}
+
+// One thread per workgroup, after every wave of the workgroup is done with the
+// unit counter: the last workgroup of the call resets the counters and records
+// the epoch for the next call.
+__device__ __forceinline__ void finish_call(const MsUnitWs& ws, uint32_t epoch) {
+  const uint32_t done = __hip_atomic_fetch_add(ws.header + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == gridDim.x - 1) {
+    __hip_atomic_store(ws.header + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws.header + 3, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws.header + 2, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The kind of a flag raised in this call, 0 for anything else.
+__device__ __forceinline__ uint32_t flag_kind(uint64_t f, uint32_t epoch) {
+  return (uint32_t(f >> 32) == epoch && (uint32_t(f) & 0xffff0000u) == kFlagMagic) ? (uint32_t(f) & 3u) : 0u;
+}
+
+// Raises a flag once every earlier memory access of this wave has completed.
+__device__ __forceinline__ void raise_flag(uint64_t* flag, uint32_t kind, uint32_t epoch, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0)
+    __hip_atomic_store(flag, (uint64_t(epoch) << 32) | kFlagMagic | kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t read_flag(const uint64_t* flag, uint32_t epoch) {
+  return flag_kind(__hip_atomic_load(const_cast<uint64_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
+}
+
+// Four published values of one lane (consecutive words), written and read with
+// relaxed agent-scope atomic accesses: workgroups that exchange them may sit on
+// different XCDs, whose L2 caches are not coherent with each other, and these
+// accesses are (by the memory model), with no cache write-back or invalidate.
+__device__ __forceinline__ void pub_store4(float* p, f32x4 v) {
+  uint32_t* u = reinterpret_cast<uint32_t*>(p);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) __hip_atomic_store(u + q, __float_as_uint(v[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 pub_load4(const float* p) {
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(p);
+  f32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(u + q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return v;
+}
 
 __device__ __forceinline__ f32x4 identity_d(int r, int c) {  // I in result-register order
   f32x4 v;
@@ -330,31 +400,66 @@ __device__ __forceinline__ void store_h_col1(TOut* op, f32x4 h, int n, int r, bo
   }
 }
 
-// Device-coherent transfer of look-back data between workgroups, which may sit
-// on different XCDs: relaxed agent-scope atomic accesses (coherent by the memory
-// model), with the payload's completion awaited before the flag is raised. No
-// L2 write-back or invalidate is needed, because no published word is ever
-// written or read through the non-coherent path.
-__device__ __forceinline__ void dev_store4(float* p, f32x4 v) {
-  uint32_t* u = reinterpret_cast<uint32_t*>(p);
+// Decoupled look-back for the unit at position `chunk` of the slots starting at
+// `base` (one (batch, column tile)): finds the nearest earlier unit whose leaving
+// state is published, with every unit in between at least aggregated (a window
+// of 64 flags per poll, one per lane), then applies the maps of the units in
+// between to that state in scan order. Returns the state entering the unit in
+// result-register order (zero in lanes past the tile's columns). The spin limit
+// bounds the wait: a look-back that reaches it records the give-up in the status
+// word and returns whatever it has, so no wave can hang.
+__device__ __forceinline__ f32x4 look_back(const MsUnitWs& ws, uint32_t base, int chunk, bool live, int lane, int r,
+                                           int c, uint32_t epoch) {
+  int hi = chunk - 1, j = 0;
+  uint32_t spins = 0;
+  bool gave_up = false;
+  auto poll = [&]() -> uint32_t {
+    const int cand = hi - lane;
+    return cand >= 0 ? read_flag(ws.flags + base + cand, epoch) : 0u;
+  };
+  uint32_t f = poll();
+  for (;;) {
+    const uint64_t inc = __ballot(hi - lane >= 0 && f == kFlagInclusive);
+    const uint64_t none = __ballot(hi - lane >= 0 && f == 0);
+    if (inc != 0) {
+      const int l = __ffsll((unsigned long long)inc) - 1;
+      if ((none & ((1ull << l) - 1ull)) == 0) {
+        j = hi - l;
+        break;
+      }
+    } else if (none == 0 && hi >= 64) {
+      hi -= 64;  // 64 aggregates and no leaving state yet: look further back
+      f = poll();
+      continue;
+    }
+    if (++spins >= ws.spin_limit || hi < 0) {
+      gave_up = true;
+      j = 0;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    f = poll();
+  }
+  // the state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, eight at a time
+  f32x4 h = zero4();
+  if (live) h = pub_load4(ws.H + size_t(base + j) * 256 + lane * 4);
+  for (int i = j + 1; i < chunk; i += 8) {
+    f32x4 Pb[8], Lb[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) __hip_atomic_store(u + q, __float_as_uint(v[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4 dev_load4(const float* p) {
-  const uint32_t* u = reinterpret_cast<const uint32_t*>(p);
-  f32x4 v;
+    for (int u = 0; u < 8; ++u) {
+      Pb[u] = zero4();
+      Lb[u] = zero4();
+      if (i + u < chunk) {
+        Pb[u] = pub_load4(ws.P + size_t(base + i + u) * 256 + c * 16 + 4 * r);
+        if (live) Lb[u] = pub_load4(ws.L + size_t(base + i + u) * 256 + lane * 4);
+      }
+    }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    v[q] = __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(u + q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return v;
-}
-
-__device__ __forceinline__ void raise_flag(uint32_t* flag, uint32_t value, int lane) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // every earlier memory access of this wave has completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (lane == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = 0; u < 8; ++u)
+      if (i + u < chunk) h = mfma_16x16x16(Pb[u], h, Lb[u]);
+  }
+  if (gave_up && lane == 0) __hip_atomic_store(ws.header + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return h;
 }
 
 // Wave-private LDS transpose: 16x16 block from result-register order to row-major,
@@ -375,25 +480,13 @@ __device__ __forceinline__ f32x4 to_a_operand(float* scratch, f32x4 d, int r, in
 // look-back over earlier units of the same (batch, tile), and publishes the
 // leaving state. Every wave then applies the maps of the waves before it to
 // that state and replays its K steps, storing h at every step.
-template <int NW, int K, typename TIn, typename TOut, bool VEC, bool M1, bool ADJ = false>
-__global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, const MsUnitWs ws) {
-  static_assert(K == 16, "the m == 1 path keeps one step per lane column");
-  __shared__ float sP[NW][256];  // wave maps: P row-major (A-operand order readable)
-  __shared__ float sL[NW][256];  // wave maps: L in result-register order
-  __shared__ float sX[256];      // last wave: transpose scratch, then the unit's entering state
-  __shared__ uint32_t sUnit;
-
+template <int NW, int K, typename TIn, typename TOut, bool VEC, bool M1, bool ADJ>
+__device__ __forceinline__ void ms_unit_body(const MsParams& p, const MsUnitWs& ws, uint32_t unit, uint32_t epoch,
+                                             float (*sP)[256], float (*sL)[256], float* sX) {
   const int tid = int(threadIdx.x);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: index math stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane >> 4, c = lane & 15;
-
-  // One counter increment per workgroup, in launch order: every unit this one
-  // waits for was taken earlier by a running workgroup, so look-back progresses.
-  if (tid == 0) sUnit = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t unit = __builtin_amdgcn_readfirstlane(sUnit);
-  if (unit >= ws.num_units) return;
 
   const uint32_t num_bt = uint32_t(p.num_batch) * uint32_t(ws.col_tiles);
   const uint32_t chunk = unit / num_bt;  // chunk-major: all tiles' chunk 0 first
@@ -467,62 +560,17 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
     }
     f32x4 h_in = zero4();
     if (chunk == 0) {
-      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, GL);  // entering 0: leaving = B
-      raise_flag(ws.flags + slot, kFlagInclusive, lane);
+      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, GL);  // entering 0: leaving = B
+      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
     } else {
       const f32x4 GA = to_a_operand(sX, G, r, c);
-      dev_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-      if (live) dev_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
-      raise_flag(ws.flags + slot, kFlagAggregate, lane);
-
-      // Look back: scan up to 64 earlier units at once for the nearest one whose
-      // leaving state is published, with every unit in between at least aggregated.
-      const uint32_t base = bt * ws.chunks;
-      int hi = int(chunk) - 1, j = 0;
-      uint32_t spins = 0;
-      for (;;) {
-        const int cand = hi - lane;
-        uint32_t f = 0;
-        if (cand >= 0) f = __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t inc = __ballot(cand >= 0 && f == kFlagInclusive);
-        const uint64_t none = __ballot(cand >= 0 && f == 0);
-        if (inc != 0) {
-          const int l = __ffsll((unsigned long long)inc) - 1;
-          if ((none & ((1ull << l) - 1ull)) == 0) {
-            j = hi - l;
-            break;
-          }
-        } else if (none == 0 && hi >= 64) {
-          hi -= 64;  // 64 aggregates and no leaving state yet: look further back
-          continue;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins == kSpinLimit || hi < 0) {  // never hang: record it and go on
-          if (lane == 0) __hip_atomic_store(ws.header + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          j = 0;
-          break;
-        }
-      }
-      // state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, four at a time
-      if (live) h_in = dev_load4(ws.H + size_t(base + j) * 256 + lane * 4);
-      for (int i = j + 1; i < int(chunk); i += 4) {
-        f32x4 Pb[4], Lb[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          Pb[u] = zero4();
-          Lb[u] = zero4();
-          if (i + u < int(chunk)) {
-            Pb[u] = dev_load4(ws.P + size_t(base + i + u) * 256 + c * 16 + 4 * r);
-            if (live) Lb[u] = dev_load4(ws.L + size_t(base + i + u) * 256 + lane * 4);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i + u < int(chunk)) h_in = mfma_16x16x16(Pb[u], h_in, Lb[u]);
-      }
+      pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
+      if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+      raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
+      h_in = look_back(ws, bt * ws.chunks, int(chunk), live, lane, r, c, epoch);
       const f32x4 h_out = mfma_16x16x16(GA, h_in, GL);
-      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
-      raise_flag(ws.flags + slot, kFlagInclusive, lane);
+      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -552,6 +600,27 @@ __global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, cons
      ...);
   }(std::make_integer_sequence<int, K>{});
 }
+
+template <int NW, int K, typename TIn, typename TOut, bool VEC, bool M1, bool ADJ = false>
+__global__ __launch_bounds__(NW * 64) void ms_unit_kernel(const MsParams p, const MsUnitWs ws) {
+  static_assert(K == 16, "the m == 1 path keeps one step per lane column");
+  __shared__ float sP[NW][256];  // wave maps: P row-major (A-operand order readable)
+  __shared__ float sL[NW][256];  // wave maps: L in result-register order
+  __shared__ float sX[256];      // last wave: transpose scratch, then the unit's entering state
+  __shared__ uint32_t sUnit;
+
+  const int tid = int(threadIdx.x);
+  // One counter increment per workgroup, in launch order: every unit this one
+  // waits for was taken earlier by a running workgroup, so look-back progresses.
+  if (tid == 0) sUnit = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t unit = __builtin_amdgcn_readfirstlane(sUnit);
+  const uint32_t epoch = call_epoch(ws);
+  if (unit < ws.num_units) ms_unit_body<NW, K, TIn, TOut, VEC, M1, ADJ>(p, ws, unit, epoch, sP, sL, sX);
+  __syncthreads();
+  if (tid == 0) finish_call(ws, epoch);
+}
+
 
 // ------------------------------------------------------------------ pipelined kernel
 //
@@ -1017,6 +1086,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   const int r = lane >> 4, c = lane & 15;
   const int64_t T = p.T;
   const uint32_t NU = ws.num_units;
+  const uint32_t epoch = call_epoch(ws);
 
   if (tid == 0) {
     sIdCount = 0;
@@ -1079,33 +1149,31 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       }
       if (n_pending > 0) flush();
     }
-    return;
-  }
+  } else
 
   if (hw_wave == LEADER) {
     // ------------------------------------------------------------ leader
     __builtin_amdgcn_s_setprio(2);  // its look-back is on every replay's path
-    auto take = [&](int k) {
-      uint32_t id = 0;
-      if (lane == 0) id = __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      id = __builtin_amdgcn_readfirstlane(id);
-      lds_signal_set(&sId[k & 3], id, lane);
+    auto publish_id = [&](int k, uint32_t id) {
+      lds_signal_set(&sId[k & 3], __builtin_amdgcn_readfirstlane(id), lane);
       lds_signal_set(&sIdCount, uint32_t(k) + 1, lane);
     };
-    take(0);
-    take(1);
+    auto fetch_id = [&]() -> uint32_t {
+      return lane == 0 ? __hip_atomic_fetch_add(ws.header, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    };
+    publish_id(0, fetch_id());
+    publish_id(1, fetch_id());
+    // The id of unit k+2 is published as unit k starts; it was fetched as unit
+    // k-1 started, so its round trip is long over and never stalls the leader.
+    uint32_t pending = fetch_id();
     for (int k = 0;; ++k) {
-      take(k + 2);
+      publish_id(k + 2, pending);
       const uint32_t unit = __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
-      if (unit >= NU) break;
+      if (unit >= NU) break;  // (ids only grow: every later unit is past the end as well)
+      pending = fetch_id();
       const PipeGeo g = pipe_geo(p, ws, unit, 0, kUnit);
       const bool live = c < min(16, p.m - g.ct * 16);
       const uint32_t base = g.bt * ws.chunks, slot = base + g.chunk;
-      int hi = int(g.chunk) - 1;
-      auto scan_flags = [&]() -> uint32_t {
-        const int cand = hi - lane;
-        return cand >= 0 ? __hip_atomic_load(ws.flags + base + cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-      };
       const int kb = k % kBufs;
       // Compose the wave maps in step order. Slot i is overwritten with the
       // composition of maps 0 .. i, so that wave i+1 carries the unit's
@@ -1126,67 +1194,21 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const f32x4 GA = to_a_operand(sT, G, r, c);
       f32x4 h_in = zero4();
       if (g.chunk > 0) {
-        // the aggregate goes out first, so that later units need not wait for this one;
-        // the first look-back window is read while its stores complete
-        dev_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-        if (live) dev_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
-        uint32_t f = scan_flags();
-        raise_flag(ws.flags + slot, kFlagAggregate, lane);  // waits for the stores (and the window)
-        // nearest earlier unit whose leaving state is published, with every unit in
-        // between at least aggregated
-        int j = 0;
-        uint32_t spins = 0;
-        for (;;) {
-          const uint64_t inc = __ballot(hi - lane >= 0 && f == kFlagInclusive);
-          const uint64_t none = __ballot(hi - lane >= 0 && f == 0);
-          if (inc != 0) {
-            const int l = __ffsll((unsigned long long)inc) - 1;
-            if ((none & ((1ull << l) - 1ull)) == 0) {
-              j = hi - l;
-              break;
-            }
-          } else if (none == 0 && hi >= 64) {
-            hi -= 64;  // 64 aggregates and no leaving state yet: look further back
-            f = scan_flags();
-            continue;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins == kSpinLimit || hi < 0) {  // never hang: record it and go on
-            if (lane == 0) __hip_atomic_store(ws.header + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            j = 0;
-            break;
-          }
-          f = scan_flags();
-        }
-        // state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, eight at a time
-        if (live) h_in = dev_load4(ws.H + size_t(base + j) * 256 + lane * 4);
-        for (int i = j + 1; i < int(g.chunk); i += 8) {
-          f32x4 Pb[8], Lb[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            Pb[u] = zero4();
-            Lb[u] = zero4();
-            if (i + u < int(g.chunk)) {
-              Pb[u] = dev_load4(ws.P + size_t(base + i + u) * 256 + c * 16 + 4 * r);
-              if (live) Lb[u] = dev_load4(ws.L + size_t(base + i + u) * 256 + lane * 4);
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (i + u < int(g.chunk)) h_in = mfma_16x16x16(Pb[u], h_in, Lb[u]);
-        }
+        // the aggregate goes out first, so that later units need not wait for this one
+        pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
+        if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+        raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
+        h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch);
       }
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
-      if (live) dev_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
       // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
       *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
       lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
-      raise_flag(ws.flags + slot, kFlagInclusive, lane);
     }
-    return;
-  }
-
+  } else {
   // -------------------------------------------------------------- compute waves
   const char* st = &sStage[wave][0];
   UnitRegs<TIn, M1> RA, RB;
@@ -1234,6 +1256,10 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     }
     finish(RA, gA, k);
   }
+  }  // compute waves
+
+  __syncthreads();
+  if (tid == 0) finish_call(ws, epoch);
 }
 
 // ------------------------------------------------------------------ :projective
@@ -1432,9 +1458,12 @@ __global__ __launch_bounds__(64) void ms_proj_scale_kernel(const MsParams p, con
   }
 }
 
-__global__ void fill_u32_kernel(uint32_t* p, size_t count) {
-  const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0u;
+std::atomic<uint32_t> g_spin_limit{0};
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // about a tenth of a second of polling
+
+uint32_t lookback_spin_limit() {
+  const uint32_t v = g_spin_limit.load(std::memory_order_relaxed);
+  return v == 0 ? kDefaultSpinLimit : v;
 }
 
 constexpr int kWaves = 8;          // ms_unit_kernel: waves per workgroup
@@ -1452,10 +1481,26 @@ UnitPlan unit_plan(const MsParams& p, int unit_steps) {
   u.chunks = uint64_t((p.T + unit_steps - 1) / unit_steps);
   u.col_tiles = (p.m + 15) / 16;
   u.num_units = u.chunks * uint64_t(p.num_batch) * uint64_t(u.col_tiles);
-  u.flags_bytes = (u.num_units * 4 + 255) / 256 * 256;
+  u.flags_bytes = (u.num_units * sizeof(uint64_t) + 255) / 256 * 256;
   u.block_bytes = size_t(u.num_units) * 256 * sizeof(float);
   u.total = 256 + u.flags_bytes + 3 * u.block_bytes;
   return u;
+}
+
+// The look-back state of a unit plan in a workspace (see MsUnitWs).
+MsUnitWs unit_ws(const UnitPlan& up, void* workspace) {
+  char* base = static_cast<char*>(workspace);
+  MsUnitWs ws;
+  ws.header = reinterpret_cast<uint32_t*>(base);
+  ws.flags = reinterpret_cast<uint64_t*>(base + 256);
+  ws.P = reinterpret_cast<float*>(base + 256 + up.flags_bytes);
+  ws.L = ws.P + up.num_units * 256;
+  ws.H = ws.L + up.num_units * 256;
+  ws.num_units = uint32_t(up.num_units);
+  ws.chunks = uint32_t(up.chunks);
+  ws.col_tiles = up.col_tiles;
+  ws.spin_limit = lookback_spin_limit();
+  return ws;
 }
 
 template <typename TIn, typename TOut, bool ADJ>
@@ -1508,20 +1553,7 @@ template <typename TIn, typename TOut, bool ADJ>
 hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream) {
   const bool pipe = pipe_fits(p);
   const UnitPlan up = unit_plan(p, pipe ? kLeadCompute * kSteps : kWaves * kSteps);
-  char* base = static_cast<char*>(workspace);
-  MsUnitWs ws;
-  ws.header = reinterpret_cast<uint32_t*>(base);
-  ws.flags = reinterpret_cast<uint32_t*>(base + 256);
-  ws.P = reinterpret_cast<float*>(base + 256 + up.flags_bytes);
-  ws.L = ws.P + up.num_units * 256;
-  ws.H = ws.L + up.num_units * 256;
-  ws.num_units = uint32_t(up.num_units);
-  ws.chunks = uint32_t(up.chunks);
-  ws.col_tiles = up.col_tiles;
-
-  // the unit counter, the status word and every flag start at zero
-  const size_t words = (256 + up.flags_bytes) / 4;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((words + 255) / 256)), dim3(256), 0, stream, ws.header, words);
+  const MsUnitWs ws = unit_ws(up, workspace);
   // Vector access needs n == 16 and every a[t] (and, for m == 1, b[t] and out[t]) aligned
   // to four elements' width.
   const int64_t va = 4 * int64_t(sizeof(TIn)), vo = 4 * int64_t(sizeof(TOut));
@@ -1616,17 +1648,7 @@ hipError_t launch_projective_passes(const MsParams& p0, void* workspace, hipStre
   }
   // the scan of a[t] s[t], b[t] s[t]: the pipelined kernel with its factors
   const UnitPlan up = unit_plan(p, kLeadCompute * kSteps);
-  MsUnitWs ws;
-  ws.header = reinterpret_cast<uint32_t*>(base);
-  ws.flags = reinterpret_cast<uint32_t*>(base + 256);
-  ws.P = reinterpret_cast<float*>(base + 256 + up.flags_bytes);
-  ws.L = ws.P + up.num_units * 256;
-  ws.H = ws.L + up.num_units * 256;
-  ws.num_units = uint32_t(up.num_units);
-  ws.chunks = uint32_t(up.chunks);
-  ws.col_tiles = up.col_tiles;
-  const size_t words = (256 + up.flags_bytes) / 4;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(unsigned((words + 255) / 256)), dim3(256), 0, stream, ws.header, words);
+  const MsUnitWs ws = unit_ws(up, workspace);
   const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cu_count())));
   if (p.m == 1)
     hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true, false, true>), dim3(blocks), dim3(512), 0, stream,
@@ -1674,6 +1696,8 @@ hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, siz
   }
   return hipGetLastError();
 }
+
+void set_lookback_spin_limit(uint32_t limit) { g_spin_limit.store(limit, std::memory_order_relaxed); }
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;

@@ -476,6 +476,30 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
                        "matrix-scan launch");
 }
 
+sx_status sx_matrix_scan_workspace_status(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr)
+    return fail(SX_E_DIM_003, "matrix-scan workspace status: the workspace is NULL; a buffer was expected");
+  if (workspace_bytes < 256)
+    return fail(SX_E_WORKSPACE, "matrix-scan workspace status: %zu bytes is smaller than a workspace header (256)",
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* word = static_cast<char*>(workspace) + sx::kMatrixScanStatusOffset;
+  uint32_t status = 0;
+  hipError_t e = hipMemcpyAsync(&status, word, sizeof status, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_status(e, "matrix-scan workspace status: reading the status word");
+  if (status == 0) return ok();
+  static const uint32_t zero = 0;
+  e = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_status(e, "matrix-scan workspace status: clearing the status word");
+  return fail(SX_E_DEVICE,
+              "matrix-scan: a look-back gave up waiting for an earlier unit's published state (spin limit reached); "
+              "results of the calls on this workspace since its last check are not valid");
+}
+
+void sx_set_lookback_spin_limit(uint32_t limit) { sx::set_lookback_spin_limit(limit); }
+
 }  // extern "C"
 
 // ------------------------------------------------------------------ matrix-scan gradient

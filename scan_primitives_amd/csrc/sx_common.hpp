@@ -146,6 +146,12 @@ hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspa
 hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 size_t matrix_scan_workspace(const MsParams& p);
+// Polls a matrix-scan look-back makes before it gives up (0: the default,
+// about a tenth of a second); process-wide, for the calls launched after it.
+void set_lookback_spin_limit(uint32_t limit);
+// Byte offset, in a matrix-scan workspace, of the status word a look-back
+// that gave up sets (a 32-bit word, zero while every look-back completed).
+constexpr size_t kMatrixScanStatusOffset = 4;
 
 // ---------------------------------------------------------------- matrix-scan gradient
 

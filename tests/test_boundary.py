@@ -39,6 +39,7 @@ def test_header_declares_the_entry_points():
                      "sx_matrix_scan_workspace_bytes", "sx_matrix_scan_out_shape", "sx_linear_scan",
                      "sx_linear_scan_out_shape", "sx_matrix_scan_backward", "sx_matrix_scan_backward_workspace_bytes",
                      "sx_element_scan_backward", "sx_element_scan_backward_workspace_bytes", "sx_table_scan",
+                     "sx_matrix_scan_workspace_status", "sx_set_lookback_spin_limit",
                      "sx_status_name", "sx_last_error", "sx_version"):
         assert required in names
 
@@ -150,6 +151,14 @@ def test_matrix_scan_out_shape_broadcasts(lib):
     r = lib.sx_matrix_scan_out_shape(4, B.i64_array([3, 1, 4, 4]), 3, B.i64_array([5, 4, 1]), out)
     assert r == 4 and list(out[:4]) == [3, 5, 4, 1]
     assert lib.sx_matrix_scan_out_shape(3, B.i64_array([2, 4, 4]), 3, B.i64_array([3, 4, 1]), out) == -1
+
+
+def test_matrix_scan_workspace_status_checks_arguments_on_the_host(lib):
+    # refused before any HIP call: no workspace, or one smaller than its header
+    assert lib.sx_matrix_scan_workspace_status(None, 1 << 20, None) == B.SX_E_DIM_003
+    assert b"NULL" in lib.sx_last_error()
+    assert lib.sx_matrix_scan_workspace_status(ctypes.c_void_p(4096), 64, None) == B.SX_E_WORKSPACE
+    assert b"256" in lib.sx_last_error()
 
 
 def test_matrix_scan_workspace_query_is_host_only(lib):

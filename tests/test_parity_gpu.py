@@ -304,8 +304,11 @@ def test_matrix_pipelined_broadcast_a(dtype, m):
 
 # The pipelined kernel hands staged inputs and look-back state between waves and
 # workgroups; a handoff made too early shows up only now and then (it did: a
-# stage signalled before its last copy landed). Repeated calls, each on a
-# workspace refilled with random bytes, are checked one by one.
+# stage signalled before its last copy landed). Repeated calls on one workspace,
+# zero-filled once, are checked one by one; before each call everything after
+# the workspace header (flags and published maps and states, whatever earlier
+# calls left) is overwritten with random bytes, none of which may count as
+# published by the next call.
 @pytest.mark.parametrize("idx", [3, 4])
 def test_matrix_repeated_calls_dirty_workspace(idx):
     from scan_primitives_amd import _binding as Bd
@@ -317,18 +320,18 @@ def test_matrix_repeated_calls_dirty_workspace(idx):
     lib = Bd.load_library()
     i64 = Bd.i64_array
     ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), i64(a.shape), b.dim(), i64(b.shape), w.axis)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
     out = torch.empty_like(b)
     code = Bd._DTYPES[a.dtype]
     tol = MS_TOL_F32 if a.dtype == torch.float32 else MS_TOL_BF16
     for rep in range(6):
-        ws.random_(0, 256)
+        ws[256:].random_(0, 256)
         st = lib.sx_matrix_scan(code, a.dim(), i64(a.shape), i64(a.stride()), a.data_ptr(), b.dim(), i64(b.shape),
                                 i64(b.stride()), b.data_ptr(), w.axis, 1 if w.reverse else 0, 0, code, out.data_ptr(),
                                 ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
         assert st == 0, lib.sx_last_error()
-        torch.cuda.synchronize()
-        assert int(ws[4:8].view(torch.int32).item()) == 0, "a look-back hit its spin limit"
+        st = lib.sx_matrix_scan_workspace_status(ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
+        assert st == 0, lib.sx_last_error()
         assert_matrix_close(out, ref, tol)
 
 
@@ -351,12 +354,12 @@ def test_matrix_step_residual_repeated_calls(idx):
     lib = Bd.load_library()
     i64 = Bd.i64_array
     ws_bytes = lib.sx_matrix_scan_workspace_bytes(a.dim(), i64(a.shape), b.dim(), i64(b.shape), w.axis)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
     out = torch.empty_like(b)
     code = Bd._DTYPES[a.dtype]
     bar = 1e-4 if out.dtype == torch.float32 else 1.5e-2
     for rep in range(20):
-        ws.random_(0, 256)
+        ws[256:].random_(0, 256)
         st = lib.sx_matrix_scan(code, a.dim(), i64(a.shape), i64(a.stride()), a.data_ptr(), b.dim(), i64(b.shape),
                                 i64(b.stride()), b.data_ptr(), w.axis, 1 if w.reverse else 0, 0, code, out.data_ptr(),
                                 ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
@@ -370,6 +373,35 @@ def test_matrix_step_residual_repeated_calls(idx):
         worst = int(torch.argmax(rel).item())
         assert rel.max().item() <= bar, (f"call {rep}: residual {rel.max().item():.3g} at (batch, t) = "
                                          f"{divmod(worst, rel.shape[1])}")
+    st = lib.sx_matrix_scan_workspace_status(ws.data_ptr(), ws_bytes, Bd._stream_handle(a.device))
+    assert st == 0, lib.sx_last_error()
+
+
+# "Tensor operations", Errors: a failure is a reported code. A look-back that
+# gives up waiting for an earlier chunk (its bounded wait reaches the limit)
+# must be reported, not return wrong states silently. A spin limit of one poll,
+# set from the host, makes every look-back that finds an earlier chunk not yet
+# published give up at once; every kernel still runs to its end. The next
+# check after the default limit is back must find nothing.
+def test_matrix_lookback_give_up_is_reported():
+    w = W.make_matrix(32, 8192, 16, 1, torch.float32, seed=4)
+    _announce(w)
+    t = w.on(DEV)
+    sx.matrix_scan(t["a"], t["b"], axis=1)
+    sx.matrix_scan_status()  # nothing to report before
+    sx.set_lookback_spin_limit(1)
+    try:
+        for _ in range(4):
+            sx.matrix_scan(t["a"], t["b"], axis=1)
+        with pytest.raises(sx.SxError) as e:
+            sx.matrix_scan_status()
+        assert e.value.name == "E-DEVICE" and "gave up" in str(e.value)
+    finally:
+        sx.set_lookback_spin_limit(0)
+    sx.matrix_scan_status()  # cleared by the check that reported it
+    got = sx.matrix_scan(t["a"], t["b"], axis=1)
+    sx.matrix_scan_status()
+    assert_matrix_close(got, run_oracle(w), MS_TOL_F32)
 
 
 def _worst_state_error(got, ref, axis=1):
