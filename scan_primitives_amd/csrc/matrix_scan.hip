@@ -869,20 +869,65 @@ __device__ __forceinline__ f32x4 bterm_of(const UnitRegs<TIn, M1>& R, int c) {
   else return R.Bv[k].get();
 }
 
+// m = 1: the vector recurrence x <- a x + b on the VALU. A 16x16 by 16 product
+// has no reuse of a, so on the MFMA it would fill one of sixteen columns (a
+// sixteenth of the instruction's work); here it is 256 multiply-adds over the
+// wave's 64 lanes. a is in A-operand order (lane (r, c) holds a[c][4r .. 4r+3]);
+// x is held as lane (r, c) -> x[4r .. 4r+3], the same four values across each
+// row of 16 lanes. Lane (r, c) forms row c's products with columns 4r .. 4r+3;
+// two cross-row swaps (v_permlane16_swap, v_permlane32_swap) sum the four
+// column blocks, so that every lane holds y[c]; a round trip through a wave-
+// private LDS area gives lane (r, c) y[4r .. 4r+3] (row r reads its own copy).
+template <typename TIn>
+__device__ __forceinline__ f32x4 matvec_m1(const ARow<TIn>& A, f32x4 x, f32x4 b, float* sv, int r, int c) {
+  const f32x4 a = A.get();
+  float p = a[0] * x[0];
+  p = fmaf(a[1], x[1], p);
+  p = fmaf(a[2], x[2], p);
+  p = fmaf(a[3], x[3], p);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  const float q = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+  const float y = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  sv[16 * r + c] = y;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f32x4 v = *reinterpret_cast<const f32x4*>(sv + 20 * r);  // words 16 r + 4 r .. +3: y[4r .. 4r+3]
+  return v + b;
+}
+
+// b of the wave's step k for m = 1 in the layout above: lane (r, k) holds
+// b[step k][4r .. 4r+3] (see UnitRegs), and a row broadcast of lane k gives it
+// to its whole row.
+template <int k>
+__device__ __forceinline__ f32x4 b_row_m1(f32x4 b1) {
+  f32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b1[q]), 0x150 + k, 0xF, 0xF, false));
+  return o;
+}
+
 // The wave's map: P = a[last] ... a[first] (written row-major), L = the scan of
 // its steps from h = 0 (written in result-register order). issue(k) runs at
 // step k: it starts the copies of the next unit, spread over the steps so that
 // they never back up the memory pipeline.
 // SCALED: each step's result is multiplied by its factor, h[t] = (a[t] h + b[t]) * s[t].
 template <typename TIn, bool M1, bool SCALED, typename Issue>
-__device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw, float* sLw, int lane, int r, int c,
-                                          Issue&& issue) {
+__device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw, float* sLw, float* sv, int lane,
+                                          int r, int c, Issue&& issue) {
   f32x4 P = identity_d(r, c), L = zero4();
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
     (([&] {
        issue(ks);
        P = mfma_a<TIn>(R.A[ks], P, zero4());
-       L = mfma_a<TIn>(R.A[ks], L, bterm_of<TIn, M1, ks>(R, c));
+       if constexpr (M1) {  // L in the VALU layout of matvec_m1; from L = 0 the first step is b
+         if constexpr (ks == 0) L = b_row_m1<ks>(R.b1);
+         else L = matvec_m1<TIn>(R.A[ks], L, b_row_m1<ks>(R.b1), sv, r, c);
+       } else {
+         L = mfma_a<TIn>(R.A[ks], L, bterm_of<TIn, M1, ks>(R, c));
+       }
        if constexpr (SCALED) {
          const float sk = step_scale<ks>(R);
          P *= sk;
@@ -893,6 +938,7 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
   }(std::make_integer_sequence<int, 16>{});
 #pragma unroll
   for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = P[v];
+  if constexpr (M1) L = c == 0 ? L : zero4();  // result-register order: column 0 only
   *reinterpret_cast<f32x4*>(&sLw[lane * 4]) = L;
 }
 
@@ -903,7 +949,7 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
 // lane four consecutive values of one row, stored as one piece per step.
 template <typename TIn, typename TOut, bool M1, bool SCALED>
 __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h, const MsParams& p, const PipeGeo& g,
-                                             int lane, int r, int c) {
+                                             float* sv, int lane, int r, int c) {
   const int64_t T = p.T;
   const int m = p.m;
   TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
@@ -916,40 +962,22 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
   // that chain executes.
   const bool full = g.q0 + 16 <= T;
   if constexpr (M1) {
-    f32x4 acc = zero4();  // lane (r, c) ends up with h[step c][4r .. 4r+3]
-    auto gather = [&](auto ks_c, const f32x4& hv) {  // h[ks] (lanes (r, 0)) into column ks
-      constexpr int ks = decltype(ks_c)::value;
+    // the recurrence on the VALU (matvec_m1); h arrives in result-register order (column 0:
+    // lanes (r, 0)) and a row broadcast of lane 0 puts it in the VALU layout
+    f32x4 x;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = hv[v];
-        if constexpr (ks > 0)
-          x = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(hv[v]), 0x110 + ks, 0xF, 0xF, false));
-        acc[v] = c == ks ? x : acc[v];
-      }
-    };
-    if (full) {
-      [&]<int... ks>(std::integer_sequence<int, ks...>) {
-        (([&] {
-           f32x4 hn = mfma_a<TIn>(R.A[ks], h, bterm_of<TIn, M1, ks>(R, c));
-           if constexpr (SCALED) hn *= step_scale<ks>(R);
-           if constexpr (ks > 0) gather(std::integral_constant<int, ks - 1>{}, h);
-           h = hn;
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, 16>{});
-      gather(std::integral_constant<int, 15>{}, h);
-    } else {
-      [&]<int... ks>(std::integer_sequence<int, ks...>) {
-        (([&] {
-           if (g.q0 + ks < T) {
-             h = mfma_a<TIn>(R.A[ks], h, bterm_of<TIn, M1, ks>(R, c));
-             if constexpr (SCALED) h *= step_scale<ks>(R);
-             gather(std::integral_constant<int, ks>{}, h);
-           }
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, 16>{});
-    }
+    for (int v = 0; v < 4; ++v) x[v] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h[v]), 0x150, 0xF, 0xF, false));
+    f32x4 acc = zero4();  // lane (r, c) ends up with h[step c][4r .. 4r+3]
+    [&]<int... ks>(std::integer_sequence<int, ks...>) {
+      (([&] {
+         // steps past the end hold the identity and a zero b: x stays, and is not stored
+         x = matvec_m1<TIn>(R.A[ks], x, b_row_m1<ks>(R.b1), sv, r, c);
+         if constexpr (SCALED) x *= step_scale<ks>(R);
+#pragma unroll
+         for (int v = 0; v < 4; ++v) acc[v] = c == ks ? x[v] : acc[v];
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, 16>{});
     if (g.q0 + c < T) {
       TOut* op = out_at(c) + 4 * r;
       if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), acc);
@@ -1074,7 +1102,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   __shared__ __attribute__((aligned(16))) float sP[kBufs][NC][256];
   __shared__ __attribute__((aligned(16))) float sL[kBufs][NC][256];
   __shared__ __attribute__((aligned(16))) float sX[kBufs][256];
-  __shared__ __attribute__((aligned(16))) float sT[256];
+  __shared__ __attribute__((aligned(16))) float sV[NC][M1 ? 64 : 4];  // m = 1: each compute wave's matvec_m1 area
   __shared__ uint32_t sId[4];
   __shared__ uint32_t sIdCount, sSumDone[NC], sCarryDone[kBufs], sHinIt[kBufs], sLanded[NC], sConsumed[NC];
 
@@ -1112,43 +1140,49 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     // ------------------------------------------------------------ loader
     const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const uint32_t*>(&sStage[0][0])));
     // Stage w of unit k is filled once compute wave w has read unit k-1 from it,
-    // in whatever order the compute waves free their stages. Landings are
-    // confirmed with vmcnt(0), which relies on no ordering among the copies:
-    // whenever three stages are in flight or there is nothing to issue, the
-    // loader waits for all of them and signals them all. (Signalling the
-    // oldest stage alone with a partial vmcnt wait measured no faster.)
+    // in whatever order the compute waves free their stages. Up to three stages
+    // are in flight; they are retired in the order they were issued (loads
+    // return in order, so vmcnt(n) with n the copies issued after a stage means
+    // that stage has landed), each one signalled as soon as it has landed, and
+    // the queue carries over from one unit to the next, so the copies in flight
+    // never drain to zero while there is a stage to fill.
+    int qw[3] = {0, 0, 0}, qk[3] = {0, 0, 0};  // stages in flight, oldest first: wave and unit index
+    int head = 0, n_pending = 0;
+    auto retire_oldest = [&]() {
+      if (n_pending == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kPieces));
+      else if (n_pending == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kPieces));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_signal_set(&sLanded[qw[head]], uint32_t(qk[head]) + 1, lane);
+      head = head == 2 ? 0 : head + 1;
+      --n_pending;
+    };
     for (int k = 0;; ++k) {
       const uint32_t unit = unit_id(k);
       if (unit >= NU) break;
-      uint32_t issued = 0, pending = 0;  // stages started / started but not yet signalled
-      int n_issued = 0, n_pending = 0;
-      auto flush = [&]() {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        for (int w = 0; w < NC; ++w)
-          if ((pending >> w) & 1u) lds_signal_set(&sLanded[w], uint32_t(k) + 1, lane);
-        pending = 0;
-        n_pending = 0;
-      };
+      uint32_t issued = 0;  // stages of unit k started
+      int n_issued = 0;
       while (n_issued < NC) {
         bool progress = false;
         for (int w = 0; w < NC; ++w) {
           if ((issued >> w) & 1u) continue;
           if (lds_read_u32(&sConsumed[w]) < uint32_t(k)) continue;
-          if (n_pending == 3) flush();
+          if (n_pending == 3) retire_oldest();
           stage_wave<TIn, M1, ADJ>(p, pipe_geo(p, ws, unit, w, kUnit), &sStage[w][0], stage_lds + w * S::kWave, lane);
-          pending |= 1u << w;
+          const int tail = head + n_pending >= 3 ? head + n_pending - 3 : head + n_pending;
+          qw[tail] = w;
+          qk[tail] = k;
           ++n_pending;
           issued |= 1u << w;
           ++n_issued;
           progress = true;
         }
         if (!progress) {
-          if (n_pending > 0) flush();
+          if (n_pending > 0) retire_oldest();
           else __builtin_amdgcn_s_sleep(1);
         }
       }
-      if (n_pending > 0) flush();
     }
+    while (n_pending > 0) retire_oldest();
   } else
 
   if (hw_wave == LEADER) {
@@ -1175,38 +1209,21 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const bool live = c < min(16, p.m - g.ct * 16);
       const uint32_t base = g.bt * ws.chunks, slot = base + g.chunk;
       const int kb = k % kBufs;
-      // Compose the wave maps in step order. Slot i is overwritten with the
-      // composition of maps 0 .. i, so that wave i+1 carries the unit's
-      // entering state over all the waves before it with one map.
-      f32x4 G = identity_d(r, c), GL = zero4();
-      for (int i = 0; i < NC; ++i) {
-        lds_wait_at_least(&sSumDone[i], uint32_t(k) + 1);  // wave i's map of unit k is in LDS
-        const f32x4 Pa = *reinterpret_cast<const f32x4*>(&sP[kb][i][c * 16 + 4 * r]);
-        const f32x4 Li = *reinterpret_cast<const f32x4*>(&sL[kb][i][lane * 4]);
-        G = mfma_16x16x16(Pa, G, zero4());
-        GL = mfma_16x16x16(Pa, GL, Li);
-        if (i + 1 < NC) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sP[kb][i][(4 * r + v) * 16 + c] = G[v];
-          *reinterpret_cast<f32x4*>(&sL[kb][i][lane * 4]) = GL;
-        }
-      }
-      const f32x4 GA = to_a_operand(sT, G, r, c);
+      // the state entering the unit, from the units before it, found while the
+      // compute waves summarise this one
       f32x4 h_in = zero4();
-      if (g.chunk > 0) {
-        // the aggregate goes out first, so that later units need not wait for this one
-        pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-        if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
-        raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
-        h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch);
-      }
+      if (g.chunk > 0) h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch);
+      // the unit's map: the compute waves leave the composition of all its waves' maps in the last slot
+      lds_wait_at_least(&sSumDone[NC - 1], uint32_t(k) + 1);
+      const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
+      const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
       if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
-      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
       // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
       *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
       lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
+      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores of the leaving state)
     }
   } else {
   // -------------------------------------------------------------- compute waves
@@ -1228,8 +1245,43 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     lds_signal_set(&sConsumed[wave], uint32_t(k) + 1, lane);  // (waits for the stage reads first)
     const int kb = k % kBufs;
     lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
-    summarize<TIn, M1, SCALED>(Rc, &sP[kb][wave][0], &sL[kb][wave][0], lane, r, c, [](int) {});
+    float* sPw = &sP[kb][wave][0];
+    float* sLw = &sL[kb][wave][0];
+    summarize<TIn, M1, SCALED>(Rc, sPw, sLw, &sV[wave][0], lane, r, c, [](int) {});
+    if (wave > 0) {
+      // this wave's map after the composition of the maps of waves 0 .. wave-1 (left in
+      // slot wave-1 by the wave before), written back over this wave's own slot
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const f32x4 PA = *reinterpret_cast<const f32x4*>(sPw + c * 16 + 4 * r);  // own map, A-operand order
+      const f32x4 Lw = *reinterpret_cast<const f32x4*>(sLw + lane * 4);
+      lds_wait_at_least(&sSumDone[wave - 1], uint32_t(k) + 1);
+      const float* sPp = &sP[kb][wave - 1][0];
+      f32x4 Gp;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Gp[v] = sPp[(4 * r + v) * 16 + c];  // result-register order
+      const f32x4 GLp = *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]);
+      const f32x4 G = mfma_16x16x16(PA, Gp, zero4());
+      const f32x4 GL = mfma_16x16x16(PA, GLp, Lw);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = G[v];
+      *reinterpret_cast<f32x4*>(sLw + lane * 4) = GL;
+    }
     lds_signal_set(&sSumDone[wave], uint32_t(k) + 1, lane);
+    if (wave == NC - 1 && gc.chunk > 0) {
+      // the unit's map goes out as soon as it is composed, so that later units' look-backs
+      // need not wait for this workgroup's leader
+      const f32x4 GA = *reinterpret_cast<const f32x4*>(sPw + c * 16 + 4 * r);
+      const f32x4 GL = *reinterpret_cast<const f32x4*>(sLw + lane * 4);
+      const uint32_t slot = gc.bt * ws.chunks + gc.chunk;
+      pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
+      if (c < min(16, p.m - gc.ct * 16)) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+      raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
+    }
     return true;
   };
   // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.
@@ -1241,7 +1293,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][wave - 1][c * 16 + 4 * r]), h,
                         *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]));
     lds_signal_add(&sCarryDone[kb], lane);
-    replay_steps<TIn, TOut, M1, SCALED>(R, h, p, g, lane, r, c);
+    replay_steps<TIn, TOut, M1, SCALED>(R, h, p, g, &sV[wave][0], lane, r, c);
   };
 
   for (int k = 0;; k += 2) {
