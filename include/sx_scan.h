@@ -233,6 +233,33 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
                          const void* b, int axis, int reverse, int projective, sx_dtype out_dtype,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device memory sx_matrix_scan_noalloc keeps, per device, for its
+ * look-back state. */
+#define SX_MATRIX_SCAN_SCRATCH_BYTES (16u << 20)
+
+/*
+ * sx_matrix_scan_noalloc: sx_matrix_scan (the same arguments, the same result)
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace: the look-back state lives in a fixed array of
+ * SX_MATRIX_SCAN_SCRATCH_BYTES bytes in device memory, one per device the
+ * library runs on, kept until the process ends. It calls no allocation
+ * routine. The first call on a device sets the array up (its address, and a
+ * synchronous zero-fill): make that first call outside graph capture.
+ *
+ * Shapes whose look-back state is larger than the array (sx_matrix_scan_workspace_bytes
+ * above SX_MATRIX_SCAN_SCRATCH_BYTES: about 5000 units of 96 steps of one
+ * 16-column tile, e.g. 32 x 8192 and 16 x 16384 fit) return SX_E_WORKSPACE
+ * before anything is launched. Every call on a device shares that device's
+ * array and leaves it ready for the next call: calls that overlap on one
+ * device (concurrent streams, host threads) race. A look-back give-up is
+ * recorded in the array, which sx_matrix_scan_workspace_status cannot reach.
+ */
+sx_status sx_matrix_scan_noalloc(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                                 const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides,
+                                 const void* b, int axis, int reverse, int projective, sx_dtype out_dtype, void* out,
+                                 void* stream);
+
 /* Workspace bytes sx_matrix_scan needs for these shapes (0 for invalid ones),
  * with or without :projective (the size covers both). */
 size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank,

@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sx_matrix_scan.restype = c_int
     lib.sx_matrix_scan.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
                                    c_int, c_int, c_int, c_int, vp, vp, c_size, vp]
+    lib.sx_matrix_scan_noalloc.restype = c_int
+    lib.sx_matrix_scan_noalloc.argtypes = [c_int, c_int, _i64p, _i64p, vp, c_int, _i64p, _i64p, vp,
+                                           c_int, c_int, c_int, c_int, vp, vp]
     lib.sx_matrix_scan_workspace_bytes.restype = c_size
     lib.sx_matrix_scan_workspace_bytes.argtypes = [c_int, _i64p, c_int, _i64p, c_int]
     lib.sx_matrix_scan_out_shape.restype = c_int

@@ -37,6 +37,7 @@
 // straight back as the next B operand, with no data movement between steps.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <utility>
 
 #include "ms_mfma.hpp"
@@ -1750,6 +1751,42 @@ hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, siz
 }
 
 void set_lookback_spin_limit(uint32_t limit) { g_spin_limit.store(limit, std::memory_order_relaxed); }
+
+// The look-back state of sx_matrix_scan_noalloc: a fixed array in device memory,
+// one per device the library runs on, held until the process ends. Host code
+// reaches it only through the address hipGetSymbolAddress gives on each device
+// (the array's name in host code is a stand-in, not a device address).
+__device__ __align__(256) unsigned char scratch[kMatrixScanScratchBytes];
+
+hipError_t matrix_scan_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex init_mutex;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(init_mutex);
+    ptr = ptrs[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      // once per device, with the device current: its address, zero-filled once as every
+      // matrix-scan workspace must be; synchronous, so no stream can run ahead of it
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      e = hipMemset(ptr, 0, kMatrixScanScratchBytes);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) return e;
+      // every call above succeeded; what they may have left in the runtime's
+      // last-error slot is not this call's error (launch checks read that slot)
+      (void)hipGetLastError();
+      ptrs[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (p.num_batch <= 0 || p.T <= 0 || p.n == 0 || p.m == 0) return hipSuccess;

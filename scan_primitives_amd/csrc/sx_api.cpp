@@ -412,10 +412,16 @@ size_t sx_matrix_scan_workspace_bytes(int a_rank, const int64_t* a_shape, int b_
   return sx::matrix_scan_workspace(p);
 }
 
-sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides, const void* a,
-                         int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b, int axis,
-                         int reverse, int projective, sx_dtype out_dtype, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// sx_matrix_scan, and with scratch = true sx_matrix_scan_noalloc: the look-back
+// state then goes to the library's fixed device array instead of `workspace`.
+sx_status matrix_scan_call(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                           const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b,
+                           int axis, int reverse, int projective, sx_dtype out_dtype, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream, bool scratch) {
   if (dtype != SX_F32 && dtype != SX_BF16)
     return fail(SX_E_DIM_002, "matrix-scan: a and b must be f32 or bf16 (dtype code %d)", int(dtype));
   if (out_dtype != SX_F32 && out_dtype != SX_BF16)
@@ -450,6 +456,20 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
     if (overlaps(olo, ohi, lo, hi)) return fail(SX_E_ALIAS, "matrix-scan: out overlaps b");
   }
   const size_t need = sx::matrix_scan_workspace(p);
+  if (scratch) {
+    if (need > sx::kMatrixScanScratchBytes)
+      return fail(SX_E_WORKSPACE,
+                  "matrix-scan: a %s by %s scan needs %zu bytes of look-back state, more than the %zu bytes the "
+                  "allocation-free entry point keeps; use sx_matrix_scan with a workspace",
+                  shape_str(a_rank, a_shape).c_str(), shape_str(b_rank, b_shape).c_str(), need,
+                  sx::kMatrixScanScratchBytes);
+    workspace_bytes = sx::kMatrixScanScratchBytes;
+    workspace = nullptr;
+    if (need > 0) {
+      const hipError_t e = sx::matrix_scan_scratch(&workspace);
+      if (e != hipSuccess) return device_status(e, "matrix-scan: setting up the scratch array");
+    }
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(SX_E_WORKSPACE, "matrix-scan: workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -474,6 +494,26 @@ sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, con
   p.out = out;
   return device_status(sx::launch_matrix_scan(p, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
                        "matrix-scan launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+sx_status sx_matrix_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides, const void* a,
+                         int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b, int axis,
+                         int reverse, int projective, sx_dtype out_dtype, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return matrix_scan_call(dtype, a_rank, a_shape, a_strides, a, b_rank, b_shape, b_strides, b, axis, reverse,
+                          projective, out_dtype, out, workspace, workspace_bytes, stream, false);
+}
+
+sx_status sx_matrix_scan_noalloc(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+                                 const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides,
+                                 const void* b, int axis, int reverse, int projective, sx_dtype out_dtype, void* out,
+                                 void* stream) {
+  return matrix_scan_call(dtype, a_rank, a_shape, a_strides, a, b_rank, b_shape, b_strides, b, axis, reverse,
+                          projective, out_dtype, out, nullptr, 0, stream, true);
 }
 
 sx_status sx_matrix_scan_workspace_status(void* workspace, size_t workspace_bytes, void* stream) {

@@ -152,6 +152,11 @@ void set_lookback_spin_limit(uint32_t limit);
 // Byte offset, in a matrix-scan workspace, of the status word a look-back
 // that gave up sets (a 32-bit word, zero while every look-back completed).
 constexpr size_t kMatrixScanStatusOffset = 4;
+// sx_matrix_scan_noalloc: the look-back state lives in a fixed device array of
+// this many bytes (SX_MATRIX_SCAN_SCRATCH_BYTES); matrix_scan_scratch gives its
+// address on the current device, set up (and zero-filled) on first use.
+constexpr size_t kMatrixScanScratchBytes = SX_MATRIX_SCAN_SCRATCH_BYTES;
+hipError_t matrix_scan_scratch(void** out);
 
 // ---------------------------------------------------------------- matrix-scan gradient
 
