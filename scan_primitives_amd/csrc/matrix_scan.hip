@@ -1104,7 +1104,12 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   __shared__ __attribute__((aligned(16))) float sL[kBufs][NC][256];
   __shared__ __attribute__((aligned(16))) float sX[kBufs][256];
   __shared__ __attribute__((aligned(16))) float sV[NC][M1 ? 64 : 4];  // m = 1: each compute wave's matvec_m1 area
-  __shared__ uint32_t sId[4];
+  // Unit ids in a ring of 8. The leader publishes id k+2 as it starts unit k, and
+  // it starts unit k once unit k-1's summaries are in, so the readers (the
+  // compute waves, the loader) may still need ids from k-1 on: four ids are live
+  // at once; the ring leaves room to spare.
+  constexpr int kIdRing = 8;
+  __shared__ uint32_t sId[kIdRing];
   __shared__ uint32_t sIdCount, sSumDone[NC], sCarryDone[kBufs], sHinIt[kBufs], sLanded[NC], sConsumed[NC];
 
   const int tid = int(threadIdx.x);
@@ -1134,7 +1139,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   // is working on, whose predecessors are all done, so look-back ends.
   auto unit_id = [&](int k) -> uint32_t {
     lds_wait_at_least(&sIdCount, uint32_t(k) + 1);
-    return __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
+    return __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k % kIdRing]));
   };
 
   if (hw_wave == LOADER) {
@@ -1190,7 +1195,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     // ------------------------------------------------------------ leader
     __builtin_amdgcn_s_setprio(2);  // its look-back is on every replay's path
     auto publish_id = [&](int k, uint32_t id) {
-      lds_signal_set(&sId[k & 3], __builtin_amdgcn_readfirstlane(id), lane);
+      lds_signal_set(&sId[k % kIdRing], __builtin_amdgcn_readfirstlane(id), lane);
       lds_signal_set(&sIdCount, uint32_t(k) + 1, lane);
     };
     auto fetch_id = [&]() -> uint32_t {
@@ -1203,28 +1208,30 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     uint32_t pending = fetch_id();
     for (int k = 0;; ++k) {
       publish_id(k + 2, pending);
-      const uint32_t unit = __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k & 3]));
+      const uint32_t unit = __builtin_amdgcn_readfirstlane(lds_read_u32(&sId[k % kIdRing]));
       if (unit >= NU) break;  // (ids only grow: every later unit is past the end as well)
       pending = fetch_id();
       const PipeGeo g = pipe_geo(p, ws, unit, 0, kUnit);
       const bool live = c < min(16, p.m - g.ct * 16);
-      const uint32_t base = g.bt * ws.chunks, slot = base + g.chunk;
+      const uint32_t base = g.bt * ws.chunks;
       const int kb = k % kBufs;
       // the state entering the unit, from the units before it, found while the
       // compute waves summarise this one
       f32x4 h_in = zero4();
       if (g.chunk > 0) h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch);
-      // the unit's map: the compute waves leave the composition of all its waves' maps in the last slot
-      lds_wait_at_least(&sSumDone[NC - 1], uint32_t(k) + 1);
-      const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
-      const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
-      const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
-      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
       // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
       *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
       lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
-      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores of the leaving state)
+      // the leaving state: the unit's map (the compute waves leave the composition of all
+      // its waves' maps in the last slot) applied to the entering state
+      lds_wait_at_least(&sSumDone[NC - 1], uint32_t(k) + 1);
+      const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
+      const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
+      const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
+      const uint32_t slot = base + g.chunk;
+      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores)
     }
   } else {
   // -------------------------------------------------------------- compute waves
