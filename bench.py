@@ -48,6 +48,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+LLC_BYTES = 256 * 1024 * 1024  # MI355X last-level (Infinity) cache
+# MI355X dense MFMA peaks, AMD's published figures (TFLOP/s)
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 METRIC = "scan elements/s and achieved HBM GB/s vs MI355X peak (rocprof), per config"
 KERNEL_SOURCES = ["scan_primitives_amd/csrc/element_scan.hip", "scan_primitives_amd/csrc/normcap_quad.hip",
                   "scan_primitives_amd/csrc/matrix_scan.hip", "scan_primitives_amd/csrc/matrix_scan_grad.hip",
@@ -89,34 +92,141 @@ def measured_traffic(kernel_label: str):
     return None if entry is None else entry.get("bytes")
 
 
+def mfma_figures(w, sec: float) -> dict:
+    """Matrix-scan MFMA utilisation for one call taking ``sec`` seconds.
+
+    Algorithmic: the recurrence's own work, one n x n by n x m product a step
+    (2 n^2 m flops), against the f32 MFMA peak (the scan computes in f32 for f32
+    and bf16 operands alike). Executed: the MFMA operations the kernels issue
+    per call, from the committed rocprofv3 counter summary (SQ_INSTS_VALU_MFMA_
+    MOPS_*) when it was taken on the current kernel sources, against each
+    precision's own peak; null otherwise."""
+    if w.op != "matrix_scan":
+        return {}
+    b = w.tensors["b"]
+    n, m = int(b.shape[-2]), int(b.shape[-1])
+    steps = b.numel() // (n * m)
+    alg = 2.0 * n * n * m * steps / sec / 1e12
+    out = {"mfma_algorithmic_tflops": round(alg, 3),
+           "mfma_algorithmic_util": round(alg / MFMA_PEAK_TFLOPS["f32"], 5),
+           "mfma_executed": None}
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return out
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return out
+    counted = data.get("per_call", {}).get(w.name)
+    if counted:
+        ex = {}
+        for prec, flops in counted.items():
+            tf = flops / sec / 1e12
+            ex[prec] = {"tflops": round(tf, 3), "util": round(tf / MFMA_PEAK_TFLOPS[prec], 5)}
+        out["mfma_executed"] = ex
+    return out
+
+
+def _oracle_call(w_op, w_body, w_axis, w_state_axis, w_reverse, arrays):
+    import oracle
+    if w_op == "element_scan":
+        return oracle.element_scan(w_body, arrays["initial"], [arrays["x"], arrays["s"]], axis=w_axis,
+                                   state_axis=w_state_axis, reverse=w_reverse)
+    return oracle.matrix_scan(arrays["a"], arrays["b"], axis=w_axis, reverse=w_reverse)
+
+
+# CPU baseline workers (spawned processes): the inputs sit in shared memory, one
+# block per array, and a task names a workload and a slice of its batch dim (dim
+# 0; the scans run along dim 1, so a slice is an independent sub-problem).
+_SHARED = {}
+
+
+def _oracle_worker_init(specs):
+    from multiprocessing import shared_memory
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)  # one core per worker
+    for key, (name, shape, dtype) in specs.items():
+        shm = shared_memory.SharedMemory(name=name)
+        _SHARED[key] = (shm, np.ndarray(shape, dtype=dtype, buffer=shm.buf))
+
+
+def _oracle_worker_task(task):
+    j, meta, names, lo, hi = task
+    arrays = {k: _SHARED[(j, k)][1][lo:hi] for k in names}
+    _oracle_call(*meta, arrays)
+    return 0
+
+
 def cpu_baseline(workloads, min_seconds: float = 10.0) -> dict:
-    """Time the CPU oracle, as it stands, on the same workloads: whole passes
-    over every workload at full size, repeated until at least ``min_seconds``
-    of oracle time have been spent (one pass takes well under a second)."""
+    """Time the CPU oracle, as it stands, on the same workloads, on 1 core and
+    on the machine's cores (at most 16, the CPU share of one GPU on the box): whole
+    passes over every workload at full size, repeated until at least
+    ``min_seconds`` have been spent each way. The multi-core passes split each
+    workload's batch dim across worker processes (the oracle itself is
+    unchanged); the inputs are shared, not copied per pass."""
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
-    import oracle
+    hosts = [{k: np.ascontiguousarray(v.float().numpy()) for k, v in w.tensors.items()} for w in workloads]
+    metas = [(w.op, getattr(w, "body", None), w.axis, w.state_axis, w.reverse) for w in workloads]
+    elems_per_pass = sum(w.out_numel for w in workloads)
 
-    total_elems, total_s, passes = 0, 0.0, 0
-    hosts = [{k: v.float().numpy() for k, v in w.tensors.items()} for w in workloads]
+    # 1 core, after one untimed pass (first-touch and import costs stay out, as for the workers)
+    one_s, one_passes = 0.0, 0
     with threadpool_limits(limits=1):
-        while passes == 0 or total_s < min_seconds:
-            for w, host in zip(workloads, hosts):
+        for meta, host in zip(metas, hosts):
+            _oracle_call(*meta, host)
+        while one_passes == 0 or one_s < min_seconds:
+            for meta, host in zip(metas, hosts):
                 t0 = time.perf_counter()
-                if w.op == "element_scan":
-                    oracle.element_scan(w.body, host["initial"], [host["x"], host["s"]], axis=w.axis,
-                                        state_axis=w.state_axis, reverse=w.reverse)
-                else:
-                    oracle.matrix_scan(host["a"], host["b"], axis=w.axis, reverse=w.reverse)
-                dt = time.perf_counter() - t0
-                if passes == 0:
-                    log(f"cpu oracle {w.name}: {dt:.3f} s")
-                total_elems += w.out_numel
-                total_s += dt
-            passes += 1
-    return {"value": total_elems / total_s, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes of the float64 numpy oracle over every selected workload at full size, "
-                      f"single-threaded; {total_elems} output elements in {total_s:.2f} s"}
+                _oracle_call(*meta, host)
+                one_s += time.perf_counter() - t0
+            one_passes += 1
+    one_rate = one_passes * elems_per_pass / one_s
+
+    # the box's cores: worker processes over shared inputs
+    cores = max(1, min(16, os.cpu_count() or 1))
+    blocks, specs = [], {}
+    try:
+        for j, host in enumerate(hosts):
+            for k, arr in host.items():
+                shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+                np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+                blocks.append(shm)
+                specs[(j, k)] = (shm.name, arr.shape, arr.dtype.str)
+        tasks = []
+        for j, (w, host) in enumerate(zip(workloads, hosts)):
+            lead = next(iter(host.values())).shape[0]
+            cuts = np.linspace(0, lead, min(cores, lead) + 1).astype(int)
+            names = list(host.keys())
+            tasks += [(j, metas[j], names, int(lo), int(hi)) for lo, hi in zip(cuts[:-1], cuts[1:]) if hi > lo]
+        with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn"),
+                                 initializer=_oracle_worker_init, initargs=(specs,)) as pool:
+            list(pool.map(_oracle_worker_task, tasks))  # start the workers, warm them up
+            many_s, many_passes = 0.0, 0
+            while many_passes == 0 or many_s < min_seconds:
+                t0 = time.perf_counter()
+                list(pool.map(_oracle_worker_task, tasks))
+                many_s += time.perf_counter() - t0
+                many_passes += 1
+    finally:
+        for shm in blocks:
+            shm.close()
+            shm.unlink()
+    many_rate = many_passes * elems_per_pass / many_s
+    log(f"cpu oracle: {one_rate:.3e} elements/s on 1 core, {many_rate:.3e} on {cores} cores")
+    return {"value": many_rate, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "single_core_value": one_rate,
+            "sample": f"the float64 numpy oracle over every selected workload at full size: {one_passes} passes on "
+                      f"1 core ({one_s:.1f} s) and {many_passes} passes on {cores} worker processes, each workload's "
+                      f"batch dim split across them ({many_s:.1f} s wall); os.cpu_count() = {os.cpu_count()}"}
 
 
 def main() -> int:
@@ -237,16 +347,18 @@ def main() -> int:
         torch.cuda.synchronize()
         sec = e0.elapsed_time(e1) / 1e3 / (args.steps * r)
         gbs = w.algorithmic_bytes / sec / 1e9
-        per_config.append({
+        entry = {
             "workload": w.name,
             "call_us": round(sec * 1e6, 3),
             "calls_per_replay": r,
             "elements_per_s": w.out_numel / sec,
             "algorithmic_bytes": w.algorithmic_bytes,
             "hbm_gbs": round(gbs, 2),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "hbm_frac_warm": round(gbs / HBM_PEAK_GBS, 4),
             "in_step": j < len(workloads),
-        })
+        }
+        entry.update(mfma_figures(w, sec))
+        per_config.append(entry)
         log(f"{w.name}: {sec * 1e6:.2f} us/call, {w.out_numel / sec:.3e} elements/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak)")
 
@@ -267,6 +379,11 @@ def main() -> int:
         gbs = w.algorithmic_bytes / sec / 1e9
         per_config[j]["call_us_cold"] = round(sec * 1e6, 3)
         per_config[j]["hbm_frac_cold"] = round(gbs / HBM_PEAK_GBS, 4)
+        # the quoted HBM fraction: cold for a workload that fits the last-level cache (its warm
+        # figure would measure that cache), warm (back-to-back calls) otherwise
+        fits = w.algorithmic_bytes <= LLC_BYTES
+        per_config[j]["hbm_frac"] = per_config[j]["hbm_frac_cold" if fits else "hbm_frac_warm"]
+        per_config[j]["hbm_frac_basis"] = "cold" if fits else "warm"
         log(f"{w.name} (cold, median of {len(times)} single calls): {sec * 1e6:.2f} us/call, {gbs:.1f} GB/s")
     del flush
 
@@ -284,9 +401,9 @@ def main() -> int:
 
     dom = max(range(len(workloads)), key=lambda j: per_config[j]["call_us"])
     dw, dc = workloads[dom], per_config[dom]
-    roofline = {"bound": "hbm", "achieved": dc["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dc["hbm_frac"], "traffic": measured_traffic(dw.name), "kernel": dw.name,
-                "algorithmic_bytes_per_call": dw.algorithmic_bytes}
+    roofline = {"bound": "hbm", "achieved": round(dc["hbm_frac"] * HBM_PEAK_GBS, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dc["hbm_frac"], "traffic": measured_traffic(dw.name), "kernel": dw.name,
+                "basis": dc["hbm_frac_basis"], "algorithmic_bytes_per_call": dw.algorithmic_bytes}
 
     result = {
         "metric": METRIC,

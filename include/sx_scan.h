@@ -203,14 +203,16 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *                have any stride, including 0. Otherwise SX_E_UNSUPPORTED.
  *  axis          the scan axis among the broadcast leading dims.
  *  reverse       0 forward, nonzero reverse.
- *  projective    nonzero: the :projective variant of the same section. A
- *                running product P of the a's, from the identity, takes each
- *                step's a (P = a[t] @ P); m, the largest |entry| of P (1 if
- *                P is zero), divides P and the new state:
- *                h[t] = (a[t] @ h[prev] + b[t]) / m. The result is h up to a
- *                positive factor per step when b is zero after its first
- *                step, and stays in range where the plain product would
- *                overflow. With n = 16, on the shapes the chunked scan
+ *  projective    nonzero: the :projective variant of the same section,
+ *                meant for chains of projective maps whose plain product
+ *                would leave f32's range. Each step multiplies a running
+ *                product P (starting at the identity) by that step's a,
+ *                P = a[t] @ P, then rescales: with m the entry of P of
+ *                largest magnitude (m = 1 for a zero P), both P and the new
+ *                state are divided by m, h[t] = (a[t] @ h[prev] + b[t]) / m.
+ *                When b vanishes after its first step, every state then
+ *                equals the plain scan's state times a positive number of
+ *                its own. With n = 16, on the shapes the chunked scan
  *                takes, it runs in parallel in the workspace (passes that
  *                compute every step's factor, then the scan); on other
  *                shapes it runs serially in time.
@@ -344,8 +346,10 @@ size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shap
  * For every index outside `axis` of the broadcast shape the scalar state runs
  *   forward  h[t] = a[t] * h[t-1] + b[t]  from h[-1] = 0  (h[0] = b[0]),
  *   reverse  h[t] = a[t] * h[t+1] + b[t]  from h[T] = 0  (h[T-1] = b[T-1]),
- * and out[t] = h[t]; a[0] (forward) or a[T-1] (reverse) is never read for
- * its value. Computation is f32 for f32 and bf16 operands alike.
+ * and out[t] = h[t]. a[0] (forward) or a[T-1] (reverse) multiplies the zero
+ * state, so any finite value there gives the same result (the kernels do form
+ * that product: an infinite or NaN entry there gives NaN). Computation is f32
+ * for f32 and bf16 operands alike.
  *
  *  dtype         SX_F32 or SX_BF16, shared by a and b (else E-DIM-002).
  *  a_*, b_*      rank (0..SX_MAX_RANK; 0 is a number, its shape may be

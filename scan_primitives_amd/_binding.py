@@ -14,7 +14,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsx_scan.so")
+# SX_SCAN_LIB selects another build of the same library (the host-sanitized one the
+# boundary tests run under); by default the in-tree libsx_scan.so.
+LIB_PATH = os.environ.get("SX_SCAN_LIB") or os.path.join(HERE, "libsx_scan.so")
 
 SX_OK = 0
 SX_E_DIM_001 = 1
@@ -519,6 +521,16 @@ class _MatrixScanFunction(torch.autograd.Function):
             raise SxError(SX_E_UNSUPPORTED, "matrix-scan: :projective true has no gradient; differentiating "
                                             "through it is an error")
         a, h = ctx.saved_tensors
+        g = g.to(h.dtype)
+        # The gradient scan takes a, h and g of one dtype. With an out_dtype other than the
+        # operands' one, widen to f32 (exact): a for bf16 operands with an f32 result; h and g
+        # for f32 operands with a bf16 result (grad_a then uses the result as rounded to bf16,
+        # a relative change of at most 2^-9 per element). Gradients take the operands' dtype.
+        if a.dtype != h.dtype:
+            if h.dtype == torch.float32:
+                a = a.float()
+            else:
+                h, g = h.float(), g.float()
         grad_a, grad_b = matrix_scan_backward(a, ctx.b_shape, h, g, axis=ctx.axis, reverse=ctx.reverse,
                                               grad_dtype=ctx.b_dtype)
         return grad_a, grad_b, None, None, None, None

@@ -83,5 +83,45 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+ASAN_LIB_PATH = os.path.join(HERE, "_build", "libsx_scan_asan.so")
+# Host-side sanitizers for the C ABI layer (argument checks, planning, index maps).
+# Each -fsanitize= sits behind -Xarch_host so that only host code is instrumented;
+# the device objects are the ordinary ones.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libasan"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that a sanitized library needs preloaded."""
+    import glob
+    root = os.path.dirname(os.path.dirname(hipcc_path()))
+    found = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("the AddressSanitizer runtime was not found beside hipcc")
+    return found[-1]
+
+
+def build_asan(verbose: bool = False) -> str:
+    """A copy of the library whose host API layer (sx_api.cpp) runs under AddressSanitizer
+    and UndefinedBehaviorSanitizer, linked with the ordinary device objects (built first
+    if missing). Written under the build folder; returns its path."""
+    objdir = os.path.join(HERE, "_build")
+    objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "sx_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    api_obj = os.path.join(objdir, "sx_api_asan.o")
+    cmd = [hipcc_path(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++20", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+           *DEVICE_FLAGS, *HOST_SANITIZE, "-c", os.path.join(CSRC, "sx_api.cpp"), "-o", api_obj]
+    rc, msgs = _run(cmd)
+    if rc != 0:
+        raise RuntimeError("hipcc (sanitized sx_api.cpp) failed:\n" + "\n".join(msgs))
+    rc, msgs = _run([hipcc_path(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_SANITIZE, "-o", ASAN_LIB_PATH,
+                     api_obj, *objs])
+    if rc != 0:
+        raise RuntimeError("hipcc link (sanitized library) failed:\n" + "\n".join(msgs))
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstring>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -46,6 +47,28 @@ sx_status fail(sx_status st, const char* fmt, ...) {
 sx_status ok() {
   g_last_error.clear();
   return SX_OK;
+}
+
+// The integer an enum argument holds. A C caller may pass any int where the
+// ABI declares an enum; reading it as the C++ enum type before it is checked
+// would be undefined for values outside the enum's range, so every entry point
+// checks the bits first.
+template <typename E>
+int enum_code(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool body_ok(const sx_body& b) {
+  const int v = enum_code(b);
+  return v == SX_BODY_TANH_AFFINE || v == SX_BODY_NORM_CAP || v == SX_BODY_MAX_PLUS;
+}
+
+bool dtype_ok(const sx_dtype& d) {
+  const int v = enum_code(d);
+  return v == SX_F32 || v == SX_BF16;
 }
 
 std::string shape_str(int rank, const int64_t* shape) {
@@ -229,7 +252,7 @@ sx_status plan_element_scan(sx_body body, int rank, const int64_t* shape, int ax
 extern "C" {
 
 const char* sx_status_name(sx_status status) {
-  switch (status) {
+  switch (enum_code(status)) {
     case SX_OK: return "OK";
     case SX_E_DIM_001: return "E-DIM-001";
     case SX_E_DIM_002: return "E-DIM-002";
@@ -247,6 +270,7 @@ const char* sx_last_error(void) { return g_last_error.c_str(); }
 const char* sx_version(void) { return "sx_scan 0.1 gfx950"; }
 
 size_t sx_element_scan_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis, int state_axis) {
+  if (!body_ok(body)) return 0;
   EsPlan plan;
   const int64_t w = 1;
   if (plan_element_scan(body, rank, shape, axis, state_axis, nullptr, w, nullptr, w, nullptr, &plan) != SX_OK)
@@ -258,6 +282,7 @@ sx_status sx_element_scan(sx_body body, int rank, const int64_t* shape, int axis
                           const float* initial, const int64_t* initial_strides, const float* x, int64_t x_width,
                           const int64_t* x_strides, const float* s, int64_t s_width, const int64_t* s_strides,
                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!body_ok(body)) return fail(SX_E_UNSUPPORTED, "element-scan: unknown body %d", enum_code(body));
   EsPlan plan;
   sx_status st = plan_element_scan(body, rank, shape, axis, state_axis, initial_strides, x_width, x_strides,
                                    s_width, s_strides, &plan);
@@ -418,14 +443,14 @@ namespace {
 
 // sx_matrix_scan, and with scratch = true sx_matrix_scan_noalloc: the look-back
 // state then goes to the library's fixed device array instead of `workspace`.
-sx_status matrix_scan_call(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
+sx_status matrix_scan_call(const sx_dtype& dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides,
                            const void* a, int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b,
-                           int axis, int reverse, int projective, sx_dtype out_dtype, void* out, void* workspace,
+                           int axis, int reverse, int projective, const sx_dtype& out_dtype, void* out, void* workspace,
                            size_t workspace_bytes, void* stream, bool scratch) {
-  if (dtype != SX_F32 && dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "matrix-scan: a and b must be f32 or bf16 (dtype code %d)", int(dtype));
-  if (out_dtype != SX_F32 && out_dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "matrix-scan: out must be f32 or bf16 (dtype code %d)", int(out_dtype));
+  if (!dtype_ok(dtype))
+    return fail(SX_E_DIM_002, "matrix-scan: a and b must be f32 or bf16 (dtype code %d)", enum_code(dtype));
+  if (!dtype_ok(out_dtype))
+    return fail(SX_E_DIM_002, "matrix-scan: out must be f32 or bf16 (dtype code %d)", enum_code(out_dtype));
   sx::MsParams p;
   int64_t shp[sx::kMaxRank + 2];
   int r = 0;
@@ -642,7 +667,7 @@ extern "C" {
 size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shape, int b_rank, const int64_t* b_shape,
                                                int axis, sx_dtype grad_dtype) {
   MsBackPlan bp;
-  if (grad_dtype != SX_F32 && grad_dtype != SX_BF16) return 0;
+  if (!dtype_ok(grad_dtype)) return 0;
   if (plan_matrix_scan_backward(a_rank, a_shape, nullptr, b_rank, b_shape, nullptr, axis, &bp) != SX_OK) return 0;
   return bp.total;
 }
@@ -651,10 +676,10 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
                                   const void* a, int b_rank, const int64_t* b_shape, const void* h,
                                   const int64_t* g_strides, const void* g, int axis, int reverse, sx_dtype grad_dtype,
                                   void* grad_a, void* grad_b, void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != SX_F32 && dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "matrix-scan gradient: a, h and g must be f32 or bf16 (dtype code %d)", int(dtype));
-  if (grad_dtype != SX_F32 && grad_dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "matrix-scan gradient: gradients must be f32 or bf16 (dtype code %d)", int(grad_dtype));
+  if (!dtype_ok(dtype))
+    return fail(SX_E_DIM_002, "matrix-scan gradient: a, h and g must be f32 or bf16 (dtype code %d)", enum_code(dtype));
+  if (!dtype_ok(grad_dtype))
+    return fail(SX_E_DIM_002, "matrix-scan gradient: gradients must be f32 or bf16 (dtype code %d)", enum_code(grad_dtype));
   MsBackPlan bp;
   sx_status st = plan_matrix_scan_backward(a_rank, a_shape, a_strides, b_rank, b_shape, g_strides, axis, &bp);
   if (st != SX_OK) return st;
@@ -760,6 +785,7 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
 
 size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const int64_t* shape, int axis, int state_axis,
                                                 int64_t x_width, int64_t s_width) {
+  if (!body_ok(body)) return 0;
   EsPlan plan;
   if (plan_element_scan(body, rank, shape, axis, state_axis, nullptr, x_width, nullptr, s_width, nullptr, &plan) !=
       SX_OK)
@@ -786,6 +812,7 @@ sx_status sx_element_scan_backward(sx_body body, int rank, const int64_t* shape,
                                    const float* s, int64_t s_width, const int64_t* s_strides, const float* h,
                                    const float* g, float* grad_initial, float* grad_x, float* grad_s, void* workspace,
                                    size_t workspace_bytes, void* stream) {
+  if (!body_ok(body)) return fail(SX_E_UNSUPPORTED, "element-scan gradient: unknown body %d", enum_code(body));
   EsPlan plan;
   sx_status st = plan_element_scan(body, rank, shape, axis, state_axis, nullptr, x_width, x_strides, s_width,
                                    s_strides, &plan);
@@ -1019,10 +1046,10 @@ int sx_linear_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, con
 sx_status sx_linear_scan(sx_dtype dtype, int a_rank, const int64_t* a_shape, const int64_t* a_strides, const void* a,
                          int b_rank, const int64_t* b_shape, const int64_t* b_strides, const void* b, int axis,
                          int reverse, sx_dtype out_dtype, void* out, void* stream) {
-  if (dtype != SX_F32 && dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "linear-scan: a and b must be f32 or bf16 (dtype code %d)", int(dtype));
-  if (out_dtype != SX_F32 && out_dtype != SX_BF16)
-    return fail(SX_E_DIM_002, "linear-scan: out must be f32 or bf16 (dtype code %d)", int(out_dtype));
+  if (!dtype_ok(dtype))
+    return fail(SX_E_DIM_002, "linear-scan: a and b must be f32 or bf16 (dtype code %d)", enum_code(dtype));
+  if (!dtype_ok(out_dtype))
+    return fail(SX_E_DIM_002, "linear-scan: out must be f32 or bf16 (dtype code %d)", enum_code(out_dtype));
   sx::EsParams p;
   int64_t shp[sx::kMaxRank];
   int r = 0;

@@ -160,6 +160,25 @@ def test_autograd_through_matrix_scan(reverse):
     _blocks_close(ad.grad, ra, MS_TOL_F32, "grad_a")
 
 
+# autograd with a result dtype other than the operands': bf16 operands with an f32
+# result (the bf16 bar: the operands are bf16 and grad_a, grad_b round to bf16), and
+# f32 operands with a bf16 result (the bf16 bar: the rounded result enters grad_a).
+# The gradients take the operands' dtype.
+@pytest.mark.parametrize("dtype,out_dtype", [(torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
+@pytest.mark.parametrize("m", [1, 16])
+def test_autograd_with_another_result_dtype(dtype, out_dtype, m):
+    a, b, _ = _draw((2, 300, 16, 16), (2, 300, 16, m), dtype, seed=95 + m)
+    w = torch.randn((2, 300, 16, m), generator=torch.Generator().manual_seed(96))
+    ad, bd = a.to(DEV).requires_grad_(), b.to(DEV).requires_grad_()
+    h = sx.matrix_scan(ad, bd, axis=1, reverse=True, out_dtype=out_dtype)
+    assert h.dtype == out_dtype
+    (h.float() * w.to(DEV)).sum().backward()
+    assert ad.grad.dtype == dtype and bd.grad.dtype == dtype
+    ra, rb = oracle.matrix_scan_vjp(a.float().numpy(), b.float().numpy(), w.numpy(), axis=1, reverse=True)
+    _blocks_close(bd.grad, rb, MS_TOL_BF16, "grad_b")
+    _blocks_close(ad.grad, ra, MS_TOL_BF16, "grad_a")
+
+
 def test_grad_empty_and_errors():
     a = torch.zeros((2, 0, 4, 4), device=DEV)
     b = torch.zeros((2, 0, 4, 3), device=DEV)

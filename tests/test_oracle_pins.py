@@ -727,10 +727,11 @@ def test_norm_cap_vjp_uncapped_is_the_linear_scan_gradient():
 
 # ---------------------------------------------------------------- matrix-scan :projective
 #
-# "Tensor operations", the "matrix-scan" section: the running product of a,
-# from the identity, is divided by its largest magnitude after every step and
-# h by the same number; with b zero after its first step the result is h up
-# to a positive factor per step.
+# "Tensor operations", the "matrix-scan" section (:projective): every step
+# rescales both the accumulated product of the a's (from the identity) and the
+# state by that product's largest entry in absolute value. Pinned below: when b
+# vanishes after its first step, each state must be the plain scan's state
+# scaled by a positive number.
 
 
 @pytest.mark.parametrize("reverse", [False, True])
