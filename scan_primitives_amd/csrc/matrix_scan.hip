@@ -12,11 +12,12 @@
 //                     scan steps of one (batch, 16-column tile) from a counter.
 //                     The loader copies a unit's a and b straight into LDS;
 //                     each compute wave summarises its 16 steps into an affine
-//                     map with MFMA; the leader composes the unit's map,
-//                     publishes it, finds the state entering the unit by
-//                     decoupled look-back over earlier units, and hands it
-//                     back; the compute waves replay their steps from it,
-//                     storing every h[t].
+//                     map with MFMA and composes it onto the maps of the
+//                     waves before it; the leader publishes the unit's map,
+//                     finds the state entering the unit by decoupled
+//                     look-back over earlier units, and hands it back; the
+//                     compute waves replay their steps from it, storing every
+//                     h[t].
 //   ms_unit_kernel    the same scan with one workgroup of eight waves per unit
 //                     of 128 steps and inputs loaded into registers; it takes
 //                     every shape and alignment the pipelined kernel does not.
@@ -408,9 +409,14 @@ __device__ __forceinline__ void store_h_col1(TOut* op, f32x4 h, int n, int r, bo
 // between to that state in scan order. Returns the state entering the unit in
 // result-register order (zero in lanes past the tile's columns). The spin limit
 // bounds the wait: a look-back that reaches it records the give-up in the status
-// word and returns whatever it has, so no wave can hang.
+// word and returns whatever it has, so no wave can hang. idle() runs between
+// polls that found the look-back unresolved (before the wave sleeps).
+struct NoIdle {
+  __device__ void operator()() const {}
+};
+template <typename Idle = NoIdle>
 __device__ __forceinline__ f32x4 look_back(const MsUnitWs& ws, uint32_t base, int chunk, bool live, int lane, int r,
-                                           int c, uint32_t epoch) {
+                                           int c, uint32_t epoch, Idle&& idle = Idle{}) {
   int hi = chunk - 1, j = 0;
   uint32_t spins = 0;
   bool gave_up = false;
@@ -438,6 +444,7 @@ __device__ __forceinline__ f32x4 look_back(const MsUnitWs& ws, uint32_t base, in
       j = 0;
       break;
     }
+    idle();
     __builtin_amdgcn_s_sleep(1);
     f = poll();
   }
@@ -1058,22 +1065,25 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     LDS stages (global_load_lds, no registers held) as soon as a stage has
 //     been read, and signals when a stage has landed. It is the only wave that
 //     waits on input copies, so those waits never stall an MFMA chain.
-//   - For unit k the compute waves move their stages into registers,
-//     summarise their 16 steps each into an affine map (LDS, slot k % 4),
-//     then replay unit k-1, whose entering state the leader has found in the
-//     meantime, storing every h[t]. Each compute wave keeps two units in
-//     registers (the one it summarises and the one it replays).
-//   - The leader composes unit k's map from the wave maps (leaving in wave i's
-//     slot the composition of maps 0 .. i, so that every wave carries the
-//     entering state in one step), publishes it, finds
-//     the state entering the unit by decoupled look-back over earlier units of
-//     the same (batch, tile), hands that state to the compute waves and
-//     publishes the state leaving the unit. Its round trips overlap the
-//     summary of the next unit, so a replay never waits for its own look-back.
+//   - For unit k the compute waves move their stages into registers and
+//     summarise their 16 steps each into an affine map (LDS, slot k % 4);
+//     wave i then composes its map onto the composition of maps 0 .. i-1 that
+//     wave i-1 left in its slot, leaving the composition of maps 0 .. i in
+//     its own (so every wave carries the entering state in one step, and the
+//     last slot holds the unit's map). Then each replays unit k-1, whose
+//     entering state the leader has found in the meantime, storing every
+//     h[t]. Each compute wave keeps two units in registers (the one it
+//     summarises and the one it replays).
+//   - The leader finds the state entering unit k by decoupled look-back over
+//     earlier units of the same (batch, tile), publishing the unit's map
+//     while it waits (no compute wave waits for a store), hands that state to
+//     the compute waves and publishes the state leaving the unit. Its round
+//     trips overlap the summary of the next unit, so a replay never waits for
+//     its own look-back.
 // The waves run a unit apart and never meet at s_barrier after the start; they
 // hand work over through LDS words. Per-unit LDS slots rotate over four
 // units. Each compute wave announces its summary of unit k in a word of its
-// own (set to k + 1), so the leader composes wave i's map as soon as it is
+// own (set to k + 1), so the next wave composes onto it as soon as it is
 // in. The carry counts that guard slot reuse are kept per slot: a count that
 // several waves raise only says "all of unit k are in" if no wave can add for
 // a later unit on the same count first. A compute wave summarises unit k into
@@ -1215,10 +1225,31 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const bool live = c < min(16, p.m - g.ct * 16);
       const uint32_t base = g.bt * ws.chunks;
       const int kb = k % kBufs;
+      const uint32_t slot = base + g.chunk;
+      // The unit's map (the compute waves leave the composition of all their
+      // maps in the last slot) goes out as an aggregate while the look-back
+      // waits for earlier units, so that later units' look-backs need not wait
+      // for this one's leaving state: its stores are issued between two polls
+      // once the map is in, and the flag is raised after the next poll, whose
+      // wait for its own loads has seen the stores complete as well. No compute
+      // wave waits for a store to complete.
+      int agg = g.chunk > 0 ? 0 : 2;  // 0: map not yet out, 1: stores issued, 2: flag raised (or not needed)
+      auto publish_aggregate = [&]() {
+        if (agg == 1) {
+          raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
+          agg = 2;
+        } else if (agg == 0 && __builtin_amdgcn_readfirstlane(lds_read_u32(&sSumDone[NC - 1])) >= uint32_t(k) + 1) {
+          const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
+          const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
+          pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
+          if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+          agg = 1;
+        }
+      };
       // the state entering the unit, from the units before it, found while the
       // compute waves summarise this one
       f32x4 h_in = zero4();
-      if (g.chunk > 0) h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch);
+      if (g.chunk > 0) h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch, publish_aggregate);
       // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
       *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
@@ -1229,7 +1260,6 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
       const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
-      const uint32_t slot = base + g.chunk;
       if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
       raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores)
     }
@@ -1280,16 +1310,6 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       *reinterpret_cast<f32x4*>(sLw + lane * 4) = GL;
     }
     lds_signal_set(&sSumDone[wave], uint32_t(k) + 1, lane);
-    if (wave == NC - 1 && gc.chunk > 0) {
-      // the unit's map goes out as soon as it is composed, so that later units' look-backs
-      // need not wait for this workgroup's leader
-      const f32x4 GA = *reinterpret_cast<const f32x4*>(sPw + c * 16 + 4 * r);
-      const f32x4 GL = *reinterpret_cast<const f32x4*>(sLw + lane * 4);
-      const uint32_t slot = gc.bt * ws.chunks + gc.chunk;
-      pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-      if (c < min(16, p.m - gc.ct * 16)) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
-      raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
-    }
     return true;
   };
   // Replay unit k (registers R, geometry g) once the leader has handed over its entering state.

@@ -116,19 +116,12 @@ __device__ __forceinline__ Walk walk_of(int64_t lane_off, int64_t t_stride, int6
   return w;
 }
 
-// Workgroups go to the eight XCDs in turn (block b to XCD b mod 8), and each
-// XCD has its own L2. Renumbering the blocks so that each XCD holds one
-// contiguous range of rows (rows are chunk-major: a range is a run of chunks
-// of every state vector) keeps a chunk's warm-up, which reads the chunks just
-// before it, and the data one pass leaves for the next, in one L2.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_block() {
-  const int64_t nb = gridDim.x, b = blockIdx.x;
-  const int64_t per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds, slot = b / kXcds;
-  return xcd * per + (xcd < rem ? xcd : rem) + slot;
-}
-
 // ----------------------------------------------------------------- forward
+//
+// Rows are chunk-major (a run of rows is a run of chunks of every state
+// vector), and the blocks are renumbered per XCD (xcd_block): a chunk's
+// warm-up, which reads the chunks just before it, and the data one pass
+// leaves for the next then stay in one L2.
 
 template <bool X1, bool S1>
 __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQuadSpans sp, int64_t len,

@@ -195,6 +195,16 @@ hipError_t launch_sum_to(const SumToParams& p, void* out, bool out_bf16, hipStre
 // the stream from displacing lines in L2 and the last-level cache that the
 // kernel's stores and other data still use; on MI355X it raises a two-reads-
 // one-write stream from 5.6 to 7.0 TB/s (measured, plain vs hinted loads).
+// Workgroups go to the eight XCDs in turn (block b to XCD b mod 8), and each
+// XCD has its own L2. xcd_block() renumbers the blocks so that each XCD holds
+// one contiguous range of them, so that neighbouring blocks share an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_block() {
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  const int64_t per = nb / kXcds, rem = nb % kXcds, xcd = b % kXcds, slot = b / kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 
