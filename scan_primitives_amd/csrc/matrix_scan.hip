@@ -135,8 +135,8 @@ struct MsUnitWs {
   uint32_t* header;  // [0] next unit id, [1] status (nonzero: a look-back gave up), [2] epoch of the last call,
                      // [3] workgroups of this call that have finished
   uint64_t* flags;   // per slot: (epoch << 32) | kFlagMagic | kind
-  float* P;          // per slot, the unit's A as a row-major 16x16 block
-  float* L;          // per slot, the unit's B in result-register order (lane * 4 + v)
+  float* P;          // per slot, the unit's A: row c, entries 4r .. 4r+3 from lane index 4c + r (see pub_store4)
+  float* L;          // per slot, the unit's B in result-register order, lane index = lane
   float* H;          // per slot, the state leaving the unit, same order as L
   uint32_t num_units;
   uint32_t chunks;   // units per bt along the scan axis
@@ -179,22 +179,27 @@ __device__ __forceinline__ uint32_t read_flag(const uint64_t* flag, uint32_t epo
   return flag_kind(__hip_atomic_load(const_cast<uint64_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), epoch);
 }
 
-// Four published values of one lane (consecutive words), written and read with
-// relaxed agent-scope atomic accesses: workgroups that exchange them may sit on
+// Four published values of one lane, written and read with relaxed
+// agent-scope atomic accesses: workgroups that exchange them may sit on
 // different XCDs, whose L2 caches are not coherent with each other, and these
 // accesses are (by the memory model), with no cache write-back or invalidate.
-__device__ __forceinline__ void pub_store4(float* p, f32x4 v) {
-  uint32_t* u = reinterpret_cast<uint32_t*>(p);
+// A published 16x16 block holds value q of lane index i at word 64 q + i, so
+// that each of the four 32-bit accesses of a wave covers 256 contiguous bytes
+// (with the four values of a lane side by side, each access would touch a
+// quarter of every 64-byte piece of the block, and each piece would be
+// written four times).
+__device__ __forceinline__ void pub_store4(float* block, int i, f32x4 v) {
+  uint32_t* u = reinterpret_cast<uint32_t*>(block) + i;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) __hip_atomic_store(u + q, __float_as_uint(v[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int q = 0; q < 4; ++q) __hip_atomic_store(u + 64 * q, __float_as_uint(v[q]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ f32x4 pub_load4(const float* p) {
-  const uint32_t* u = reinterpret_cast<const uint32_t*>(p);
+__device__ __forceinline__ f32x4 pub_load4(const float* block, int i) {
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(block) + i;
   f32x4 v;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    v[q] = __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(u + q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    v[q] = __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(u + 64 * q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   return v;
 }
 
@@ -450,7 +455,7 @@ __device__ __forceinline__ f32x4 look_back(const MsUnitWs& ws, uint32_t base, in
   }
   // the state leaving unit j, then the maps of units j+1 .. chunk-1 in scan order, eight at a time
   f32x4 h = zero4();
-  if (live) h = pub_load4(ws.H + size_t(base + j) * 256 + lane * 4);
+  if (live) h = pub_load4(ws.H + size_t(base + j) * 256, lane);
   for (int i = j + 1; i < chunk; i += 8) {
     f32x4 Pb[8], Lb[8];
 #pragma unroll
@@ -458,8 +463,8 @@ __device__ __forceinline__ f32x4 look_back(const MsUnitWs& ws, uint32_t base, in
       Pb[u] = zero4();
       Lb[u] = zero4();
       if (i + u < chunk) {
-        Pb[u] = pub_load4(ws.P + size_t(base + i + u) * 256 + c * 16 + 4 * r);
-        if (live) Lb[u] = pub_load4(ws.L + size_t(base + i + u) * 256 + lane * 4);
+        Pb[u] = pub_load4(ws.P + size_t(base + i + u) * 256, 4 * c + r);
+        if (live) Lb[u] = pub_load4(ws.L + size_t(base + i + u) * 256, lane);
       }
     }
 #pragma unroll
@@ -568,16 +573,16 @@ __device__ __forceinline__ void ms_unit_body(const MsParams& p, const MsUnitWs& 
     }
     f32x4 h_in = zero4();
     if (chunk == 0) {
-      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, GL);  // entering 0: leaving = B
+      if (live) pub_store4(ws.H + size_t(slot) * 256, lane, GL);  // entering 0: leaving = B
       raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
     } else {
       const f32x4 GA = to_a_operand(sX, G, r, c);
-      pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-      if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+      pub_store4(ws.P + size_t(slot) * 256, 4 * c + r, GA);
+      if (live) pub_store4(ws.L + size_t(slot) * 256, lane, GL);
       raise_flag(ws.flags + slot, kFlagAggregate, epoch, lane);
       h_in = look_back(ws, bt * ws.chunks, int(chunk), live, lane, r, c, epoch);
       const f32x4 h_out = mfma_16x16x16(GA, h_in, GL);
-      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      if (live) pub_store4(ws.H + size_t(slot) * 256, lane, h_out);
       raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1241,8 +1246,8 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
         } else if (agg == 0 && __builtin_amdgcn_readfirstlane(lds_read_u32(&sSumDone[NC - 1])) >= uint32_t(k) + 1) {
           const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
           const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
-          pub_store4(ws.P + size_t(slot) * 256 + c * 16 + 4 * r, GA);
-          if (live) pub_store4(ws.L + size_t(slot) * 256 + lane * 4, GL);
+          pub_store4(ws.P + size_t(slot) * 256, 4 * c + r, GA);
+          if (live) pub_store4(ws.L + size_t(slot) * 256, lane, GL);
           agg = 1;
         }
       };
@@ -1260,7 +1265,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
       const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
-      if (live) pub_store4(ws.H + size_t(slot) * 256 + lane * 4, h_out);
+      if (live) pub_store4(ws.H + size_t(slot) * 256, lane, h_out);
       raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores)
     }
   } else {
