@@ -802,6 +802,18 @@ __device__ __forceinline__ void stage_wave(const MsParams& p, const PipeGeo& g, 
   }
 }
 
+// FOLD: the forward result h at the positions one after each of the wave's 16
+// steps (the step before each in the forward scan), into the wave's h area:
+// lane L copies elements 4 (L % 4) .. 4 (L % 4) + 3 of position q0 + 1 + L / 4,
+// so that word 16 k + j holds h[position q0 + 1 + k][j] (positions past the end
+// read the last one; the replay zeroes them). h has the result's layout (m = 1).
+__device__ __forceinline__ void stage_fold_h(const MsParams& p, const PipeGeo& g, uint32_t dst_lds, int lane) {
+  const int64_t q = g.q0 + 1 + (lane >> 2);
+  const int64_t qc = q < p.T ? q : p.T - 1;
+  const int64_t t = p.reverse ? p.T - 1 - qc : qc;
+  copy16_to_lds_at(static_cast<const float*>(p.fold_h) + g.off[MS_OUT] + t * p.t_stride[MS_OUT] + 4 * (lane & 3), dst_lds);
+}
+
 // A compute wave's inputs for one unit, in registers: a[t] in A-operand order
 // (identity past the end) and b[t] in result-register order (zero past the end;
 // for m = 1, b of all 16 steps with step c in lane column c).
@@ -922,6 +934,26 @@ __device__ __forceinline__ f32x4 b_row_m1(f32x4 b1) {
   return o;
 }
 
+// An L slot (or entering state) of the pipelined kernel in LDS: a 16x16 block
+// in result-register order (lane * 4 + v), or, for m = 1, only its live
+// column, lanes (r, 0), at 4 r + v: the other lanes read zeros and write
+// nothing (the m = 1 blocks are zero there anyway).
+template <bool M1>
+struct LSlot {
+  static constexpr int kW = M1 ? 16 : 256;  // floats per slot
+  __device__ static f32x4 load(const float* s, int lane, int r, int c) {
+    if constexpr (M1) return c == 0 ? *reinterpret_cast<const f32x4*>(s + 4 * r) : zero4();
+    else return *reinterpret_cast<const f32x4*>(s + lane * 4);
+  }
+  __device__ static void store(float* s, f32x4 v, int lane, int r, int c) {
+    if constexpr (M1) {
+      if (c == 0) *reinterpret_cast<f32x4*>(s + 4 * r) = v;
+    } else {
+      *reinterpret_cast<f32x4*>(s + lane * 4) = v;
+    }
+  }
+};
+
 // The wave's map: P = a[last] ... a[first] (written row-major), L = the scan of
 // its steps from h = 0 (written in result-register order). issue(k) runs at
 // step k: it starts the copies of the next unit, spread over the steps so that
@@ -952,7 +984,7 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
 #pragma unroll
   for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = P[v];
   if constexpr (M1) L = c == 0 ? L : zero4();  // result-register order: column 0 only
-  *reinterpret_cast<f32x4*>(&sLw[lane * 4]) = L;
+  LSlot<M1>::store(sLw, L, lane, r, c);
 }
 
 // Replay of one wave's 16 steps from its entering state h, storing every h[t].
@@ -960,9 +992,16 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
 // (lanes (r, 0)) is moved to lanes (r, step) with a DPP shift and one store per
 // lane writes all 16 steps at the end; for m = 16 a quad transpose gives each
 // lane four consecutive values of one row, stored as one piece per step.
-template <typename TIn, typename TOut, bool M1, bool SCALED>
+// FOLD (the gradient's adjoint scan, f32, m = 1): each step also stores
+// grad_a[t] = lam[t] h[prev]^T, 16x16, where lam[t] is the state just computed
+// and hb holds h at the position after each of the wave's steps (the step
+// before it in the forward scan), 16 values per step; there is none after the
+// last position, whose grad_a is zero. Lane (r, c) forms lam[4r .. 4r+3] times
+// h[prev][c], and a quad transpose gives it four consecutive values of one row,
+// so each step's 1 KiB block goes out as one contiguous store.
+template <typename TIn, typename TOut, bool M1, bool SCALED, bool FOLD = false>
 __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h, const MsParams& p, const PipeGeo& g,
-                                             float* sv, int lane, int r, int c) {
+                                             float* sv, int lane, int r, int c, const float* hb = nullptr) {
   const int64_t T = p.T;
   const int m = p.m;
   TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
@@ -981,11 +1020,23 @@ __device__ __forceinline__ void replay_steps(const UnitRegs<TIn, M1>& R, f32x4 h
 #pragma unroll
     for (int v = 0; v < 4; ++v) x[v] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(h[v]), 0x150, 0xF, 0xF, false));
     f32x4 acc = zero4();  // lane (r, c) ends up with h[step c][4r .. 4r+3]
+    float* ga0 = nullptr;
+    int64_t gto = 0;
+    if constexpr (FOLD) {
+      ga0 = static_cast<float*>(p.fold_grad_a) + 16 * (g.off[MS_OUT] + g.t0 * p.t_stride[MS_OUT]) +
+            (4 * r + (c & 3)) * 16 + 4 * (c >> 2);
+      gto = 16 * to;
+    }
     [&]<int... ks>(std::integer_sequence<int, ks...>) {
       (([&] {
          // steps past the end hold the identity and a zero b: x stays, and is not stored
          x = matvec_m1<TIn>(R.A[ks], x, b_row_m1<ks>(R.b1), sv, r, c);
          if constexpr (SCALED) x *= step_scale<ks>(R);
+         if constexpr (FOLD) {
+           const float hv = g.q0 + ks + 1 < T ? hb[ks * 16 + c] : 0.0f;
+           const f32x4 row = quad_transpose(x * hv, c & 3);  // grad_a[t][4r + c % 4][4 (c / 4) ..]
+           if (g.q0 + ks < T) st_stream(reinterpret_cast<f32x4*>(ga0 + ks * gto), row);
+         }
 #pragma unroll
          for (int v = 0; v < 4; ++v) acc[v] = c == ks ? x[v] : acc[v];
        }()),
@@ -1104,20 +1155,26 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 // falls from 6.6 to 0.9 TB/s). So the six compute waves are waves 0, 1, 2, 4,
 // 5, 6 (SIMDs 0-2, two each) and the leader (wave 3) and the loader (wave 7)
 // share SIMD 3, where no MFMA chain runs.
-template <int NC, typename TIn, typename TOut, bool M1, bool ADJ = false, bool SCALED = false>
+template <int NC, typename TIn, typename TOut, bool M1, bool ADJ = false, bool SCALED = false, bool FOLD = false>
 __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const MsUnitWs ws) {
   static_assert(NC == 6, "compute waves fill SIMDs 0-2, two each");
+  static_assert(!FOLD || (M1 && ADJ && !SCALED && sizeof(TIn) == 4 && sizeof(TOut) == 4), "grad_a folds into the f32 m = 1 adjoint");
   constexpr int K = 16, kUnit = NC * K, LEADER = 3, LOADER = 7;
   using S = PipeStage<TIn, M1>;
-  static_assert(3 * S::kPieces <= 63, "the loader keeps up to three stages in flight");
+  constexpr int kPieces = S::kPieces + (FOLD ? 1 : 0);  // copies per stage (FOLD: one more, for h)
+  static_assert(3 * kPieces <= 63, "the loader keeps up to three stages in flight");
   __shared__ __attribute__((aligned(16))) char sStage[NC][S::kWave];
   // Per-unit LDS slots (wave maps, entering state and their signals) rotate
   // over kBufs units, so that a wave can run up to kBufs - 2 units ahead of
   // the slowest wave's carry before it has to wait.
   constexpr int kBufs = 4;
   __shared__ __attribute__((aligned(16))) float sP[kBufs][NC][256];
-  __shared__ __attribute__((aligned(16))) float sL[kBufs][NC][256];
-  __shared__ __attribute__((aligned(16))) float sX[kBufs][256];
+  __shared__ __attribute__((aligned(16))) float sL[kBufs][NC][LSlot<M1>::kW];
+  __shared__ __attribute__((aligned(16))) float sX[kBufs][LSlot<M1>::kW];
+  // FOLD: each compute wave's h values for three units (the one being staged, and the two it holds
+  // in registers until their replays): the loader fills unit k's area when the wave frees its stage
+  // of unit k-1, which it does after replaying unit k-3, the area's last user.
+  __shared__ __attribute__((aligned(16))) float sH[FOLD ? 3 : 1][NC][FOLD ? 256 : 4];
   __shared__ __attribute__((aligned(16))) float sV[NC][M1 ? 64 : 4];  // m = 1: each compute wave's matvec_m1 area
   // Unit ids in a ring of 8. The leader publishes id k+2 as it starts unit k, and
   // it starts unit k once unit k-1's summaries are in, so the readers (the
@@ -1170,8 +1227,8 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     int qw[3] = {0, 0, 0}, qk[3] = {0, 0, 0};  // stages in flight, oldest first: wave and unit index
     int head = 0, n_pending = 0;
     auto retire_oldest = [&]() {
-      if (n_pending == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * S::kPieces));
-      else if (n_pending == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::kPieces));
+      if (n_pending == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPieces));
+      else if (n_pending == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPieces));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_signal_set(&sLanded[qw[head]], uint32_t(qk[head]) + 1, lane);
       head = head == 2 ? 0 : head + 1;
@@ -1188,7 +1245,10 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
           if ((issued >> w) & 1u) continue;
           if (lds_read_u32(&sConsumed[w]) < uint32_t(k)) continue;
           if (n_pending == 3) retire_oldest();
-          stage_wave<TIn, M1, ADJ>(p, pipe_geo(p, ws, unit, w, kUnit), &sStage[w][0], stage_lds + w * S::kWave, lane);
+          const PipeGeo gw = pipe_geo(p, ws, unit, w, kUnit);
+          stage_wave<TIn, M1, ADJ>(p, gw, &sStage[w][0], stage_lds + w * S::kWave, lane);
+          if constexpr (FOLD)
+            stage_fold_h(p, gw, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const uint32_t*>(&sH[k % 3][w][0]))), lane);
           const int tail = head + n_pending >= 3 ? head + n_pending - 3 : head + n_pending;
           qw[tail] = w;
           qk[tail] = k;
@@ -1245,7 +1305,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
           agg = 2;
         } else if (agg == 0 && __builtin_amdgcn_readfirstlane(lds_read_u32(&sSumDone[NC - 1])) >= uint32_t(k) + 1) {
           const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
-          const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
+          const f32x4 GL = LSlot<M1>::load(&sL[kb][NC - 1][0], lane, r, c);
           pub_store4(ws.P + size_t(slot) * 256, 4 * c + r, GA);
           if (live) pub_store4(ws.L + size_t(slot) * 256, lane, GL);
           agg = 1;
@@ -1257,13 +1317,13 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       if (g.chunk > 0) h_in = look_back(ws, base, int(g.chunk), live, lane, r, c, epoch, publish_aggregate);
       // hand the entering state over once the carries of unit k-4 (same slot) have read theirs
       lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
-      *reinterpret_cast<f32x4*>(&sX[kb][lane * 4]) = h_in;
+      LSlot<M1>::store(&sX[kb][0], h_in, lane, r, c);
       lds_signal_set(&sHinIt[kb], uint32_t(k) + 1, lane);
       // the leaving state: the unit's map (the compute waves leave the composition of all
       // its waves' maps in the last slot) applied to the entering state
       lds_wait_at_least(&sSumDone[NC - 1], uint32_t(k) + 1);
       const f32x4 GA = *reinterpret_cast<const f32x4*>(&sP[kb][NC - 1][c * 16 + 4 * r]);
-      const f32x4 GL = *reinterpret_cast<const f32x4*>(&sL[kb][NC - 1][lane * 4]);
+      const f32x4 GL = LSlot<M1>::load(&sL[kb][NC - 1][0], lane, r, c);
       const f32x4 h_out = g.chunk == 0 ? GL : mfma_16x16x16(GA, h_in, GL);
       if (live) pub_store4(ws.H + size_t(slot) * 256, lane, h_out);
       raise_flag(ws.flags + slot, kFlagInclusive, epoch, lane);  // (waits for the stores)
@@ -1298,13 +1358,13 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const f32x4 PA = *reinterpret_cast<const f32x4*>(sPw + c * 16 + 4 * r);  // own map, A-operand order
-      const f32x4 Lw = *reinterpret_cast<const f32x4*>(sLw + lane * 4);
+      const f32x4 Lw = LSlot<M1>::load(sLw, lane, r, c);
       lds_wait_at_least(&sSumDone[wave - 1], uint32_t(k) + 1);
       const float* sPp = &sP[kb][wave - 1][0];
       f32x4 Gp;
 #pragma unroll
       for (int v = 0; v < 4; ++v) Gp[v] = sPp[(4 * r + v) * 16 + c];  // result-register order
-      const f32x4 GLp = *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]);
+      const f32x4 GLp = LSlot<M1>::load(&sL[kb][wave - 1][0], lane, r, c);
       const f32x4 G = mfma_16x16x16(PA, Gp, zero4());
       const f32x4 GL = mfma_16x16x16(PA, GLp, Lw);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1312,7 +1372,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = G[v];
-      *reinterpret_cast<f32x4*>(sLw + lane * 4) = GL;
+      LSlot<M1>::store(sLw, GL, lane, r, c);
     }
     lds_signal_set(&sSumDone[wave], uint32_t(k) + 1, lane);
     return true;
@@ -1321,12 +1381,12 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   auto finish = [&](const UnitRegs<TIn, M1>& R, const PipeGeo& g, int k) {
     const int kb = k % kBufs;
     lds_wait_at_least(&sHinIt[kb], uint32_t(k) + 1);
-    f32x4 h = *reinterpret_cast<const f32x4*>(&sX[kb][lane * 4]);
+    f32x4 h = LSlot<M1>::load(&sX[kb][0], lane, r, c);
     if (wave > 0)  // slot wave-1 holds the composition of the maps of waves 0 .. wave-1
       h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][wave - 1][c * 16 + 4 * r]), h,
-                        *reinterpret_cast<const f32x4*>(&sL[kb][wave - 1][lane * 4]));
+                        LSlot<M1>::load(&sL[kb][wave - 1][0], lane, r, c));
     lds_signal_add(&sCarryDone[kb], lane);
-    replay_steps<TIn, TOut, M1, SCALED>(R, h, p, g, &sV[wave][0], lane, r, c);
+    replay_steps<TIn, TOut, M1, SCALED, FOLD>(R, h, p, g, &sV[wave][0], lane, r, c, FOLD ? &sH[k % 3][wave][0] : nullptr);
   };
 
   for (int k = 0;; k += 2) {
@@ -1654,6 +1714,13 @@ hipError_t launch_chunked(const MsParams& p, void* workspace, hipStream_t stream
   }
   if (pipe) {
     const unsigned blocks = unsigned(std::min<uint64_t>(up.num_units, uint64_t(device_cu_count())));
+    if constexpr (ADJ && sizeof(TIn) == 4 && sizeof(TOut) == 4) {
+      if (m1 && p.fold_grad_a != nullptr) {  // the caller checked matrix_scan_folds_grad_a
+        hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true, true, false, true>), dim3(blocks), dim3(512),
+                           0, stream, p, ws);
+        return hipGetLastError();
+      }
+    }
     if (m1)
       hipLaunchKernelGGL((ms_lead_kernel<kLeadCompute, TIn, TOut, true, ADJ>), dim3(blocks), dim3(512), 0, stream, p,
                          ws);
@@ -1818,6 +1885,18 @@ hipError_t matrix_scan_scratch(void** out) {
   }
   *out = ptr;
   return hipSuccess;
+}
+
+bool matrix_scan_folds_grad_a(const MsParams& p, const void* workspace, size_t workspace_bytes) {
+  if (!p.adjoint || p.in_bf16 || p.out_bf16 || p.n != 16 || p.m != 1 || p.fold_h == nullptr || p.fold_grad_a == nullptr)
+    return false;
+  if (p.num_batch <= 0 || p.T <= 0) return false;
+  const size_t need = matrix_scan_workspace(p);
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) return false;  // not the chunked scan
+  // h is copied in 16-byte pieces and grad_a stored in 16-byte pieces, at out's offsets (x 16 for grad_a)
+  const bool al = reinterpret_cast<uintptr_t>(p.fold_h) % 16 == 0 && reinterpret_cast<uintptr_t>(p.fold_grad_a) % 16 == 0 &&
+                  (p.t_stride[MS_OUT] * 4) % 16 == 0;
+  return al && pipe_fits(p);
 }
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream) {

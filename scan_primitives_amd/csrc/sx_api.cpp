@@ -743,9 +743,18 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
   bp.p.a = a;
   bp.p.b = g;
   bp.p.out = lam;
+  // f32 with grad_a at a's full shape: the pipelined adjoint scan forms grad_a in its replay
+  bool folded = false;
+  if (dtype == SX_F32 && grad_dtype == SX_F32 && bp.ga_direct && a_numel > 0 && bp.out_numel > 0) {
+    bp.p.fold_h = h;
+    bp.p.fold_grad_a = grad_a;
+    folded = sx::matrix_scan_folds_grad_a(bp.p, ws, bp.scan_ws);
+    if (!folded) bp.p.fold_h = bp.p.fold_grad_a = nullptr;
+  }
   hipError_t e = sx::launch_matrix_scan(bp.p, ws, bp.scan_ws, s);
   if (e != hipSuccess) return device_status(e, "matrix-scan gradient: adjoint scan launch");
-  // 2. grad_a = lam h[prev]^T per step (and grad_b = lam rounded, when that is all grad_b is)
+  // 2. grad_a = lam h[prev]^T per step (and grad_b = lam rounded, when that is all grad_b is), unless
+  // the scan formed it (f32 gradients: grad_b is lam itself, at the result's shape or summed below)
   const int L = bp.out_rank - 2;
   const int ax = axis < 0 ? axis + L : axis;
   sx::GradAParams gp{};
@@ -763,8 +772,10 @@ sx_status sx_matrix_scan_backward(sx_dtype dtype, int a_rank, const int64_t* a_s
   gp.grad_a = bp.ga_direct ? grad_a : static_cast<void*>(ws + bp.ga_off);
   const bool b_full = same_shape(b_rank, b_shape, bp.out_rank, bp.out_shape);
   gp.grad_b = (b_full && !bp.lam_direct) ? grad_b : nullptr;
-  e = sx::launch_grad_a(gp, dtype == SX_BF16, grad_dtype == SX_BF16 && bp.ga_direct, s);
-  if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_a launch");
+  if (!folded) {
+    e = sx::launch_grad_a(gp, dtype == SX_BF16, grad_dtype == SX_BF16 && bp.ga_direct, s);
+    if (e != hipSuccess) return device_status(e, "matrix-scan gradient: grad_a launch");
+  }
   // 3. sums over broadcast dims
   if (!bp.ga_direct && a_numel > 0) {
     bp.sum_a.src = reinterpret_cast<const float*>(ws + bp.ga_off);

@@ -138,9 +138,18 @@ struct MsParams {
   const void* a;
   const void* b;
   void* out;
+  // The gradient's adjoint scan may form grad_a[t] = lam[t] h[prev]^T in its replay (f32, n = 16,
+  // m = 1, where the pipelined kernel runs: matrix_scan_folds_grad_a says when). fold_h is the
+  // forward result, laid out as out; fold_grad_a is contiguous f32, the leading dims + [16, 16].
+  // Both nullptr otherwise.
+  const void* fold_h;
+  void* fold_grad_a;
 };
 
 hipError_t launch_matrix_scan(const MsParams& p, void* workspace, size_t workspace_bytes, hipStream_t stream);
+// Whether launch_matrix_scan, given p with fold_h and fold_grad_a set and this workspace, forms
+// grad_a in the adjoint scan itself (else the caller runs launch_grad_a).
+bool matrix_scan_folds_grad_a(const MsParams& p, const void* workspace, size_t workspace_bytes);
 // :projective: the running product's largest entry divides P and h every step. In parallel (two passes
 // for the factors, then the pipelined scan) when the shape and the workspace allow, else serially.
 hipError_t launch_matrix_scan_projective(const MsParams& p, void* workspace, size_t workspace_bytes,

@@ -11,7 +11,8 @@ h, rounded to bf16, enters grad_a).
 Shapes cover the pipelined kernel (n = 16 with m = 1, and bf16 with m = 16)
 and the per-unit kernel (n < 16, m = 3, m = 17, f32 m = 16), several units
 with a ragged last one, both directions, broadcast operands (gradients
-summed over the broadcast dims), a strided g, autograd through
+summed over the broadcast dims), grad_a's runs of steps with ragged ends and
+a scan over the first dim, a strided g, autograd through
 ``sx.matrix_scan``, and the two matrix workloads at full size on sampled
 batch rows (a row is an exact sub-problem) plus a per-step residual check of
 the adjoint recurrence over every row.
@@ -95,6 +96,19 @@ def test_grad_pipelined_bf16_tiles(B, T, m, reverse):
 def test_grad_unit_kernel_shapes(n, m, T, dtype, reverse):
     a, b, _ = _draw((2, T, n, n), (2, T, n, m), dtype, seed=51 + n + m)
     _check(a, b, 1, reverse, seed=51 + n + m)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("a_shape,axis,dt", [
+    ((3, 37, 16, 16), 1, torch.float32),   # 111 steps: the last run of four ends past the last step
+    ((1, 5, 16, 16), 1, torch.bfloat16),   # fewer steps than two runs
+    ((37, 3, 16, 16), 0, torch.bfloat16),  # scan over the first dim: the step before is 3 steps apart
+])
+def test_grad_a_m16_runs(a_shape, axis, dt, reverse):
+    # grad_a for m = 16 takes runs of consecutive steps per wave: ragged ends and a scan axis that is
+    # not the innermost leading dim
+    a, b, _ = _draw(a_shape, a_shape, dt, seed=91 + a_shape[0])
+    _check(a, b, axis, reverse, seed=91 + a_shape[0])
 
 
 def test_grad_bf16_operands_f32_gradients():
