@@ -12,7 +12,8 @@ Shapes cover the pipelined kernel (n = 16 with m = 1, and bf16 with m = 16)
 and the per-unit kernel (n < 16, m = 3, m = 17, f32 m = 16), several units
 with a ragged last one, both directions, broadcast operands (gradients
 summed over the broadcast dims), grad_a's runs of steps with ragged ends and
-a scan over the first dim, a strided g, autograd through
+a scan over the first dim, grad_a formed inside the f32 m = 1 adjoint scan
+(batch dims, a scan over the first dim, one step), a strided g, autograd through
 ``sx.matrix_scan``, and the two matrix workloads at full size on sampled
 batch rows (a row is an exact sub-problem) plus a per-step residual check of
 the adjoint recurrence over every row.
@@ -109,6 +110,19 @@ def test_grad_a_m16_runs(a_shape, axis, dt, reverse):
     # not the innermost leading dim
     a, b, _ = _draw(a_shape, a_shape, dt, seed=91 + a_shape[0])
     _check(a, b, axis, reverse, seed=91 + a_shape[0])
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("a_shape,b_shape,axis", [
+    ((2, 3, 130, 16, 16), (2, 3, 130, 16, 1), 2),  # two batch dims
+    ((130, 3, 16, 16), (130, 3, 16, 1), 0),        # scan over the first dim: the time stride is 3 steps
+    ((1, 1, 16, 16), (1, 1, 16, 1), 1),            # one step: its grad_a is zero
+])
+def test_grad_f32_m1_grad_a_in_the_scan(a_shape, b_shape, axis, reverse):
+    # f32 gradients with n = 16, m = 1: the adjoint scan forms grad_a in its replay, at 16 times the
+    # result's offsets; these layouts move the time and batch strides away from the plain [B, T] case
+    a, b, _ = _draw(a_shape, b_shape, torch.float32, seed=95 + axis)
+    _check(a, b, axis, reverse, seed=95 + axis)
 
 
 def test_grad_bf16_operands_f32_gradients():
