@@ -17,7 +17,9 @@
 //                     finds the state entering the unit by decoupled
 //                     look-back over earlier units, and hands it back; the
 //                     compute waves replay their steps from it, storing every
-//                     h[t].
+//                     h[t]. In the gradient's adjoint scan (f32, m = 1) the
+//                     replay can also form grad_a[t] = lam[t] h[prev]^T
+//                     (template flag FOLD), with h staged beside a and b.
 //   ms_unit_kernel    the same scan with one workgroup of eight waves per unit
 //                     of 128 steps and inputs loaded into registers; it takes
 //                     every shape and alignment the pipelined kernel does not.
