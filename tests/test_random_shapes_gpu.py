@@ -5,8 +5,11 @@ shapes, axes, directions and dtypes at random (a fixed seed per case, so every
 case is reproducible by its id) to reach combinations the fixed cases do not:
 matrix-scan forward and gradient over n, m, the scan axis among the leading
 dims and both dtypes (which selects the pipelined, per-unit or fused-gradient
-paths), and element-scan bodies, linear-scan and table-scan over shapes both
-below and above the slab kernel's thresholds. Bars as in the fixed tests.
+paths), element-scan bodies, linear-scan and table-scan over shapes both
+below and above the slab kernel's thresholds, the element-scan gradients
+(scalar and vector states, width-one sequences, long axes that norm-cap's
+gradient splits) and :projective (products that shrink or grow). Bars as in
+the fixed tests.
 """
 
 import random
@@ -121,3 +124,51 @@ def test_element_linear_table_random(case):
         got = sx.table_scan(t["table"].to(DEV), t["symbols"].to(DEV), axis=w.axis, start=w.meta["start"])
         ref = oracle.table_scan(t["table"].numpy(), t["symbols"].numpy(), axis=w.axis, start=w.meta["start"])
         assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_element_gradient_random(case):
+    # the element-scan gradients (scalar and vector states, width-one sequences, norm-cap's split along
+    # the axis), checked as the fixed gradient tests check them, near-tie handling included
+    from tests.test_element_grad_gpu import _draw, _run
+
+    rng = random.Random(9000 + case)
+    body = rng.choice(["tanh_affine", "max_plus", "norm_cap"])
+    reverse = rng.random() < 0.5
+    if body != "norm_cap" and rng.random() < 0.5:  # scalar state
+        nd = rng.choice([2, 3])
+        shape = tuple(rng.choice([1, 2, 5, 37, 130, 600]) for _ in range(nd))
+        axis = rng.randrange(nd) - (nd if rng.random() < 0.5 else 0)
+        x, s, _, gen = _draw(body, shape, None, seed=9000 + case)
+        ax = axis % nd
+        init = torch.randn(shape[:ax] + shape[ax + 1:], generator=gen)
+        g = torch.randn(shape, generator=gen)
+        _run(body, x, s, init, g, axis, None, reverse)
+    else:  # vector state along the last axis, the scan along axis 1
+        n = rng.choice([16, 16, 5, 1])
+        lead = (rng.choice([1, 2]), rng.choice([1, 7, 45, 300, 1500]), rng.choice([1, 3]))
+        xw, sw = rng.choice([n, 1]), rng.choice([n, 1])
+        x, s, full, gen = _draw(body, lead, n, seed=9000 + case, x_width=xw, s_width=sw)
+        init = 0.3 * torch.randn((lead[0], lead[2], n), generator=gen)
+        g = torch.randn(full, generator=gen)
+        _run(body, x, s, init, g, 1, -1, reverse)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_projective_random(case):
+    rng = random.Random(9500 + case)
+    n = rng.choice([16, 16, 5, 1])
+    m = rng.choice([1, 16, 3, 17])
+    dt = torch.bfloat16 if (n == 16 and m == 16 and rng.random() < 0.5) else torch.float32
+    T = rng.choice([1, 5, 127, 128, 129, 300, 1000])
+    B = rng.choice([1, 2, 3])
+    reverse = rng.random() < 0.5
+    g = torch.Generator().manual_seed(9500 + case)
+    a = (rng.choice([0.9, 1.5]) * torch.eye(n) + 0.05 * torch.randn((B, T, n, n), generator=g)).to(dt)
+    b = torch.randn((B, T, n, m), generator=g).to(dt)
+    print(f"\n[case] projective a {tuple(a.shape)} b {tuple(b.shape)} {dt} reverse {reverse}", flush=True)
+    got = sx.matrix_scan(a.to(DEV), b.to(DEV), axis=1, reverse=reverse, projective=True)
+    torch.cuda.synchronize()
+    ref = oracle.matrix_scan_projective(a.float().numpy(), b.float().numpy(), axis=1, reverse=reverse)
+    assert np.all(np.isfinite(got.float().cpu().numpy()))
+    assert_matrix_close(got, ref, MS_TOL_F32 if dt == torch.float32 else MS_TOL_BF16, axis=1)
