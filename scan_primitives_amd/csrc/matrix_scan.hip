@@ -961,9 +961,14 @@ struct LSlot {
 // step k: it starts the copies of the next unit, spread over the steps so that
 // they never back up the memory pipeline.
 // SCALED: each step's result is multiplied by its factor, h[t] = (a[t] h + b[t]) * s[t].
-template <typename TIn, bool M1, bool SCALED, typename Issue>
-__device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw, float* sLw, float* sv, int lane,
+// KEEP (f32, m = 1): every step's prefix product P (the product of the wave's
+// steps up to it, result-register order) replaces its a in R.A, and its local
+// state L (the scan from zero) goes to lane (r, step) of R.b1, rows 4r .. 4r+3;
+// the replay then needs neither a nor b (see replay_prefix_m1).
+template <typename TIn, bool M1, bool SCALED, bool KEEP = false, typename Issue>
+__device__ __forceinline__ void summarize(UnitRegs<TIn, M1>& R, float* sPw, float* sLw, float* sv, int lane,
                                           int r, int c, Issue&& issue) {
+  static_assert(!KEEP || (M1 && sizeof(TIn) == 4), "prefix products are kept for f32 m = 1 only");
   f32x4 P = identity_d(r, c), L = zero4();
   [&]<int... ks>(std::integer_sequence<int, ks...>) {
     (([&] {
@@ -980,6 +985,11 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
          P *= sk;
          L *= sk;
        }
+       if constexpr (KEEP) {  // (later steps read b from lanes (r, k > ks) only)
+         if constexpr (sizeof(TIn) == 4) R.A[ks].v = P;
+#pragma unroll
+         for (int v = 0; v < 4; ++v) R.b1[v] = c == ks ? L[v] : R.b1[v];
+       }
      }()),
      ...);
   }(std::make_integer_sequence<int, 16>{});
@@ -987,6 +997,60 @@ __device__ __forceinline__ void summarize(const UnitRegs<TIn, M1>& R, float* sPw
   for (int v = 0; v < 4; ++v) sPw[(4 * r + v) * 16 + c] = P[v];
   if constexpr (M1) L = c == 0 ? L : zero4();  // result-register order: column 0 only
   LSlot<M1>::store(sLw, L, lane, r, c);
+}
+
+// The replay of a KEEP summary (f32, m = 1): h[t] = P_t h + L_t for the wave's 16
+// steps, independent of each other (with SCALED both already carry the steps'
+// factors). Lane (r, c) holds P_t[4r+v][c] and multiplies
+// it by h[c]; the 64 products of each row of 16 lanes are summed over the row by
+// recursive halving, each round pairing lanes whose sets of summed lanes are
+// disjoint (row rotation by 8, half-row mirror, quad reversal, quad swap), each
+// lane keeping the half of the steps its lane bit picks, so that lane (r, c) ends
+// with step c's rows 4r .. 4r+3, the layout of the store.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL, int N>
+__device__ __forceinline__ void halve(float (&x)[2 * N], bool upper) {
+  // x[i] belongs to the lower half of the steps, x[i + N] to the upper; keep this lane's half
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = upper ? x[i + N] : x[i];
+    const float send = upper ? x[i] : x[i + N];
+    x[i] = keep + dpp_mov<CTRL>(send);
+  }
+}
+
+template <typename TOut>
+__device__ __forceinline__ void replay_prefix_m1(const UnitRegs<float, true>& R, f32x4 h, const MsParams& p,
+                                                 const PipeGeo& g, float* sv, int r, int c) {
+  // h arrives in result-register order (lanes (r, 0) hold h[4r .. 4r+3]); every lane needs h[c]
+  if (c == 0) *reinterpret_cast<f32x4*>(sv + 4 * r) = h;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float hc = sv[c];
+  // x[4 t + v]: step t, row 4r + v, this lane's column's share
+  float x[64];
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[4 * t + v] = R.A[t].v[v] * hc;
+  // steps are halved by their bit 3, 2, 1, 0 (index bit 5, 4, 3, 2), against lane bit 3, 2, 1, 0
+  halve<0x128, 32>(x, (c & 8) != 0);                                   // row_ror:8 (lane c ^ 8)
+  halve<0x141, 16>(reinterpret_cast<float (&)[32]>(x), (c & 4) != 0);  // row_half_mirror (c ^ 7)
+  halve<0x1B, 8>(reinterpret_cast<float (&)[16]>(x), (c & 2) != 0);    // quad_perm [3,2,1,0] (c ^ 3)
+  halve<0xB1, 4>(reinterpret_cast<float (&)[8]>(x), (c & 1) != 0);     // quad_perm [1,0,3,2] (c ^ 1)
+  const f32x4 out = f32x4{x[0], x[1], x[2], x[3]} + R.b1;
+  if (g.q0 + c < p.T) {
+    TOut* o0 = static_cast<TOut*>(p.out) + g.off[MS_OUT];
+    const int64_t to = p.reverse ? -p.t_stride[MS_OUT] : p.t_stride[MS_OUT];
+    TOut* op = o0 + (g.t0 * p.t_stride[MS_OUT] + c * to) + 4 * r;
+    if constexpr (sizeof(TOut) == 4) st_stream(reinterpret_cast<f32x4*>(op), out);
+    else st_stream(reinterpret_cast<u32x2*>(op), u32x2{pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3])});
+  }
 }
 
 // Replay of one wave's 16 steps from its entering state h, storing every h[t].
@@ -1131,7 +1195,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF
 //     last slot holds the unit's map). Then each replays unit k-1, whose
 //     entering state the leader has found in the meantime, storing every
 //     h[t]. Each compute wave keeps two units in registers (the one it
-//     summarises and the one it replays).
+//     summarises and the one it replays). For f32 m = 1 the summary keeps
+//     each step's prefix product and local state in place of its a and b, and
+//     the replay forms h[t] = P_t h + L_t for all 16 steps at once instead of
+//     stepping through them.
 //   - The leader finds the state entering unit k by decoupled look-back over
 //     earlier units of the same (batch, tile), publishing the unit's map
 //     while it waits (no compute wave waits for a store), hands that state to
@@ -1162,6 +1229,8 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
   static_assert(NC == 6, "compute waves fill SIMDs 0-2, two each");
   static_assert(!FOLD || (M1 && ADJ && !SCALED && sizeof(TIn) == 4 && sizeof(TOut) == 4), "grad_a folds into the f32 m = 1 adjoint");
   constexpr int K = 16, kUnit = NC * K, LEADER = 3, LOADER = 7;
+  // f32 m = 1 without the gradient fold: the summary keeps its prefix products and the replay uses them
+  constexpr bool kKeep = M1 && sizeof(TIn) == 4 && !FOLD;
   using S = PipeStage<TIn, M1>;
   constexpr int kPieces = S::kPieces + (FOLD ? 1 : 0);  // copies per stage (FOLD: one more, for h)
   static_assert(3 * kPieces <= 63, "the loader keeps up to three stages in flight");
@@ -1352,7 +1421,7 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
     lds_wait_at_least(&sCarryDone[kb], uint32_t(NC) * uint32_t(k / kBufs));  // unit k-kBufs's carries are done
     float* sPw = &sP[kb][wave][0];
     float* sLw = &sL[kb][wave][0];
-    summarize<TIn, M1, SCALED>(Rc, sPw, sLw, &sV[wave][0], lane, r, c, [](int) {});
+    summarize<TIn, M1, SCALED, kKeep>(Rc, sPw, sLw, &sV[wave][0], lane, r, c, [](int) {});
     if (wave > 0) {
       // this wave's map after the composition of the maps of waves 0 .. wave-1 (left in
       // slot wave-1 by the wave before), written back over this wave's own slot
@@ -1388,7 +1457,8 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
       h = mfma_16x16x16(*reinterpret_cast<const f32x4*>(&sP[kb][wave - 1][c * 16 + 4 * r]), h,
                         LSlot<M1>::load(&sL[kb][wave - 1][0], lane, r, c));
     lds_signal_add(&sCarryDone[kb], lane);
-    replay_steps<TIn, TOut, M1, SCALED, FOLD>(R, h, p, g, &sV[wave][0], lane, r, c, FOLD ? &sH[k % 3][wave][0] : nullptr);
+    if constexpr (kKeep) replay_prefix_m1<TOut>(R, h, p, g, &sV[wave][0], r, c);
+    else replay_steps<TIn, TOut, M1, SCALED, FOLD>(R, h, p, g, &sV[wave][0], lane, r, c, FOLD ? &sH[k % 3][wave][0] : nullptr);
   };
 
   for (int k = 0;; k += 2) {
@@ -1419,18 +1489,13 @@ __global__ __launch_bounds__(512) void ms_lead_kernel(const MsParams p, const Ms
 // maximum over the wave (lane, DPP row, then the four row leaders), and the
 // operands of the next K steps are in flight meanwhile.
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 // Largest |entry| of a 16x16 tile held four values per lane, the same in every lane.
 __device__ __forceinline__ float wave_max_abs(f32x4 v) {
   float x = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror: every lane holds its row's maximum
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror: every lane holds its row's maximum
   const int xi = __float_as_int(x);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(xi, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(xi, 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(xi, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(xi, 48));
