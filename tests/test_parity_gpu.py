@@ -274,6 +274,7 @@ def test_matrix_small(B, T, n, m, reverse, dtype):
     (5, 1000, 1, torch.bfloat16, None, False),
     (5, 1000, 1, torch.bfloat16, torch.float32, True),
     (3, 77, 1, torch.float32, torch.bfloat16, False),
+    (4, 2021, 1, torch.float32, None, False),
     (4, 40000, 16, torch.bfloat16, None, False),
     (2, 90000, 1, torch.float32, None, True),
 ])
