@@ -79,16 +79,20 @@ def _norm_cap_ties(init, x, s, axis, reverse):
     return mask, hit[..., None] if init.dim() == hit.ndim + 1 else hit
 
 
-def _close(got, ref, axis, what, summed_scale=None, skip=None):
+def _close(got, ref, axis, what, summed_scale=None, skip=None, g_rms=0.0):
     """summed_scale: for a width-one sequence's gradient (a sum over the state of
     full-width terms), the sum of those terms' scales, so that the bar is the
     per-element bar carried through the sum (cancellation in the sum leaves the
-    f32 result with an error of the size of its terms, not of the result)."""
+    f32 result with an error of the size of its terms, not of the result).
+    g_rms: the RMS of the incoming gradient; a gradient that vanishes by
+    cancellation (a capped trip of a width-one norm-cap state maps y to y / |y|,
+    whose derivative is zero) keeps an f32 residue of a few ulps of the terms
+    that cancel, so the scale has a floor of 8 ulps of g_rms over the bar."""
     g = got.detach().float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (what, g.shape, ref.shape)
     if ref.size == 0:
         return
-    scale = np.maximum(_scale(ref, axis), 1e-6)
+    scale = np.maximum(_scale(ref, axis), max(1e-6, 8 * 2.0 ** -24 / TOL * g_rms))
     if summed_scale is not None:
         scale = np.maximum(scale, summed_scale)
     if skip is not None:  # near-tie dependent elements: either branch is correct; they must be finite
@@ -145,9 +149,10 @@ def _run(body, x, s, init, g, axis, state_axis, reverse):
     skip_h, skip_i = (None, None)
     if body == "norm_cap":
         skip_h, skip_i = _norm_cap_ties(init, x, s, axis, reverse)
-    _close(gi, ri, None, "grad_initial", skip=skip_i)
-    _close(gx, rx, ax, "grad_x", sums[0], skip=_width(skip_h, x))
-    _close(gs, rs, ax, "grad_s", sums[1], skip=_width(skip_h, s))
+    g_rms = float(np.sqrt(np.mean(g.numpy().astype(np.float64) ** 2))) if g.numel() else 0.0
+    _close(gi, ri, None, "grad_initial", skip=skip_i, g_rms=g_rms)
+    _close(gx, rx, ax, "grad_x", sums[0], skip=_width(skip_h, x), g_rms=g_rms)
+    _close(gs, rs, ax, "grad_s", sums[1], skip=_width(skip_h, s), g_rms=g_rms)
 
 
 def _width(mask, t):
@@ -247,6 +252,17 @@ def test_norm_cap_width_one_sums(lead, xw, sw):
     init = 0.3 * torch.randn((lead[0], lead[2], 16), generator=gen)
     g = torch.randn(full, generator=gen)
     _run("norm_cap", x, s, init, g, 1, -1, False)
+
+
+@pytest.mark.parametrize("lead,reverse", [((1, 1, 1), False), ((2, 1, 1), True), ((2, 7, 1), False), ((3, 300, 2), True)])
+def test_norm_cap_state_width_one(lead, reverse):
+    """A norm-cap state of width one: a capped trip maps y to y / |y| = +-1, whose
+    derivative is zero, so the gradient through it vanishes by cancellation (the
+    oracle's float64 gives zeros, f32 a residue of a few ulps of the terms)."""
+    x, s, full, gen = _draw("norm_cap", lead, 1, seed=181 + lead[1], x_width=1, s_width=1)
+    init = 0.3 * torch.randn((lead[0], lead[2], 1), generator=gen)
+    g = torch.randn(full, generator=gen)
+    _run("norm_cap", x, s, init, g, 1, -1, reverse)
 
 
 @pytest.mark.parametrize("T", [20, 600])
