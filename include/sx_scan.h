@@ -3,8 +3,8 @@
  *
  * The scans of the SexpGPU documentation pages:
  *
- *   element-scan  "Nonlinear element scans": a nonlinear recurrence run
- *                 independently at every position outside one sequence axis,
+ *   element-scan  "Nonlinear element scans": a nonlinear recurrence along
+ *                 one axis, one independent lane per index of the other axes,
  *                 with one of three fixed bodies (tanh-affine, norm-capped
  *                 vector state, max-plus), forward or reverse.
  *   element-scan gradient  the chain rule through those bodies, trips last
@@ -44,8 +44,8 @@
  *    sx_last_error() then returns a message that names the operands with
  *    their shapes and dtypes, as the pages' error notes do.
  *  - Status codes mirror the pages' error table ("Tensor operations",
- *    Errors): E-DIM-001 shapes do not fit, E-DIM-002 dtypes differ or are
- *    not allowed, E-DIM-003 a tensor was expected.
+ *    Errors): E-DIM-001 for a shape mismatch, E-DIM-002 for mismatched or
+ *    unsupported dtypes, E-DIM-003 for a missing tensor.
  */
 #ifndef SX_SCAN_H
 #define SX_SCAN_H
@@ -187,8 +187,8 @@ size_t sx_element_scan_backward_workspace_bytes(sx_body body, int rank, const in
  *
  * a is [lead_a..., n, n] and b [lead_b..., n, m], n <= 16, one float dtype.
  * The leading dims broadcast (NumPy: right-aligned, each equal or 1) to one
- * shape `lead`, and `axis` counts among them (-1 is the one before the
- * matrices). For every other leading index the n-by-m state runs
+ * shape `lead`, and `axis` indexes them (-1: the last leading dim, next to
+ * the matrix dims). For every other leading index the n-by-m state runs
  *   forward  h[t] = a[t] @ h[t-1] + b[t]  from h[-1] = 0  (h[0] = b[0]),
  *   reverse  h[t] = a[t] @ h[t+1] + b[t]  from h[T] = 0  (h[T-1] = b[T-1]),
  * and out[t] = h[t]. Computation is f32 for f32 and bf16 operands alike:
@@ -290,7 +290,7 @@ int sx_matrix_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, con
 
 /*
  * sx_matrix_scan_backward: "Tensor operations", the "matrix-scan" section (its
- * gradient is the same scan run backwards on a's transposes) and the
+ * gradient is a scan in the opposite direction over transposed a) and the
  * "gradient" section (a gradient has its operand's shape and dtype).
  *
  * Given the forward call's a and b shapes, its result h and the gradient g of
@@ -340,7 +340,7 @@ size_t sx_matrix_scan_backward_workspace_bytes(int a_rank, const int64_t* a_shap
 /*
  * sx_linear_scan: "Tensor operations", the "matrix-scan" section, on the
  * prelude's linear-scan: matrix-scan over one-by-one matrices, with a and b
- * (numbers included) broadcast to one shape. cumsum is linear-scan with
+ * (tensors or plain numbers) broadcast together. cumsum is linear-scan with
  * a = 1 (a rank-0 a holding 1).
  *
  * For every index outside `axis` of the broadcast shape the scalar state runs
@@ -379,10 +379,10 @@ int sx_linear_scan_out_shape(int a_rank, const int64_t* a_shape, int b_rank, con
 /*
  * sx_table_scan: "Tensor operations", the "table-scan" section.
  *
- * Runs a deterministic automaton along `axis` of `symbols`: the state after
- * each symbol is table[previous, symbol], from state `start`; out holds every
+ * Runs a deterministic automaton along `axis` of `symbols`: each symbol
+ * moves the state to table[previous, symbol], starting at `start`; out holds every
  * state, in symbols' shape. A symbol outside [0, nsym) is clamped into that
- * range, and so is a table entry the run reaches outside [0, states), as the
+ * range, and so is any table value the run lands on outside [0, states), as the
  * pages' GPU backend does (their CPU backend refuses them instead). States
  * have no gradient.
  *

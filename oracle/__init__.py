@@ -41,9 +41,9 @@ Sources, all from the SexpGPU documentation pages:
   out-of-range symbol or reached entry is refused on the CPU and clamped on
   the GPU (both are here; the GPU's is the default).
 * "Tensor operations", the "matrix-scan" section, on the prelude's
-  ``linear-scan``: the same recurrence over one-by-one matrices, taking ``a``
-  and ``b`` (numbers included) broadcast to one shape; ``cumsum`` is built on
-  it, which makes it the linear scan with ``a = 1``.
+  ``linear-scan``: the same recurrence over one-by-one matrices, with ``a``
+  and ``b`` (tensors or plain numbers) broadcast together; ``cumsum`` is
+  defined through it, so it is the linear scan with ``a = 1``.
 
 Readings where the pages leave a point open (each is listed with its reason
 in the design notes of the repository):
@@ -100,8 +100,9 @@ BODIES = {
     "max_plus": _max_plus,
 }
 
-# Bodies that reduce over the state vector need a vector state: the page's
-# "Arguments and body" section says a scalar state's body cannot reduce.
+# Bodies that reduce over the state vector need a vector state: by the page's
+# "Arguments and body" section, a reduction over components has nothing to
+# reduce when the state is a single number.
 _REDUCING = {"norm_cap"}
 
 
@@ -111,8 +112,8 @@ def element_scan(body, initial, sequences, axis=0, state_axis=None,
 
     ``body`` is one of ``BODIES``; ``sequences`` is the list of the body's
     sequence arguments in page order (``[x, decay]`` or ``[x, cost]``).
-    ``state_axis`` is ``None`` (scalar state) or ``-1`` (the state is a
-    vector along the last axis). Returns an array of the sequences' shape
+    ``state_axis`` is ``None`` (scalar state) or ``-1`` (the last axis
+    holds the components of a vector state). Returns an array of the sequences' shape
     (with the last axis equal to the state's width under ``state_axis``).
 
     Follows "Nonlinear element scans", introduction and "Arguments and body".
@@ -164,7 +165,7 @@ def element_scan(body, initial, sequences, axis=0, state_axis=None,
     order = range(T - 1, -1, -1) if reverse else range(T)
     for t in order:
         h = step(h, *(s[t] for s in seq_t))
-        out[t] = h  # each position holds the state after its own trip
+        out[t] = h  # the state reached at position t is stored at t
     return np.moveaxis(out, 0, ax)
 
 
@@ -426,8 +427,8 @@ def table_scan(table, symbols, axis=-1, start=0, clamp=True):
     """Run a deterministic automaton the plain way, one symbol at a time.
 
     ``table`` is ``[states, symbols]`` of integers and ``symbols`` any shape of
-    integers; along ``axis`` (the last by default) the state after each
-    symbol is ``table[previous, symbol]``, from ``start`` (0 by default).
+    integers; along ``axis`` (the last by default) each symbol moves the
+    state to ``table[previous, symbol]``, starting at ``start`` (0 by default).
     Returns every state, in ``symbols``' shape (int32).
 
     Out-of-range values: with ``clamp`` (the GPU reading) a symbol is clamped

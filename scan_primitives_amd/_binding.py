@@ -430,8 +430,8 @@ def linear_scan(a, b, axis: int = 0, reverse: bool = False, out_dtype=None) -> t
 
 
 def table_scan(table: torch.Tensor, symbols: torch.Tensor, axis: int = -1, start: int = 0) -> torch.Tensor:
-    """Deterministic automaton on the GPU: along ``axis`` the state after each
-    symbol is ``table[previous, symbol]``, from ``start``. ``table`` is
+    """Deterministic automaton on the GPU: along ``axis``, reading a symbol
+    moves the state to ``table[previous, symbol]``, starting at ``start``. ``table`` is
     ``[states, symbols]``, both int32; returns every state (int32, symbols'
     shape). Out-of-range symbols and reached entries are clamped into range."""
     _require_device_tensor("table", table)

@@ -1,8 +1,8 @@
 // matrix_scan_grad.hip: the parts of the matrix-scan gradient that follow the
 // adjoint scan, for gfx950.
 //
-// "Tensor operations", the "matrix-scan" section: the gradient is the same
-// scan run backwards on a's transposes. With lam[t] the adjoint of h[t] (that
+// "Tensor operations", the "matrix-scan" section: the gradient is a scan in
+// the opposite direction over transposed a. With lam[t] the adjoint of h[t] (that
 // scan, run by launch_matrix_scan in adjoint mode), the chain rule through
 // h[t] = a[t] @ h[p] + b[t] (p the step before t in scan order) gives
 //   grad_b[t] = lam[t],   grad_a[t] = lam[t] @ h[p]^T   (zero at the first step),

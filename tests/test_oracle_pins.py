@@ -243,8 +243,8 @@ def test_max_plus_float32_mode_close_to_float64():
 @pytest.mark.parametrize("body,state_axis", [("tanh_affine", None), ("max_plus", None), ("norm_cap", -1),
                                              ("tanh_affine", -1), ("max_plus", -1)])
 def test_reverse_is_flip_scan_flip(body, state_axis):
-    # "Nonlinear element scans": a reverse scan computes the same values as
-    # flipping the sequences along the axis, scanning forward and flipping back.
+    # "Nonlinear element scans": reversing the sequences along the axis, scanning
+    # forward and reversing the result gives what the :reverse scan gives.
     r = _rng(20)
     x = r.standard_normal((3, 13, 2, 4))
     s = r.uniform(0, 1, (3, 13, 2, 1 if state_axis is not None else 4))
@@ -365,7 +365,7 @@ def test_matrix_scan_first_a_unused_forward_last_unused_reverse():
 
 
 def test_matrix_scan_columns_are_independent():
-    # "Tensor operations", matrix-scan: every column of h is its own recurrence on the shared a.
+    # "Tensor operations", matrix-scan: the columns of b never mix; each runs through the same a's alone.
     r = _rng(35)
     a = r.standard_normal((10, 4, 4)) * 0.5
     b = r.standard_normal((10, 4, 3))
@@ -532,8 +532,8 @@ def test_linear_scan_empty_axis_and_numbers():
 
 # ---------------------------------------------------------------- matrix-scan gradient
 #
-# "Tensor operations", the "matrix-scan" section: the gradient is the same
-# scan run backwards on a's transposes; the "gradient" section: a gradient
+# "Tensor operations", the "matrix-scan" section: the gradient is a scan in
+# the opposite direction over transposed a; the "gradient" section: a gradient
 # has its operand's shape. The pins below fix the vector-Jacobian product by
 # what it is, the derivative of L = sum(g * h), without reusing its loop.
 

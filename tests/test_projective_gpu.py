@@ -1,8 +1,8 @@
 """Parity of the HIP matrix-scan ``:projective`` path with the CPU oracle.
 
-The oracle (``oracle.matrix_scan_projective``) keeps the running product of
-a from the identity, divides it after every step by its largest magnitude
-and divides h by the same number. The GPU runs the same recurrence in f32.
+The oracle (``oracle.matrix_scan_projective``) multiplies a running matrix,
+started at the identity, by each step's a and rescales it and h after every
+step by that matrix's entry of largest absolute value. The GPU runs the same recurrence in f32.
 The bar is the matrix-scan bar: ||gpu[t] - ref[t]||_F <= tol * max(||ref[t]||_F,
 RMS of the state norms of the same scan), tol = 1e-4 for f32 operands and
 2e-2 for bf16.
