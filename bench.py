@@ -52,9 +52,12 @@ LLC_BYTES = 256 * 1024 * 1024  # MI355X last-level (Infinity) cache
 # MI355X dense MFMA peaks, AMD's published figures (TFLOP/s)
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 METRIC = "scan elements/s and achieved HBM GB/s vs MI355X peak (rocprof), per config"
+# Every file whose code shapes what the kernels do: the kernels, their shared headers and the
+# host code that picks kernels and launch shapes.
 KERNEL_SOURCES = ["scan_primitives_amd/csrc/element_scan.hip", "scan_primitives_amd/csrc/normcap_quad.hip",
                   "scan_primitives_amd/csrc/matrix_scan.hip", "scan_primitives_amd/csrc/matrix_scan_grad.hip",
-                  "scan_primitives_amd/csrc/table_scan.hip"]
+                  "scan_primitives_amd/csrc/table_scan.hip", "scan_primitives_amd/csrc/ms_mfma.hpp",
+                  "scan_primitives_amd/csrc/sx_common.hpp", "scan_primitives_amd/csrc/sx_api.cpp"]
 
 
 def log(*a):
@@ -69,11 +72,39 @@ def git_sha() -> str | None:
         return None
 
 
+def code_only(text: str) -> str:
+    """C/C++ source with its comments removed and blank lines dropped, so that
+    a change to comments alone keeps the hash below (string and character
+    literals are kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            k = text.find("*/", i + 2)
+            i = n if k < 0 else k + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash() -> str:
+    """First 16 hex digits of the sha256 of KERNEL_SOURCES' code (comments removed)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
