@@ -123,7 +123,18 @@ __device__ __forceinline__ Walk walk_of(int64_t lane_off, int64_t t_stride, int6
 // warm-up, which reads the chunks just before it, and the data one pass
 // leaves for the next then stay in one L2.
 
-template <bool X1, bool S1>
+// CL > 0: chunks of at most CL trips (len <= CL), each started WB trips
+// early. Every load a quad needs, its chunk and the WB trips before it, is
+// issued before any arithmetic, so the quad waits for memory once. The
+// per-trip bounds of the WB trips are independent, so they are all formed at
+// once; the quad is certified when the product over some run of trips ending
+// at s - 1 is at most 2^-26. Every trip maps into the unit ball, so running
+// all WB trips from 0 is as good as starting where that run starts, and the
+// run needs no per-quad start point (chunks within WB trips of the axis start
+// run exactly from `initial`). A quad that is not certified within WB trips
+// takes the general path below, which walks further back a block of loads at
+// a time. CL = 0: the general path only.
+template <bool X1, bool S1, int CL, int WB>
 __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQuadSpans sp, int64_t len,
                                                           int64_t nchunks) {
   const int64_t row = (xcd_block() * blockDim.x + threadIdx.x) >> 2;
@@ -140,8 +151,63 @@ __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQu
   const Walk wo = walk_of(off[ES_OUT] + 4 * j, p.t_stride[ES_OUT], T, rev, false);
   const int32_t s = int32_t(chunk * len);
   const int32_t e = int32_t(s + len < T ? s + len : T);
+  // one trip from h: y = a h + x, h = y / max(1, |y|)
+  auto trip = [&](f4& h, f4 xq, f4 sq) {
+    const f4 y = fma4(sq, h, xq);
+    const float ss = quad_sum(dot4(y, y));
+    h = y * fminf(1.0f, __builtin_amdgcn_rsqf(ss));  // rsqrt(ss) >= 1 exactly when ss <= 1
+  };
+  auto initial_state = [&]() -> f4 {
+    const float* ip = p.init + off[ES_INIT] + 4 * j * p.n_stride[ES_INIT];
+    const int64_t is = p.n_stride[ES_INIT];
+    return f4{ip[0], ip[is], ip[2 * is], ip[3 * is]};
+  };
+  if constexpr (CL > 0) {
+    // positions past either end of the axis read zero or another element of the tensor (not used)
+    Comp<X1> xc[CL], xw[WB];
+    Comp<S1> sc[CL], sw[WB];
+#pragma unroll
+    for (int u = 0; u < CL; ++u) {
+      xc[u] = bload<X1>(rx, wx.base + (s + u) * wx.step);
+      sc[u] = bload<S1>(rs, ws.base + (s + u) * ws.step);
+    }
+#pragma unroll
+    for (int u = 0; u < WB; ++u) {  // position s - 1 - u
+      xw[u] = bload<X1>(rx, wx.base + (s - 1 - u) * wx.step);
+      sw[u] = bload<S1>(rs, ws.base + (s - 1 - u) * ws.step);
+    }
+    // Certified when some run of trips ending at s - 1, within the WB kept, has a product of bounds
+    // of at most 2^-26 (the bounds are independent, so they are formed at once). Every trip maps into
+    // the unit ball, so starting all WB trips early from 0 is as good as starting at that run's start.
+    // A chunk within WB trips of the axis start runs exactly from `initial` at position 0 (the
+    // warm-up must not start at position 0 from 0: `initial` need not lie in the unit ball).
+    const bool from_start = s <= WB;  // uniform over the chunk
+    bool certified = from_start;
+    if (!from_start) {
+      float prod = 1.0f;
+#pragma unroll
+      for (int u = 0; u < WB; ++u) {
+        prod *= quad_lipschitz<S1>(as4(xw[u]), as4(sw[u]));
+        certified = certified || prod <= kCertBound;
+      }
+    }
+    if (certified) {  // quad-uniform
+      f4 h = from_start ? initial_state() : splat(0.0f);
+#pragma unroll
+      for (int u = WB - 1; u >= 0; --u)
+        if (s - 1 - u >= 0) trip(h, as4(xw[u]), as4(sw[u]));  // uniform over the chunk
+#pragma unroll
+      for (int u = 0; u < CL; ++u) {
+        if (s + u < e) {
+          trip(h, as4(xc[u]), as4(sc[u]));
+          bstore(ro, wo.base + (s + u) * wo.step, h);
+        }
+      }
+      return;
+    }
+  }
   constexpr int U = 8;
-  // ---- walk back from s - 1 while the bound is above 2^-26
+  // ---- general path: walk back from s - 1 while the bound is above 2^-26
   int32_t start = 0;
   if (s > 0) {  // quad-uniform
     float prod = 1.0f;
@@ -173,11 +239,7 @@ __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQu
   }
   // ---- from `initial` at position 0, else from 0 (in the unit ball)
   f4 h = splat(0.0f);
-  if (start == 0) {
-    const float* ip = p.init + off[ES_INIT] + 4 * j * p.n_stride[ES_INIT];
-    const int64_t is = p.n_stride[ES_INIT];
-    h = f4{ip[0], ip[is], ip[2 * is], ip[3 * is]};
-  }
+  if (start == 0) h = initial_state();
   struct Block {
     Comp<X1> x[U];
     Comp<S1> s[U];
@@ -197,9 +259,7 @@ __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQu
     for (int u = 0; u < U; ++u) {
       const int32_t q = q0 + u;
       if (q < e) {  // quad-uniform
-        const f4 y = fma4(as4(B.s[u]), h, as4(B.x[u]));
-        const float ss = quad_sum(dot4(y, y));
-        h = y * fminf(1.0f, __builtin_amdgcn_rsqf(ss));  // rsqrt(ss) >= 1 exactly when ss <= 1
+        trip(h, as4(B.x[u]), as4(B.s[u]));
         if (q >= s) bstore(ro, wo.base + q * wo.step, h);
       }
     }
@@ -456,11 +516,16 @@ __global__ __launch_bounds__(256) void nc_quad_grad_kernel(const EsVjpParams v, 
 // Quads in flight: about kFwdRows (forward) or kGradRows (gradient) rows, in
 // chunks of at least kFwdMinLen or kGradMinLen trips. Measured on [8,1024,16,16]
 // and [64,1024,16,16]: more rows help the gradient's longer per-row chains on
-// the larger shape and slow the forward there.
+// the larger shape and slow the forward there. Forward chunks of at most
+// kFwdRegLen trips keep the chunk and kFwdWarm warm-up trips in registers;
+// 20 warm-up trips certify every chunk of the standard norm-cap workload
+// (|x| about 4, gate in [0.8, 1]: the most any chunk needs is 20).
 constexpr int64_t kFwdRows = 16384;
 constexpr int64_t kGradRows = 32768;
-constexpr int64_t kFwdMinLen = 16;
+constexpr int64_t kFwdMinLen = 8;
 constexpr int64_t kGradMinLen = 8;
+constexpr int kFwdRegLen = 8;
+constexpr int kFwdWarm = 20;
 constexpr int64_t kMaxSpan = int64_t(1) << 31;  // bytes a buffer resource here may cover
 
 bool split_of(const EsParams& p, int64_t rows, int64_t min_len, int64_t* len, int64_t* nchunks) {
@@ -542,8 +607,12 @@ hipError_t launch_normcap_quad_forward(const EsParams& p, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   by_widths(p, [&](auto x1c, auto s1c) {
     constexpr bool X1 = decltype(x1c)::value, S1 = decltype(s1c)::value;
-    hipLaunchKernelGGL((nc_quad_fwd_kernel<X1, S1>), dim3(unsigned(blocks)), dim3(256), 0, stream, p, sp, len,
-                       nchunks);
+    if (len <= kFwdRegLen)
+      hipLaunchKernelGGL((nc_quad_fwd_kernel<X1, S1, kFwdRegLen, kFwdWarm>), dim3(unsigned(blocks)), dim3(256), 0,
+                         stream, p, sp, len, nchunks);
+    else
+      hipLaunchKernelGGL((nc_quad_fwd_kernel<X1, S1, 0, 1>), dim3(unsigned(blocks)), dim3(256), 0, stream, p, sp, len,
+                         nchunks);
   });
   return hipGetLastError();
 }

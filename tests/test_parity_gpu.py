@@ -151,6 +151,21 @@ def test_norm_cap_chunked_without_contraction(reverse):
     assert_element_close(got, ref)
 
 
+@pytest.mark.parametrize("x_scale,reverse", [(0.8, False), (0.85, True)])
+def test_norm_cap_partly_certified_warm_ups(x_scale, reverse):
+    # x scaled so that about 40% (0.8) or 87% (0.85) of the 8-trip chunks certify their warm-up within
+    # the 20 trips the register path keeps: certified and uncertified quads share waves, and the
+    # uncertified ones walk further back. initial lies far outside the unit ball (|initial| about 100),
+    # so chunks within reach of the axis start must run exactly from it.
+    w = W.make_norm_cap(8, 512, 16, 16, gate_width=1, reverse=reverse, seed=127, zero_initial=False,
+                        x_scale=x_scale)
+    w.tensors["initial"] = 25.0 * w.tensors["initial"]
+    _announce(w)
+    got = run_gpu(w, DEV)
+    assert_element_close(got, run_oracle(w))
+    assert float(torch.linalg.vector_norm(got, dim=-1).max()) <= 1 + 1e-5
+
+
 @pytest.mark.parametrize("case", ["x_width_one", "both_width_one", "aligned_view", "unaligned_view",
                                   "strided_initial", "axis0", "many_vectors", "reverse_long"])
 def test_norm_cap_layouts(case):
