@@ -137,12 +137,15 @@ __device__ __forceinline__ Walk walk_of(int64_t lane_off, int64_t t_stride, int6
 template <bool X1, bool S1, int CL, int WB>
 __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQuadSpans sp, int64_t len,
                                                           int64_t nchunks) {
-  const int64_t row = (xcd_block() * blockDim.x + threadIdx.x) >> 2;
-  if (row >= p.num_lanes * nchunks) return;  // whole quads
-  const int64_t chunk = row / p.num_lanes, lane = row - chunk * p.num_lanes;
+  // rows, lanes, dims and strides all lie below 2^31 here (the launcher checks the row count,
+  // and every tensor spans less than 2 GiB), so the index arithmetic is 32-bit
+  const uint32_t row = uint32_t((xcd_block() * blockDim.x + threadIdx.x) >> 2);
+  const uint32_t nl = uint32_t(p.num_lanes);
+  if (row >= nl * uint32_t(nchunks)) return;  // whole quads
+  const uint32_t chunk = row / nl, lane = row - chunk * nl;
   const int j = int(threadIdx.x & 3);
   int64_t off[4];
-  index_offsets(p.lanes, lane, off);
+  index_offsets32(p.lanes, lane, off);
   const int64_t T = p.T;
   const bool rev = p.reverse != 0;
   const Rsrc rx = rsrc(p.x, sp.x), rs = rsrc(p.s, sp.s), ro = rsrc(p.out, sp.out);
@@ -163,19 +166,25 @@ __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQu
     return f4{ip[0], ip[is], ip[2 * is], ip[3 * is]};
   };
   if constexpr (CL > 0) {
-    // positions past either end of the axis read zero or another element of the tensor (not used)
-    Comp<X1> xc[CL], xw[WB];
-    Comp<S1> sc[CL], sw[WB];
+    // Registers hold positions s - WB .. s + CL - 1 (index i = position - (s - WB)); positions past
+    // either end of the axis read zero or another element of the tensor (not used). A width-one
+    // gate is the same for the quad's four threads, so thread j loads every fourth position
+    // (i = 4k + j) and a quad broadcast hands each out when it is used.
+    constexpr int NP = WB + CL;
+    const int32_t p0 = s - WB;
+    Comp<X1> xa[NP];
 #pragma unroll
-    for (int u = 0; u < CL; ++u) {
-      xc[u] = bload<X1>(rx, wx.base + (s + u) * wx.step);
-      sc[u] = bload<S1>(rs, ws.base + (s + u) * ws.step);
-    }
+    for (int i = 0; i < NP; ++i) xa[i] = bload<X1>(rx, wx.base + (p0 + i) * wx.step);
+    constexpr int NS = S1 ? (NP + 3) / 4 : NP;
+    Comp<S1> sa[NS];
 #pragma unroll
-    for (int u = 0; u < WB; ++u) {  // position s - 1 - u
-      xw[u] = bload<X1>(rx, wx.base + (s - 1 - u) * wx.step);
-      sw[u] = bload<S1>(rs, ws.base + (s - 1 - u) * ws.step);
-    }
+    for (int k = 0; k < NS; ++k)
+      sa[k] = bload<S1>(rs, ws.base + (p0 + (S1 ? 4 * k + j : k)) * ws.step);
+    auto gate = [&](auto ic) -> f4 {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (S1) return splat(quad_dpp<(i & 3) * 0x55>(as4(sa[i >> 2]).x));
+      else return as4(sa[i]);
+    };
     // Certified when some run of trips ending at s - 1, within the WB kept, has a product of bounds
     // of at most 2^-26 (the bounds are independent, so they are formed at once). Every trip maps into
     // the unit ball, so starting all WB trips early from 0 is as good as starting at that run's start.
@@ -185,24 +194,31 @@ __global__ __launch_bounds__(256) void nc_quad_fwd_kernel(const EsParams p, NcQu
     bool certified = from_start;
     if (!from_start) {
       float prod = 1.0f;
-#pragma unroll
-      for (int u = 0; u < WB; ++u) {
-        prod *= quad_lipschitz<S1>(as4(xw[u]), as4(sw[u]));
-        certified = certified || prod <= kCertBound;
-      }
+      [&]<int... us>(std::integer_sequence<int, us...>) {
+        ((prod *= quad_lipschitz<S1>(as4(xa[WB - 1 - us]), gate(std::integral_constant<int, WB - 1 - us>{})),
+          certified = certified || prod <= kCertBound),
+         ...);
+      }(std::make_integer_sequence<int, WB>{});
     }
     if (certified) {  // quad-uniform
       f4 h = from_start ? initial_state() : splat(0.0f);
-#pragma unroll
-      for (int u = WB - 1; u >= 0; --u)
-        if (s - 1 - u >= 0) trip(h, as4(xw[u]), as4(sw[u]));  // uniform over the chunk
-#pragma unroll
-      for (int u = 0; u < CL; ++u) {
-        if (s + u < e) {
-          trip(h, as4(xc[u]), as4(sc[u]));
-          bstore(ro, wo.base + (s + u) * wo.step, h);
-        }
-      }
+      // each trip's gate is formed one trip ahead, off the recurrence's path
+      f4 gcur = gate(std::integral_constant<int, 0>{});
+      [&]<int... is>(std::integer_sequence<int, is...>) {
+        (([&] {
+           const f4 gnext = gate(std::integral_constant<int, is + 1 < NP ? is + 1 : is>{});
+           if constexpr (is < WB) {
+             if (p0 + is >= 0) trip(h, as4(xa[is]), gcur);  // uniform over the chunk
+           } else {
+             if (s + (is - WB) < e) {
+               trip(h, as4(xa[is]), gcur);
+               bstore(ro, wo.base + (s + (is - WB)) * wo.step, h);
+             }
+           }
+           gcur = gnext;
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, NP>{});
       return;
     }
   }
@@ -604,7 +620,7 @@ hipError_t launch_normcap_quad_forward(const EsParams& p, hipStream_t stream) {
   int64_t len = 0, nchunks = 1;
   split_of(p, kFwdRows, kFwdMinLen, &len, &nchunks);
   const int64_t blocks = (p.num_lanes * nchunks * 4 + 255) / 256;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks * 256 > 0x7fffffff) return hipErrorInvalidConfiguration;  // 32-bit row arithmetic
   by_widths(p, [&](auto x1c, auto s1c) {
     constexpr bool X1 = decltype(x1c)::value, S1 = decltype(s1c)::value;
     if (len <= kFwdRegLen)

@@ -38,6 +38,32 @@ __device__ __forceinline__ void index_offsets(const IndexMap<NT>& m, int64_t idx
   }
 }
 
+// The same for an index below 2^31 of a map whose dims and strides all lie
+// below 2^31 in magnitude (every tensor of the caller spans less than 2 GiB):
+// 32-bit divisions, and the loop unrolled over the largest rank so that every
+// dimension's descriptor is loaded before the first is used (a loop over the
+// runtime rank waits for each load in turn, which measured slower even though
+// the unrolled form holds more descriptors than fit in scalar registers).
+template <int NT>
+__device__ __forceinline__ void index_offsets32(const IndexMap<NT>& m, uint32_t idx, int64_t (&off)[NT]) {
+  int32_t o[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) o[k] = 0;
+#pragma unroll
+  for (int d = kMaxRank - 1; d >= 0; --d) {
+    if (d < m.nd) {
+      const uint32_t dd = uint32_t(m.dim[d]);
+      const uint32_t q = dd == 1 ? idx : idx / dd;
+      const uint32_t i = idx - q * dd;
+      idx = q;
+#pragma unroll
+      for (int k = 0; k < NT; ++k) o[k] += int32_t(i) * int32_t(m.st[k][d]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NT; ++k) off[k] = o[k];
+}
+
 // Compute units of the current device (the persistent kernels keep one or two
 // workgroups resident on each); cached per device.
 int device_cu_count();
