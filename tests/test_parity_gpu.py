@@ -55,6 +55,9 @@ def test_tanh_small(shape, axis, reverse):
     ((3, 200, 19), 1, False),
     ((257, 3, 5), 0, True),
     ((2, 9, 1000), -1, False),
+    ((3, 40, 19), 1, True),     # axes of at most 64 trips: every position loaded before the first trip
+    ((64, 7), 0, False),
+    ((2, 5, 63), -1, True),
 ])
 def test_max_plus_small(shape, axis, reverse):
     w = W.make_max_plus(shape, axis=axis, reverse=reverse, seed=110)
@@ -241,6 +244,15 @@ def test_max_plus_matches_float32_serial_evaluation():
     err = np.abs(got.astype(np.float64) - ref32.astype(np.float64))
     print(f"max-plus vs float32 oracle: {int((err == 0).sum())} of {err.size} bit-identical, max err {err.max():.3e}")
     assert err.max() <= 1e-5 * (1 + np.abs(ref32).max())
+
+
+def test_max_plus_short_axis_is_a_serial_float32_evaluation():
+    # On an axis of at most 64 trips one thread runs each lane's trips in order, so the result is
+    # the float32 oracle's (subtract and maximum are correctly rounded) bit for bit.
+    for shape, reverse in (((4, 64, 64), True), ((5, 33, 17), False)):
+        w = W.make_max_plus(shape, reverse=reverse, seed=133)
+        got = run_gpu(w, DEV).cpu().numpy()
+        assert np.array_equal(got, run_oracle(w, dtype=np.float32))
 
 
 def test_element_scan_errors_on_device_tensors():
