@@ -76,12 +76,16 @@ __device__ __forceinline__ void st_elem_stream(float* p, float v) { st_stream(p,
 __device__ __forceinline__ void st_elem_stream(uint16_t* p, float v) { st_stream(p, f32_to_bf16_rne(v)); }
 
 // TI, TO: element types of the sequences and of out (float unless linear-scan).
-template <int BODY, typename TI = float, typename TO = float>
+// IDX32: every lane offset fits 32 bits (the host checks), so the lane's
+// offsets come from 32-bit divisions instead of 64-bit ones, whose expansion
+// costs a short lane a large share of its time.
+template <int BODY, typename TI = float, typename TO = float, bool IDX32 = false>
 __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   const int64_t lane = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (lane >= p.num_lanes) return;
   int64_t off[4];
-  index_offsets(p.lanes, lane, off);
+  if constexpr (IDX32) index_offsets32(p.lanes, uint32_t(lane), off);
+  else index_offsets(p.lanes, lane, off);
   const int64_t T = p.T;
   int64_t dx = p.t_stride[ES_X], ds = p.t_stride[ES_S], dout = p.t_stride[ES_OUT];
   const TI* xp = reinterpret_cast<const TI*>(p.x) + off[ES_X];
@@ -1068,6 +1072,23 @@ constexpr int64_t kSlabMinTrips = 512;
 
 size_t element_scan_workspace(sx_body, const EsParams&) { return 0; }
 
+namespace {
+// Lanes below 2^31 whose dims, strides and offsets (lane part) all lie below 2^31.
+bool lane_offsets_fit32(const EsParams& p) {
+  if (p.num_lanes >= (int64_t(1) << 31)) return false;
+  for (int k = 0; k < 4; ++k) {
+    int64_t span = 0;
+    for (int d = 0; d < p.lanes.nd; ++d) {
+      const int64_t st = p.lanes.st[k][d] < 0 ? -p.lanes.st[k][d] : p.lanes.st[k][d];
+      if (p.lanes.dim[d] >= (int64_t(1) << 31) || st >= (int64_t(1) << 31)) return false;
+      span += (p.lanes.dim[d] - 1) * st;
+      if (span >= (int64_t(1) << 31)) return false;
+    }
+  }
+  return true;
+}
+}  // namespace
+
 hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stream) {
   if (p.num_lanes <= 0) return hipSuccess;
   if (body == SX_BODY_NORM_CAP) {
@@ -1094,10 +1115,17 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
     const int64_t blocks = (p.num_lanes + 63) / 64;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (body == SX_BODY_TANH_AFFINE) {
-      hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
+      if (lane_offsets_fit32(p))
+        hipLaunchKernelGGL((es_lane_kernel<SX_BODY_TANH_AFFINE, float, float, true>), dim3(unsigned(blocks)), dim3(64),
+                           0, stream, p);
+      else
+        hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     } else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips) {
       // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries
       hipLaunchKernelGGL((es_slab_kernel<SX_BODY_MAX_PLUS, 16, 16>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
+    } else if (lane_offsets_fit32(p)) {
+      hipLaunchKernelGGL((es_lane_kernel<SX_BODY_MAX_PLUS, float, float, true>), dim3(unsigned(blocks)), dim3(64), 0,
+                         stream, p);
     } else {
       hipLaunchKernelGGL(es_lane_kernel<SX_BODY_MAX_PLUS>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     }
@@ -1114,6 +1142,8 @@ void launch_linear(const EsParams& p, int64_t blocks, hipStream_t stream) {
   else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)
     hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 16, TI, TO>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
                        stream, p);
+  else if (lane_offsets_fit32(p))
+    hipLaunchKernelGGL((es_lane_kernel<kBodyLinear, TI, TO, true>), dim3(unsigned(blocks)), dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL((es_lane_kernel<kBodyLinear, TI, TO>), dim3(unsigned(blocks)), dim3(64), 0, stream, p);
 }

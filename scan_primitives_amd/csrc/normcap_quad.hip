@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void nc_quad_bound_kernel(const EsVjpParams v,
   const int64_t group = blockIdx.x % kXcds, lane = blockIdx.x / kXcds;
   const int R = int(blockDim.x >> 2), r = int(threadIdx.x >> 2), j = int(threadIdx.x & 3);
   int64_t off[4];
-  index_offsets(p.lanes, lane, off);
+  index_offsets32(p.lanes, uint32_t(lane), off);  // every tensor spans less than 2 GiB
   const int64_t T = p.T;
   const bool rev = p.reverse != 0;
   const Rsrc rx = rsrc(p.x, sp.x), rs = rsrc(p.s, sp.s), rg = rsrc(v.g, sp.out);
@@ -384,12 +384,14 @@ template <bool X1, bool S1>
 __global__ __launch_bounds__(256) void nc_quad_grad_kernel(const EsVjpParams v, NcQuadSpans sp, int64_t len,
                                                            int64_t nchunks) {
   const EsParams& p = v.p;
-  const int64_t row = (xcd_block() * blockDim.x + threadIdx.x) >> 2;
-  if (row >= p.num_lanes * nchunks) return;  // whole quads
-  const int64_t chunk = row / p.num_lanes, lane = row - chunk * p.num_lanes;
+  // 32-bit index arithmetic, as in the forward kernel (the launcher checks the row count)
+  const uint32_t row = uint32_t((xcd_block() * blockDim.x + threadIdx.x) >> 2);
+  const uint32_t nl = uint32_t(p.num_lanes);
+  if (row >= nl * uint32_t(nchunks)) return;  // whole quads
+  const uint32_t chunk = row / nl, lane = row - chunk * nl;
   const int j = int(threadIdx.x & 3);
   int64_t off[4];
-  index_offsets(p.lanes, lane, off);
+  index_offsets32(p.lanes, lane, off);
   const int64_t T = p.T;
   const bool rev = p.reverse != 0;
   const Rsrc rx = rsrc(p.x, sp.x), rs = rsrc(p.s, sp.s), rh = rsrc(v.h, sp.out), rg = rsrc(v.g, sp.out);
@@ -653,7 +655,7 @@ hipError_t launch_normcap_quad_backward(const EsVjpParams& v, hipStream_t stream
     nchunks = 1;
   }
   const int64_t blocks = (p.num_lanes * nchunks * 4 + 255) / 256;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks * 256 > 0x7fffffff) return hipErrorInvalidConfiguration;  // 32-bit row arithmetic
   const int64_t per_group = (nchunks + kXcds - 1) / kXcds;
   // the bound kernel's quads per workgroup: one chunk of the group each, at most 64, and at
   // least a whole wave (its maxima read every lane of the wave)
