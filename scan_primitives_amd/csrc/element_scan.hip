@@ -38,6 +38,7 @@
 //                          loads are in flight meanwhile. Inputs are read
 //                          once and no state leaves the workgroup.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "sx_common.hpp"
@@ -608,13 +609,14 @@ __device__ __forceinline__ VjpTrip vjp_trip(float h, float hp, float x, float s,
 // position q is time tq(q); the state before it is h at position q - 1
 // (initial at q = 0). Loads of a block of U trips are issued before any of
 // its trips is computed.
-template <int BODY>
+template <int BODY, bool IDX32 = false>  // IDX32: as in es_lane_kernel
 __global__ __launch_bounds__(64) void es_vjp_lane_kernel(const EsVjpParams v) {
   const EsParams& p = v.p;
   const int64_t lane = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (lane >= p.num_lanes) return;
   int64_t off[4];
-  index_offsets(p.lanes, lane, off);
+  if constexpr (IDX32) index_offsets32(p.lanes, uint32_t(lane), off);
+  else index_offsets(p.lanes, lane, off);
   const int64_t T = p.T;
   const int64_t sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
   const float* xl = p.x + off[ES_X];
@@ -670,7 +672,7 @@ __global__ __launch_bounds__(64) void es_vjp_lane_kernel(const EsVjpParams v) {
 // each wave composes the ones before it onto the slab's carry, and replays
 // its trips storing both gradients. The next slab's loads are in flight
 // meanwhile. Sweep position w is scan position T - 1 - w.
-template <int BODY, int NW, int S>
+template <int BODY, int NW, int S, bool IDX32 = false>  // IDX32: as in es_lane_kernel
 __global__ __launch_bounds__(NW * 64) void es_vjp_slab_kernel(const EsVjpParams v) {
   const EsParams& p = v.p;
   __shared__ float sP[2][NW][64];
@@ -680,7 +682,8 @@ __global__ __launch_bounds__(NW * 64) void es_vjp_slab_kernel(const EsVjpParams 
   const int64_t lane = int64_t(blockIdx.x) * 64 + l;
   const bool live = lane < p.num_lanes;
   int64_t off[4];
-  index_offsets(p.lanes, live ? lane : 0, off);
+  if constexpr (IDX32) index_offsets32(p.lanes, uint32_t(live ? lane : 0), off);
+  else index_offsets(p.lanes, live ? lane : 0, off);
   const int64_t T = p.T;
   const int64_t sx = p.t_stride[ES_X], ss = p.t_stride[ES_S], so = p.t_stride[ES_OUT];
   const float* xl = p.x + off[ES_X];
@@ -1221,18 +1224,23 @@ hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipS
   // still takes every load of a slab at once, where the lane kernel would wait
   // on memory each block of trips.
   const bool slab = p.T >= kSlabMinTrips || (p.num_lanes < kSlabMinLanes && p.T >= 64);
+  auto launch = [&](auto bodyc, auto idxc) {
+    constexpr int B = decltype(bodyc)::value;
+    constexpr bool I32 = decltype(idxc)::value;
+    if (slab)
+      hipLaunchKernelGGL((es_vjp_slab_kernel<B, 16, 8, I32>), dim3(unsigned(blocks)), dim3(1024), 0, stream, v);
+    else
+      hipLaunchKernelGGL((es_vjp_lane_kernel<B, I32>), dim3(unsigned(blocks)), dim3(64), 0, stream, v);
+  };
+  const bool i32 = lane_offsets_fit32(p);
+  using TanhC = std::integral_constant<int, SX_BODY_TANH_AFFINE>;
+  using MaxC = std::integral_constant<int, SX_BODY_MAX_PLUS>;
   if (body == SX_BODY_TANH_AFFINE) {
-    if (slab)
-      hipLaunchKernelGGL((es_vjp_slab_kernel<SX_BODY_TANH_AFFINE, 16, 8>), dim3(unsigned(blocks)), dim3(1024), 0,
-                         stream, v);
-    else
-      hipLaunchKernelGGL(es_vjp_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, v);
+    if (i32) launch(TanhC{}, std::true_type{});
+    else launch(TanhC{}, std::false_type{});
   } else {
-    if (slab)
-      hipLaunchKernelGGL((es_vjp_slab_kernel<SX_BODY_MAX_PLUS, 16, 8>), dim3(unsigned(blocks)), dim3(1024), 0,
-                         stream, v);
-    else
-      hipLaunchKernelGGL(es_vjp_lane_kernel<SX_BODY_MAX_PLUS>, dim3(unsigned(blocks)), dim3(64), 0, stream, v);
+    if (i32) launch(MaxC{}, std::true_type{});
+    else launch(MaxC{}, std::false_type{});
   }
   return hipGetLastError();
 }
