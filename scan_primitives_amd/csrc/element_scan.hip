@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   }
   float h = p.init ? p.init[off[ES_INIT]] : 0.0f;  // no initial: linear-scan starts from zero
 
-  constexpr int U = 8;
+  constexpr int U = 16;  // trips per block of loads (8-trip blocks left more of each block's load latency exposed)
   const int64_t full = T / U * U;
   float cx[U], cs[U];
   if (full > 0) {
