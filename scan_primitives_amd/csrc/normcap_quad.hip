@@ -588,6 +588,10 @@ bool spans_of(const EsParams& p, NcQuadSpans* sp) {
   if (p.n != 16 || p.n_stride[ES_OUT] != 1 || p.T > 0x7fffffff) return false;
   const int64_t sx = span_bytes_of(p, ES_X), ss = span_bytes_of(p, ES_S), so = span_bytes_of(p, ES_OUT);
   if (sx <= 0 || ss <= 0 || so <= 0 || sx >= kMaxSpan || ss >= kMaxSpan || so >= kMaxSpan) return false;
+  // initial (and the gradient's grad_initial, in its layout) is addressed by a pointer, but its lane
+  // offsets come from the same 32-bit index arithmetic: they must fit as well
+  const int64_t si = span_bytes_of(p, ES_INIT);
+  if (si <= 0 || si >= kMaxSpan) return false;
   const bool x1 = p.n_stride[ES_X] == 0, s1 = p.n_stride[ES_S] == 0;
   if (!x1 && (p.n_stride[ES_X] != 1 || !quad_strides_ok(p, ES_X) || !aligned16(p.x))) return false;
   if (!s1 && (p.n_stride[ES_S] != 1 || !quad_strides_ok(p, ES_S) || !aligned16(p.s))) return false;

@@ -223,6 +223,47 @@ def test_element_scan_strided_and_broadcast_operands():
     assert_element_close(got, ref)
 
 
+def _view_past_32_bits(shape, lead_stride, fill):
+    """A view of `shape` into a device buffer of more than 2^31 floats: its first
+    dim steps `lead_stride` (>= 2^31) elements, so lane offsets pass 32 bits.
+    Only the viewed elements are written."""
+    inner = int(np.prod(shape[1:]))
+    base = torch.empty(lead_stride * (shape[0] - 1) + inner + 64, device=DEV)
+    strides = (lead_stride,) + tuple(torch.empty(shape[1:]).stride())
+    v = base.as_strided(shape, strides)
+    v.copy_(fill.to(DEV))
+    return base, v
+
+
+def test_lane_offsets_past_32_bits():
+    """x whose lane offsets pass 2^31 elements: the lane kernel takes its
+    64-bit index path (checked on the host), and the results match."""
+    g = torch.Generator().manual_seed(134)
+    x = torch.randn(2, 64, 32, generator=g)
+    decay = torch.rand(2, 64, 32, generator=g)
+    init = torch.randn(2, 32, generator=g)
+    base, xv = _view_past_32_bits((2, 64, 32), 2 ** 31, x)
+    ref = oracle.element_scan("tanh_affine", init.numpy(), [x.numpy(), decay.numpy()], axis=1)
+    got = sx.element_scan("tanh_affine", init.to(DEV), [xv, decay.to(DEV)], axis=1)
+    assert_element_close(got, ref)
+    del base, xv
+    torch.cuda.empty_cache()
+
+
+def test_norm_cap_initial_offsets_past_32_bits():
+    """A norm-cap initial whose offsets pass 2^31 elements: the four-components
+    -per-thread kernels index in 32 bits, so they must not take it (regression:
+    their check covered x, the gate and out but not initial)."""
+    w = W.make_norm_cap(B=2, T=40, H=3, n=16, zero_initial=False, seed=135)
+    t = w.tensors
+    base, iv = _view_past_32_bits((2, 3, 16), 2 ** 31, t["initial"])
+    ref = run_oracle(w)
+    got = sx.element_scan("norm_cap", iv, [t["x"].to(DEV), t["s"].to(DEV)], axis=1, state_axis=-1)
+    assert_element_close(got, ref)
+    del base, iv
+    torch.cuda.empty_cache()
+
+
 def test_vector_state_elementwise_bodies():
     g = torch.Generator().manual_seed(131)
     x = torch.randn(4, 60, 3, 7, generator=g)
