@@ -508,6 +508,24 @@ def test_matrix_bf16_in_f32_out_matches_f32_path(B, T, n, m, reverse):
     assert e_bf16 <= 2.0 * e_f32 + 1e-7, (e_bf16, e_f32)
 
 
+@pytest.mark.parametrize("dtype,m,reverse", [(torch.float32, 1, False), (torch.bfloat16, 16, True)])
+def test_matrix_batch_offsets_past_32_bits(dtype, m, reverse):
+    """a as a view whose batch stride is 2^31 elements (offsets past 32 bits)
+    on the pipelined kernels' shapes: every offset is formed in 64 bits."""
+    g = torch.Generator().manual_seed(153 + m)
+    T = 500
+    a = (0.9 * torch.eye(16) + 0.01 * torch.randn(2, T, 16, 16, generator=g)).to(dtype)
+    b = torch.randn(2, T, 16, m, generator=g).to(dtype)
+    base = torch.empty(2 ** 31 + T * 256 + 64, dtype=dtype, device=DEV)
+    av = base.as_strided((2, T, 16, 16), (2 ** 31, 256, 16, 1))
+    av.copy_(a.to(DEV))
+    ref = oracle.matrix_scan(a.float().numpy(), b.float().numpy(), axis=1, reverse=reverse)
+    got = sx.matrix_scan(av, b.to(DEV), axis=1, reverse=reverse)
+    assert_matrix_close(got, ref, MS_TOL_F32 if dtype == torch.float32 else MS_TOL_BF16)
+    del base, av
+    torch.cuda.empty_cache()
+
+
 def test_matrix_broadcast_leading_dims_and_negative_axis():
     g = torch.Generator().manual_seed(151)
     a = 0.9 * torch.eye(5) + 0.05 * torch.randn(1, 40, 5, 5, generator=g)  # shared across the batch
