@@ -499,31 +499,26 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
     return rev ? T - 1 - qc : qc;
   };
   const float c_once = CS ? ld_elem(cl) : 0.0f;
-  float cx[S], cc[CS ? 1 : S];
+  // this wave's trips of the slab starting at position q_slab, into xs (and cs)
+  auto load = [&](int64_t q_slab, float (&xs)[S], float (&cs)[CS ? 1 : S]) {
 #pragma unroll
-  for (int k = 0; k < S; ++k) {
-    const int64_t q = int64_t(wave) * S + k;
-    const int64_t t = time_of(q);
-    cx[k] = q < T ? ld_elem(xl + t * sx) : M::x_pad();
-    if constexpr (!CS) {
-      const float cv = ld_elem(cl + t * sc);
-      cc[k] = q < T ? cv : M::s_pad();
+    for (int k = 0; k < S; ++k) {
+      const int64_t q = q_slab + int64_t(wave) * S + k;
+      const int64_t t = time_of(q);
+      const float xv = ld_elem(xl + t * sx);
+      xs[k] = q < T ? xv : M::x_pad();
+      if constexpr (!CS) {
+        const float cv = ld_elem(cl + t * sc);
+        cs[k] = q < T ? cv : M::s_pad();
+      }
     }
-  }
+  };
+  float cx[S], cc[CS ? 1 : S];
+  load(0, cx, cc);
   for (int64_t sl = 0; sl < nslabs; ++sl) {
     const int64_t qw = sl * kSlab + int64_t(wave) * S;  // this wave's first position in the slab
     float nx[S], nc[CS ? 1 : S];
-#pragma unroll
-    for (int k = 0; k < S; ++k) {  // next slab, in flight during this one
-      const int64_t q = qw + kSlab + k;
-      const int64_t t = time_of(q);
-      const float xv = ld_elem(xl + t * sx);
-      nx[k] = q < T ? xv : M::x_pad();
-      if constexpr (!CS) {
-        const float cv = ld_elem(cl + t * sc);
-        nc[k] = q < T ? cv : M::s_pad();
-      }
-    }
+    load((sl + 1) * kSlab, nx, nc);  // the next slab, in flight during this one
     // this slab's c at trip k
     auto c_of = [&](int k) -> float {
       if constexpr (CS) return qw + k < T ? c_once : M::s_pad();
@@ -1124,8 +1119,10 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
       else
         hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     } else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips) {
-      // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries
-      hipLaunchKernelGGL((es_slab_kernel<SX_BODY_MAX_PLUS, 16, 16>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
+      // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries;
+      // slabs of 8 trips a wave (measured on [64,4096,256]: 147.0 us against 149.7 with 16 trips, 147.5 with
+      // 6, 155.4 with 4, 149.6 with 12, and 149.1 with 8 trips and two slabs in flight)
+      hipLaunchKernelGGL((es_slab_kernel<SX_BODY_MAX_PLUS, 16, 8>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
     } else if (lane_offsets_fit32(p)) {
       hipLaunchKernelGGL((es_lane_kernel<SX_BODY_MAX_PLUS, float, float, true>), dim3(unsigned(blocks)), dim3(64), 0,
                          stream, p);
@@ -1142,8 +1139,8 @@ void launch_linear(const EsParams& p, int64_t blocks, hipStream_t stream) {
   if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips && p.t_stride[ES_S] == 0)  // a constant in time
     hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 32, TI, TO, true>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
                        stream, p);
-  else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)
-    hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 16, TI, TO>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
+  else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips)  // 8 trips a wave, as max-plus (147.7 against 150.0 us)
+    hipLaunchKernelGGL((es_slab_kernel<kBodyLinear, 16, 8, TI, TO>), dim3(unsigned(blocks)), dim3(16 * 64), 0,
                        stream, p);
   else if (lane_offsets_fit32(p))
     hipLaunchKernelGGL((es_lane_kernel<kBodyLinear, TI, TO, true>), dim3(unsigned(blocks)), dim3(64), 0, stream, p);
