@@ -499,16 +499,21 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
     return rev ? T - 1 - qc : qc;
   };
   const float c_once = CS ? ld_elem(cl) : 0.0f;
-  // this wave's trips of the slab starting at position q_slab, into xs (and cs)
+  // this wave's trips of the slab starting at position q_slab, into xs (and cs): every x, then every c
+  // (grouped by tensor, the requests reach memory in fewer row runs: 143.4 against 146.4 us on
+  // max-plus [64,4096,256], 143.2 against 147.0 on linear-scan; interleaved per trip before)
   auto load = [&](int64_t q_slab, float (&xs)[S], float (&cs)[CS ? 1 : S]) {
 #pragma unroll
     for (int k = 0; k < S; ++k) {
       const int64_t q = q_slab + int64_t(wave) * S + k;
-      const int64_t t = time_of(q);
-      const float xv = ld_elem(xl + t * sx);
+      const float xv = ld_elem(xl + time_of(q) * sx);
       xs[k] = q < T ? xv : M::x_pad();
-      if constexpr (!CS) {
-        const float cv = ld_elem(cl + t * sc);
+    }
+    if constexpr (!CS) {
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const int64_t q = q_slab + int64_t(wave) * S + k;
+        const float cv = ld_elem(cl + time_of(q) * sc);
         cs[k] = q < T ? cv : M::s_pad();
       }
     }
