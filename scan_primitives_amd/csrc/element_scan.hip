@@ -107,20 +107,18 @@ __global__ __launch_bounds__(64) void es_lane_kernel(const EsParams p) {
   float cx[U], cs[U];
   if (full > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cx[u] = ld_elem(xp + u * dx);
-      cs[u] = ld_elem(sp + u * ds);
-    }
+    for (int u = 0; u < U; ++u) cx[u] = ld_elem(xp + u * dx);  // grouped by tensor, as the slab kernels load
+#pragma unroll
+    for (int u = 0; u < U; ++u) cs[u] = ld_elem(sp + u * ds);
   }
   for (int64_t t = 0; t < full; t += U) {
     float nx[U], ns[U];
     const bool more = t + U < full;
     if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        nx[u] = ld_elem(xp + (U + u) * dx);
-        ns[u] = ld_elem(sp + (U + u) * ds);
-      }
+      for (int u = 0; u < U; ++u) nx[u] = ld_elem(xp + (U + u) * dx);
+#pragma unroll
+      for (int u = 0; u < U; ++u) ns[u] = ld_elem(sp + (U + u) * ds);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
