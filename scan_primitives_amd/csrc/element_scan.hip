@@ -498,8 +498,9 @@ __global__ __launch_bounds__(NW * 64) void es_slab_kernel(const EsParams p) {
   };
   const float c_once = CS ? ld_elem(cl) : 0.0f;
   // this wave's trips of the slab starting at position q_slab, into xs (and cs): every x, then every c
-  // (grouped by tensor, the requests reach memory in fewer row runs: 143.4 against 146.4 us on
-  // max-plus [64,4096,256], 143.2 against 147.0 on linear-scan; interleaved per trip before)
+  // (grouped by tensor, the requests reach memory in fewer row runs: on one box 143.4 against 146.4 us on
+  // max-plus [64,4096,256] and 143.2 against 147.0 on linear-scan, interleaved per trip before; on another,
+  // this and the 8-trip slabs together took max-plus from 149.2 to 148.7 us)
   auto load = [&](int64_t q_slab, float (&xs)[S], float (&cs)[CS ? 1 : S]) {
 #pragma unroll
     for (int k = 0; k < S; ++k) {
@@ -1123,8 +1124,9 @@ hipError_t launch_element_scan(sx_body body, const EsParams& p, hipStream_t stre
         hipLaunchKernelGGL(es_lane_kernel<SX_BODY_TANH_AFFINE>, dim3(unsigned(blocks)), dim3(64), 0, stream, p);
     } else if (p.num_lanes >= kSlabMinLanes && p.T >= kSlabMinTrips) {
       // enough 64-lane groups to give every CU a workgroup, and a long enough axis to pay for the summaries;
-      // slabs of 8 trips a wave (measured on [64,4096,256]: 147.0 us against 149.7 with 16 trips, 147.5 with
-      // 6, 155.4 with 4, 149.6 with 12, and 149.1 with 8 trips and two slabs in flight)
+      // slabs of 8 trips a wave (measured on [64,4096,256], one box: 147.0 us against 149.7 with 16 trips,
+      // 147.5 with 6, 155.4 with 4, 149.6 with 12, and 149.1 with 8 trips and two slabs in flight; the gain
+      // differs from box to box, see the load order below)
       hipLaunchKernelGGL((es_slab_kernel<SX_BODY_MAX_PLUS, 16, 8>), dim3(unsigned(blocks)), dim3(16 * 64), 0, stream, p);
     } else if (lane_offsets_fit32(p)) {
       hipLaunchKernelGGL((es_lane_kernel<SX_BODY_MAX_PLUS, float, float, true>), dim3(unsigned(blocks)), dim3(64), 0,
