@@ -1229,7 +1229,9 @@ hipError_t launch_element_scan_backward(sx_body body, const EsVjpParams& v, hipS
   auto launch = [&](auto bodyc, auto idxc) {
     constexpr int B = decltype(bodyc)::value;
     constexpr bool I32 = decltype(idxc)::value;
-    if (slab)
+    if (slab && p.T <= 64)  // one slab of 4 trips a wave: every wave has trips (tanh-affine [4,64,32]: 5.5 against 7.0 us)
+      hipLaunchKernelGGL((es_vjp_slab_kernel<B, 16, 4, I32>), dim3(unsigned(blocks)), dim3(1024), 0, stream, v);
+    else if (slab)
       hipLaunchKernelGGL((es_vjp_slab_kernel<B, 16, 8, I32>), dim3(unsigned(blocks)), dim3(1024), 0, stream, v);
     else
       hipLaunchKernelGGL((es_vjp_lane_kernel<B, I32>), dim3(unsigned(blocks)), dim3(64), 0, stream, v);
